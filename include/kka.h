@@ -1,0 +1,267 @@
+/*
+ * kka.h -- Key-Key Semantic Affinity block selection for paged KV caches,
+ * C ABI of libkka.so (AMD Instinct MI355X, gfx950).
+ *
+ * The method is the one described on the page "Key-Key Semantic Affinity:
+ * Key vectors replace attention scores for KV-cache importance"
+ * (10100.com): every KV-cache block is summarised once by the mean of its
+ * keys (section 2.2 step 1, section 5.2 step 2); at every decode step the
+ * keys of the last few tokens are pooled the same way into an anchor
+ * (section 2.2 step 2, section 5.2 step 1); blocks are scored by the
+ * cosine of anchor and block vector mapped to [0, 1] (section 2.2 step 3,
+ * section 3.2) and the top-K are kept (section 5.2 step 4), optionally
+ * through the Grid -> Chunk -> Page hierarchy scored in one pass with
+ * parent masks (section 5.1).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers named "device" are HIP device pointers; structs and scalars
+ *    are read on the host during the call and may be freed afterwards.
+ *  - Every buffer is caller-owned.  The library never allocates, frees or
+ *    keeps device memory; scratch space is the caller's `workspace`.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only
+ *    enqueue work and return; nothing is synchronised except by
+ *    kka_device_error().
+ *  - Arguments are validated on the host before anything is enqueued.  A
+ *    non-zero kka_status means nothing was enqueued and no output written.
+ *    Errors that depend on device-resident values (block-table entries,
+ *    sequence lengths, page counts) cannot be seen on the host: kernels
+ *    skip the offending item, write zeros for it where an output exists,
+ *    and raise a bit in a per-device flag word read by kka_device_error().
+ *  - Results are deterministic: no floating-point atomics; the same inputs
+ *    give the same bits, wherever blocks sit in the physical pool.
+ *  - bf16 keys are widened exactly and accumulated in fp32.
+ */
+#ifndef KKA_H_
+#define KKA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define KKA_API __attribute__((visibility("default")))
+#else
+#define KKA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kka_status {
+  KKA_OK = 0,
+  KKA_ERR_NULL = 1,      /* a required pointer is NULL                          */
+  KKA_ERR_SHAPE = 2,     /* a size, count or mode is outside its documented range */
+  KKA_ERR_ALIGN = 3,     /* a pointer or stride breaks its alignment rule        */
+  KKA_ERR_WORKSPACE = 4, /* workspace NULL or smaller than the *_workspace() size */
+  KKA_ERR_DEVICE = 5     /* the HIP runtime refused a launch                      */
+} kka_status;
+
+/* Bits of the device flag word returned by kka_device_error(). */
+#define KKA_DEVERR_BLOCK_TABLE 1u /* a block-table entry outside [0, num_phys_blocks)      */
+#define KKA_DEVERR_SEQ_LEN 2u     /* a logical block holds no valid token, or a window     */
+                                  /* reaches past the sequence's blocks                    */
+#define KKA_DEVERR_ROW 4u         /* a block's index in its sequence >= vb_seq_stride      */
+#define KKA_DEVERR_PAGES 8u       /* n_pages[s] < 0 or > max_pages                         */
+#define KKA_DEVERR_OFFSETS 16u    /* block_offsets not nondecreasing / total mismatch      */
+
+/*
+ * Paged key pool.  Element (layer l, physical block p, token slot t,
+ * KV head h, dimension d) is k[l*stride_layer + p*stride_block +
+ * t*stride_token + h*stride_head + d]: one head_dim row is contiguous.
+ * A single-tensor [L][P][B][H][D] pool has strides (P*B*H*D, B*H*D, H*D, D);
+ * per-layer [P][B][H][D] caches placed at a fixed distance fit too.
+ * Rules: k 16-byte aligned; head_dim a multiple of 8 in [8, 1024];
+ * num_kv_heads * head_dim / 8 <= 1024; num_layers * num_kv_heads <= 4096;
+ * strides >= 0 and multiples of 8 elements.
+ */
+typedef struct kka_kpool {
+  const uint16_t* k; /* device, bf16 bit patterns */
+  int32_t num_layers;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int64_t num_phys_blocks;
+  int64_t stride_layer;
+  int64_t stride_block;
+  int64_t stride_token;
+  int64_t stride_head;
+} kka_kpool;
+
+/*
+ * A batch of sequences in CSR form.  Sequence s has seq_len[s] tokens in
+ * logical blocks block_offsets[s] .. block_offsets[s+1]-1 (global logical
+ * block ids), token tau in logical block tau / block_size, slot
+ * tau % block_size; logical block b lives in physical block block_table[b].
+ * A sequence normally owns ceil(seq_len / block_size) blocks; extra blocks
+ * hold no valid token and raise KKA_DEVERR_SEQ_LEN when pooled.
+ * total_blocks is the host's copy of block_offsets[num_seqs].
+ */
+typedef struct kka_seqs {
+  int32_t num_seqs;
+  int32_t total_blocks;
+  const int32_t* seq_len;       /* device [num_seqs]       */
+  const int32_t* block_offsets; /* device [num_seqs + 1]   */
+  const int32_t* block_table;   /* device [total_blocks]   */
+} kka_seqs;
+
+typedef enum kka_weight_mode {
+  KKA_WEIGHT_UNIFORM = 0,  /* plain mean over tokens, layers and heads                */
+  KKA_WEIGHT_VARIANCE = 1, /* compute per-head variance weights, write them, use them */
+  KKA_WEIGHT_GIVEN = 2     /* read frozen per-head weights                            */
+} kka_weight_mode;
+
+/*
+ * kka_pool_blocks -- block key representation v_b (page section 2.2 step 1,
+ * section 3.3, section 5.2 step 2).
+ *
+ * For each selected logical block b of sequence s, with n_b = min(B,
+ * seq_len[s] - i*B) valid tokens (i = b - block_offsets[s]):
+ *   UNIFORM:  v_b = 1/(n_b*L*H) * sum_{l,h,t<n_b} K[l][p][t][h][:]
+ *   GIVEN / VARIANCE:
+ *             v_b = sum_{l,h} w[s][l*H+h] * (1/n_b) sum_{t<n_b} K[l][p][t][h][:]
+ * where p = block_table[b].  In VARIANCE mode the weights are first
+ * computed from all seq_len[s] tokens of each sequence: w[s][l*H+h] is the
+ * temporal variance of that (layer, KV head)'s keys -- per-dimension
+ * population variance over the tokens, averaged over head_dim --
+ * normalised to sum 1 over the L*H heads (uniform when all are 0), rounded
+ * to fp32 and written to head_weight.  (The page names variance weighting
+ * but prints no formula; this is the reading used here.)
+ *
+ * blocks      device [num_blocks] global logical block ids to pool, or NULL
+ *             for all total_blocks blocks (num_blocks is then ignored).
+ *             VARIANCE mode requires NULL.
+ * head_weight device [num_seqs][L*H] fp32: written in VARIANCE mode, read in
+ *             GIVEN mode, ignored (may be NULL) in UNIFORM mode.
+ * vb_out      device fp32, 16-byte aligned; v_b of block b goes to row
+ *             s*vb_seq_stride + i (vb_seq_stride > 0: one row range per
+ *             sequence, e.g. the page rows of a level buffer) or to row b
+ *             (vb_seq_stride == 0); a row is head_dim floats.
+ * workspace   device, 16-byte aligned, >= kka_pool_blocks_workspace() bytes
+ *             (may be NULL when that size is 0).
+ */
+KKA_API kka_status kka_pool_blocks(const kka_kpool* kp, const kka_seqs* seqs, const int32_t* blocks, int32_t num_blocks,
+                           int32_t mode, float* head_weight, float* vb_out, int64_t vb_seq_stride, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Workspace bytes kka_pool_blocks needs for these shapes (0 when none). */
+KKA_API size_t kka_pool_blocks_workspace(const kka_kpool* kp, const kka_seqs* seqs, const int32_t* blocks,
+                                 int32_t num_blocks, int32_t mode);
+
+/*
+ * kka_pool_anchor -- query anchor v_anchor (page section 2.2 step 2,
+ * section 5.2 step 1): the same pooling over the last W_eff = min(window,
+ * seq_len[s]) tokens of each sequence, which may span several blocks.
+ * head_weight device [num_seqs][L*H] or NULL for uniform pooling.
+ * anchor_out  device [num_seqs][head_dim] fp32, 16-byte aligned; an empty
+ *             window gives the zero vector.
+ * workspace   >= kka_pool_anchor_workspace() bytes.
+ * Rules: window >= 0.
+ */
+KKA_API kka_status kka_pool_anchor(const kka_kpool* kp, const kka_seqs* seqs, int32_t window, const float* head_weight,
+                           float* anchor_out, void* workspace, size_t workspace_bytes, void* stream);
+
+KKA_API size_t kka_pool_anchor_workspace(const kka_kpool* kp, const kka_seqs* seqs, int32_t window);
+
+/*
+ * Level buffer geometry (page section 5.1).  Each sequence owns
+ * rows_per_seq = kka_level_rows() consecutive rows of head_dim fp32:
+ *   pages  rows [0, n_p)                   -- the block vectors v_b
+ *   chunks rows [max_pages, max_pages + n_c)
+ *   grids  rows [max_pages + C, max_pages + C + n_g)
+ * with C = ceil(max_pages / pages_per_chunk), n_c = ceil(n_p /
+ * pages_per_chunk), n_g = ceil(n_c / chunks_per_grid) and n_p the
+ * sequence's page count.  Flat layouts (hierarchical == 0) hold pages only.
+ * Sequence s starts at row s * rows_per_seq.
+ * Rules: num_seqs >= 0; 0 <= max_pages; head_dim a multiple of 8 in
+ * [8, 1024]; hierarchical layouts need pages_per_chunk >= 1,
+ * chunks_per_grid >= 1, ceil(max_pages / pages_per_chunk) <= 65536 and
+ * chunks_per_grid * head_dim <= 16384.
+ */
+typedef struct kka_level_layout {
+  int32_t num_seqs;
+  int32_t max_pages;
+  int32_t head_dim;
+  int32_t hierarchical;
+  int32_t pages_per_chunk;
+  int32_t chunks_per_grid;
+} kka_level_layout;
+
+/* Rows per sequence of a level buffer, or -1 if the layout breaks a rule. */
+KKA_API int64_t kka_level_rows(const kka_level_layout* lay);
+
+/*
+ * kka_build_levels -- chunk and grid vectors (page section 5.1: a grid's
+ * vector is the mean of its chunk vectors; a chunk's is, by the same rule,
+ * the mean of its page vectors).  Only the present children of a ragged
+ * last chunk or grid are averaged.
+ * level_buf        device, 16-byte aligned, [num_seqs][rows_per_seq][head_dim]
+ * n_pages          device [num_seqs] pages per sequence (0..max_pages)
+ * first_dirty_page device [num_seqs] or NULL: only chunks and grids that
+ *                  can contain pages >= first_dirty_page[s] are rebuilt
+ *                  (the whole grid holding that page and every later one).
+ * A flat layout is accepted and does nothing.
+ */
+KKA_API kka_status kka_build_levels(const kka_level_layout* lay, float* level_buf, const int32_t* n_pages,
+                            const int32_t* first_dirty_page, void* stream);
+
+/* How many rows to keep at each level; each in [0, 1024]. */
+typedef struct kka_select {
+  int32_t k_grid;
+  int32_t k_chunk;
+  int32_t k_page;
+} kka_select;
+
+/*
+ * kka_score_topk -- affinity of every row and top-K selection (page
+ * section 2.2 step 3, section 5.1, section 5.2 steps 3-4).
+ * Every present row r of sequence s (pages, chunks and grids alike, in one
+ * pass) gets aff = clamp((1 + cos(r, anchor_s)) / 2, 0, 1), with cos = 0
+ * when either vector has zero norm and -0 written as +0.  (The page's
+ * affinity formula did not survive; this is the reading used here.)
+ * Flat layout: the result is the top k_page pages by (aff desc, index asc).
+ * Hierarchical layout: the top k_grid grids are kept; a chunk scores its
+ * affinity if its grid was kept and +0 otherwise; the top k_chunk chunks
+ * are kept; a page scores its affinity if its chunk was kept and +0
+ * otherwise; the result is the top k_page pages by (score desc, index asc).
+ * At each level min(k, rows present) rows are kept.  Selection compares
+ * exactly the fp32 values the affinity pass produced.
+ *
+ * anchors        device [num_seqs][head_dim] fp32, 16-byte aligned
+ * affinity_out   device [num_seqs][rows_per_seq] fp32 or NULL; rows that are
+ *                not present are left untouched
+ * page_idx_out   device [num_seqs][k_page] int32 page index in its sequence,
+ *                best first; slots past the kept count hold -1
+ * page_score_out device [num_seqs][k_page] fp32 masked score, or NULL; slots
+ *                past the kept count hold 0
+ * n_selected_out device [num_seqs] int32 kept count, or NULL
+ * workspace      device, 16-byte aligned, >= kka_score_topk_workspace()
+ *                bytes, ZERO-FILLED before its first use; every completed
+ *                call leaves it zero-filled again where that matters, so it
+ *                can be reused by later calls ordered on one stream.  Calls
+ *                that run concurrently must not share a workspace.
+ */
+KKA_API kka_status kka_score_topk(const kka_level_layout* lay, const float* level_buf, const int32_t* n_pages,
+                          const float* anchors, const kka_select* sel, float* affinity_out, int32_t* page_idx_out,
+                          float* page_score_out, int32_t* n_selected_out, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+KKA_API size_t kka_score_topk_workspace(const kka_level_layout* lay, const kka_select* sel, int32_t with_affinity_out);
+
+/*
+ * kka_device_error -- waits for `stream`, returns the KKA_DEVERR_* bits
+ * raised on the current device since the last call, and clears them.
+ * Returns -1 if the wait or the read failed (HIP error).
+ */
+KKA_API int32_t kka_device_error(void* stream);
+
+/* Static description of a kka_status value. */
+KKA_API const char* kka_status_string(kka_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+KKA_API int32_t kka_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KKA_H_ */

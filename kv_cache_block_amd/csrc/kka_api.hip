@@ -1,0 +1,357 @@
+// C ABI of libkka: argument validation, workspace sizing, launch set-up.
+// Every check here runs on the host before anything is enqueued, so a
+// rejected call has no effect on the device.
+#include <mutex>
+
+#include "kka_internal.h"
+
+namespace kka {
+
+// Per-device flag word for errors that only device-resident data reveals.
+__device__ uint32_t g_device_error;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_err_mu;
+uint32_t* g_err_ptr[kMaxDevices] = {};
+
+uint32_t* device_error_word() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_err_mu);
+  if (!g_err_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_device_error)) != hipSuccess) return nullptr;
+    g_err_ptr[dev] = static_cast<uint32_t*>(p);
+  }
+  return g_err_ptr[dev];
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+kka_status check_kpool(const kka_kpool* kp) {
+  if (!kp || !kp->k) return KKA_ERR_NULL;
+  if (kp->num_layers < 1 || kp->num_kv_heads < 1 || kp->block_size < 1 || kp->num_phys_blocks < 1)
+    return KKA_ERR_SHAPE;
+  const int32_t D = kp->head_dim;
+  if (D < 8 || D > 1024 || D % 8 != 0) return KKA_ERR_SHAPE;
+  if ((int64_t)kp->num_kv_heads * (D / 8) > kMaxPoolThreads) return KKA_ERR_SHAPE;
+  if ((int64_t)kp->num_layers * kp->num_kv_heads > 4096) return KKA_ERR_SHAPE;
+  if (kp->stride_layer < 0 || kp->stride_block < 0 || kp->stride_token < 0 || kp->stride_head < 0)
+    return KKA_ERR_SHAPE;
+  if (kp->stride_layer % 8 || kp->stride_block % 8 || kp->stride_token % 8 || kp->stride_head % 8)
+    return KKA_ERR_ALIGN;
+  if (!aligned16(kp->k)) return KKA_ERR_ALIGN;
+  return KKA_OK;
+}
+
+kka_status check_seqs(const kka_seqs* sq) {
+  if (!sq) return KKA_ERR_NULL;
+  if (sq->num_seqs < 0 || sq->total_blocks < 0) return KKA_ERR_SHAPE;
+  if (sq->num_seqs > 0 && (!sq->seq_len || !sq->block_offsets)) return KKA_ERR_NULL;
+  if (sq->total_blocks > 0 && !sq->block_table) return KKA_ERR_NULL;
+  if (sq->num_seqs == 0 && sq->total_blocks > 0) return KKA_ERR_SHAPE;
+  return KKA_OK;
+}
+
+// Byte layout of the pooling workspace.
+struct PoolWs {
+  size_t partial = 0, q = 0, var = 0, total = 0;
+};
+
+PoolWs pool_ws(const kka_kpool* kp, const kka_seqs* sq, int64_t items, int32_t mode) {
+  PoolWs w;
+  const size_t D = (size_t)kp->head_dim, LH = (size_t)kp->num_layers * kp->num_kv_heads;
+  if (mode == KKA_WEIGHT_VARIANCE) {
+    const size_t tb = (size_t)sq->total_blocks;
+    w.partial = align256(tb * LH * D * sizeof(float));
+    w.q = align256(tb * LH * sizeof(float));
+    w.var = align256((size_t)sq->num_seqs * LH * sizeof(double));
+  } else {
+    const LayerSplit ls = layer_split(items, kp->num_layers);
+    if (ls.n_split > 1) w.partial = align256((size_t)items * ls.n_split * D * sizeof(float));
+  }
+  w.total = w.partial + w.q + w.var;
+  return w;
+}
+
+void fill_pool_args(PoolArgs& a, const kka_kpool* kp, const kka_seqs* sq) {
+  a.k = kp->k;
+  a.sL = kp->stride_layer;
+  a.sB = kp->stride_block;
+  a.sT = kp->stride_token;
+  a.sH = kp->stride_head;
+  a.L = kp->num_layers;
+  a.H = kp->num_kv_heads;
+  a.D = kp->head_dim;
+  a.B = kp->block_size;
+  a.P = kp->num_phys_blocks;
+  a.S = sq->num_seqs;
+  a.total_blocks = sq->total_blocks;
+  a.seq_len = sq->seq_len;
+  a.offs = sq->block_offsets;
+  a.table = sq->block_table;
+  a.ps = pool_shape(a.H, a.D);
+}
+
+struct LevelGeom {
+  int64_t rows;
+  int32_t c_cap, g_cap;
+};
+
+bool level_geom(const kka_level_layout* lay, LevelGeom& g) {
+  if (!lay) return false;
+  if (lay->num_seqs < 0 || lay->max_pages < 0) return false;
+  const int32_t D = lay->head_dim;
+  if (D < 8 || D > 1024 || D % 8 != 0) return false;
+  g.c_cap = g.g_cap = 0;
+  if (lay->hierarchical) {
+    if (lay->pages_per_chunk < 1 || lay->chunks_per_grid < 1) return false;
+    const int64_t c = ((int64_t)lay->max_pages + lay->pages_per_chunk - 1) / lay->pages_per_chunk;
+    if (c > kMaxParents) return false;
+    if ((int64_t)lay->chunks_per_grid * D > kMaxGridFloats) return false;
+    g.c_cap = (int32_t)c;
+    g.g_cap = (int32_t)((c + lay->chunks_per_grid - 1) / lay->chunks_per_grid);
+  }
+  g.rows = (int64_t)lay->max_pages + g.c_cap + g.g_cap;
+  return true;
+}
+
+inline kka_status launched(hipError_t e) { return e == hipSuccess ? KKA_OK : KKA_ERR_DEVICE; }
+
+}  // namespace
+}  // namespace kka
+
+using namespace kka;
+
+extern "C" {
+
+size_t kka_pool_blocks_workspace(const kka_kpool* kp, const kka_seqs* seqs, const int32_t* blocks,
+                                 int32_t num_blocks, int32_t mode) {
+  if (check_kpool(kp) != KKA_OK || check_seqs(seqs) != KKA_OK) return 0;
+  const int64_t items = blocks ? (num_blocks > 0 ? num_blocks : 0) : seqs->total_blocks;
+  return pool_ws(kp, seqs, items, mode).total;
+}
+
+kka_status kka_pool_blocks(const kka_kpool* kp, const kka_seqs* seqs, const int32_t* blocks, int32_t num_blocks,
+                           int32_t mode, float* head_weight, float* vb_out, int64_t vb_seq_stride, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  kka_status st = check_kpool(kp);
+  if (st != KKA_OK) return st;
+  if ((st = check_seqs(seqs)) != KKA_OK) return st;
+  if (mode != KKA_WEIGHT_UNIFORM && mode != KKA_WEIGHT_VARIANCE && mode != KKA_WEIGHT_GIVEN) return KKA_ERR_SHAPE;
+  if (blocks && num_blocks < 0) return KKA_ERR_SHAPE;
+  if (blocks && num_blocks > 0 && seqs->total_blocks == 0) return KKA_ERR_SHAPE;
+  if (mode == KKA_WEIGHT_VARIANCE && blocks) return KKA_ERR_SHAPE;
+  if (mode != KKA_WEIGHT_UNIFORM && seqs->num_seqs > 0 && !head_weight) return KKA_ERR_NULL;
+  if (vb_seq_stride < 0) return KKA_ERR_SHAPE;
+  const int64_t items = blocks ? num_blocks : seqs->total_blocks;
+  if (items > 0 && !vb_out) return KKA_ERR_NULL;
+  if (vb_out && !aligned16(vb_out)) return KKA_ERR_ALIGN;
+  const PoolWs ws = pool_ws(kp, seqs, items, mode);
+  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return KKA_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return KKA_ERR_ALIGN;
+  uint32_t* err = device_error_word();
+  if (!err) return KKA_ERR_DEVICE;
+  (void)hipGetLastError();
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  PoolArgs a = {};
+  fill_pool_args(a, kp, seqs);
+  a.subset = blocks;
+  a.n_items = (int32_t)items;
+  a.out = vb_out;
+  a.vb_stride = vb_seq_stride;
+  a.err = err;
+  char* wsb = static_cast<char*>(workspace);
+  if (mode == KKA_WEIGHT_VARIANCE) {
+    if (seqs->num_seqs == 0) return KKA_OK;
+    const LayerSplit ls = layer_split(items, a.L);
+    a.n_split = ls.n_split;
+    a.lps = ls.lps;
+    a.partial = reinterpret_cast<float*>(wsb);
+    a.stats_q = reinterpret_cast<float*>(wsb + ws.partial);
+    hipError_t e = launch_pool_stats(a, s);
+    if (e != hipSuccess) return KKA_ERR_DEVICE;
+    WeightArgs w = {};
+    w.s1 = a.partial;
+    w.q = a.stats_q;
+    w.var = reinterpret_cast<double*>(wsb + ws.partial + ws.q);
+    w.head_weight = head_weight;
+    w.seq_len = seqs->seq_len;
+    w.offs = seqs->block_offsets;
+    w.S = seqs->num_seqs;
+    w.LH = a.L * a.H;
+    w.D = a.D;
+    w.B = a.B;
+    w.total_blocks = seqs->total_blocks;
+    w.err = err;
+    if ((e = launch_head_weights(w, s)) != hipSuccess) return KKA_ERR_DEVICE;
+    return launched(launch_pool_combine(a, head_weight, s));
+  }
+  if (items == 0) return KKA_OK;
+  const LayerSplit ls = layer_split(items, a.L);
+  a.n_split = ls.n_split;
+  a.lps = ls.lps;
+  a.partial = ls.n_split > 1 ? reinterpret_cast<float*>(wsb) : nullptr;
+  a.weights = mode == KKA_WEIGHT_GIVEN ? head_weight : nullptr;
+  return launched(launch_pool(a, mode, s));
+}
+
+size_t kka_pool_anchor_workspace(const kka_kpool* kp, const kka_seqs* seqs, int32_t window) {
+  (void)window;
+  if (check_kpool(kp) != KKA_OK || check_seqs(seqs) != KKA_OK) return 0;
+  const LayerSplit ls = layer_split(seqs->num_seqs, kp->num_layers);
+  return ls.n_split > 1 ? align256((size_t)seqs->num_seqs * ls.n_split * kp->head_dim * sizeof(float)) : 0;
+}
+
+kka_status kka_pool_anchor(const kka_kpool* kp, const kka_seqs* seqs, int32_t window, const float* head_weight,
+                           float* anchor_out, void* workspace, size_t workspace_bytes, void* stream) {
+  kka_status st = check_kpool(kp);
+  if (st != KKA_OK) return st;
+  if ((st = check_seqs(seqs)) != KKA_OK) return st;
+  if (window < 0) return KKA_ERR_SHAPE;
+  if (seqs->num_seqs > 0 && !anchor_out) return KKA_ERR_NULL;
+  if (anchor_out && !aligned16(anchor_out)) return KKA_ERR_ALIGN;
+  const size_t need = kka_pool_anchor_workspace(kp, seqs, window);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return KKA_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return KKA_ERR_ALIGN;
+  if (seqs->num_seqs == 0) return KKA_OK;
+  uint32_t* err = device_error_word();
+  if (!err) return KKA_ERR_DEVICE;
+  (void)hipGetLastError();
+  PoolArgs a = {};
+  fill_pool_args(a, kp, seqs);
+  const LayerSplit ls = layer_split(seqs->num_seqs, a.L);
+  a.n_split = ls.n_split;
+  a.lps = ls.lps;
+  a.n_items = seqs->num_seqs;
+  a.weights = head_weight;
+  a.out = anchor_out;
+  a.partial = ls.n_split > 1 ? static_cast<float*>(workspace) : nullptr;
+  a.window = window;
+  a.err = err;
+  return launched(launch_anchor(a, static_cast<hipStream_t>(stream)));
+}
+
+int64_t kka_level_rows(const kka_level_layout* lay) {
+  LevelGeom g;
+  if (!level_geom(lay, g)) return -1;
+  return g.rows;
+}
+
+kka_status kka_build_levels(const kka_level_layout* lay, float* level_buf, const int32_t* n_pages,
+                            const int32_t* first_dirty_page, void* stream) {
+  if (!lay) return KKA_ERR_NULL;
+  LevelGeom g;
+  if (!level_geom(lay, g)) return KKA_ERR_SHAPE;
+  if (!lay->hierarchical || lay->num_seqs == 0 || g.g_cap == 0) return KKA_OK;
+  if (!level_buf || !n_pages) return KKA_ERR_NULL;
+  if (!aligned16(level_buf)) return KKA_ERR_ALIGN;
+  uint32_t* err = device_error_word();
+  if (!err) return KKA_ERR_DEVICE;
+  (void)hipGetLastError();
+  LevelArgs a = {};
+  a.lvl = level_buf;
+  a.rows_per_seq = g.rows;
+  a.S = lay->num_seqs;
+  a.max_pages = lay->max_pages;
+  a.D = lay->head_dim;
+  a.ppc = lay->pages_per_chunk;
+  a.cpg = lay->chunks_per_grid;
+  a.c_cap = g.c_cap;
+  a.g_cap = g.g_cap;
+  a.n_pages = n_pages;
+  a.first_dirty = first_dirty_page;
+  a.err = err;
+  return launched(launch_levels(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t kka_score_topk_workspace(const kka_level_layout* lay, const kka_select* sel, int32_t with_affinity_out) {
+  (void)sel;
+  LevelGeom g;
+  if (!level_geom(lay, g)) return 0;
+  size_t n = align256((size_t)lay->num_seqs * sizeof(uint32_t));
+  if (!with_affinity_out) n += align256((size_t)lay->num_seqs * (size_t)g.rows * sizeof(float));
+  return n;
+}
+
+kka_status kka_score_topk(const kka_level_layout* lay, const float* level_buf, const int32_t* n_pages,
+                          const float* anchors, const kka_select* sel, float* affinity_out, int32_t* page_idx_out,
+                          float* page_score_out, int32_t* n_selected_out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (!lay || !sel) return KKA_ERR_NULL;
+  LevelGeom g;
+  if (!level_geom(lay, g)) return KKA_ERR_SHAPE;
+  if (sel->k_page < 0 || sel->k_page > kMaxK) return KKA_ERR_SHAPE;
+  if (lay->hierarchical &&
+      (sel->k_grid < 0 || sel->k_grid > kMaxK || sel->k_chunk < 0 || sel->k_chunk > kMaxK))
+    return KKA_ERR_SHAPE;
+  if (lay->num_seqs == 0) return KKA_OK;
+  if (!level_buf || !n_pages || !anchors) return KKA_ERR_NULL;
+  if (sel->k_page > 0 && !page_idx_out) return KKA_ERR_NULL;
+  if (!aligned16(level_buf) || !aligned16(anchors)) return KKA_ERR_ALIGN;
+  const size_t need = kka_score_topk_workspace(lay, sel, affinity_out != nullptr);
+  if (!workspace || workspace_bytes < need) return KKA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KKA_ERR_ALIGN;
+  uint32_t* err = device_error_word();
+  if (!err) return KKA_ERR_DEVICE;
+  (void)hipGetLastError();
+  ScoreArgs a = {};
+  a.lvl = level_buf;
+  a.rows_per_seq = g.rows;
+  a.S = lay->num_seqs;
+  a.max_pages = lay->max_pages;
+  a.D = lay->head_dim;
+  a.hier = lay->hierarchical ? 1 : 0;
+  a.ppc = lay->hierarchical ? lay->pages_per_chunk : 1;
+  a.cpg = lay->hierarchical ? lay->chunks_per_grid : 1;
+  a.c_cap = g.c_cap;
+  a.n_pages = n_pages;
+  a.anchors = anchors;
+  char* wsb = static_cast<char*>(workspace);
+  a.tickets = reinterpret_cast<uint32_t*>(wsb);
+  a.aff = affinity_out ? affinity_out
+                       : reinterpret_cast<float*>(wsb + align256((size_t)lay->num_seqs * sizeof(uint32_t)));
+  a.k_g = lay->hierarchical ? sel->k_grid : 0;
+  a.k_c = lay->hierarchical ? sel->k_chunk : 0;
+  a.k_p = sel->k_page;
+  a.idx_out = page_idx_out;
+  a.score_out = page_score_out;
+  a.cnt_out = n_selected_out;
+  a.rows_per_tile = score_rows_per_tile(a.D);
+  const int64_t tiles = (g.rows + a.rows_per_tile - 1) / a.rows_per_tile;
+  a.tiles_per_seq = (int32_t)(tiles > 0 ? tiles : 1);
+  if ((int64_t)a.S * a.tiles_per_seq > 0x7fffffffLL) return KKA_ERR_SHAPE;
+  a.err = err;
+  return launched(launch_score_topk(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t kka_device_error(void* stream) {
+  uint32_t* p = device_error_word();
+  if (!p) return -1;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return -1;
+  uint32_t v = 0;
+  if (hipMemcpy(&v, p, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return -1;
+  const uint32_t zero = 0;
+  if (v != 0 && hipMemcpy(p, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return -1;
+  return (int32_t)v;
+}
+
+const char* kka_status_string(kka_status s) {
+  switch (s) {
+    case KKA_OK: return "ok";
+    case KKA_ERR_NULL: return "a required pointer is NULL";
+    case KKA_ERR_SHAPE: return "a size, count or mode is out of range";
+    case KKA_ERR_ALIGN: return "a pointer or stride breaks its alignment rule";
+    case KKA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KKA_ERR_DEVICE: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t kka_version(void) { return 100; }
+
+}  // extern "C"

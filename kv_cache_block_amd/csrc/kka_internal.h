@@ -1,0 +1,146 @@
+// Internal declarations shared by the libkka translation units: launch
+// argument blocks, small device helpers and the launchers each kernel file
+// provides to the C-ABI layer (kka_api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kka.h"
+
+namespace kka {
+
+// Largest block size any pool kernel is launched with (one thread per 16-byte
+// chunk of a token's H*D key row, H*D/8 <= 1024).
+constexpr int kMaxPoolThreads = 1024;
+// Target work-groups for one pooling launch: 256 CUs x 8 resident groups.
+constexpr int kPoolTargetGroups = 2048;
+// Largest k at any selection level.
+constexpr int kMaxK = 1024;
+// Largest number of parents whose keep flags one selecting group tracks.
+constexpr int kMaxParents = 65536;
+// Largest chunks_per_grid * head_dim (LDS of the level builder, floats).
+constexpr int kMaxGridFloats = 16384;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Thread layout of the pooling kernels: a token's H*D key row is cut into
+// H*D/8 chunks of 16 bytes; `rg` consecutive threads cover one row and `m`
+// rows (tokens) are in flight per pass, nt = rg * m threads per group.
+struct PoolShape {
+  int32_t rg, m, nt;
+};
+
+inline PoolShape pool_shape(int32_t H, int32_t D) {
+  PoolShape ps;
+  ps.rg = H * (D / 8);
+  ps.m = ps.rg >= 256 ? 1 : 256 / ps.rg;
+  ps.nt = ps.rg * ps.m;
+  return ps;
+}
+
+// Layer split of a pooling launch: enough groups to fill the chip, never a
+// split finer than one layer.  Depends only on (items, L).
+struct LayerSplit {
+  int32_t n_split, lps;
+};
+
+inline LayerSplit layer_split(int64_t items, int32_t L) {
+  LayerSplit ls;
+  int64_t want = items >= kPoolTargetGroups ? 1 : (kPoolTargetGroups + items - 1) / (items > 0 ? items : 1);
+  if (want > L) want = L;
+  if (want < 1) want = 1;
+  ls.lps = (int32_t)((L + want - 1) / want);
+  ls.n_split = (L + ls.lps - 1) / ls.lps;
+  return ls;
+}
+
+struct PoolArgs {
+  const uint16_t* k;
+  int64_t sL, sB, sT, sH;
+  int32_t L, H, D, B;
+  int64_t P;
+  int32_t S, total_blocks;
+  const int32_t* seq_len;
+  const int32_t* offs;
+  const int32_t* table;
+  const int32_t* subset;  // global logical block per item, or null (item == block)
+  int32_t n_items;
+  int32_t n_split, lps;
+  const float* weights;   // [S][L*H] (given-weight pooling and the anchor)
+  float* out;             // v_b rows / anchor rows
+  int64_t vb_stride;      // rows per sequence in `out`, 0 = row is the global block id
+  float* partial;         // layer-split partial sums, or per-(l,h) token sums
+  float* stats_q;         // per-(item, l, h) sums of squares
+  uint32_t* err;
+  PoolShape ps;
+  int32_t window;         // anchor only
+};
+
+struct WeightArgs {
+  const float* s1;  // [total_blocks][L*H][D] token sums
+  const float* q;   // [total_blocks][L*H] sums of squares
+  double* var;      // [S][L*H]
+  float* head_weight;
+  const int32_t* seq_len;
+  const int32_t* offs;
+  int32_t S, LH, D, B, total_blocks;
+  uint32_t* err;
+};
+
+struct LevelArgs {
+  float* lvl;
+  int64_t rows_per_seq;
+  int32_t S, max_pages, D, ppc, cpg, c_cap, g_cap;
+  const int32_t* n_pages;
+  const int32_t* first_dirty;
+  uint32_t* err;
+};
+
+struct ScoreArgs {
+  const float* lvl;
+  int64_t rows_per_seq;
+  int32_t S, max_pages, D, hier, ppc, cpg, c_cap;
+  const int32_t* n_pages;
+  const float* anchors;
+  float* aff;            // affinity rows, aff + s * rows_per_seq + row
+  int32_t k_g, k_c, k_p;
+  int32_t* idx_out;
+  float* score_out;
+  int32_t* cnt_out;
+  uint32_t* tickets;     // [S], zero between calls
+  int32_t tiles_per_seq, rows_per_tile;
+  uint32_t* err;
+};
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Largest s in [0, S) with offs[s] <= b (offsets nondecreasing).
+__device__ __forceinline__ int32_t find_seq(const int32_t* __restrict__ offs, int32_t S, int32_t b) {
+  int32_t lo = 0, hi = S - 1;
+  while (lo < hi) {
+    int32_t mid = (lo + hi + 1) >> 1;
+    if (offs[mid] <= b) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ void raise_err(uint32_t* err, uint32_t bit) { atomicOr(err, bit); }
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; arguments are already valid.
+
+hipError_t launch_pool(const PoolArgs& a, int mode, hipStream_t st);          // uniform / given
+hipError_t launch_pool_stats(const PoolArgs& a, hipStream_t st);              // variance pass 1
+hipError_t launch_head_weights(const WeightArgs& w, hipStream_t st);          // variance pass 2
+hipError_t launch_pool_combine(const PoolArgs& a, const float* w, hipStream_t st);  // variance pass 3
+hipError_t launch_anchor(const PoolArgs& a, hipStream_t st);
+hipError_t launch_levels(const LevelArgs& a, hipStream_t st);
+hipError_t launch_score_topk(const ScoreArgs& a, hipStream_t st);
+int32_t score_rows_per_tile(int32_t D);  // rows one score work-group covers
+
+}  // namespace kka

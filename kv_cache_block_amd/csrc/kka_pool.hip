@@ -1,0 +1,527 @@
+// Pooling kernels: block vectors v_b and the query anchor.
+//
+// Page "Key-Key Semantic Affinity: Key vectors replace attention scores for
+// KV-cache importance" (10100.com), section 2.2 steps 1-2 and section 5.2
+// steps 1-2: a block is summarised by the mean of its keys over every token,
+// KV head and layer; the anchor is the same mean over the last few tokens.
+// Section 3.3 adds weighting of heads by their variance.
+//
+// The pool is streamed once.  Every thread owns one 16-byte chunk (8 bf16
+// values of one head_dim row) of a token's H*D key row and walks tokens and
+// layers, so a wavefront issues 1 KB-contiguous loads for the 7B shape
+// (4 heads x 128 dims x 2 B) and keeps 8 independent 16-byte loads in
+// flight per lane.  Partial sums stay in fp32 registers; a fixed-order LDS
+// reduction finishes each group, so results do not depend on where blocks
+// sit in the physical pool or on scheduling.
+#include "kka_internal.h"
+
+#ifndef KKA_NT_LOADS
+#define KKA_NT_LOADS 1
+#endif
+
+namespace kka {
+namespace {
+
+constexpr int kUnroll = 8;
+enum : int { kUniform = 0, kGiven = 2 };
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+#if KKA_NT_LOADS
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+  return *reinterpret_cast<const u32x4*>(p);
+#endif
+}
+
+template <int MODE>
+__device__ __forceinline__ void accum8(float (&acc)[8], u32x4 v, float w) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t x = v[c];
+    if (MODE == kGiven) {
+      acc[2 * c] = fmaf(w, bf16_lo(x), acc[2 * c]);
+      acc[2 * c + 1] = fmaf(w, bf16_hi(x), acc[2 * c + 1]);
+    } else {
+      acc[2 * c] += bf16_lo(x);
+      acc[2 * c + 1] += bf16_hi(x);
+    }
+  }
+}
+
+// One logical block of a pooling launch.
+struct Item {
+  int32_t b, s, i, n_b;
+  int64_t p;
+  int64_t row;  // output row, -1 when it cannot be written
+};
+
+// Resolves work item -> (block, sequence, valid tokens, physical block, row).
+// Invalid device metadata zeroes n_b (the block then pools to zeros) and,
+// when `report`, raises the matching flag bit.
+__device__ Item locate(const PoolArgs& a, int32_t item, bool report) {
+  Item it;
+  it.b = a.subset ? a.subset[item] : item;
+  it.n_b = 0;
+  it.p = 0;
+  it.row = -1;
+  it.s = 0;
+  it.i = 0;
+  if (it.b < 0 || it.b >= a.total_blocks || a.S <= 0) {
+    if (report) raise_err(a.err, KKA_DEVERR_OFFSETS);
+    return it;
+  }
+  it.s = find_seq(a.offs, a.S, it.b);
+  it.i = it.b - a.offs[it.s];
+  if (it.i < 0 || it.b >= a.offs[it.s + 1]) {
+    if (report) raise_err(a.err, KKA_DEVERR_OFFSETS);
+    return it;
+  }
+  if (a.vb_stride > 0) {
+    if ((int64_t)it.i < a.vb_stride) it.row = (int64_t)it.s * a.vb_stride + it.i;
+    else if (report) raise_err(a.err, KKA_DEVERR_ROW);
+  } else {
+    it.row = it.b;
+  }
+  int64_t nb = (int64_t)a.seq_len[it.s] - (int64_t)it.i * a.B;
+  if (nb > a.B) nb = a.B;
+  if (nb <= 0) {
+    if (report) raise_err(a.err, KKA_DEVERR_SEQ_LEN);
+    return it;
+  }
+  const int64_t p = a.table[it.b];
+  if (p < 0 || p >= a.P) {
+    if (report) raise_err(a.err, KKA_DEVERR_BLOCK_TABLE);
+    return it;
+  }
+  it.p = p;
+  it.n_b = (int32_t)nb;
+  return it;
+}
+
+// Fixed-order reduction of every thread's 8 partial sums into head_dim sums:
+// the threads sharing a 16-byte column are tid = dg + r * (D/8).
+__device__ __forceinline__ float column_sum(const float* red, int32_t D, int32_t nt, int32_t d) {
+  const int32_t DG = D >> 3;
+  const int32_t per = nt / DG;
+  const int32_t base = ((d >> 3) << 3) + (d & 7);
+  float sum = 0.f;
+  for (int32_t r = 0; r < per; ++r) sum += red[base + r * DG * 8];
+  return sum;
+}
+
+__device__ __forceinline__ void stash8(float* red, int tid, const float (&acc)[8]) {
+  float4* r4 = reinterpret_cast<float4*>(red);
+  r4[2 * tid] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  r4[2 * tid + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
+// ------------------------------------------------------------ v_b, one pass
+
+template <int MODE, int MAXT>
+__global__ __launch_bounds__(MAXT) void pool_kernel(PoolArgs a) {
+  __shared__ float red[MAXT * 8];
+  extern __shared__ float wsh[];  // [L*H] head weights (given-weight mode)
+  const int tid = threadIdx.x;
+  const int32_t item = blockIdx.x / a.n_split;
+  const int32_t j = blockIdx.x - item * a.n_split;
+  const Item it = locate(a, item, tid == 0 && j == 0);
+  const int32_t LH = a.L * a.H;
+  if (MODE == kGiven) {
+    for (int x = tid; x < LH; x += a.ps.nt) wsh[x] = a.weights[(int64_t)it.s * LH + x];
+    __syncthreads();
+  }
+  const int32_t DG = a.D >> 3;
+  const int32_t q = tid % a.ps.rg;
+  const int32_t h = q / DG;
+  const int32_t dg = q - h * DG;
+  const int32_t toff = tid / a.ps.rg;
+  const int32_t l0 = j * a.lps;
+  const int32_t nl = min(a.L, l0 + a.lps) - l0;
+  const int32_t n_tok = it.n_b > toff ? (it.n_b - toff + a.ps.m - 1) / a.ps.m : 0;
+  const int32_t total = n_tok * nl;
+  const int64_t step_t = (int64_t)a.ps.m * a.sT;
+
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const uint16_t* tp = a.k + it.p * a.sB + (int64_t)h * a.sH + (int64_t)dg * 8 + (int64_t)toff * a.sT +
+                       (int64_t)l0 * a.sL;
+  const uint16_t* ptr = tp;
+  int32_t li = 0;
+  int32_t n = 0;
+  // layer-inner walk over (token, layer): kUnroll independent loads per step
+  for (; n + kUnroll <= total; n += kUnroll) {
+    u32x4 v[kUnroll];
+    float w[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      v[u] = load16(ptr);
+      w[u] = MODE == kGiven ? wsh[(l0 + li) * a.H + h] : 0.f;
+      ++li;
+      ptr += a.sL;
+      if (li == nl) {
+        li = 0;
+        tp += step_t;
+        ptr = tp;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) accum8<MODE>(acc, v[u], w[u]);
+  }
+  for (; n < total; ++n) {
+    const u32x4 v = load16(ptr);
+    const float w = MODE == kGiven ? wsh[(l0 + li) * a.H + h] : 0.f;
+    accum8<MODE>(acc, v, w);
+    ++li;
+    ptr += a.sL;
+    if (li == nl) {
+      li = 0;
+      tp += step_t;
+      ptr = tp;
+    }
+  }
+
+  stash8(red, tid, acc);
+  __syncthreads();
+  for (int32_t d = tid; d < a.D; d += a.ps.nt) {
+    const float sum = column_sum(red, a.D, a.ps.nt, d);
+    if (a.n_split == 1) {
+      if (it.row >= 0) {
+        const float denom = MODE == kGiven ? (float)it.n_b : (float)((int64_t)it.n_b * LH);
+        a.out[it.row * a.D + d] = it.n_b > 0 ? sum / denom : 0.f;
+      }
+    } else {
+      a.partial[((int64_t)item * a.n_split + j) * a.D + d] = sum;
+    }
+  }
+}
+
+// Sums the layer-split partials of each item in split order.
+template <int MODE>
+__global__ __launch_bounds__(256) void pool_finish_kernel(PoolArgs a) {
+  const int32_t item = blockIdx.x;
+  const Item it = locate(a, item, false);
+  if (it.row < 0) return;
+  const int32_t LH = a.L * a.H;
+  for (int32_t d = threadIdx.x; d < a.D; d += blockDim.x) {
+    float sum = 0.f;
+    for (int32_t j = 0; j < a.n_split; ++j) sum += a.partial[((int64_t)item * a.n_split + j) * a.D + d];
+    const float denom = MODE == kGiven ? (float)it.n_b : (float)((int64_t)it.n_b * LH);
+    a.out[it.row * a.D + d] = it.n_b > 0 ? sum / denom : 0.f;
+  }
+}
+
+// ------------------------------------------------- variance weights, 3 passes
+
+// Pass 1: per block and (layer, head): token sums s1[b][l][h][:] and the sum
+// of squares q[b][l][h], one streaming pass over the keys.
+template <int MAXT>
+__global__ __launch_bounds__(MAXT) void pool_stats_kernel(PoolArgs a) {
+  __shared__ float red[MAXT * 9];
+  const int tid = threadIdx.x;
+  const int32_t item = blockIdx.x / a.n_split;
+  const int32_t j = blockIdx.x - item * a.n_split;
+  const Item it = locate(a, item, tid == 0 && j == 0);
+  const int32_t DG = a.D >> 3;
+  const int32_t q = tid % a.ps.rg;
+  const int32_t h = q / DG;
+  const int32_t dg = q - h * DG;
+  const int32_t toff = tid / a.ps.rg;
+  const int32_t l0 = j * a.lps;
+  const int32_t l1 = min(a.L, l0 + a.lps);
+  const int32_t n_tok = it.n_b > toff ? (it.n_b - toff + a.ps.m - 1) / a.ps.m : 0;
+  const int64_t step_t = (int64_t)a.ps.m * a.sT;
+  float* redq = red + MAXT * 8;
+
+  for (int32_t l = l0; l < l1; ++l) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float sq = 0.f;
+    const uint16_t* tp = a.k + (int64_t)l * a.sL + it.p * a.sB + (int64_t)h * a.sH + (int64_t)dg * 8 +
+                         (int64_t)toff * a.sT;
+    int32_t ti = 0;
+    for (; ti + kUnroll <= n_tok; ti += kUnroll) {
+      u32x4 v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) v[u] = load16(tp + (int64_t)(ti + u) * step_t);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float x0 = bf16_lo(v[u][c]), x1 = bf16_hi(v[u][c]);
+          acc[2 * c] += x0;
+          acc[2 * c + 1] += x1;
+          sq = fmaf(x0, x0, sq);
+          sq = fmaf(x1, x1, sq);
+        }
+      }
+    }
+    for (; ti < n_tok; ++ti) {
+      const u32x4 v = load16(tp + (int64_t)ti * step_t);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float x0 = bf16_lo(v[c]), x1 = bf16_hi(v[c]);
+        acc[2 * c] += x0;
+        acc[2 * c + 1] += x1;
+        sq = fmaf(x0, x0, sq);
+        sq = fmaf(x1, x1, sq);
+      }
+    }
+    stash8(red, tid, acc);
+    redq[tid] = sq;
+    __syncthreads();
+    const int64_t lh_row = ((int64_t)item * a.L + l) * a.H;  // (item, l, h=0)
+    if (tid < a.ps.rg) {
+      float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int32_t r = 0; r < a.ps.m; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s8[e] += red[(tid + r * a.ps.rg) * 8 + e];
+      float4* dst = reinterpret_cast<float4*>(a.partial + lh_row * a.D + (int64_t)tid * 8);
+      dst[0] = make_float4(s8[0], s8[1], s8[2], s8[3]);
+      dst[1] = make_float4(s8[4], s8[5], s8[6], s8[7]);
+    }
+    if (tid < a.H) {
+      float s = 0.f;
+      for (int32_t r = 0; r < a.ps.m; ++r)
+        for (int32_t x = 0; x < DG; ++x) s += redq[r * a.ps.rg + tid * DG + x];
+      a.stats_q[lh_row + tid] = s;
+    }
+    __syncthreads();
+  }
+}
+
+// Pass 2: one group per (sequence, head): temporal variance of the head,
+//   var = ( sum_tau |x_tau|^2 / T  -  sum_d (sum_tau x_tau,d / T)^2 ) / D,
+// from the pass-1 sums, combined in fp64.
+__global__ __launch_bounds__(256) void head_var_kernel(WeightArgs w) {
+  __shared__ double r1[256];
+  __shared__ double r2[256];
+  const int tid = threadIdx.x;
+  const int32_t s = blockIdx.x / w.LH;
+  const int32_t lh = blockIdx.x - s * w.LH;
+  // offsets are device data: clamp to the sums the pass-1 launch wrote
+  const int32_t b1 = min(max(w.offs[s + 1], 0), w.total_blocks);
+  const int32_t b0 = min(max(w.offs[s], 0), b1);
+  const int64_t T = w.seq_len[s] > 0 ? w.seq_len[s] : 0;
+  double m2 = 0.0;
+  for (int32_t d = tid; d < w.D; d += 256) {
+    double s1 = 0.0;
+    for (int32_t b = b0; b < b1; ++b) s1 += (double)w.s1[((int64_t)b * w.LH + lh) * w.D + d];
+    const double mean = T > 0 ? s1 / (double)T : 0.0;
+    m2 += mean * mean;
+  }
+  double qs = 0.0;
+  for (int32_t b = b0 + tid; b < b1; b += 256) qs += (double)w.q[(int64_t)b * w.LH + lh];
+  r1[tid] = m2;
+  r2[tid] = qs;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) {
+      r1[tid] += r1[tid + off];
+      r2[tid] += r2[tid + off];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    double v = T > 0 ? (r2[0] / (double)T - r1[0]) / (double)w.D : 0.0;
+    w.var[(int64_t)s * w.LH + lh] = v > 0.0 ? v : 0.0;
+  }
+}
+
+// Pass 2b: weights = variance / sum of variances (uniform when the sum is 0).
+__global__ __launch_bounds__(256) void head_norm_kernel(WeightArgs w) {
+  __shared__ double r[256];
+  const int tid = threadIdx.x;
+  const int32_t s = blockIdx.x;
+  double v = 0.0;
+  for (int32_t x = tid; x < w.LH; x += 256) v += w.var[(int64_t)s * w.LH + x];
+  r[tid] = v;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) r[tid] += r[tid + off];
+    __syncthreads();
+  }
+  const double total = r[0];
+  for (int32_t x = tid; x < w.LH; x += 256)
+    w.head_weight[(int64_t)s * w.LH + x] =
+        total > 0.0 ? (float)(w.var[(int64_t)s * w.LH + x] / total) : (float)(1.0 / (double)w.LH);
+}
+
+// Pass 3: v_b = sum_{l,h} w[s][l,h] * s1[b][l][h][:] / n_b.
+__global__ __launch_bounds__(256) void pool_combine_kernel(PoolArgs a, const float* __restrict__ wts) {
+  const int32_t item = blockIdx.x;
+  const Item it = locate(a, item, false);
+  if (it.row < 0) return;
+  const int32_t LH = a.L * a.H;
+  for (int32_t d = threadIdx.x; d < a.D; d += blockDim.x) {
+    float acc = 0.f;
+    const float* src = a.partial + (int64_t)item * LH * a.D + d;
+    const float* wr = wts + (int64_t)it.s * LH;
+    for (int32_t lh = 0; lh < LH; ++lh) acc = fmaf(wr[lh], src[(int64_t)lh * a.D], acc);
+    a.out[it.row * a.D + d] = it.n_b > 0 ? acc / (float)it.n_b : 0.f;
+  }
+}
+
+// ------------------------------------------------------------------ anchor
+
+// One group per (sequence, layer range): the last W_eff tokens of the
+// sequence, gathered through the block table (the window may straddle
+// blocks); token-outer, layer-inner so each token's block id is read once.
+template <int MODE, int MAXT>
+__global__ __launch_bounds__(MAXT) void anchor_kernel(PoolArgs a) {
+  __shared__ float red[MAXT * 8];
+  extern __shared__ float wsh[];
+  const int tid = threadIdx.x;
+  const int32_t s = blockIdx.x / a.n_split;
+  const int32_t j = blockIdx.x - s * a.n_split;
+  const int32_t LH = a.L * a.H;
+  if (MODE == kGiven) {
+    for (int x = tid; x < LH; x += a.ps.nt) wsh[x] = a.weights[(int64_t)s * LH + x];
+    __syncthreads();
+  }
+  const int32_t T = a.seq_len[s] > 0 ? a.seq_len[s] : 0;
+  const int32_t W = a.window < T ? a.window : T;
+  // offsets are device data: never index the table outside [0, total_blocks)
+  const int32_t b1 = min(max(a.offs[s + 1], 0), a.total_blocks);
+  const int32_t b0 = min(max(a.offs[s], 0), b1);
+  const int32_t nb_s = b1 - b0;
+  const int32_t DG = a.D >> 3;
+  const int32_t q = tid % a.ps.rg;
+  const int32_t h = q / DG;
+  const int32_t dg = q - h * DG;
+  const int32_t toff = tid / a.ps.rg;
+  const int32_t l0 = j * a.lps;
+  const int32_t nl = min(a.L, l0 + a.lps) - l0;
+  bool bad_len = false, bad_tab = false;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int32_t tau = T - W + toff; tau < T; tau += a.ps.m) {
+    const int32_t i = tau / a.B;
+    const int32_t t = tau - i * a.B;
+    if (i >= nb_s) {
+      bad_len = true;
+      continue;
+    }
+    const int64_t p = a.table[b0 + i];
+    if (p < 0 || p >= a.P) {
+      bad_tab = true;
+      continue;
+    }
+    const uint16_t* base = a.k + p * a.sB + (int64_t)t * a.sT + (int64_t)h * a.sH + (int64_t)dg * 8 +
+                           (int64_t)l0 * a.sL;
+    int32_t l = 0;
+    for (; l + kUnroll <= nl; l += kUnroll) {
+      u32x4 v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) v[u] = load16(base + (int64_t)(l + u) * a.sL);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        accum8<MODE>(acc, v[u], MODE == kGiven ? wsh[(l0 + l + u) * a.H + h] : 0.f);
+    }
+    for (; l < nl; ++l)
+      accum8<MODE>(acc, load16(base + (int64_t)l * a.sL), MODE == kGiven ? wsh[(l0 + l) * a.H + h] : 0.f);
+  }
+  if (bad_len) raise_err(a.err, KKA_DEVERR_SEQ_LEN);
+  if (bad_tab) raise_err(a.err, KKA_DEVERR_BLOCK_TABLE);
+  stash8(red, tid, acc);
+  __syncthreads();
+  for (int32_t d = tid; d < a.D; d += a.ps.nt) {
+    const float sum = column_sum(red, a.D, a.ps.nt, d);
+    if (a.n_split == 1) {
+      const float denom = MODE == kGiven ? (float)W : (float)((int64_t)W * LH);
+      a.out[(int64_t)s * a.D + d] = W > 0 ? sum / denom : 0.f;
+    } else {
+      a.partial[((int64_t)s * a.n_split + j) * a.D + d] = sum;
+    }
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void anchor_finish_kernel(PoolArgs a) {
+  const int32_t s = blockIdx.x;
+  const int32_t T = a.seq_len[s] > 0 ? a.seq_len[s] : 0;
+  const int32_t W = a.window < T ? a.window : T;
+  const int32_t LH = a.L * a.H;
+  for (int32_t d = threadIdx.x; d < a.D; d += blockDim.x) {
+    float sum = 0.f;
+    for (int32_t j = 0; j < a.n_split; ++j) sum += a.partial[((int64_t)s * a.n_split + j) * a.D + d];
+    const float denom = MODE == kGiven ? (float)W : (float)((int64_t)W * LH);
+    a.out[(int64_t)s * a.D + d] = W > 0 ? sum / denom : 0.f;
+  }
+}
+
+inline int small_block(int32_t D) { return D >= 256 ? 256 : ((D + 63) / 64) * 64; }
+
+}  // namespace
+
+hipError_t launch_pool(const PoolArgs& a, int mode, hipStream_t st) {
+  const dim3 grid((unsigned)((int64_t)a.n_items * a.n_split));
+  const dim3 block((unsigned)a.ps.nt);
+  const size_t dyn = mode == kGiven ? sizeof(float) * (size_t)a.L * a.H : 0;
+  if (a.n_items > 0) {
+    if (a.ps.nt <= 256) {
+      if (mode == kGiven) hipLaunchKernelGGL((pool_kernel<kGiven, 256>), grid, block, dyn, st, a);
+      else hipLaunchKernelGGL((pool_kernel<kUniform, 256>), grid, block, dyn, st, a);
+    } else {
+      if (mode == kGiven) hipLaunchKernelGGL((pool_kernel<kGiven, 1024>), grid, block, dyn, st, a);
+      else hipLaunchKernelGGL((pool_kernel<kUniform, 1024>), grid, block, dyn, st, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.n_split > 1) {
+      const dim3 fb((unsigned)small_block(a.D));
+      if (mode == kGiven) hipLaunchKernelGGL((pool_finish_kernel<kGiven>), dim3(a.n_items), fb, 0, st, a);
+      else hipLaunchKernelGGL((pool_finish_kernel<kUniform>), dim3(a.n_items), fb, 0, st, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_pool_stats(const PoolArgs& a, hipStream_t st) {
+  if (a.n_items <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((int64_t)a.n_items * a.n_split));
+  const dim3 block((unsigned)a.ps.nt);
+  if (a.ps.nt <= 256) hipLaunchKernelGGL((pool_stats_kernel<256>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((pool_stats_kernel<1024>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_head_weights(const WeightArgs& w, hipStream_t st) {
+  if (w.S <= 0) return hipSuccess;
+  hipLaunchKernelGGL(head_var_kernel, dim3((unsigned)((int64_t)w.S * w.LH)), dim3(256), 0, st, w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(head_norm_kernel, dim3((unsigned)w.S), dim3(256), 0, st, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_combine(const PoolArgs& a, const float* wts, hipStream_t st) {
+  if (a.n_items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(pool_combine_kernel, dim3((unsigned)a.n_items), dim3((unsigned)small_block(a.D)), 0, st, a,
+                     wts);
+  return hipGetLastError();
+}
+
+hipError_t launch_anchor(const PoolArgs& a, hipStream_t st) {
+  if (a.S <= 0) return hipSuccess;
+  const bool given = a.weights != nullptr;
+  const dim3 grid((unsigned)((int64_t)a.S * a.n_split));
+  const dim3 block((unsigned)a.ps.nt);
+  const size_t dyn = given ? sizeof(float) * (size_t)a.L * a.H : 0;
+  if (a.ps.nt <= 256) {
+    if (given) hipLaunchKernelGGL((anchor_kernel<kGiven, 256>), grid, block, dyn, st, a);
+    else hipLaunchKernelGGL((anchor_kernel<kUniform, 256>), grid, block, dyn, st, a);
+  } else {
+    if (given) hipLaunchKernelGGL((anchor_kernel<kGiven, 1024>), grid, block, dyn, st, a);
+    else hipLaunchKernelGGL((anchor_kernel<kUniform, 1024>), grid, block, dyn, st, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.n_split > 1) {
+    const dim3 fb((unsigned)small_block(a.D));
+    if (given) hipLaunchKernelGGL((anchor_finish_kernel<kGiven>), dim3((unsigned)a.S), fb, 0, st, a);
+    else hipLaunchKernelGGL((anchor_finish_kernel<kUniform>), dim3((unsigned)a.S), fb, 0, st, a);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace kka

@@ -1,0 +1,184 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and rejects invalid arguments on the host before anything
+reaches the device.
+
+Every validation case below breaks at least one rule that is checked before
+the library's first HIP call, so the fake (never dereferenced) pointers are
+never handed to a kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kv_cache_block_amd as kka
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kka.h")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+FAKE_ODD = 0x10004
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kka.LIB_PATH):
+        pytest.skip("libkka.so not built")
+    return kka.lib()
+
+
+def declared():
+    text = open(HEADER).read()
+    return re.findall(r"KKA_API\s+[\w\s\*]+?\b(kka_\w+)\s*\(", text)
+
+
+def test_header_declares_all_entry_points():
+    names = declared()
+    assert sorted(names) == sorted(kka.ENTRY_POINTS)
+    for n in ("kka_pool_blocks", "kka_pool_anchor", "kka_build_levels", "kka_score_topk"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared():
+        assert hasattr(L, name), name
+    assert L.kka_version() == 100
+    assert L.kka_status_string(0) == b"ok"
+    assert L.kka_status_string(4).startswith(b"workspace")
+
+
+def kpool(**kw):
+    d = dict(k=FAKE, num_layers=28, num_kv_heads=4, head_dim=128, block_size=16, num_phys_blocks=64)
+    d.update(kw)
+    P, B, H, D = d["num_phys_blocks"], d["block_size"], d["num_kv_heads"], d["head_dim"]
+    strides = d.pop("strides", (P * B * H * D, B * H * D, H * D, D))
+    return kka.c_kpool(d["k"], d["num_layers"], d["num_kv_heads"], d["head_dim"], d["block_size"],
+                       d["num_phys_blocks"], *strides)
+
+
+def seqs(**kw):
+    d = dict(num_seqs=2, total_blocks=64, seq_len=FAKE, block_offsets=FAKE, block_table=FAKE)
+    d.update(kw)
+    return kka.c_seqs(d["num_seqs"], d["total_blocks"], d["seq_len"], d["block_offsets"], d["block_table"])
+
+
+def pool(L, kp, sq, blocks=None, nb=0, mode=0, hw=FAKE, out=FAKE, stride=0, ws=None, wsb=0):
+    return L.kka_pool_blocks(ctypes.byref(kp), ctypes.byref(sq), blocks, nb, mode, hw, out, stride, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=0), 1),
+    (dict(head_dim=12), 2),
+    (dict(head_dim=2048), 2),
+    (dict(num_layers=0), 2),
+    (dict(block_size=0), 2),
+    (dict(num_phys_blocks=0), 2),
+    (dict(num_kv_heads=128, head_dim=128), 2),      # H*D/8 > 1024 threads
+    (dict(num_layers=2048, num_kv_heads=4), 2),     # L*H > 4096 weights
+    (dict(k=FAKE_ODD), 3),
+    (dict(strides=(8, 8, 8, 4)), 3),
+    (dict(strides=(8, -8, 8, 8)), 2),
+])
+def test_pool_rejects_bad_kpool(L, kw, code):
+    assert pool(L, kpool(**kw), seqs()) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_seqs=-1), 2),
+    (dict(total_blocks=-3), 2),
+    (dict(seq_len=None), 1),
+    (dict(block_offsets=None), 1),
+    (dict(block_table=None), 1),
+    (dict(num_seqs=0, total_blocks=5), 2),
+])
+def test_pool_rejects_bad_seqs(L, kw, code):
+    assert pool(L, kpool(), seqs(**kw)) == code
+
+
+def test_pool_rejects_bad_call_arguments(L):
+    kp, sq = kpool(), seqs()
+    assert pool(L, kp, sq, mode=3) == 2
+    assert pool(L, kp, sq, blocks=FAKE, nb=-1) == 2
+    assert pool(L, kp, sq, blocks=FAKE, nb=4, mode=1) == 2          # variance needs every block
+    assert pool(L, kp, sq, mode=2, hw=None) == 1                    # given weights missing
+    assert pool(L, kp, sq, mode=1, hw=None) == 1
+    assert pool(L, kp, sq, stride=-1) == 2
+    assert pool(L, kp, sq, out=None) == 1
+    assert pool(L, kp, sq, out=FAKE_ODD) == 3
+    assert pool(L, kp, seqs(num_seqs=1, total_blocks=0, block_table=None), blocks=FAKE, nb=2) == 2
+    # variance mode needs a workspace
+    need = L.kka_pool_blocks_workspace(ctypes.byref(kp), ctypes.byref(sq), None, 0, 1)
+    assert need > 0
+    assert pool(L, kp, sq, mode=1) == 4
+    assert pool(L, kp, sq, mode=1, ws=FAKE, wsb=need - 1) == 4
+    assert pool(L, kp, sq, mode=1, ws=FAKE_ODD, wsb=need) == 3
+
+
+def test_workspace_sizes(L):
+    kp = kpool(num_phys_blocks=8192)
+    big = seqs(num_seqs=1, total_blocks=8192)
+    small = seqs(num_seqs=1, total_blocks=256)
+    # enough blocks to fill the chip: one pass, no partials
+    assert L.kka_pool_blocks_workspace(ctypes.byref(kp), ctypes.byref(big), None, 0, 0) == 0
+    # few blocks: split over layers, D floats per (block, split)
+    n = L.kka_pool_blocks_workspace(ctypes.byref(kp), ctypes.byref(small), None, 0, 0)
+    assert n >= 256 * 2 * 128 * 4 and n % 256 == 0
+    # variance: per-(block, layer, head) sums + squares + per-(seq, head) fp64 variances
+    v = L.kka_pool_blocks_workspace(ctypes.byref(kp), ctypes.byref(big), None, 0, 1)
+    assert v >= 8192 * 112 * 129 * 4 + 112 * 8
+    a = L.kka_pool_anchor_workspace(ctypes.byref(kp), ctypes.byref(big), 16)
+    assert a >= 28 * 128 * 4  # one sequence: split over every layer
+
+
+def test_level_rows_and_score_validation(L):
+    lay = kka.c_level_layout(64, 8192, 128, 1, 16, 16)
+    assert L.kka_level_rows(ctypes.byref(lay)) == 8192 + 512 + 32
+    flat = kka.c_level_layout(4, 1025, 128, 0, 16, 16)
+    assert L.kka_level_rows(ctypes.byref(flat)) == 1025
+    for bad in (kka.c_level_layout(1, 100, 12, 1, 16, 16), kka.c_level_layout(1, 100, 128, 1, 0, 16),
+                kka.c_level_layout(1, 16 * 65537, 128, 1, 16, 16), kka.c_level_layout(1, 100, 1024, 1, 16, 17),
+                kka.c_level_layout(-1, 100, 128, 0, 16, 16)):
+        assert L.kka_level_rows(ctypes.byref(bad)) == -1
+    sel = kka.c_select(4, 16, 64)
+    ws = L.kka_score_topk_workspace(ctypes.byref(lay), ctypes.byref(sel), 0)
+    assert ws >= 64 * 4 + 64 * 8736 * 4
+    ws_aff = L.kka_score_topk_workspace(ctypes.byref(lay), ctypes.byref(sel), 1)
+    assert 0 < ws_aff < ws
+
+    def score(lay_, sel_, lvl=FAKE, npg=FAKE, anc=FAKE, idx=FAKE, w=FAKE, wb=ws):
+        return L.kka_score_topk(ctypes.byref(lay_), lvl, npg, anc, ctypes.byref(sel_), None, idx, None, None, w,
+                                wb, None)
+
+    assert score(lay, kka.c_select(4, 16, 1025)) == 2
+    assert score(lay, kka.c_select(-1, 16, 64)) == 2
+    assert score(lay, sel, lvl=None) == 1
+    assert score(lay, sel, idx=None) == 1
+    assert score(lay, sel, anc=FAKE_ODD) == 3
+    assert score(lay, sel, w=None) == 4
+    assert score(lay, sel, wb=ws - 4) == 4
+    assert score(kka.c_level_layout(1, 100, 12, 1, 16, 16), sel) == 2
+    assert L.kka_build_levels(ctypes.byref(kka.c_level_layout(1, 100, 12, 1, 16, 16)), FAKE, FAKE, None,
+                              None) == 2
+    assert L.kka_build_levels(ctypes.byref(lay), None, FAKE, None, None) == 1
+    assert L.kka_build_levels(ctypes.byref(lay), FAKE_ODD, FAKE, None, None) == 3
+
+
+def test_anchor_validation(L):
+    kp, sq = kpool(), seqs()
+    f = lambda kp_, sq_, W=16, out=FAKE, ws=FAKE, wb=1 << 20: L.kka_pool_anchor(
+        ctypes.byref(kp_), ctypes.byref(sq_), W, None, out, ws, wb, None)
+    assert f(kp, sq, W=-1) == 2
+    assert f(kp, sq, out=None) == 1
+    assert f(kp, sq, out=FAKE_ODD) == 3
+    assert f(kp, sq, ws=None) == 4
+    assert f(kpool(head_dim=7), sq) == 2
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    if not os.path.exists(kka.LIB_PATH):
+        pytest.skip("libkka.so not built")
+    k = torch.zeros(16 * 4 * 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        kka.KPool(k, 1, 4, 128, 16, 1)

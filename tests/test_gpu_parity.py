@@ -1,0 +1,431 @@
+"""GPU parity: the HIP library (called through the C ABI) against the CPU
+oracle on the same seeded inputs, stage by stage.  Small cases span several
+work-groups, layer splits and ragged tails; edge cases cover empty
+sequences, k larger than the level, k = 0, exact ties and masked fills."""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_block_amd as kka
+import oracle
+import synth
+from kv_cache_block_amd.pipeline import Selector
+
+from gpu_harness import ATOL, WEIGHT_RTOL, check_selection, mode_of, n_pages_of, oracle_vb, run_selector, say, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kka.lib()  # raises loudly when the library is missing
+    yield
+    assert kka.kka_device_error() == 0
+
+
+def ragged_workload(seed, S, L, H, D, B, len_lo, len_hi, mode="uniform", select=None, window=16, noise=1.0,
+                    offset=0.0, lengths=None):
+    """Random ragged batch over a permuted shared pool (keys N(offset, noise))."""
+    if lengths is None:
+        T = synth.uniform_int(seed, 101, S, len_lo, len_hi).astype(np.int32)
+    else:
+        T = np.asarray(lengths, dtype=np.int32)
+        S = len(T)
+    nb = (T + B - 1) // B
+    off = np.zeros(S + 1, np.int32)
+    off[1:] = np.cumsum(nb)
+    P = int(off[-1]) + 3  # a few physical blocks nobody uses
+    table = synth.permutation(seed, 102, P)[:off[-1]].astype(np.int32)
+    std = np.full(L * H, noise, np.float32)
+    bias = np.full((L, H, D), offset, np.float32) if offset else None
+    k = synth._gen_kpool(L, H, D, B, P, T, off, table, None, None, 0.0, 0.0, std, bias, seed)
+    sel = select or {"hierarchical": 0, "k_grid": 0, "k_chunk": 0, "k_page": 8, "pages_per_chunk": 4,
+                     "chunks_per_grid": 3}
+    return synth.KWorkload(name="ragged", L=L, H=H, D=D, B=B, P=P, k=k, seq_len=T, block_offsets=off,
+                           block_table=table, window=window, mode=mode, select=sel, seed=seed)
+
+
+def vb_rows(sel, w):
+    out = {}
+    lvl = sel.level.cpu().numpy()
+    for s in range(w.S):
+        for i in range(int(w.block_offsets[s + 1] - w.block_offsets[s])):
+            out[int(w.block_offsets[s]) + i] = lvl[s, i]
+    return out
+
+
+# ------------------------------------------------------------------ pooling
+
+POOL_SHAPES = [
+    # (S, L, H, D, B, len_lo, len_hi)
+    (3, 4, 4, 128, 16, 1, 200),      # ragged tails, splits over layers
+    (2, 3, 2, 64, 16, 100, 700),
+    (4, 5, 3, 24, 7, 1, 90),         # odd head count / width: 9 threads per token row
+    (1, 2, 1, 256, 33, 500, 500),
+    (2, 2, 16, 512, 4, 30, 60),      # 1024 threads per group
+]
+
+
+@pytest.mark.parametrize("shape", POOL_SHAPES)
+def test_pool_uniform_matches_oracle(shape):
+    S, L, H, D, B, lo, hi = shape
+    say(f"pool uniform {shape}")
+    w = ragged_workload(1, S, L, H, D, B, lo, hi)
+    sel, _ = run_selector(w)
+    got = vb_rows(sel, w)
+    ref = oracle_vb(w, range(w.total_blocks))
+    for b, v in ref.items():
+        np.testing.assert_allclose(got[b], v, atol=ATOL, rtol=0, err_msg=f"block {b}")
+
+
+@pytest.mark.parametrize("shape", POOL_SHAPES[:3])
+def test_pool_variance_weights_match_oracle(shape):
+    S, L, H, D, B, lo, hi = shape
+    say(f"pool variance {shape}")
+    w = ragged_workload(2, S, L, H, D, B, lo, hi, mode="variance", offset=0.75)
+    # distinct head scales so the weights are far from uniform
+    sc = synth.uniform(2, 103, L * H).astype(np.float32) * 3 + 0.2
+    f = synth.bf16_bits_to_f32(w.k).reshape(L, w.P, B, H, D) * sc.reshape(L, 1, 1, H, 1)
+    w.k = synth.to_bf16_bits(f)
+    sel, _ = run_selector(w)
+    okp = oracle.KPool.of(w)
+    wref = oracle.weights_all(okp, w.seq_len, w.block_offsets, w.block_table)
+    wgpu = sel.head_weight.cpu().numpy()
+    np.testing.assert_allclose(wgpu, wref, rtol=WEIGHT_RTOL, atol=0)
+    got = vb_rows(sel, w)
+    ref = oracle_vb(w, range(w.total_blocks), wref)
+    for b, v in ref.items():
+        np.testing.assert_allclose(got[b], v, atol=ATOL, rtol=0, err_msg=f"block {b}")
+    anc = sel.anchors.cpu().numpy()
+    for s in range(w.S):
+        a = oracle.pool_anchor(okp, oracle.seq_table(w.block_offsets, w.block_table, s), int(w.seq_len[s]),
+                               w.window, wref[s])
+        np.testing.assert_allclose(anc[s], a, atol=ATOL, rtol=0)
+
+
+def test_pool_physical_permutation_is_bitwise_invariant():
+    say("pool permutation invariance")
+    w = ragged_workload(3, 2, 4, 4, 128, 16, 300, 600)
+    sel0, _ = run_selector(w)
+    v0 = vb_rows(sel0, w)
+    a0 = sel0.anchors.cpu().numpy()
+    # move every block to another physical slot, content unchanged
+    perm = synth.permutation(3, 104, w.P)
+    k = w.k.reshape(w.L, w.P, -1)
+    moved = np.empty_like(k)
+    moved[:, perm] = k
+    w2 = synth.KWorkload(**{**w.__dict__, "k": moved.reshape(w.k.shape),
+                            "block_table": perm[w.block_table].astype(np.int32)})
+    sel1, _ = run_selector(w2)
+    v1 = vb_rows(sel1, w2)
+    for b in v0:
+        np.testing.assert_array_equal(v0[b].view(np.uint32), v1[b].view(np.uint32))
+    np.testing.assert_array_equal(a0.view(np.uint32), sel1.anchors.cpu().numpy().view(np.uint32))
+
+
+def test_pool_token_order_within_block():
+    say("pool token order")
+    w = ragged_workload(4, 1, 3, 4, 128, 16, 160, 160)
+    sel0, _ = run_selector(w)
+    v0 = vb_rows(sel0, w)
+    k = w.k.reshape(w.L, w.P, w.B, -1).copy()
+    rng = np.random.default_rng(0)
+    for p in range(w.P):
+        k[:, p] = k[:, p][:, rng.permutation(w.B)]
+    w2 = synth.KWorkload(**{**w.__dict__, "k": k.reshape(w.k.shape)})
+    sel1, _ = run_selector(w2)
+    v1 = vb_rows(sel1, w2)
+    for b in v0:
+        np.testing.assert_allclose(v0[b], v1[b], atol=1e-6, rtol=0)
+
+
+def test_pool_is_deterministic():
+    say("pool determinism")
+    w = ragged_workload(5, 3, 4, 4, 128, 16, 10, 900, mode="variance")
+    s0, _ = run_selector(w)
+    s1, _ = run_selector(w)
+    assert torch.equal(s0.level, s1.level)
+    assert torch.equal(s0.head_weight, s1.head_weight)
+    assert torch.equal(s0.affinity, s1.affinity)
+
+
+def test_incremental_repool_equals_scratch():
+    """Append one token per sequence, re-pool only each sequence's newest
+    block with the frozen weights: equals pooling that block from scratch
+    (oracle) and the GPU's full pool with the same weights."""
+    say("incremental repool")
+    w = synth.config5(6, n_seqs=5, len_lo=60, len_hi=400, L=3, H=4, D=128, B=16)
+    after = w.extra["after"]
+    kp, seqs_before = upload(w)
+    sel = Selector(kp, seqs_before, w.select, max_pages=int(np.max(np.diff(after["block_offsets"]))),
+                   window=w.window, mode=kka.WEIGHT_VARIANCE)
+    sel.pool()
+    frozen = sel.head_weight.clone()
+    # state after the append
+    dev = "cuda"
+    seqs_after = kka.Seqs(torch.from_numpy(after["seq_len"]).to(dev),
+                          torch.from_numpy(after["block_offsets"]).to(dev),
+                          torch.from_numpy(after["block_table"]).to(dev), int(after["block_offsets"][-1]))
+    sel.seqs = seqs_after
+    newest = (after["block_offsets"][1:] - 1).astype(np.int32)
+    sel.repool(torch.from_numpy(newest).to(dev))
+    torch.cuda.synchronize()
+    assert torch.equal(sel.head_weight, frozen)
+    lvl = sel.level.cpu().numpy()
+    okp = oracle.KPool.of(w)
+    wf = frozen.cpu().numpy()
+    full = torch.zeros_like(sel.level)
+    kka.kka_pool_blocks(kp, seqs_after, full, mode=kka.WEIGHT_GIVEN, head_weight=frozen,
+                        vb_seq_stride=sel.lay.rows_per_seq)
+    full = full.cpu().numpy()
+    for s in range(w.S):
+        i = int(newest[s] - after["block_offsets"][s])
+        n_b = int(after["seq_len"][s]) - i * w.B
+        ref = oracle.pool_block(okp, int(after["block_table"][newest[s]]), n_b, wf[s])
+        np.testing.assert_allclose(lvl[s, i], ref, atol=ATOL, rtol=0)
+        np.testing.assert_allclose(lvl[s, i], full[s, i], atol=1e-6, rtol=0)
+
+
+# ------------------------------------------------------------------ anchor
+
+@pytest.mark.parametrize("W", [0, 1, 5, 16, 17, 40, 1000])
+def test_anchor_windows(W):
+    """Windows inside one block, straddling blocks, longer than the
+    sequence, and an empty sequence (zero anchor)."""
+    say(f"anchor W={W}")
+    w = ragged_workload(7, 4, 3, 2, 64, 16, 0, 0, window=W, lengths=[37, 0, 16, 70])
+    kp, seqs = upload(w)
+    out = torch.full((w.S, w.D), 5.0, dtype=torch.float32, device="cuda")
+    kka.kka_pool_anchor(kp, seqs, W, out)
+    torch.cuda.synchronize()
+    okp = oracle.KPool.of(w)
+    for s in range(w.S):
+        ref = oracle.pool_anchor(okp, oracle.seq_table(w.block_offsets, w.block_table, s), int(w.seq_len[s]), W)
+        np.testing.assert_allclose(out[s].cpu().numpy(), ref, atol=ATOL, rtol=0)
+    assert (out[1] == 0).all()
+
+
+# ------------------------------------------------------------------ levels + selection
+
+@pytest.mark.parametrize("case", [
+    dict(hierarchical=1, k_grid=2, k_chunk=3, k_page=5, pages_per_chunk=4, chunks_per_grid=3),
+    dict(hierarchical=1, k_grid=1, k_chunk=1, k_page=40, pages_per_chunk=4, chunks_per_grid=3),  # zero fill
+    dict(hierarchical=1, k_grid=0, k_chunk=2, k_page=6, pages_per_chunk=2, chunks_per_grid=2),   # all masked
+    dict(hierarchical=1, k_grid=1000, k_chunk=1000, k_page=7, pages_per_chunk=16, chunks_per_grid=16),
+    dict(hierarchical=0, k_grid=0, k_chunk=0, k_page=0, pages_per_chunk=16, chunks_per_grid=16),
+    dict(hierarchical=0, k_grid=0, k_chunk=0, k_page=1024, pages_per_chunk=16, chunks_per_grid=16),
+    dict(hierarchical=0, k_grid=0, k_chunk=0, k_page=13, pages_per_chunk=16, chunks_per_grid=16),
+])
+def test_levels_and_selection_match_oracle(case):
+    say(f"select {case}")
+    w = ragged_workload(8, 5, 2, 2, 64, 4, 0, 900, select=case)
+    sel, npg = run_selector(w)
+    for s in range(w.S):
+        check_selection(sel, s, int(npg[s]), tag=str(case))
+
+
+def test_selection_exact_ties_and_zero_scores():
+    """Integer-valued page vectors force exact ties and exact 0/0.5/1
+    affinities; the anchor is orthogonal to some pages and opposite to
+    others."""
+    say("select ties")
+    S, n_p, D = 3, 300, 8
+    lay = kka.LevelLayout(S, 320, D, True, 4, 5)
+    rng = np.random.default_rng(9)
+    lvl = np.zeros((S, lay.rows_per_seq, D), np.float32)
+    lvl[:, :n_p] = rng.integers(-1, 2, (S, n_p, D)).astype(np.float32)
+    lvl[:, 7] = 0.0
+    anchors = np.zeros((S, D), np.float32)
+    anchors[:, 0] = 1.0
+    lvl[:, 11] = -anchors[:, None, :][:, 0]
+    dev = "cuda"
+    sels = [dict(hierarchical=1, k_grid=2, k_chunk=4, k_page=9, pages_per_chunk=4, chunks_per_grid=5),
+            dict(hierarchical=1, k_grid=3, k_chunk=30, k_page=64, pages_per_chunk=4, chunks_per_grid=5)]
+    for cfg in sels:
+        level = torch.from_numpy(lvl).to(dev)
+        npg = torch.full((S,), n_p, dtype=torch.int32, device=dev)
+        kka.kka_build_levels(lay, level, npg)
+        sel = Selector.__new__(Selector)
+        sel.lay, sel.sel, sel.level = lay, cfg, level
+        sel.anchors = torch.from_numpy(anchors).to(dev)
+        sel.page_idx = torch.zeros((S, cfg["k_page"]), dtype=torch.int32, device=dev)
+        sel.page_score = torch.zeros((S, cfg["k_page"]), dtype=torch.float32, device=dev)
+        sel.n_selected = torch.zeros(S, dtype=torch.int32, device=dev)
+        sel.affinity = torch.zeros((S, lay.rows_per_seq), dtype=torch.float32, device=dev)
+        sel.ws_score = kka.new_workspace(kka.kka_score_topk_workspace(lay, True))
+        sel.score(npg)
+        torch.cuda.synchronize()
+        for s in range(S):
+            check_selection(sel, s, n_p, tag="ties")
+
+
+def test_dirty_rebuild_equals_full_rebuild():
+    say("levels dirty rebuild")
+    w = ragged_workload(10, 4, 2, 2, 64, 4, 50, 700,
+                        select=dict(hierarchical=1, k_grid=2, k_chunk=3, k_page=5, pages_per_chunk=4,
+                                    chunks_per_grid=3))
+    sel, npg = run_selector(w)
+    ref = sel.level.clone()
+    # scribble over chunk and grid rows, then rebuild only from a dirty page on
+    fd = torch.tensor([0, 5, 37, 10_000], dtype=torch.int32, device="cuda")
+    lay = sel.lay
+    sel.level[:, lay.chunk_row0:] = -7.0
+    kka.kka_build_levels(lay, sel.level, npg, fd)
+    torch.cuda.synchronize()
+    ppc, cpg = lay.pages_per_chunk, lay.chunks_per_grid
+    for s in range(w.S):
+        n_p = int(npg[s])
+        n_c = -(-n_p // ppc)
+        n_g = -(-n_c // cpg)
+        g0 = (int(fd[s]) // ppc) // cpg
+        for g in range(n_g):
+            rows_c = range(lay.chunk_row0 + g * cpg, lay.chunk_row0 + min(n_c, (g + 1) * cpg))
+            row_g = lay.grid_row0 + g
+            if g >= g0:
+                assert torch.equal(sel.level[s, row_g], ref[s, row_g])
+                for r in rows_c:
+                    assert torch.equal(sel.level[s, r], ref[s, r])
+            else:
+                assert (sel.level[s, row_g] == -7.0).all()
+
+
+def test_score_workspace_reuse_and_smaller_batch():
+    """The ticket words return to zero: a second call on the same workspace,
+    then a call with fewer sequences and pages, still match the oracle."""
+    say("score workspace reuse")
+    w = ragged_workload(11, 6, 2, 2, 64, 4, 100, 800,
+                        select=dict(hierarchical=1, k_grid=2, k_chunk=3, k_page=6, pages_per_chunk=4,
+                                    chunks_per_grid=3))
+    sel, npg = run_selector(w)
+    for _ in range(2):
+        sel.score(npg)
+        torch.cuda.synchronize()
+        for s in range(w.S):
+            check_selection(sel, s, int(npg[s]))
+    ws = sel.ws_score
+    lay2 = kka.LevelLayout(3, sel.lay.max_pages, w.D, True, 4, 3)
+    npg2 = torch.clamp(npg[:3] // 2, min=1)
+    level2 = sel.level[:3].contiguous()
+    kka.kka_build_levels(lay2, level2, npg2)
+    sel2 = Selector.__new__(Selector)
+    sel2.lay, sel2.sel, sel2.level, sel2.anchors = lay2, sel.sel, level2, sel.anchors[:3].contiguous()
+    sel2.page_idx, sel2.page_score = sel.page_idx[:3].contiguous(), sel.page_score[:3].contiguous()
+    sel2.n_selected, sel2.affinity = sel.n_selected[:3].contiguous(), sel.affinity[:3].contiguous()
+    sel2.ws_score = ws
+    sel2.score(npg2)
+    torch.cuda.synchronize()
+    for s in range(3):
+        check_selection(sel2, s, int(npg2[s]))
+
+
+def test_device_error_flags_bad_table_entries():
+    """Block-table entries outside the pool are skipped (zero vectors) and
+    reported through the device flag; nothing outside the pool is read."""
+    say("device error flags")
+    w = ragged_workload(12, 2, 2, 2, 64, 16, 40, 90)
+    w.block_table = w.block_table.copy()
+    w.block_table[1] = w.P + 5
+    kp, seqs = upload(w)
+    out = torch.full((w.total_blocks, w.D), 3.0, dtype=torch.float32, device="cuda")
+    kka.kka_pool_blocks(kp, seqs, out)
+    assert kka.kka_device_error() & kka.DEVERR_BLOCK_TABLE
+    assert (out[1] == 0).all()
+    assert kka.kka_device_error() == 0
+    lay = kka.LevelLayout(2, 8, w.D, True, 2, 2)
+    level = lay.new_buffer()
+    kka.kka_build_levels(lay, level, torch.tensor([3, 9], dtype=torch.int32, device="cuda"))
+    assert kka.kka_device_error() & kka.DEVERR_PAGES
+
+
+# ------------------------------------------------------------------ configs (reduced + full)
+
+def test_config1_parity_and_recovery():
+    say("config1")
+    w = synth.config1(0)
+    sel, npg = run_selector(w)
+    ref = oracle_vb(w, range(w.total_blocks))
+    got = vb_rows(sel, w)
+    for b in ref:
+        np.testing.assert_allclose(got[b], ref[b], atol=ATOL, rtol=0)
+    okp = oracle.KPool.of(w)
+    a = oracle.pool_anchor(okp, w.block_table, int(w.seq_len[0]), w.window)
+    np.testing.assert_allclose(sel.anchors[0].cpu().numpy(), a, atol=ATOL, rtol=0)
+    idx = check_selection(sel, 0, int(npg[0]), "c1")
+    prec = np.mean(w.block_topic[0][idx] == w.anchor_topic[0])
+    assert prec >= 0.75
+
+
+def test_config1_variance_mode_parity():
+    say("config1 variance")
+    w = synth.config1(0)
+    w.mode = "variance"
+    sel, npg = run_selector(w)
+    okp = oracle.KPool.of(w)
+    wref = oracle.weights_all(okp, w.seq_len, w.block_offsets, w.block_table)
+    np.testing.assert_allclose(sel.head_weight.cpu().numpy(), wref, rtol=WEIGHT_RTOL, atol=0)
+    ref = oracle_vb(w, range(w.total_blocks), wref)
+    got = vb_rows(sel, w)
+    for b in ref:
+        np.testing.assert_allclose(got[b], ref[b], atol=ATOL, rtol=0)
+    check_selection(sel, 0, int(npg[0]), "c1v")
+
+
+def test_config2_parity_and_recovery():
+    say("config2 (939 MB keys)")
+    w = synth.config2(0)
+    sel, npg = run_selector(w)
+    ref = oracle_vb(w, range(w.total_blocks))
+    got = vb_rows(sel, w)
+    for b in ref:
+        np.testing.assert_allclose(got[b], ref[b], atol=ATOL, rtol=0)
+    idx = check_selection(sel, 0, int(npg[0]), "c2")
+    assert (w.block_topic[0][idx[:8]] == w.anchor_topic[0]).all()
+
+
+def test_config3_full_size_sampled_parity_and_recovery():
+    """7B shape at 131072 tokens (3.76 GB of keys), launched exactly as the
+    benchmark launches it: sampled block vectors against the oracle, the
+    anchor, every level and affinity, and the selection."""
+    say("config3 generate (3.76 GB keys)")
+    w = synth.config3(0)
+    say("config3 run")
+    sel, npg = run_selector(w)
+    rng = np.random.default_rng(0)
+    sample = sorted(set(rng.choice(w.total_blocks, 96, replace=False).tolist()) | {0, w.total_blocks - 1})
+    ref = oracle_vb(w, sample)
+    got = vb_rows(sel, w)
+    for b in sample:
+        np.testing.assert_allclose(got[b], ref[b], atol=ATOL, rtol=0, err_msg=f"block {b}")
+    okp = oracle.KPool.of(w)
+    a = oracle.pool_anchor(okp, w.block_table, int(w.seq_len[0]), w.window)
+    np.testing.assert_allclose(sel.anchors[0].cpu().numpy(), a, atol=ATOL, rtol=0)
+    idx = check_selection(sel, 0, int(npg[0]), "c3")
+    run = w.extra["anchor_run"]
+    assert set(range(run * 32, run * 32 + 32)) <= set(idx.tolist())
+
+
+def test_config4_full_size_parity_and_recovery():
+    """64 sequences x 8192 fp32 block vectors written directly."""
+    say("config4")
+    v = synth.config4(0)
+    S, n_p, D = v.vb.shape
+    lay = kka.LevelLayout(S, n_p, D, True, 16, 16)
+    level = lay.new_buffer()
+    level[:, :n_p] = torch.from_numpy(v.vb).cuda()
+    npg = torch.full((S,), n_p, dtype=torch.int32, device="cuda")
+    kka.kka_build_levels(lay, level, npg)
+    sel = Selector.__new__(Selector)
+    sel.lay, sel.sel, sel.level = lay, v.select, level
+    sel.anchors = torch.from_numpy(v.anchors).cuda()
+    sel.page_idx = torch.zeros((S, 64), dtype=torch.int32, device="cuda")
+    sel.page_score = torch.zeros((S, 64), dtype=torch.float32, device="cuda")
+    sel.n_selected = torch.zeros(S, dtype=torch.int32, device="cuda")
+    sel.affinity = torch.zeros((S, lay.rows_per_seq), dtype=torch.float32, device="cuda")
+    sel.ws_score = kka.new_workspace(kka.kka_score_topk_workspace(lay, True))
+    sel.score(npg)
+    torch.cuda.synchronize()
+    for s in range(S):
+        idx = check_selection(sel, s, n_p, "c4")
+        assert (v.page_topic[s][idx] == v.anchor_topic[s]).all()
