@@ -1,0 +1,335 @@
+"""Benchmark of the Key-Key Semantic Affinity path on one MI355X.
+
+Timed step = the whole path over one batch of the 128K-context 7B-shape
+workload (28 layers x 4 KV heads x head_dim 128, 131072 tokens in blocks of
+16 = 8192 blocks behind a permuted block table, 3.76 GB of bf16 keys):
+block pooling -> anchor pooling -> grid/chunk vectors -> affinity of all
+8736 level rows + Grid->Chunk->Page top-4/16/64.  Inputs are resident in
+HBM before timing starts.  Also measured: the serving-scale decode step
+(score + top-K for 64 sequences x 8192 block vectors, rotating three
+buffer sets so no step finds its rows in the 256 MB last-level cache) and
+the CPU oracle on the same workload.
+
+Prints one JSON line.  Algorithmic bytes are counted once per launch:
+  K-pool   = sum(n_b * L * H * D * 2) + n_blocks * D * 4 + n_blocks * 4
+  anchor   = W * L * H * D * 2 + D * 4
+  levels   = n_pages * D * 4 + (n_chunks + n_grids) * D * 4
+  score    = rows * D * 4 + S * D * 4 + rows * 4 + S * k_page * 8
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "K-pool HBM GB/s (% peak); score+top-K µs/decode step, 7B shape @128K ctx"
+COUNTERS = os.path.join(ROOT, "profiles", "kpool_c3_hbm_counters.json")
+
+
+def kernel_source_hash(name: str) -> str:
+    with open(os.path.join(ROOT, "kv_cache_block_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def kpool_bytes(w) -> int:
+    import numpy as np
+    B = w.B
+    n_tok = 0
+    for s in range(w.S):
+        n_tok += int(w.seq_len[s])
+    nb = w.total_blocks
+    return n_tok * w.L * w.H * w.D * 2 + nb * w.D * 4 + nb * 4
+
+
+def score_bytes(S, rows, D, k_page) -> int:
+    return S * rows * D * 4 + S * D * 4 + S * rows * 4 + S * k_page * 8
+
+
+def traffic_from_counters(algo_bytes_unused=None):
+    """HBM bytes per K-pool launch from the committed rocprofv3 counter runs,
+    if they were taken on the current kernel source; else None."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha256_16") != kernel_source_hash("kka_pool.hip"):
+        return None
+    return c.get("traffic_bytes_per_launch")
+
+
+def run(args):
+    import numpy as np
+    import torch
+
+    import kv_cache_block_amd as kka
+    import synth
+    from kv_cache_block_amd.pipeline import Selector
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    # ---------------------------------------------------------------- c3 step
+    t_gen = time.perf_counter()
+    w = synth.config3(args.seed)
+    gen_s = time.perf_counter() - t_gen
+    k = torch.from_numpy(w.k.reshape(-1).view(np.int16)).to(dev)
+    kp = kka.KPool(k, w.L, w.H, w.D, w.B, w.P)
+    seqs = kka.Seqs(torch.from_numpy(w.seq_len).to(dev), torch.from_numpy(w.block_offsets).to(dev),
+                    torch.from_numpy(w.block_table).to(dev), w.total_blocks)
+    sel = Selector(kp, seqs, w.select, max_pages=w.total_blocks, window=w.window, device=dev)
+    npg = torch.tensor([w.total_blocks], dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        sel.pool()
+        if evs is not None:
+            evs[1].record(stream)
+        sel.anchor()
+        sel.levels(npg)
+        if evs is not None:
+            evs[2].record(stream)
+        sel.score(npg)
+        if evs is not None:
+            evs[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if kka.kka_device_error() != 0:
+        raise RuntimeError("device error flag raised during the benchmark")
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    pool_ms = [e[0].elapsed_time(e[1]) for e in events]
+    score_ms = [e[2].elapsed_time(e[3]) for e in events]
+    pool_us = 1e3 * float(np.mean(pool_ms))
+    c3_score_us = 1e3 * float(np.mean(score_ms))
+
+    n_p = w.total_blocks
+    n_c = -(-n_p // w.select["pages_per_chunk"])
+    n_g = -(-n_c // w.select["chunks_per_grid"])
+    rows = n_p + n_c + n_g
+    b_pool = kpool_bytes(w)
+    b_anchor = w.window * w.L * w.H * w.D * 2 + w.D * 4
+    b_levels = n_p * w.D * 4 + (n_c + n_g) * w.D * 4
+    b_score = score_bytes(1, rows, w.D, w.select["k_page"])
+    step_bytes = b_pool + b_anchor + b_levels + b_score
+    kpool_gbps = b_pool / (pool_us * 1e-6) / 1e9
+    step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # c3 oracle cross-check of this run's selection (cheap, on the GPU's affinities)
+    import oracle
+    aff = sel.affinity[0].cpu().numpy()
+    lay = sel.lay
+    idx_o, _ = oracle.select(aff[:n_p], aff[lay.chunk_row0:lay.chunk_row0 + n_c],
+                             aff[lay.grid_row0:lay.grid_row0 + n_g], **w.select)
+    if not np.array_equal(sel.page_idx[0, :len(idx_o)].cpu().numpy(), idx_o):
+        raise RuntimeError("benchmark selection differs from the oracle on the GPU's affinities")
+
+    del sel, k, kp
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- c4 decode step
+    v = synth.config4(args.seed)
+    S, NP, D = v.vb.shape
+    lay4 = kka.LevelLayout(S, NP, D, True, 16, 16)
+    npg4 = torch.full((S,), NP, dtype=torch.int32, device=dev)
+    n_sets = 3
+    levels = []
+    base = lay4.new_buffer(dev)
+    base[:, :NP] = torch.from_numpy(v.vb).to(dev)
+    kka.kka_build_levels(lay4, base, npg4)
+    levels.append(base)
+    for _ in range(n_sets - 1):
+        levels.append(base.clone())
+    anchors = torch.from_numpy(v.anchors).to(dev)
+    kp4 = v.select["k_page"]
+    idx4 = torch.zeros((S, kp4), dtype=torch.int32, device=dev)
+    sc4 = torch.zeros((S, kp4), dtype=torch.float32, device=dev)
+    cnt4 = torch.zeros(S, dtype=torch.int32, device=dev)
+    affs = [torch.zeros((S, lay4.rows_per_seq), dtype=torch.float32, device=dev) for _ in range(n_sets)]
+    ws4 = kka.new_workspace(kka.kka_score_topk_workspace(lay4, True), dev)
+
+    def score4(i):
+        kka.kka_score_topk(lay4, levels[i % n_sets], npg4, anchors, k_page=kp4, k_grid=v.select["k_grid"],
+                           k_chunk=v.select["k_chunk"], page_idx_out=idx4, page_score_out=sc4, n_selected_out=cnt4,
+                           affinity_out=affs[i % n_sets], workspace=ws4)
+
+    for i in range(max(3, args.warmup)):
+        score4(i)
+    torch.cuda.synchronize()
+    ev4 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev4[i][0].record(stream)
+        score4(i)
+        ev4[i][1].record(stream)
+    torch.cuda.synchronize()
+    c4_us = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in ev4]))
+    rows4 = lay4.rows_per_seq
+    b4 = score_bytes(S, rows4, D, kp4)
+    c4_gbps = b4 / (c4_us * 1e-6) / 1e9
+    # every sequence must select its planted topic
+    got = idx4.cpu().numpy()
+    recovered = int(sum((v.page_topic[s][got[s]] == v.anchor_topic[s]).all() for s in range(S)))
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, step_bytes, args.cpu_seconds)
+
+    traffic = traffic_from_counters()
+    out = {
+        "metric": METRIC,
+        "value": round(step_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "7B key shape (28 layers x 4 KV heads x head_dim 128), 131072-token context, "
+                        "block 16 = 8192 blocks behind a permuted block table, bf16 keys, 256 planted topics; "
+                        "uniform pooling, anchor = last 16 tokens, grid/chunk/page 16x16, top 4/16/64",
+            "step": "pool all blocks + anchor + build levels + score all 8736 rows + hierarchical top-K",
+            "key_dtype": "bf16",
+            "accumulate_dtype": "f32",
+            "step_algorithmic_bytes": step_bytes,
+        },
+        "kpool_GBps": round(kpool_gbps, 2),
+        "kpool_frac_of_peak": round(kpool_gbps / PEAK_HBM_GBPS, 4),
+        "kpool_us": round(pool_us, 2),
+        "kpool_algorithmic_bytes": b_pool,
+        "score_topk_us_per_step": round(c3_score_us, 2),
+        "serving_score_topk_us_per_step": round(c4_us, 2),
+        "serving_score_topk_GBps": round(c4_gbps, 2),
+        "serving_score_topk_frac_of_peak": round(c4_gbps / PEAK_HBM_GBPS, 4),
+        "serving_workload": "64 sequences x 8192 fp32 block vectors (D=128) + 512 chunk + 32 grid rows each, "
+                            "top 4/16/64, three rotating buffer sets (cold last-level cache)",
+        "serving_algorithmic_bytes": b4,
+        "serving_topic_recovered_seqs": recovered,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pool_kernel<uniform> (kka_pool_blocks)",
+            "achieved": round(kpool_gbps, 2),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(kpool_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+        },
+        "roofline_serving_score": {
+            "bound": "hbm",
+            "kernel": "score_topk_kernel (kka_score_topk)",
+            "achieved": round(c4_gbps, 2),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(c4_gbps / PEAK_HBM_GBPS, 4),
+        },
+        "cpu_baseline": cpu,
+        "generation_s": round(gen_s, 2),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, step_bytes, seconds):
+    """The oracle as it stands (single-threaded C) over the same workload:
+    whole steps (pool every block, anchor, levels, affinity, selection)
+    repeated until `seconds` have passed; GB/s on the step's algorithmic
+    bytes."""
+    import numpy as np
+    import oracle
+
+    kp = oracle.KPool.of(w)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        vb = oracle.pool_blocks(kp, w.seq_len, w.block_offsets, w.block_table)
+        pages = np.stack([vb[b] for b in range(w.total_blocks)])
+        a = oracle.pool_anchor(kp, w.block_table, int(w.seq_len[0]), w.window)
+        oracle.score_select(pages, a, w.select)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    gbps = reps * step_bytes / el / 1e9
+    return {"value": round(gbps, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} whole step(s) of the same 131072-token workload ({reps * step_bytes / 1e9:.2f} GB "
+                      f"of algorithmic bytes) in {el:.1f} s on one host core",
+            "ms_per_step": round(el * 1e3 / reps, 1)}
+
+
+def profile_pass(args):
+    """Short run for hardware-counter passes: a plain 1 GiB device copy
+    (calibrates FETCH_SIZE / WRITE_SIZE against known bytes), then a few
+    K-pool and score launches on the same workload as the benchmark."""
+    import numpy as np
+    import torch
+
+    import kv_cache_block_amd as kka
+    import synth
+    from kv_cache_block_amd.pipeline import Selector
+
+    dev = "cuda:0"
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    w = synth.config3(args.seed)
+    k = torch.from_numpy(w.k.reshape(-1).view(np.int16)).to(dev)
+    kp = kka.KPool(k, w.L, w.H, w.D, w.B, w.P)
+    seqs = kka.Seqs(torch.from_numpy(w.seq_len).to(dev), torch.from_numpy(w.block_offsets).to(dev),
+                    torch.from_numpy(w.block_table).to(dev), w.total_blocks)
+    sel = Selector(kp, seqs, w.select, max_pages=w.total_blocks, window=w.window, device=dev)
+    npg = torch.tensor([w.total_blocks], dtype=torch.int32, device=dev)
+    for _ in range(3):
+        sel.step(npg)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_pass": "done", "copy_bytes": (1 << 28) * 4, "kpool_algorithmic_bytes":
+                      kpool_bytes(w), "kernel_source_sha256_16": kernel_source_hash("kka_pool.hip")}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true", help="short run for rocprofv3 counter passes")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the selection path is independent per sequence and per block, "
+              "and this library runs it on a single MI355X; shard sequences or blocks across processes for more GPUs. "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.profile_pass:
+        profile_pass(args)
+    else:
+        run(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -227,18 +227,19 @@ typedef struct kka_select {
  * exactly the fp32 values the affinity pass produced.
  *
  * anchors        device [num_seqs][head_dim] fp32, 16-byte aligned
- * affinity_out   device [num_seqs][rows_per_seq] fp32 or NULL; rows that are
- *                not present are left untouched
+ * affinity_out   device [num_seqs][rows_per_seq] fp32, 16-byte aligned, or
+ *                NULL; rows that are not present are left untouched
  * page_idx_out   device [num_seqs][k_page] int32 page index in its sequence,
  *                best first; slots past the kept count hold -1
  * page_score_out device [num_seqs][k_page] fp32 masked score, or NULL; slots
  *                past the kept count hold 0
  * n_selected_out device [num_seqs] int32 kept count, or NULL
  * workspace      device, 16-byte aligned, >= kka_score_topk_workspace()
- *                bytes, ZERO-FILLED before its first use; every completed
- *                call leaves it zero-filled again where that matters, so it
- *                can be reused by later calls ordered on one stream.  Calls
- *                that run concurrently must not share a workspace.
+ *                bytes: scratch affinities when affinity_out is NULL (size 0
+ *                and may be NULL otherwise).  Calls that run concurrently
+ *                must not share a workspace.
+ * Runs as two launches on `stream`: the scoring pass over every row, then
+ * one selecting work-group per sequence.
  */
 KKA_API kka_status kka_score_topk(const kka_level_layout* lay, const float* level_buf, const int32_t* n_pages,
                           const float* anchors, const kka_select* sel, float* affinity_out, int32_t* page_idx_out,

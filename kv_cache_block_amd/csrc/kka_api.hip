@@ -273,9 +273,7 @@ size_t kka_score_topk_workspace(const kka_level_layout* lay, const kka_select* s
   (void)sel;
   LevelGeom g;
   if (!level_geom(lay, g)) return 0;
-  size_t n = align256((size_t)lay->num_seqs * sizeof(uint32_t));
-  if (!with_affinity_out) n += align256((size_t)lay->num_seqs * (size_t)g.rows * sizeof(float));
-  return n;
+  return with_affinity_out ? 0 : align256((size_t)lay->num_seqs * (size_t)g.rows * sizeof(float));
 }
 
 kka_status kka_score_topk(const kka_level_layout* lay, const float* level_buf, const int32_t* n_pages,
@@ -294,8 +292,9 @@ kka_status kka_score_topk(const kka_level_layout* lay, const float* level_buf, c
   if (sel->k_page > 0 && !page_idx_out) return KKA_ERR_NULL;
   if (!aligned16(level_buf) || !aligned16(anchors)) return KKA_ERR_ALIGN;
   const size_t need = kka_score_topk_workspace(lay, sel, affinity_out != nullptr);
-  if (!workspace || workspace_bytes < need) return KKA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return KKA_ERR_ALIGN;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return KKA_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return KKA_ERR_ALIGN;
+  if (affinity_out && !aligned16(affinity_out)) return KKA_ERR_ALIGN;
   uint32_t* err = device_error_word();
   if (!err) return KKA_ERR_DEVICE;
   (void)hipGetLastError();
@@ -311,10 +310,7 @@ kka_status kka_score_topk(const kka_level_layout* lay, const float* level_buf, c
   a.c_cap = g.c_cap;
   a.n_pages = n_pages;
   a.anchors = anchors;
-  char* wsb = static_cast<char*>(workspace);
-  a.tickets = reinterpret_cast<uint32_t*>(wsb);
-  a.aff = affinity_out ? affinity_out
-                       : reinterpret_cast<float*>(wsb + align256((size_t)lay->num_seqs * sizeof(uint32_t)));
+  a.aff = affinity_out ? affinity_out : static_cast<float*>(workspace);
   a.k_g = lay->hierarchical ? sel->k_grid : 0;
   a.k_c = lay->hierarchical ? sel->k_chunk : 0;
   a.k_p = sel->k_page;

@@ -108,7 +108,6 @@ struct ScoreArgs {
   int32_t* idx_out;
   float* score_out;
   int32_t* cnt_out;
-  uint32_t* tickets;     // [S], zero between calls
   int32_t tiles_per_seq, rows_per_tile;
   uint32_t* err;
 };

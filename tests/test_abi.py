@@ -142,9 +142,8 @@ def test_level_rows_and_score_validation(L):
         assert L.kka_level_rows(ctypes.byref(bad)) == -1
     sel = kka.c_select(4, 16, 64)
     ws = L.kka_score_topk_workspace(ctypes.byref(lay), ctypes.byref(sel), 0)
-    assert ws >= 64 * 4 + 64 * 8736 * 4
-    ws_aff = L.kka_score_topk_workspace(ctypes.byref(lay), ctypes.byref(sel), 1)
-    assert 0 < ws_aff < ws
+    assert ws >= 64 * 8736 * 4  # scratch affinities
+    assert L.kka_score_topk_workspace(ctypes.byref(lay), ctypes.byref(sel), 1) == 0
 
     def score(lay_, sel_, lvl=FAKE, npg=FAKE, anc=FAKE, idx=FAKE, w=FAKE, wb=ws):
         return L.kka_score_topk(ctypes.byref(lay_), lvl, npg, anc, ctypes.byref(sel_), None, idx, None, None, w,

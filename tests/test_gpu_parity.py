@@ -292,8 +292,8 @@ def test_dirty_rebuild_equals_full_rebuild():
 
 
 def test_score_workspace_reuse_and_smaller_batch():
-    """The ticket words return to zero: a second call on the same workspace,
-    then a call with fewer sequences and pages, still match the oracle."""
+    """Repeated calls on the same buffers, then a call with fewer sequences
+    and pages on the same workspace, still match the oracle."""
     say("score workspace reuse")
     w = ragged_workload(11, 6, 2, 2, 64, 4, 100, 800,
                         select=dict(hierarchical=1, k_grid=2, k_chunk=3, k_page=6, pages_per_chunk=4,
