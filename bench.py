@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "K-pool HBM GB/s (% peak); score+top-K µs/decode step, 7B shape @128K ctx"
-COUNTERS = os.path.join(ROOT, "profiles", "kpool_c3_hbm_counters.json")
+COUNTERS = os.path.join(ROOT, "profiles", "kpool_7b_128k_hbm_counters.json")
 
 
 def kernel_source_hash(name: str) -> str:
@@ -310,6 +310,77 @@ def profile_pass(args):
                       kpool_bytes(w), "kernel_source_sha256_16": kernel_source_hash("kka_pool.hip")}), flush=True)
 
 
+def _short(name: str) -> str:
+    name = name.replace("void ", "").replace("kka::(anonymous namespace)::", "")
+    return name.split("(kka::")[0] if "(kka::" in name else name[:60]
+
+
+def write_counter_summary(fetch_csv: str, write_csv: str, out_json: str, command: str):
+    """Per-dispatch HBM bytes of the K-pool kernel from two rocprofv3 --pmc
+    runs of --profile-pass (FETCH_SIZE, then WRITE_SIZE, in KiB), each scaled
+    by what the same counter reads for the plain 1 GiB device copy that the
+    profile pass runs first (known bytes: 1 GiB read and 1 GiB written)."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            out.setdefault((r["Kernel_Name"], r["Grid_Size"]), []).append(float(r["Counter_Value"]))
+        return out
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    copy_bytes = float(1 << 30)
+    copy_key = [k for k in f if "copyBuffer" in k[0] and max(f[k]) > 4e5]
+    if not copy_key:
+        raise SystemExit("no 1 GiB copy dispatch found in the counter run")
+    fetch_factor = copy_bytes / (statistics.median(f[copy_key[0]]) * 1024.0)
+    write_factor = copy_bytes / (statistics.median(w[copy_key[0]]) * 1024.0)
+    pool = [k for k in f if "pool_kernel" in k[0]]
+    kernels = {}
+    for k in f:
+        if "kka::" not in k[0]:
+            continue
+        fk = statistics.mean(f[k]) * 1024.0 * fetch_factor
+        wk = statistics.mean(w.get(k, [0.0])) * 1024.0 * write_factor
+        kernels[f"{_short(k[0])} grid={k[1]}"] = {"fetch_bytes": round(fk), "write_bytes": round(wk),
+                                                  "dispatches": len(f[k])}
+    pk = pool[0]
+    traffic = statistics.mean(f[pk]) * 1024.0 * fetch_factor + statistics.mean(w[pk]) * 1024.0 * write_factor
+    summary = {
+        "kernel": _short(pk[0]),
+        "workload": "7B key shape, 131072 tokens, block 16 (8192 blocks), uniform pooling",
+        "kernel_source_sha256_16": kernel_source_hash("kka_pool.hip"),
+        "fetch_factor": round(fetch_factor, 5),
+        "write_factor": round(write_factor, 5),
+        "traffic_bytes_per_launch": round(traffic),
+        "kpool_algorithmic_bytes": 3762323456,
+        "traffic_over_algorithmic": round(traffic / 3762323456, 5),
+        "per_kernel": kernels,
+        "commands": command,
+    }
+    with open(out_json, "w") as fh:
+        json.dump(summary, fh, indent=1)
+    print(json.dumps({"traffic_bytes_per_launch": summary["traffic_bytes_per_launch"],
+                      "fetch_factor": summary["fetch_factor"], "write_factor": summary["write_factor"]}))
+
+
+def write_stats_summary(stats_csv: str, out_md: str, title: str, command: str = ""):
+    """Markdown table of a rocprofv3 --kernel-trace --stats kernel summary."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```", command, "```",
+             "", "| kernel | calls | average us | min us | max us | share % |", "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -319,7 +390,18 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true", help="short run for rocprofv3 counter passes")
+    ap.add_argument("--write-counter-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
+                    help="summarise two rocprofv3 --pmc runs of --profile-pass (no GPU needed)")
+    ap.add_argument("--write-stats-summary", nargs=3, metavar=("STATS_CSV", "OUT_MD", "TITLE"),
+                    help="summarise a rocprofv3 --kernel-trace --stats run (no GPU needed)")
+    ap.add_argument("--command", default="", help="command line recorded in a summary")
     args = ap.parse_args()
+    if args.write_counter_summary:
+        write_counter_summary(*args.write_counter_summary, command=args.command)
+        return
+    if args.write_stats_summary:
+        write_stats_summary(*args.write_stats_summary, command=args.command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the selection path is independent per sequence and per block, "
               "and this library runs it on a single MI355X; shard sequences or blocks across processes for more GPUs. "

@@ -10,55 +10,93 @@
 // by HBM bandwidth.  Each sequence's present rows are cut into tiles spread
 // over the whole chip; in a tile, 8 lanes share one row (each lane reads
 // 16-byte pieces 128 bytes apart, so 8 lanes read whole 128-byte lines) and
-// every lane keeps 16 loads in flight.  Dot product and row norm are reduced
-// over the 8 lanes with a fixed butterfly.  No cross-group communication:
-// the kernel boundary publishes the affinities.
+// every lane keeps 8 non-temporal loads in flight (rows are read once per
+// step; a serving batch's level rows exceed the last-level cache anyway).
+// Dot product and row norm are reduced over the 8 lanes with a fixed
+// butterfly.  No cross-group communication: the kernel boundary publishes
+// the affinities.
 //
-// select_kernel: one work-group per sequence.  The sequence's affinity rows
-// are staged into LDS with one coalesced pass, then each level is selected
-// from LDS: candidates (children of kept parents, or every row) with a
-// positive score are compacted with wave ballots; up to 512 of them are
-// ranked directly (rank = number of larger keys, so rank < k places the
-// element at its final position); larger sets use an MSB-first radix select.
-// Keys are (affinity bits << 32 | ~index): unique, and larger means higher
-// score then lower index.  When fewer than k candidates score above zero,
-// the lowest-index rows scoring exactly 0 (masked or zero affinity) fill the
-// remaining slots in index order.
+// select_kernel: one work-group per sequence, written for latency: the
+// sequence's whole affinity row block is staged into LDS in one round of
+// loads, then each level is selected from LDS: candidates (children of kept
+// parents, or every row) with a positive score are compacted with wave
+// ballots; up to 512 of them are ranked directly (rank = number of larger
+// keys, so rank < k places the element at its final position); larger sets
+// use an MSB-first radix select.  Keys are (affinity bits << 32 | ~index):
+// unique, and larger means higher score then lower index.  When fewer than
+// k candidates score above zero, the lowest-index rows scoring exactly 0
+// (masked or zero affinity) fill the remaining slots in index order.
 #include "kka_internal.h"
 
 namespace kka {
 namespace {
 
-constexpr int kSelThreads = 256;
+#ifndef KKA_SELECT_THREADS
+#define KKA_SELECT_THREADS 512
+#endif
+constexpr int kSelThreads = KKA_SELECT_THREADS;
 constexpr int kRankMax = 512;
 constexpr int kLdsRows = 9216;  // affinity rows staged per sequence (36 KB)
+constexpr int kBitmapWords = kMaxParents / 32;
+
+// float4 row loads each lane keeps in flight in the scoring pass, and how
+// many passes of the row-groups one scoring work-group makes.
+#ifndef KKA_SCORE_LOADS
+#define KKA_SCORE_LOADS 8
+#endif
+#ifndef KKA_SCORE_PASSES
+#define KKA_SCORE_PASSES 1
+#endif
+// lanes sharing one row, and whether row loads bypass cache allocation
+#ifndef KKA_SCORE_LPR
+#define KKA_SCORE_LPR 8
+#endif
+#ifndef KKA_SCORE_NT
+#define KKA_SCORE_NT 1
+#endif
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 load_row4(const f32x4* p) {
+#if KKA_SCORE_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
 
 struct SelectShared {
   float aff[kLdsRows];
   uint64_t ck[kRankMax];
   uint64_t buf[kMaxK];
-  uint32_t bitmap[kMaxParents / 32];
+  uint32_t kept_grid[kBitmapWords];   // grids kept (parents of chunks)
+  uint32_t kept_chunk[kBitmapWords];  // chunks kept (parents of pages)
   int32_t plist[kMaxK];
   uint32_t hist[256];
   uint32_t digit, above, bucket;
-  int32_t cnt;
-  int32_t np_sel;
+  int32_t cnt[4];
   int32_t wave_tot[kSelThreads / 64];
 };
 
 struct Level {
-  const float* aff;  // score of element e is aff[e] when live (LDS or global)
-  int32_t n;         // elements in the level
-  int32_t fanout;    // children per parent; 0 = no parent level (all live)
-  int32_t n_par;     // kept parents listed in plist (fanout > 0)
+  const float* aff;        // global scores: element e at aff[e] (used when not staged)
+  int32_t off;             // row offset of element 0 in the staged LDS copy
+  bool staged;             // read scores from sm.aff[off + e]
+  int32_t n;               // elements in the level
+  int32_t fanout;          // children per parent; 0 = no parent level (all live)
+  int32_t n_par;           // kept parents listed in plist (fanout > 0)
+  const uint32_t* parent;  // keep flags of the parent level (fanout > 0)
+  int32_t slot;            // counter of sm.cnt this level uses
 };
 
-__device__ __forceinline__ uint32_t aff_key(const Level& L, int32_t e) { return __float_as_uint(L.aff[e]); }
+__device__ __forceinline__ uint32_t aff_key(const Level& L, const SelectShared& sm, int32_t e) {
+  return __float_as_uint(L.staged ? sm.aff[L.off + e] : L.aff[e]);
+}
 
-__device__ __forceinline__ bool is_live(const Level& L, const SelectShared& sm, int32_t e) {
+__device__ __forceinline__ bool is_live(const Level& L, int32_t e) {
   if (L.fanout == 0) return true;
   const int32_t p = e / L.fanout;
-  return (sm.bitmap[p >> 5] >> (p & 31)) & 1u;
+  return (L.parent[p >> 5] >> (p & 31)) & 1u;
 }
 
 // Candidate c -> element index (or -1 when past the level's end).
@@ -66,6 +104,13 @@ __device__ __forceinline__ int32_t cand(const Level& L, const SelectShared& sm, 
   if (L.fanout == 0) return (int32_t)c;
   const int32_t pi = (int32_t)(c / L.fanout);
   const int32_t e = sm.plist[pi] * L.fanout + (int32_t)(c - (int64_t)pi * L.fanout);
+  return e < L.n ? e : -1;
+}
+
+__device__ __forceinline__ int32_t cand32(const Level& L, const SelectShared& sm, int32_t c) {
+  if (L.fanout == 0) return c;
+  const int32_t pi = c / L.fanout;
+  const int32_t e = sm.plist[pi] * L.fanout + (c - pi * L.fanout);
   return e < L.n ? e : -1;
 }
 
@@ -130,12 +175,12 @@ __device__ void radix_top(const Level& L, int64_t m, int32_t k_eff, SelectShared
   uint64_t prefix = 0, mask = 0;
   int32_t kk = k_eff;
   for (int shift = 56; shift >= 0; shift -= 8) {
-    sm.hist[tid] = 0u;
+    for (int b = tid; b < 256; b += kSelThreads) sm.hist[b] = 0u;
     __syncthreads();
     for (int64_t c = tid; c < m; c += kSelThreads) {
       const int32_t e = cand(L, sm, c);
       if (e < 0) continue;
-      const uint32_t key = aff_key(L, e);
+      const uint32_t key = aff_key(L, sm, e);
       if (key == 0u) continue;
       const uint64_t comp = composite(key, e);
       if ((comp & mask) == prefix) atomicAdd(&sm.hist[(uint32_t)(comp >> shift) & 255u], 1u);
@@ -150,16 +195,16 @@ __device__ void radix_top(const Level& L, int64_t m, int32_t k_eff, SelectShared
     __syncthreads();
     if (done) break;
   }
-  if (tid == 0) sm.cnt = 0;
+  if (tid == 0) sm.cnt[3] = 0;
   __syncthreads();
   for (int64_t c = tid; c < m; c += kSelThreads) {
     const int32_t e = cand(L, sm, c);
     if (e < 0) continue;
-    const uint32_t key = aff_key(L, e);
+    const uint32_t key = aff_key(L, sm, e);
     if (key == 0u) continue;
     const uint64_t comp = composite(key, e);
     if (comp >= prefix) {
-      const int32_t slot = atomicAdd(&sm.cnt, 1);
+      const int32_t slot = atomicAdd(&sm.cnt[3], 1);
       if (slot < k_eff) sm.buf[slot] = comp;
     }
   }
@@ -167,59 +212,18 @@ __device__ void radix_top(const Level& L, int64_t m, int32_t k_eff, SelectShared
   sort_desc(sm, k_eff);
 }
 
-// Keeps the top min(k, n) elements of a level, sorted, in sm.buf.
-__device__ int32_t select_level(const Level& L, int32_t k, SelectShared& sm) {
+// When only P < k_eff candidates score above zero, the lowest-index rows
+// scoring exactly 0 (masked, or live with zero affinity) take slots
+// P .. k_eff-1 of sm.buf in index order.
+__device__ void fill_zeros(const Level& L, SelectShared& sm, int32_t P, int32_t k_eff) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
-  const int32_t k_eff = k < L.n ? k : L.n;
-  if (k_eff <= 0) return 0;
-  const int64_t m = L.fanout ? (int64_t)L.n_par * L.fanout : (int64_t)L.n;
-  if (tid == 0) sm.cnt = 0;
-  __syncthreads();
-  // compact the candidates scoring above zero
-  for (int64_t c0 = 0; c0 < m; c0 += kSelThreads) {
-    const int64_t c = c0 + tid;
-    const int32_t e = c < m ? cand(L, sm, c) : -1;
-    const uint32_t key = e >= 0 ? aff_key(L, e) : 0u;
-    const bool pos = key != 0u;
-    const uint64_t bal = __ballot(pos);
-    int32_t base = 0;
-    if (lane == 0 && bal) base = atomicAdd(&sm.cnt, (int32_t)__popcll(bal));
-    base = __shfl(base, 0, 64);
-    const int32_t slot = base + (int32_t)__popcll(bal & lt_mask);
-    if (pos && slot < kRankMax) sm.ck[slot] = composite(key, e);
-  }
-  __syncthreads();
-  const int32_t P = sm.cnt;
-  __syncthreads();
-  if (P > kRankMax) {
-    // too many to rank: radix select the top k_eff, or (when k_eff is larger
-    // still) all P positive candidates, sorted; zeros fill the rest below
-    const int32_t take = P >= k_eff ? k_eff : P;
-    radix_top(L, m, take, sm);
-    if (P >= k_eff) return k_eff;
-  } else {
-    // rank the positive candidates: rank r goes to slot r when r < k_eff
-    for (int32_t i = tid; i < P; i += kSelThreads) {
-      const uint64_t x = sm.ck[i];
-      int32_t r = 0;
-      int32_t j = 0;
-      for (; j + 4 <= P; j += 4)
-        r += (int32_t)(sm.ck[j] > x) + (int32_t)(sm.ck[j + 1] > x) + (int32_t)(sm.ck[j + 2] > x) +
-             (int32_t)(sm.ck[j + 3] > x);
-      for (; j < P; ++j) r += (int32_t)(sm.ck[j] > x);
-      if (r < k_eff) sm.buf[r] = x;
-    }
-    __syncthreads();
-    if (P >= k_eff) return k_eff;
-  }
-  // lowest-index rows scoring exactly 0 fill the remaining slots, in order
   const int32_t need = k_eff - P;
   int32_t found = 0;
   for (int32_t e0 = 0; e0 < L.n && found < need; e0 += kSelThreads) {
     const int32_t e = e0 + tid;
-    const bool zero = e < L.n && (!is_live(L, sm, e) || aff_key(L, e) == 0u);
+    const bool zero = e < L.n && (!is_live(L, e) || aff_key(L, sm, e) == 0u);
     const uint64_t bal = __ballot(zero);
     if (lane == 0) sm.wave_tot[wave] = (int32_t)__popcll(bal);
     __syncthreads();
@@ -233,20 +237,134 @@ __device__ int32_t select_level(const Level& L, int32_t k, SelectShared& sm) {
     found += tot;
     __syncthreads();
   }
+}
+
+// Keeps the top min(k, n) elements of a level with more candidates than
+// threads, sorted, in sm.buf.  sm.cnt[L.slot] must be zero on entry.
+__device__ int32_t select_level_big(const Level& L, int32_t k, SelectShared& sm) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  const int32_t k_eff = k < L.n ? k : L.n;
+  if (k_eff <= 0) return 0;
+  const int64_t m = L.fanout ? (int64_t)L.n_par * L.fanout : (int64_t)L.n;
+  int32_t* cnt = &sm.cnt[L.slot];
+  // compact the candidates scoring above zero
+  for (int64_t c0 = 0; c0 < m; c0 += kSelThreads) {
+    const int64_t c = c0 + tid;
+    const int32_t e = c < m ? cand(L, sm, c) : -1;
+    const uint32_t key = e >= 0 ? aff_key(L, sm, e) : 0u;
+    const bool pos = key != 0u;
+    const uint64_t bal = __ballot(pos);
+    int32_t base = 0;
+    if (lane == 0 && bal) base = atomicAdd(cnt, (int32_t)__popcll(bal));
+    base = __shfl(base, 0, 64);
+    const int32_t slot = base + (int32_t)__popcll(bal & lt_mask);
+    if (pos && slot < kRankMax) sm.ck[slot] = composite(key, e);
+  }
+  __syncthreads();
+  const int32_t P = *cnt;
+  if (P > kRankMax) {
+    // too many to rank: radix select the top k_eff, or (when k_eff is larger
+    // still) all P positive candidates, sorted; zeros fill the rest below
+    const int32_t take = P >= k_eff ? k_eff : P;
+    radix_top(L, m, take, sm);
+    if (P >= k_eff) return k_eff;
+  } else {
+    // rank the positive candidates: rank r goes to slot r when r < k_eff.
+    // tpc consecutive lanes share a candidate, each counting a strided part
+    // with 8 LDS reads in flight.
+    int32_t tpc = 1;
+    while (tpc < 16 && P * tpc * 2 <= kSelThreads) tpc <<= 1;
+    for (int32_t t0 = 0; t0 < P * tpc; t0 += kSelThreads) {
+      const int32_t t = t0 + tid;
+      const int32_t i = t / tpc, q = t - i * tpc;
+      const uint64_t x = i < P ? sm.ck[i] : ~0ull;
+      int32_t r = 0;
+      int32_t j = q;
+      for (; j + 7 * tpc < P; j += 8 * tpc) {
+        uint64_t y[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) y[u] = sm.ck[j + u * tpc];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) r += (int32_t)(y[u] > x);
+      }
+      for (; j < P; j += tpc) r += (int32_t)(sm.ck[j] > x);
+      for (int32_t o = 1; o < tpc; o <<= 1) r += __shfl_xor(r, o);
+      if (q == 0 && i < P && r < k_eff) sm.buf[r] = x;
+    }
+    __syncthreads();
+    if (P >= k_eff) return k_eff;
+  }
+  fill_zeros(L, sm, P, k_eff);
   return k_eff;
 }
 
-// Marks the kept elements of a level as parents of the next one.
-__device__ void keep_parents(SelectShared& sm, int32_t k_eff, int32_t n_parents) {
+// Number of entries of a strictly descending 64-entry run that exceed x.
+__device__ __forceinline__ int32_t count_above(const uint64_t* run, uint64_t x) {
+  int32_t pos = 0;
+#pragma unroll
+  for (int step = 32; step > 0; step >>= 1)
+    if (run[pos + step - 1] > x) pos += step;
+  return (pos == 63 && run[63] > x) ? 64 : pos;
+}
+
+// Keeps the top min(k, n) elements of a level, sorted, in sm.buf.
+// Levels with at most kSelThreads candidates hold one candidate per lane:
+// each wave ranks its 64 keys with register broadcasts and stores them as a
+// descending run; a key's rank in the level is its rank in its own run plus,
+// for every other run, how many of that run's keys exceed it (binary search).
+// Lanes without a positive-score candidate carry distinct keys below every
+// positive one, so every run is strictly ordered.
+__device__ int32_t select_level(const Level& L, int32_t k, SelectShared& sm) {
+  const int32_t k_eff = k < L.n ? k : L.n;
+  if (k_eff <= 0) return 0;
+  const int64_t m = L.fanout ? (int64_t)L.n_par * L.fanout : (int64_t)L.n;
+  if (m > kSelThreads) return select_level_big(L, k, sm);
   const int tid = threadIdx.x;
-  for (int32_t w = tid; w < (n_parents + 31) / 32; w += kSelThreads) sm.bitmap[w] = 0u;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int32_t n_runs = (int32_t)((m + 63) >> 6);
+  const int32_t e = tid < m ? cand32(L, sm, tid) : -1;
+  const uint32_t key = e >= 0 ? aff_key(L, sm, e) : 0u;
+  // positive keys: (bits << 32 | ~index); others sort below: (~index) or tid
+  const uint64_t x = e >= 0 ? composite(key, e) : (uint64_t)tid;
+  const uint64_t bal = __ballot(key != 0u);
+  if (lane == 0) sm.wave_tot[wave] = (int32_t)__popcll(bal);
+  int32_t r = 0;
+  if (wave < n_runs) {
+    const uint32_t xlo = (uint32_t)x, xhi = (uint32_t)(x >> 32);
+#pragma unroll 16
+    for (int j = 0; j < 64; ++j) {
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)xlo, j);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)xhi, j);
+      r += (int32_t)((((uint64_t)hi << 32) | lo) > x);
+    }
+    sm.ck[(wave << 6) + r] = x;
+  }
   __syncthreads();
+  int32_t P = 0;
+  for (int w = 0; w < n_runs; ++w) P += sm.wave_tot[w];
+  if (wave < n_runs && key != 0u) {
+    int32_t R = r;
+    for (int w = 0; w < n_runs; ++w)
+      if (w != wave) R += count_above(sm.ck + (w << 6), x);
+    if (R < k_eff) sm.buf[R] = x;
+  }
+  __syncthreads();
+  if (P < k_eff) fill_zeros(L, sm, P, k_eff);
+  return k_eff;
+}
+
+// Records the kept elements of a level (sm.buf[0, k_eff)) as the parents of
+// the next level: their indices in plist and their bits in `kept` (clear on
+// entry).
+__device__ void keep_parents(SelectShared& sm, int32_t k_eff, uint32_t* kept) {
+  const int tid = threadIdx.x;
   for (int32_t i = tid; i < k_eff; i += kSelThreads) {
     const int32_t e = (int32_t)(~(uint32_t)sm.buf[i]);
     sm.plist[i] = e;
-    atomicOr(&sm.bitmap[e >> 5], 1u << (e & 31));
+    atomicOr(&kept[e >> 5], 1u << (e & 31));
   }
-  if (tid == 0) sm.np_sel = k_eff;
   __syncthreads();
 }
 
@@ -266,35 +384,82 @@ __device__ __forceinline__ SeqGeom seq_geom(const ScoreArgs& a, int32_t s, bool 
   return g;
 }
 
+// Copies a sequence's whole affinity row block src[0, n) (n <= kLdsRows)
+// into LDS with one round of loads, every load issued before the first
+// store; 16-byte pieces when src is 16-byte aligned.  Rows that are not
+// present are copied too and never read.
+__device__ void stage_rows(float* dst, const float* src, int32_t n) {
+  constexpr int U = (kLdsRows / 4 + kSelThreads - 1) / kSelThreads;
+  const int tid = threadIdx.x;
+  int32_t done = 0;
+  if ((((uintptr_t)src) & 15u) == 0) {
+    const int32_t n4 = n >> 2;
+    const float4* s4 = reinterpret_cast<const float4*>(src);
+    float4* d4 = reinterpret_cast<float4*>(dst);
+    if (n4 > 0) {
+      // Clamped indices make every load and store unconditional, so all U
+      // loads are in flight before the first store; the clamped copies write
+      // the value the last slot holds anyway.
+      float4 t[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) t[u] = s4[min(u * kSelThreads + tid, n4 - 1)];
+#pragma unroll
+      for (int u = 0; u < U; ++u) d4[min(u * kSelThreads + tid, n4 - 1)] = t[u];
+    }
+    done = n4 << 2;
+  }
+  for (int32_t r0 = done; r0 < n; r0 += 8 * kSelThreads) {
+    float t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = src[min(r0 + u * kSelThreads + tid, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dst[min(r0 + u * kSelThreads + tid, n - 1)] = t[u];
+  }
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_kernel(ScoreArgs a) {
   __shared__ SelectShared sm;
   const int tid = threadIdx.x;
   const int32_t s = blockIdx.x;
-  const SeqGeom g = seq_geom(a, s, false);
   const float* aff = a.aff + (int64_t)s * a.rows_per_seq;
-  const float* base = aff;
-  if (a.rows_per_seq <= kLdsRows) {
-    // stage the present rows of every level at their row offsets
-    for (int32_t r = tid; r < g.n_p; r += kSelThreads) sm.aff[r] = aff[r];
-    for (int32_t r = tid; r < g.n_c; r += kSelThreads) sm.aff[a.max_pages + r] = aff[a.max_pages + r];
-    for (int32_t r = tid; r < g.n_g; r += kSelThreads)
-      sm.aff[a.max_pages + a.c_cap + r] = aff[a.max_pages + a.c_cap + r];
-    __syncthreads();
-    base = sm.aff;
-  }
-  int32_t kp;
+  const bool staged = a.rows_per_seq <= kLdsRows;
+  if (staged) stage_rows(sm.aff, aff, (int32_t)a.rows_per_seq);
+  const SeqGeom g = seq_geom(a, s, false);
+  if (tid < 4) sm.cnt[tid] = 0;
   if (a.hier) {
-    Level G{base + a.max_pages + a.c_cap, g.n_g, 0, 0};
-    const int32_t kg = select_level(G, a.k_g, sm);
-    keep_parents(sm, kg, g.n_g);
-    Level C{base + a.max_pages, g.n_c, a.cpg, sm.np_sel};
-    const int32_t kc = select_level(C, a.k_c, sm);
-    keep_parents(sm, kc, g.n_c);
-    Level Pg{base, g.n_p, a.ppc, sm.np_sel};
-    kp = select_level(Pg, a.k_p, sm);
-  } else {
-    Level Pg{base, g.n_p, 0, 0};
-    kp = select_level(Pg, a.k_p, sm);
+    for (int32_t w = tid; w < (g.n_g + 31) / 32; w += kSelThreads) sm.kept_grid[w] = 0u;
+    for (int32_t w = tid; w < (g.n_c + 31) / 32; w += kSelThreads) sm.kept_chunk[w] = 0u;
+  }
+  __syncthreads();
+  // Levels run as one loop so a single copy of the level code is fetched
+  // (a lone work-group per compute unit starts with a cold instruction cache).
+  int32_t kp = 0;
+  const int32_t first = a.hier ? 0 : 2;
+  for (int32_t lev = first; lev < 3; ++lev) {
+    Level L;
+    L.staged = staged;
+    L.slot = lev;
+    if (lev == 0) {  // grids: every row is a candidate
+      L.off = a.max_pages + a.c_cap;
+      L.n = g.n_g;
+      L.fanout = 0;
+      L.parent = nullptr;
+    } else if (lev == 1) {  // chunks of kept grids
+      L.off = a.max_pages;
+      L.n = g.n_c;
+      L.fanout = a.cpg;
+      L.parent = sm.kept_grid;
+    } else {  // pages of kept chunks, or every page when flat
+      L.off = 0;
+      L.n = g.n_p;
+      L.fanout = a.hier ? a.ppc : 0;
+      L.parent = sm.kept_chunk;
+    }
+    L.aff = aff + L.off;
+    L.n_par = kp;
+    const int32_t k = lev == 0 ? a.k_g : (lev == 1 ? a.k_c : a.k_p);
+    kp = select_level(L, k, sm);
+    if (lev < 2) keep_parents(sm, kp, lev == 0 ? sm.kept_grid : sm.kept_chunk);
   }
   for (int32_t i = tid; i < a.k_p; i += kSelThreads) {
     int32_t idx = -1;
@@ -317,8 +482,9 @@ __device__ __forceinline__ float affinity_of(float dot, float nr, float sqrt_na,
   return v > 0.f ? (v < 1.f ? v : 1.f) : 0.f;
 }
 
-template <int NQ, int R>
+template <int LPR, int NQ, int R>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+  constexpr int NG = 256 / LPR;  // row groups per work-group
   const int tid = threadIdx.x;
   const int32_t s = blockIdx.x / a.tiles_per_seq;
   const int32_t tile = blockIdx.x - s * a.tiles_per_seq;
@@ -328,33 +494,32 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   if (v0 >= nv) return;
   const int32_t v1 = min(nv, v0 + a.rows_per_tile);
   const int32_t Q = a.D >> 2;
-  const float4* seq = reinterpret_cast<const float4*>(a.lvl + (int64_t)s * a.rows_per_seq * a.D);
+  const f32x4* seq = reinterpret_cast<const f32x4*>(a.lvl + (int64_t)s * a.rows_per_seq * a.D);
   float* aff = a.aff + (int64_t)s * a.rows_per_seq;
 
-  const int32_t grp = tid >> 3, lg = tid & 7;
-  float4 av[NQ];
+  const int32_t grp = tid / LPR, lg = tid % LPR;
+  f32x4 av[NQ];
   float na = 0.f;
-  const float4* anc = reinterpret_cast<const float4*>(a.anchors + (int64_t)s * a.D);
+  const f32x4* anc = reinterpret_cast<const f32x4*>(a.anchors + (int64_t)s * a.D);
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
-    const int32_t qi = lg + 8 * j;
-    av[j] = qi < Q ? anc[qi] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int32_t qi = lg + LPR * j;
+    av[j] = qi < Q ? anc[qi] : f32x4{0.f, 0.f, 0.f, 0.f};
     na = fmaf(av[j].x, av[j].x, na);
     na = fmaf(av[j].y, av[j].y, na);
     na = fmaf(av[j].z, av[j].z, na);
     na = fmaf(av[j].w, av[j].w, na);
   }
-  na += __shfl_xor(na, 1);
-  na += __shfl_xor(na, 2);
-  na += __shfl_xor(na, 4);
+#pragma unroll
+  for (int o = 1; o < LPR; o <<= 1) na += __shfl_xor(na, o);
   const float sqrt_na = sqrtf(na);
 
-  for (int32_t v = v0 + grp; v < v1; v += 32 * R) {
-    float4 x[R][NQ];
+  for (int32_t v = v0 + grp; v < v1; v += NG * R) {
+    f32x4 x[R][NQ];
     int64_t row[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int32_t vr = v + 32 * r;
+      const int32_t vr = v + NG * r;
       const bool ok = vr < v1;
       row[r] = !ok ? 0
                : vr < g.n_p ? vr
@@ -362,8 +527,11 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
                                     : (int64_t)a.max_pages + a.c_cap + (vr - g.n_p - g.n_c);
 #pragma unroll
       for (int j = 0; j < NQ; ++j) {
-        const int32_t qi = lg + 8 * j;
-        x[r][j] = (ok && qi < Q) ? seq[row[r] * Q + qi] : make_float4(0.f, 0.f, 0.f, 0.f);
+        // unconditional load from a clamped, in-bounds address (row 0 stands
+        // in for a row past the tile, which is never written back)
+        const int32_t qi = lg + LPR * j;
+        const f32x4 t = load_row4(seq + row[r] * Q + min(qi, Q - 1));
+        x[r][j] = qi < Q ? t : f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
 #pragma unroll
@@ -380,22 +548,21 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         nr = fmaf(x[r][j].z, x[r][j].z, nr);
         nr = fmaf(x[r][j].w, x[r][j].w, nr);
       }
-      dot += __shfl_xor(dot, 1);
-      nr += __shfl_xor(nr, 1);
-      dot += __shfl_xor(dot, 2);
-      nr += __shfl_xor(nr, 2);
-      dot += __shfl_xor(dot, 4);
-      nr += __shfl_xor(nr, 4);
-      if (lg == 0 && v + 32 * r < v1) aff[row[r]] = affinity_of(dot, nr, sqrt_na, na);
+#pragma unroll
+      for (int o = 1; o < LPR; o <<= 1) {
+        dot += __shfl_xor(dot, o);
+        nr += __shfl_xor(nr, o);
+      }
+      if (lg == 0 && v + NG * r < v1) aff[row[r]] = affinity_of(dot, nr, sqrt_na, na);
     }
   }
 }
 
 template <int NQ>
 hipError_t launch_nq(const ScoreArgs& a, hipStream_t st) {
-  constexpr int R = NQ >= 16 ? 1 : 16 / NQ;
+  constexpr int R = NQ >= KKA_SCORE_LOADS ? 1 : KKA_SCORE_LOADS / NQ;
   const dim3 grid((unsigned)((int64_t)a.S * a.tiles_per_seq));
-  hipLaunchKernelGGL((score_kernel<NQ, R>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((score_kernel<KKA_SCORE_LPR, NQ, R>), grid, dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.S), dim3(kSelThreads), 0, st, a);
@@ -404,18 +571,18 @@ hipError_t launch_nq(const ScoreArgs& a, hipStream_t st) {
 
 }  // namespace
 
-// Rows per tile for a given head_dim: one pass of the 32 row-groups.
+// Rows one scoring work-group covers for a given head_dim.
 int32_t score_rows_per_tile(int32_t D) {
-  const int32_t nq = (D / 4 + 7) / 8;
+  const int32_t nq = (D / 4 + KKA_SCORE_LPR - 1) / KKA_SCORE_LPR;
   int32_t NQ = 1;
   while (NQ < nq) NQ <<= 1;
-  const int32_t R = NQ >= 16 ? 1 : 16 / NQ;
-  return 32 * R;
+  const int32_t R = NQ >= KKA_SCORE_LOADS ? 1 : KKA_SCORE_LOADS / NQ;
+  return (256 / KKA_SCORE_LPR) * R * KKA_SCORE_PASSES;
 }
 
 hipError_t launch_score_topk(const ScoreArgs& a, hipStream_t st) {
   if (a.S <= 0) return hipSuccess;
-  const int32_t nq = (a.D / 4 + 7) / 8;
+  const int32_t nq = (a.D / 4 + KKA_SCORE_LPR - 1) / KKA_SCORE_LPR;
   if (nq <= 1) return launch_nq<1>(a, st);
   if (nq <= 2) return launch_nq<2>(a, st);
   if (nq <= 4) return launch_nq<4>(a, st);

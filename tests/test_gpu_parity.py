@@ -226,6 +226,22 @@ def test_levels_and_selection_match_oracle(case):
         check_selection(sel, s, int(npg[s]), tag=str(case))
 
 
+@pytest.mark.parametrize("case", [
+    dict(hierarchical=0, k_grid=0, k_chunk=0, k_page=100, pages_per_chunk=16, chunks_per_grid=16),
+    dict(hierarchical=0, k_grid=0, k_chunk=0, k_page=1000, pages_per_chunk=16, chunks_per_grid=16),
+    dict(hierarchical=1, k_grid=3, k_chunk=20, k_page=300, pages_per_chunk=64, chunks_per_grid=4),
+    dict(hierarchical=1, k_grid=8, k_chunk=40, k_page=900, pages_per_chunk=32, chunks_per_grid=8),
+])
+def test_selection_large_candidate_sets(case):
+    """Levels with more candidates than the selecting group has threads
+    (radix-select path), including k larger than the positive candidates."""
+    say(f"select large {case}")
+    w = ragged_workload(13, 3, 1, 2, 64, 4, 2000, 9000, select=case)
+    sel, npg = run_selector(w)
+    for s in range(w.S):
+        check_selection(sel, s, int(npg[s]), tag=str(case))
+
+
 def test_selection_exact_ties_and_zero_scores():
     """Integer-valued page vectors force exact ties and exact 0/0.5/1
     affinities; the anchor is orthogonal to some pages and opposite to
