@@ -445,3 +445,75 @@ def test_config4_full_size_parity_and_recovery():
     for s in range(S):
         idx = check_selection(sel, s, n_p, "c4")
         assert (v.page_topic[s][idx] == v.anchor_topic[s]).all()
+
+
+@pytest.mark.timeout(900)
+def test_ragged_variance_batch_full_size_and_decode_step():
+    """32 sequences of 4096-65536 tokens (about 32 GB of bf16 keys), blocks of
+    64, one shared permuted pool, head-variance weighting, flat top-48; then
+    one decode step: one token appended per sequence, the newest block of
+    each re-pooled with the frozen weights, anchor, score and select again.
+    Sampled against the oracle: weights of two sequences, their block
+    vectors and anchors; every sequence's selection on the GPU's own
+    affinities; every re-pooled block."""
+    say("ragged variance batch: generate (~32 GB of keys)")
+    w = synth.config5(0)
+    after = w.extra["after"]
+    say(f"ragged variance batch: upload {w.k.nbytes / 1e9:.1f} GB, {w.S} sequences, {w.P} blocks")
+    kp, seqs = upload(w)
+    max_pages = int(np.max(np.diff(after["block_offsets"])))
+    sel = Selector(kp, seqs, w.select, max_pages=max_pages, window=w.window, mode=kka.WEIGHT_VARIANCE)
+    npg = n_pages_of(w)
+    say("ragged variance batch: pool + anchor + score")
+    sel.pool()
+    sel.anchor()
+    sel.score(npg)
+    torch.cuda.synchronize()
+    assert kka.kka_device_error() == 0
+    okp = oracle.KPool.of(w)
+    wg = sel.head_weight.cpu().numpy()
+    lvl = sel.level.cpu().numpy()
+    anc = sel.anchors.cpu().numpy()
+    order = np.argsort(w.seq_len)
+    sample = [int(order[0]), int(order[len(order) // 2])]
+    say(f"ragged variance batch: oracle on sequences {sample}")
+    for s in sample:
+        tab = oracle.seq_table(w.block_offsets, w.block_table, s)
+        wref = oracle.head_weights(okp, tab, int(w.seq_len[s]))
+        np.testing.assert_allclose(wg[s], wref, rtol=WEIGHT_RTOL, atol=0)
+        nb = len(tab)
+        for i in sorted({0, 1, nb // 2, nb - 2, nb - 1}):
+            n_b = min(w.B, int(w.seq_len[s]) - i * w.B)
+            ref = oracle.pool_block(okp, int(tab[i]), n_b, wref)
+            np.testing.assert_allclose(lvl[s, i], ref, atol=ATOL, rtol=0, err_msg=f"seq {s} block {i}")
+        a = oracle.pool_anchor(okp, tab, int(w.seq_len[s]), w.window, wref)
+        np.testing.assert_allclose(anc[s], a, atol=ATOL, rtol=0)
+    for s in range(w.S):
+        check_selection(sel, s, int(npg[s]), "ragged")
+
+    say("ragged variance batch: decode step")
+    dev = "cuda"
+    seqs_after = kka.Seqs(torch.from_numpy(after["seq_len"]).to(dev), torch.from_numpy(after["block_offsets"]).to(dev),
+                          torch.from_numpy(after["block_table"]).to(dev), int(after["block_offsets"][-1]))
+    frozen = sel.head_weight.clone()
+    sel.seqs = seqs_after
+    newest = (after["block_offsets"][1:] - 1).astype(np.int32)
+    npg_after = torch.from_numpy(np.diff(after["block_offsets"]).astype(np.int32)).to(dev)
+    sel.repool(torch.from_numpy(newest).to(dev))
+    sel.anchor()
+    sel.score(npg_after)
+    torch.cuda.synchronize()
+    assert kka.kka_device_error() == 0
+    assert torch.equal(sel.head_weight, frozen)
+    lvl = sel.level.cpu().numpy()
+    wf = frozen.cpu().numpy()
+    for s in range(w.S):
+        i = int(newest[s] - after["block_offsets"][s])
+        n_b = int(after["seq_len"][s]) - i * w.B
+        ref = oracle.pool_block(okp, int(after["block_table"][newest[s]]), n_b, wf[s])
+        np.testing.assert_allclose(lvl[s, i], ref, atol=ATOL, rtol=0, err_msg=f"seq {s} newest block")
+        check_selection(sel, s, int(npg_after[s]), "ragged decode")
+    for s in sample:
+        tab = oracle.seq_table(after["block_offsets"], after["block_table"], s)
+        a = oracle.pool_anchor(okp, tab, int(after["seq_len"][s]), w.window, wf[s])
+        np.testing.assert_allclose(sel.anchors[s].cpu().numpy(), a, atol=ATOL, rtol=0)
