@@ -174,7 +174,7 @@ KKA_API size_t kka_pool_anchor_workspace(const kka_kpool* kp, const kka_seqs* se
  * Sequence s starts at row s * rows_per_seq.
  * Rules: num_seqs >= 0; 0 <= max_pages; head_dim a multiple of 8 in
  * [8, 1024]; hierarchical layouts need pages_per_chunk >= 1,
- * chunks_per_grid >= 1, ceil(max_pages / pages_per_chunk) <= 32768 and
+ * chunks_per_grid >= 1, ceil(max_pages / pages_per_chunk) <= 16384 and
  * chunks_per_grid * head_dim <= 16384.
  */
 typedef struct kka_level_layout {

@@ -18,7 +18,7 @@ constexpr int kPoolTargetGroups = 2048;
 // Largest k at any selection level.
 constexpr int kMaxK = 1024;
 // Largest number of parents whose keep flags one selecting group tracks.
-constexpr int kMaxParents = 32768;
+constexpr int kMaxParents = 16384;
 // Largest chunks_per_grid * head_dim (LDS of the level builder, floats).
 constexpr int kMaxGridFloats = 16384;
 

@@ -202,8 +202,16 @@ __global__ __launch_bounds__(256) void pool_finish_kernel(PoolArgs a) {
   if (it.row < 0) return;
   const int32_t LH = a.L * a.H;
   for (int32_t d = threadIdx.x; d < a.D; d += blockDim.x) {
+    const float* src = a.partial + (int64_t)item * a.n_split * a.D + d;
     float sum = 0.f;
-    for (int32_t j = 0; j < a.n_split; ++j) sum += a.partial[((int64_t)item * a.n_split + j) * a.D + d];
+    for (int32_t j0 = 0; j0 < a.n_split; j0 += 8) {
+      float t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = src[(int64_t)min(j0 + u, a.n_split - 1) * a.D];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < a.n_split) sum += t[u];
+    }
     const float denom = MODE == kGiven ? (float)it.n_b : (float)((int64_t)it.n_b * LH);
     a.out[it.row * a.D + d] = it.n_b > 0 ? sum / denom : 0.f;
   }
@@ -363,25 +371,44 @@ __global__ __launch_bounds__(256) void pool_combine_kernel(PoolArgs a, const flo
 
 // One group per (sequence, layer range): the last W_eff tokens of the
 // sequence, gathered through the block table (the window may straddle
-// blocks); token-outer, layer-inner so each token's block id is read once.
+// blocks).  The window's block ids are read once into LDS; the (token,
+// layer) pairs of a thread are then walked like the block pool, with
+// kUnroll independent 16-byte loads in flight.
+constexpr int kWindowBlocks = 1024;  // window block ids staged in LDS
+
 template <int MODE, int MAXT>
 __global__ __launch_bounds__(MAXT) void anchor_kernel(PoolArgs a) {
   __shared__ float red[MAXT * 8];
+  __shared__ int64_t wblk[kWindowBlocks];
   extern __shared__ float wsh[];
   const int tid = threadIdx.x;
   const int32_t s = blockIdx.x / a.n_split;
   const int32_t j = blockIdx.x - s * a.n_split;
   const int32_t LH = a.L * a.H;
-  if (MODE == kGiven) {
-    for (int x = tid; x < LH; x += a.ps.nt) wsh[x] = a.weights[(int64_t)s * LH + x];
-    __syncthreads();
-  }
   const int32_t T = a.seq_len[s] > 0 ? a.seq_len[s] : 0;
   const int32_t W = a.window < T ? a.window : T;
   // offsets are device data: never index the table outside [0, total_blocks)
   const int32_t b1 = min(max(a.offs[s + 1], 0), a.total_blocks);
   const int32_t b0 = min(max(a.offs[s], 0), b1);
   const int32_t nb_s = b1 - b0;
+  const int32_t i_first = W > 0 ? (T - W) / a.B : 0;
+  const int32_t nbw = W > 0 ? (T - 1) / a.B - i_first + 1 : 0;
+  const bool staged = nbw <= kWindowBlocks;
+  if (MODE == kGiven)
+    for (int x = tid; x < LH; x += a.ps.nt) wsh[x] = a.weights[(int64_t)s * LH + x];
+  if (staged) {
+    // -1: past the sequence's blocks; -2: physical id outside the pool
+    for (int32_t x = tid; x < nbw; x += a.ps.nt) {
+      const int32_t i = i_first + x;
+      int64_t p = -1;
+      if (i < nb_s) {
+        p = a.table[b0 + i];
+        if (p < 0 || p >= a.P) p = -2;
+      }
+      wblk[x] = p;
+    }
+  }
+  __syncthreads();
   const int32_t DG = a.D >> 3;
   const int32_t q = tid % a.ps.rg;
   const int32_t h = q / DG;
@@ -389,33 +416,40 @@ __global__ __launch_bounds__(MAXT) void anchor_kernel(PoolArgs a) {
   const int32_t toff = tid / a.ps.rg;
   const int32_t l0 = j * a.lps;
   const int32_t nl = min(a.L, l0 + a.lps) - l0;
+  const int32_t n_tok = W > toff ? (W - toff + a.ps.m - 1) / a.ps.m : 0;
+  const int32_t total = n_tok * nl;
+  const uint16_t* head = a.k + (int64_t)h * a.sH + (int64_t)dg * 8 + (int64_t)l0 * a.sL;
   bool bad_len = false, bad_tab = false;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int32_t tau = T - W + toff; tau < T; tau += a.ps.m) {
-    const int32_t i = tau / a.B;
-    const int32_t t = tau - i * a.B;
-    if (i >= nb_s) {
-      bad_len = true;
-      continue;
-    }
-    const int64_t p = a.table[b0 + i];
-    if (p < 0 || p >= a.P) {
-      bad_tab = true;
-      continue;
-    }
-    const uint16_t* base = a.k + p * a.sB + (int64_t)t * a.sT + (int64_t)h * a.sH + (int64_t)dg * 8 +
-                           (int64_t)l0 * a.sL;
-    int32_t l = 0;
-    for (; l + kUnroll <= nl; l += kUnroll) {
-      u32x4 v[kUnroll];
+  // item n -> token tau = T - W + toff + (n / nl) * m, layer l0 + n % nl
+  for (int32_t n0 = 0; n0 < total; n0 += kUnroll) {
+    u32x4 v[kUnroll];
+    float wv[kUnroll];
+    bool ok[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) v[u] = load16(base + (int64_t)(l + u) * a.sL);
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-        accum8<MODE>(acc, v[u], MODE == kGiven ? wsh[(l0 + l + u) * a.H + h] : 0.f);
+    for (int u = 0; u < kUnroll; ++u) {
+      const int32_t n = n0 + u;
+      const int32_t k = n / nl, li = n - k * nl;
+      const int32_t tau = T - W + toff + k * a.ps.m;
+      const int32_t i = tau / a.B;
+      int64_t p;
+      if (staged) {
+        p = n < total ? wblk[i - i_first] : -1;
+      } else {
+        p = (n < total && i < nb_s) ? (int64_t)a.table[b0 + i] : -1;
+        if (n < total && i < nb_s && (p < 0 || p >= a.P)) p = -2;
+      }
+      ok[u] = n < total && p >= 0;
+      if (n < total && p == -1) bad_len = true;
+      if (n < total && p == -2) bad_tab = true;
+      const int64_t pc = ok[u] ? p : 0;
+      const int32_t t = tau - i * a.B;
+      v[u] = ok[u] ? load16(head + pc * a.sB + (int64_t)t * a.sT + (int64_t)li * a.sL) : u32x4{0u, 0u, 0u, 0u};
+      wv[u] = MODE == kGiven ? wsh[(l0 + li) * a.H + h] : 0.f;
     }
-    for (; l < nl; ++l)
-      accum8<MODE>(acc, load16(base + (int64_t)l * a.sL), MODE == kGiven ? wsh[(l0 + l) * a.H + h] : 0.f);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (ok[u]) accum8<MODE>(acc, v[u], wv[u]);
   }
   if (bad_len) raise_err(a.err, KKA_DEVERR_SEQ_LEN);
   if (bad_tab) raise_err(a.err, KKA_DEVERR_BLOCK_TABLE);
@@ -432,6 +466,8 @@ __global__ __launch_bounds__(MAXT) void anchor_kernel(PoolArgs a) {
   }
 }
 
+// Sums each sequence's layer-split partials in split order (loads of a
+// batch of 8 splits are issued before the first add).
 template <int MODE>
 __global__ __launch_bounds__(256) void anchor_finish_kernel(PoolArgs a) {
   const int32_t s = blockIdx.x;
@@ -439,8 +475,16 @@ __global__ __launch_bounds__(256) void anchor_finish_kernel(PoolArgs a) {
   const int32_t W = a.window < T ? a.window : T;
   const int32_t LH = a.L * a.H;
   for (int32_t d = threadIdx.x; d < a.D; d += blockDim.x) {
+    const float* src = a.partial + (int64_t)s * a.n_split * a.D + d;
     float sum = 0.f;
-    for (int32_t j = 0; j < a.n_split; ++j) sum += a.partial[((int64_t)s * a.n_split + j) * a.D + d];
+    for (int32_t j0 = 0; j0 < a.n_split; j0 += 8) {
+      float t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = src[(int64_t)min(j0 + u, a.n_split - 1) * a.D];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < a.n_split) sum += t[u];
+    }
     const float denom = MODE == kGiven ? (float)W : (float)((int64_t)W * LH);
     a.out[(int64_t)s * a.D + d] = W > 0 ? sum / denom : 0.f;
   }

@@ -68,6 +68,7 @@ __device__ __forceinline__ f32x4 load_row4(const f32x4* p) {
 struct SelectShared {
   float aff[kLdsRows];
   uint64_t ck[kRankMax];
+  uint64_t run[kSelThreads];
   uint64_t buf[kMaxK];
   uint32_t kept_grid[kBitmapWords];   // grids kept (parents of chunks)
   uint32_t kept_chunk[kBitmapWords];  // chunks kept (parents of pages)
@@ -300,54 +301,82 @@ __device__ int32_t select_level_big(const Level& L, int32_t k, SelectShared& sm)
   return k_eff;
 }
 
-// Number of entries of a strictly descending 64-entry run that exceed x.
-__device__ __forceinline__ int32_t count_above(const uint64_t* run, uint64_t x) {
-  int32_t pos = 0;
-#pragma unroll
-  for (int step = 32; step > 0; step >>= 1)
-    if (run[pos + step - 1] > x) pos += step;
-  return (pos == 63 && run[63] > x) ? 64 : pos;
+// Sum of v over lanes [lane, lane + n) of the same 16-lane row (n = 1, 2, 4
+// or 8; exact for lanes that start an aligned group of n).
+__device__ __forceinline__ int32_t group_sum(int32_t v, int32_t n) {
+  if (n >= 2) v += __builtin_amdgcn_update_dpp(0, v, 0x101, 0xF, 0xF, false);  // row_shl:1
+  if (n >= 4) v += __builtin_amdgcn_update_dpp(0, v, 0x102, 0xF, 0xF, false);  // row_shl:2
+  if (n >= 8) v += __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0xF, false);  // row_shl:4
+  return v;
 }
 
 // Keeps the top min(k, n) elements of a level, sorted, in sm.buf.
-// Levels with at most kSelThreads candidates hold one candidate per lane:
-// each wave ranks its 64 keys with register broadcasts and stores them as a
-// descending run; a key's rank in the level is its rank in its own run plus,
-// for every other run, how many of that run's keys exceed it (binary search).
-// Lanes without a positive-score candidate carry distinct keys below every
-// positive one, so every run is strictly ordered.
+// Levels with at most kSelThreads candidates: candidate keys go to LDS in
+// groups of 64 (slots past the candidates hold distinct keys below every
+// real one); all threads rank every key within its group, tpc lanes per key
+// each comparing a strided share; each group is written back as a strictly
+// descending run; a key's rank in the level is its rank in its group plus,
+// for every other group, how many keys of that run exceed it (binary
+// search).  Keys without a positive score rank below all positive ones and
+// are never kept here (the zero fill handles them).
 __device__ int32_t select_level(const Level& L, int32_t k, SelectShared& sm) {
   const int32_t k_eff = k < L.n ? k : L.n;
   if (k_eff <= 0) return 0;
-  const int64_t m = L.fanout ? (int64_t)L.n_par * L.fanout : (int64_t)L.n;
-  if (m > kSelThreads) return select_level_big(L, k, sm);
+  const int64_t m64 = L.fanout ? (int64_t)L.n_par * L.fanout : (int64_t)L.n;
+  if (m64 > kSelThreads) return select_level_big(L, k, sm);
+  const int32_t m = (int32_t)m64;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int32_t n_runs = (int32_t)((m + 63) >> 6);
-  const int32_t e = tid < m ? cand32(L, sm, tid) : -1;
-  const uint32_t key = e >= 0 ? aff_key(L, sm, e) : 0u;
-  // positive keys: (bits << 32 | ~index); others sort below: (~index) or tid
-  const uint64_t x = e >= 0 ? composite(key, e) : (uint64_t)tid;
-  const uint64_t bal = __ballot(key != 0u);
-  if (lane == 0) sm.wave_tot[wave] = (int32_t)__popcll(bal);
-  int32_t r = 0;
-  if (wave < n_runs) {
-    const uint32_t xlo = (uint32_t)x, xhi = (uint32_t)(x >> 32);
-#pragma unroll 16
-    for (int j = 0; j < 64; ++j) {
-      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)xlo, j);
-      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)xhi, j);
-      r += (int32_t)((((uint64_t)hi << 32) | lo) > x);
-    }
-    sm.ck[(wave << 6) + r] = x;
+  const int32_t n_grp = (m + 63) >> 6;
+  uint64_t* keys = sm.ck;    // [n_grp * 64] candidate keys by candidate index
+  uint64_t* runs = sm.run;   // [n_grp * 64] the same keys, each group sorted
+  // phase A: candidate keys
+  {
+    const int32_t e = tid < m ? cand32(L, sm, tid) : -1;
+    const uint32_t key = e >= 0 ? aff_key(L, sm, e) : 0u;
+    if (tid < (n_grp << 6)) keys[tid] = e >= 0 ? composite(key, e) : (uint64_t)tid;
+    const uint64_t bal = __ballot(key != 0u);
+    if (lane == 0) sm.wave_tot[wave] = (int32_t)__popcll(bal);
   }
   __syncthreads();
   int32_t P = 0;
-  for (int w = 0; w < n_runs; ++w) P += sm.wave_tot[w];
-  if (wave < n_runs && key != 0u) {
+  for (int w = 0; w < kSelThreads / 64; ++w) P += sm.wave_tot[w];
+  // phase B: rank within the group, tpc lanes per key (the largest power of
+  // two with n_grp * 64 * tpc <= kSelThreads); threads past the last group
+  // only read
+  int32_t tpc = 1;
+  while (tpc < 8 && (n_grp << 6) * tpc * 2 <= kSelThreads) tpc <<= 1;
+  const int32_t i = tid / tpc, q = tid - i * tpc;
+  const bool active = i < (n_grp << 6);
+  const int32_t ic = active ? i : 0;
+  const int32_t g0 = (ic >> 6) << 6;
+  const uint64_t x = keys[ic];
+  int32_t r = 0;
+  for (int32_t j = q; j < 64; j += 8 * tpc) {
+    uint64_t y[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) y[u] = keys[g0 + min(j + u * tpc, 63)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) r += (int32_t)(j + u * tpc < 64 && y[u] > x);
+  }
+  r = group_sum(r, tpc);
+  if (active && q == 0) runs[g0 + r] = x;
+  __syncthreads();
+  // phase C: rank in the level, positive keys only
+  if (active && q == 0 && (x >> 32) != 0ull) {
     int32_t R = r;
-    for (int w = 0; w < n_runs; ++w)
-      if (w != wave) R += count_above(sm.ck + (w << 6), x);
+    int32_t pos[kSelThreads / 64];
+#pragma unroll
+    for (int g = 0; g < kSelThreads / 64; ++g) pos[g] = 0;
+#pragma unroll
+    for (int step = 32; step > 0; step >>= 1) {
+#pragma unroll
+      for (int g = 0; g < kSelThreads / 64; ++g)
+        if (g < n_grp && (g << 6) != g0 && runs[(g << 6) + pos[g] + step - 1] > x) pos[g] += step;
+    }
+#pragma unroll
+    for (int g = 0; g < kSelThreads / 64; ++g)
+      if (g < n_grp && (g << 6) != g0) R += (pos[g] == 63 && runs[(g << 6) + 63] > x) ? 64 : pos[g];
     if (R < k_eff) sm.buf[R] = x;
   }
   __syncthreads();
@@ -422,9 +451,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(ScoreArgs a) {
   const int tid = threadIdx.x;
   const int32_t s = blockIdx.x;
   const float* aff = a.aff + (int64_t)s * a.rows_per_seq;
+  const SeqGeom g = seq_geom(a, s, false);  // issued before the staging loads
   const bool staged = a.rows_per_seq <= kLdsRows;
   if (staged) stage_rows(sm.aff, aff, (int32_t)a.rows_per_seq);
-  const SeqGeom g = seq_geom(a, s, false);
   if (tid < 4) sm.cnt[tid] = 0;
   if (a.hier) {
     for (int32_t w = tid; w < (g.n_g + 31) / 32; w += kSelThreads) sm.kept_grid[w] = 0u;

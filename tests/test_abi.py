@@ -137,7 +137,7 @@ def test_level_rows_and_score_validation(L):
     flat = kka.c_level_layout(4, 1025, 128, 0, 16, 16)
     assert L.kka_level_rows(ctypes.byref(flat)) == 1025
     for bad in (kka.c_level_layout(1, 100, 12, 1, 16, 16), kka.c_level_layout(1, 100, 128, 1, 0, 16),
-                kka.c_level_layout(1, 16 * 32769, 128, 1, 16, 16), kka.c_level_layout(1, 100, 1024, 1, 16, 17),
+                kka.c_level_layout(1, 16 * 16385, 128, 1, 16, 16), kka.c_level_layout(1, 100, 1024, 1, 16, 17),
                 kka.c_level_layout(-1, 100, 128, 0, 16, 16)):
         assert L.kka_level_rows(ctypes.byref(bad)) == -1
     sel = kka.c_select(4, 16, 64)

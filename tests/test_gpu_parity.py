@@ -231,12 +231,19 @@ def test_levels_and_selection_match_oracle(case):
     dict(hierarchical=0, k_grid=0, k_chunk=0, k_page=1000, pages_per_chunk=16, chunks_per_grid=16),
     dict(hierarchical=1, k_grid=3, k_chunk=20, k_page=300, pages_per_chunk=64, chunks_per_grid=4),
     dict(hierarchical=1, k_grid=8, k_chunk=40, k_page=900, pages_per_chunk=32, chunks_per_grid=8),
+    dict(hierarchical=1, k_grid=4, k_chunk=10, k_page=50, pages_per_chunk=16, chunks_per_grid=8),   # 160 live
+    dict(hierarchical=1, k_grid=6, k_chunk=20, k_page=200, pages_per_chunk=16, chunks_per_grid=8),  # 320 live
+    dict(hierarchical=1, k_grid=7, k_chunk=28, k_page=500, pages_per_chunk=16, chunks_per_grid=8),  # 448 live
+    dict(hierarchical=0, k_grid=0, k_chunk=0, k_page=77, pages_per_chunk=16, chunks_per_grid=16),
 ])
 def test_selection_large_candidate_sets(case):
     """Levels with more candidates than the selecting group has threads
     (radix-select path), including k larger than the positive candidates."""
     say(f"select large {case}")
     w = ragged_workload(13, 3, 1, 2, 64, 4, 2000, 9000, select=case)
+    if not case["hierarchical"] and case["k_page"] == 77:
+        # flat levels of 129-512 pages: 3 to 8 groups of candidates
+        w = ragged_workload(14, 6, 1, 2, 64, 4, 516, 2048, select=case)
     sel, npg = run_selector(w)
     for s in range(w.S):
         check_selection(sel, s, int(npg[s]), tag=str(case))
