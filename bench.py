@@ -142,6 +142,13 @@ def run(args):
     if not np.array_equal(sel.page_idx[0, :len(idx_o)].cpu().numpy(), idx_o):
         raise RuntimeError("benchmark selection differs from the oracle on the GPU's affinities")
 
+    # c3 lazy (coarse-to-fine) scoring of the same levels: must select the same pages
+    full_idx = sel.page_idx.clone()
+    c3_lazy_us = time_calls(lambda i: sel.score(npg, lazy=True), args.steps, max(3, args.warmup), stream)
+    if not torch.equal(sel.page_idx, full_idx):
+        raise RuntimeError("lazy scoring selected different pages than the full pass")
+    c3_lazy_rows = lazy_rows(n_g, w.select)
+
     del sel, k, kp
     torch.cuda.empty_cache()
 
@@ -188,6 +195,19 @@ def run(args):
     got = idx4.cpu().numpy()
     recovered = int(sum((v.page_topic[s][got[s]] == v.anchor_topic[s]).all() for s in range(S)))
 
+    # lazy (coarse-to-fine) scoring of the same batch: same selection, fewer rows read
+    def lazy4(i):
+        kka.kka_score_topk_lazy(lay4, levels[i % n_sets], npg4, anchors, k_page=kp4, k_grid=v.select["k_grid"],
+                                k_chunk=v.select["k_chunk"], page_idx_out=idx4, page_score_out=sc4,
+                                n_selected_out=cnt4, affinity_out=affs[i % n_sets], workspace=ws4)
+
+    c4_lazy_us = time_calls(lazy4, args.steps, max(3, args.warmup), stream)
+    if not np.array_equal(idx4.cpu().numpy(), got):
+        raise RuntimeError("lazy scoring selected different pages than the full pass (serving batch)")
+    n_c4 = -(-NP // 16)
+    n_g4 = -(-n_c4 // 16)
+    c4_lazy_rows = lazy_rows(n_g4, v.select)
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -227,6 +247,10 @@ def run(args):
         "serving_workload": "64 sequences x 8192 fp32 block vectors (D=128) + 512 chunk + 32 grid rows each, "
                             "top 4/16/64, three rotating buffer sets (cold last-level cache)",
         "serving_algorithmic_bytes": b4,
+        "lazy_score_topk_us_per_step": round(c3_lazy_us, 2),
+        "lazy_rows_scored_per_seq": c3_lazy_rows,
+        "serving_lazy_score_topk_us_per_step": round(c4_lazy_us, 2),
+        "serving_lazy_rows_scored_per_seq": c4_lazy_rows,
         "serving_topic_recovered_seqs": recovered,
         "roofline": {
             "bound": "hbm",
@@ -249,6 +273,28 @@ def run(args):
         "generation_s": round(gen_s, 2),
     }
     print(json.dumps(out), flush=True)
+
+
+def time_calls(fn, steps, warmup, stream):
+    """Mean device time (us) of fn(i), bracketed by events on `stream`."""
+    import numpy as np
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+
+
+def lazy_rows(n_g, select):
+    """Rows the coarse-to-fine pass scores per sequence (full-length levels):
+    every grid, the chunks of the kept grids, the pages of the kept chunks."""
+    return n_g + min(select["k_grid"], n_g) * select["chunks_per_grid"] + select["k_chunk"] * select["pages_per_chunk"]
 
 
 def cpu_baseline(w, step_bytes, seconds):
@@ -377,6 +423,22 @@ def write_stats_summary(stats_csv: str, out_md: str, title: str, command: str = 
     for r in rows:
         lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    trace_csv = stats_csv.replace("_kernel_stats.csv", "_kernel_trace.csv")
+    if trace_csv != stats_csv and os.path.exists(trace_csv):
+        # the same kernel launched on different workloads, told apart by grid size
+        per = {}
+        for r in csv.DictReader(open(trace_csv)):
+            if "kka::" not in r["Kernel_Name"]:
+                continue
+            key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+            per.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        lines += ["", "Per launch shape (from the kernel trace of the same run; grid in work-items):", "",
+                  "| kernel | grid | work-group | calls | average us | median us | min us |",
+                  "|---|---:|---:|---:|---:|---:|---:|"]
+        for (name, grid, wg), v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            v.sort()
+            lines.append(f"| `{name}` | {grid} | {wg} | {len(v)} | {sum(v) / len(v):.2f} | {v[len(v) // 2]:.2f} | "
+                         f"{v[0]:.2f} |")
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
 

@@ -172,9 +172,9 @@ KKA_API size_t kka_pool_anchor_workspace(const kka_kpool* kp, const kka_seqs* se
  * pages_per_chunk), n_g = ceil(n_c / chunks_per_grid) and n_p the
  * sequence's page count.  Flat layouts (hierarchical == 0) hold pages only.
  * Sequence s starts at row s * rows_per_seq.
- * Rules: num_seqs >= 0; 0 <= max_pages; head_dim a multiple of 8 in
- * [8, 1024]; hierarchical layouts need pages_per_chunk >= 1,
- * chunks_per_grid >= 1, ceil(max_pages / pages_per_chunk) <= 16384 and
+ * Rules: num_seqs >= 0; 0 <= max_pages <= 2^30; head_dim a multiple of 8
+ * in [8, 1024]; hierarchical layouts need pages_per_chunk >= 1,
+ * chunks_per_grid >= 1, C <= 16384, C * pages_per_chunk <= 2^30 and
  * chunks_per_grid * head_dim <= 16384.
  */
 typedef struct kka_level_layout {
@@ -247,6 +247,26 @@ KKA_API kka_status kka_score_topk(const kka_level_layout* lay, const float* leve
                           void* stream);
 
 KKA_API size_t kka_score_topk_workspace(const kka_level_layout* lay, const kka_select* sel, int32_t with_affinity_out);
+
+/*
+ * kka_score_topk_lazy -- the same selection, scored coarse to fine (page
+ * section 5.1: chunks are scored only inside kept grids, pages only inside
+ * surviving chunks).  One work-group per sequence scores the grids, keeps
+ * the top k_grid, scores only the chunks of kept grids, keeps the top
+ * k_chunk, scores only the pages of kept chunks and keeps the top k_page.
+ * Rows under unkept parents are never read; their score is +0 by
+ * definition, so page_idx_out, page_score_out and n_selected_out are bit
+ * for bit those of kka_score_topk on the same inputs.  affinity_out (if
+ * given) receives only the rows actually scored, bit-identical to
+ * kka_score_topk's values for those rows; other rows are left untouched.
+ * Arguments, rules and workspace are those of kka_score_topk (the same
+ * kka_score_topk_workspace() size suffices).  A flat layout has no parents:
+ * the call is then kka_score_topk.  One launch on `stream`.
+ */
+KKA_API kka_status kka_score_topk_lazy(const kka_level_layout* lay, const float* level_buf, const int32_t* n_pages,
+                                       const float* anchors, const kka_select* sel, float* affinity_out,
+                                       int32_t* page_idx_out, float* page_score_out, int32_t* n_selected_out,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kka_device_error -- waits for `stream`, returns the KKA_DEVERR_* bits

@@ -10,7 +10,8 @@ raises.
 
 Entry points keep the C names: :func:`kka_pool_blocks`,
 :func:`kka_pool_anchor`, :func:`kka_build_levels`, :func:`kka_score_topk`,
-:func:`kka_device_error` (plus the ``*_workspace`` size queries).
+:func:`kka_score_topk_lazy`, :func:`kka_device_error` (plus the ``*_workspace``
+size queries).
 """
 from __future__ import annotations
 
@@ -38,7 +39,8 @@ _STATUS = {0: "ok", 1: "KKA_ERR_NULL", 2: "KKA_ERR_SHAPE", 3: "KKA_ERR_ALIGN", 4
 
 ENTRY_POINTS = (
     "kka_pool_blocks", "kka_pool_blocks_workspace", "kka_pool_anchor", "kka_pool_anchor_workspace",
-    "kka_level_rows", "kka_build_levels", "kka_score_topk", "kka_score_topk_workspace", "kka_device_error",
+    "kka_level_rows", "kka_build_levels", "kka_score_topk", "kka_score_topk_workspace", "kka_score_topk_lazy",
+    "kka_device_error",
     "kka_status_string", "kka_version",
 )
 
@@ -98,9 +100,10 @@ def lib() -> ctypes.CDLL:
         L.kka_build_levels.argtypes = [P(c_level_layout), vp, vp, vp, vp]
         L.kka_score_topk.argtypes = [P(c_level_layout), vp, vp, vp, P(c_select), vp, vp, vp, vp, vp, sz, vp]
         L.kka_score_topk_workspace.argtypes = [P(c_level_layout), P(c_select), i32]
+        L.kka_score_topk_lazy.argtypes = [P(c_level_layout), vp, vp, vp, P(c_select), vp, vp, vp, vp, vp, sz, vp]
         L.kka_device_error.argtypes = [vp]
         L.kka_status_string.argtypes = [ctypes.c_int]
-        for f in ("kka_pool_blocks", "kka_pool_anchor", "kka_build_levels", "kka_score_topk"):
+        for f in ("kka_pool_blocks", "kka_pool_anchor", "kka_build_levels", "kka_score_topk", "kka_score_topk_lazy"):
             getattr(L, f).restype = ctypes.c_int
         for f in ("kka_pool_blocks_workspace", "kka_pool_anchor_workspace", "kka_score_topk_workspace"):
             getattr(L, f).restype = sz
@@ -302,9 +305,9 @@ def kka_score_topk(lay: LevelLayout, level_buf: torch.Tensor, n_pages: torch.Ten
                    k_page: int, k_grid: int = 0, k_chunk: int = 0, page_idx_out: torch.Tensor,
                    page_score_out: Optional[torch.Tensor] = None, n_selected_out: Optional[torch.Tensor] = None,
                    affinity_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                   stream=None):
-    """Affinities of every level row and the top-k pages of each sequence.
-    `workspace` must be zero-filled before its first use (new_workspace())."""
+                   stream=None, lazy: bool = False):
+    """Affinities of every level row and the top-k pages of each sequence
+    (lazy=True: kka_score_topk_lazy, scoring only children of kept parents)."""
     S, D = lay.num_seqs, lay.head_dim
     lp = _dev(level_buf, "level_buf", torch.float32, min_numel=S * lay.rows_per_seq * D)
     npp = _dev(n_pages, "n_pages", torch.int32, min_numel=S)
@@ -316,9 +319,16 @@ def kka_score_topk(lay: LevelLayout, level_buf: torch.Tensor, n_pages: torch.Ten
     need = kka_score_topk_workspace(lay, affinity_out is not None)
     wp, wbytes, keep = _ws(workspace, need, level_buf.device)
     sel = c_select(int(k_grid), int(k_chunk), int(k_page))
-    _check(lib().kka_score_topk(ctypes.byref(lay.c), lp, npp, anc, ctypes.byref(sel), aff, idx, sc, cnt, wp,
-                                wbytes, _stream(stream)), "kka_score_topk")
+    fn = lib().kka_score_topk_lazy if lazy else lib().kka_score_topk
+    _check(fn(ctypes.byref(lay.c), lp, npp, anc, ctypes.byref(sel), aff, idx, sc, cnt, wp, wbytes, _stream(stream)),
+           "kka_score_topk_lazy" if lazy else "kka_score_topk")
     return keep
+
+
+def kka_score_topk_lazy(lay: LevelLayout, level_buf: torch.Tensor, n_pages: torch.Tensor, anchors: torch.Tensor,
+                        **kw):
+    """kka_score_topk_lazy: same arguments and results as kka_score_topk."""
+    return kka_score_topk(lay, level_buf, n_pages, anchors, lazy=True, **kw)
 
 
 def kka_device_error(stream=None) -> int:

@@ -103,14 +103,16 @@ struct LevelGeom {
 
 bool level_geom(const kka_level_layout* lay, LevelGeom& g) {
   if (!lay) return false;
-  if (lay->num_seqs < 0 || lay->max_pages < 0) return false;
+  // at most 2^30 page rows per sequence, also once rounded up to whole
+  // chunks, so row and candidate counters stay far from int32 overflow
+  if (lay->num_seqs < 0 || lay->max_pages < 0 || lay->max_pages > kMaxPagesPerSeq) return false;
   const int32_t D = lay->head_dim;
   if (D < 8 || D > 1024 || D % 8 != 0) return false;
   g.c_cap = g.g_cap = 0;
   if (lay->hierarchical) {
     if (lay->pages_per_chunk < 1 || lay->chunks_per_grid < 1) return false;
     const int64_t c = ((int64_t)lay->max_pages + lay->pages_per_chunk - 1) / lay->pages_per_chunk;
-    if (c > kMaxParents) return false;
+    if (c > kMaxParents || c * lay->pages_per_chunk > kMaxPagesPerSeq) return false;
     if ((int64_t)lay->chunks_per_grid * D > kMaxGridFloats) return false;
     g.c_cap = (int32_t)c;
     g.g_cap = (int32_t)((c + lay->chunks_per_grid - 1) / lay->chunks_per_grid);
@@ -276,10 +278,15 @@ size_t kka_score_topk_workspace(const kka_level_layout* lay, const kka_select* s
   return with_affinity_out ? 0 : align256((size_t)lay->num_seqs * (size_t)g.rows * sizeof(float));
 }
 
-kka_status kka_score_topk(const kka_level_layout* lay, const float* level_buf, const int32_t* n_pages,
-                          const float* anchors, const kka_select* sel, float* affinity_out, int32_t* page_idx_out,
-                          float* page_score_out, int32_t* n_selected_out, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validates a scoring call and fills the launch arguments.
+kka_status prepare_score(const kka_level_layout* lay, const float* level_buf, const int32_t* n_pages,
+                         const float* anchors, const kka_select* sel, float* affinity_out, int32_t* page_idx_out,
+                         float* page_score_out, int32_t* n_selected_out, void* workspace, size_t workspace_bytes,
+                         size_t need, ScoreArgs& a) {
   if (!lay || !sel) return KKA_ERR_NULL;
   LevelGeom g;
   if (!level_geom(lay, g)) return KKA_ERR_SHAPE;
@@ -291,14 +298,13 @@ kka_status kka_score_topk(const kka_level_layout* lay, const float* level_buf, c
   if (!level_buf || !n_pages || !anchors) return KKA_ERR_NULL;
   if (sel->k_page > 0 && !page_idx_out) return KKA_ERR_NULL;
   if (!aligned16(level_buf) || !aligned16(anchors)) return KKA_ERR_ALIGN;
-  const size_t need = kka_score_topk_workspace(lay, sel, affinity_out != nullptr);
   if (need > 0 && (!workspace || workspace_bytes < need)) return KKA_ERR_WORKSPACE;
   if (workspace && !aligned16(workspace)) return KKA_ERR_ALIGN;
   if (affinity_out && !aligned16(affinity_out)) return KKA_ERR_ALIGN;
   uint32_t* err = device_error_word();
   if (!err) return KKA_ERR_DEVICE;
   (void)hipGetLastError();
-  ScoreArgs a = {};
+  a = ScoreArgs{};
   a.lvl = level_buf;
   a.rows_per_seq = g.rows;
   a.S = lay->num_seqs;
@@ -322,7 +328,41 @@ kka_status kka_score_topk(const kka_level_layout* lay, const float* level_buf, c
   a.tiles_per_seq = (int32_t)(tiles > 0 ? tiles : 1);
   if ((int64_t)a.S * a.tiles_per_seq > 0x7fffffffLL) return KKA_ERR_SHAPE;
   a.err = err;
+  return KKA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kka_status kka_score_topk(const kka_level_layout* lay, const float* level_buf, const int32_t* n_pages,
+                          const float* anchors, const kka_select* sel, float* affinity_out, int32_t* page_idx_out,
+                          float* page_score_out, int32_t* n_selected_out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  ScoreArgs a;
+  const size_t need = kka_score_topk_workspace(lay, sel, affinity_out != nullptr);
+  const kka_status st = prepare_score(lay, level_buf, n_pages, anchors, sel, affinity_out, page_idx_out,
+                                      page_score_out, n_selected_out, workspace, workspace_bytes, need, a);
+  if (st != KKA_OK || lay->num_seqs == 0) return st;
   return launched(launch_score_topk(a, static_cast<hipStream_t>(stream)));
+}
+
+kka_status kka_score_topk_lazy(const kka_level_layout* lay, const float* level_buf, const int32_t* n_pages,
+                               const float* anchors, const kka_select* sel, float* affinity_out,
+                               int32_t* page_idx_out, float* page_score_out, int32_t* n_selected_out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (lay && !lay->hierarchical)  // flat: every page is a candidate, the single pass is the lazy pass
+    return kka_score_topk(lay, level_buf, n_pages, anchors, sel, affinity_out, page_idx_out, page_score_out,
+                          n_selected_out, workspace, workspace_bytes, stream);
+  ScoreArgs a;
+  const size_t need = kka_score_topk_workspace(lay, sel, affinity_out != nullptr);
+  const kka_status st = prepare_score(lay, level_buf, n_pages, anchors, sel, affinity_out, page_idx_out,
+                                      page_score_out, n_selected_out, workspace, workspace_bytes, need, a);
+  if (st != KKA_OK || lay->num_seqs == 0) return st;
+  // long sequences keep scored rows in a.aff (affinity_out or workspace);
+  // short ones keep them in LDS and copy to affinity_out when it is given
+  float* lazy_out = a.rows_per_seq <= kSelectLdsRows ? affinity_out : nullptr;
+  return launched(launch_score_topk_lazy(a, lazy_out, static_cast<hipStream_t>(stream)));
 }
 
 int32_t kka_device_error(void* stream) {

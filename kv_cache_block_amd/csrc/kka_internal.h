@@ -21,6 +21,10 @@ constexpr int kMaxK = 1024;
 constexpr int kMaxParents = 16384;
 // Largest chunks_per_grid * head_dim (LDS of the level builder, floats).
 constexpr int kMaxGridFloats = 16384;
+// Largest page count of one sequence (also rounded up to whole chunks).
+constexpr int64_t kMaxPagesPerSeq = (int64_t)1 << 30;
+// Affinity rows of one sequence a selecting work-group keeps in LDS.
+constexpr int kSelectLdsRows = 9216;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -140,6 +144,9 @@ hipError_t launch_pool_combine(const PoolArgs& a, const float* w, hipStream_t st
 hipError_t launch_anchor(const PoolArgs& a, hipStream_t st);
 hipError_t launch_levels(const LevelArgs& a, hipStream_t st);
 hipError_t launch_score_topk(const ScoreArgs& a, hipStream_t st);
+// Lazy hierarchical variant: one work-group per sequence; scored affinities
+// also go to lazy_out when it is set (a.aff is scratch for long sequences).
+hipError_t launch_score_topk_lazy(const ScoreArgs& a, float* lazy_out, hipStream_t st);
 int32_t score_rows_per_tile(int32_t D);  // rows one score work-group covers
 
 }  // namespace kka

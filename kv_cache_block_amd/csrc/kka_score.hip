@@ -36,7 +36,7 @@ namespace {
 #endif
 constexpr int kSelThreads = KKA_SELECT_THREADS;
 constexpr int kRankMax = 512;
-constexpr int kLdsRows = 9216;  // affinity rows staged per sequence (36 KB)
+constexpr int kLdsRows = kSelectLdsRows;  // affinity rows staged per sequence (36 KB)
 constexpr int kBitmapWords = kMaxParents / 32;
 
 // float4 row loads each lane keeps in flight in the scoring pass, and how
@@ -446,50 +446,46 @@ __device__ void stage_rows(float* dst, const float* src, int32_t n) {
   }
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(ScoreArgs a) {
-  __shared__ SelectShared sm;
+// Level `lev` (0 grids, 1 chunks of kept grids, 2 pages of kept chunks or
+// every page when flat) of sequence geometry g; kp = kept count of the
+// level above.
+__device__ __forceinline__ Level make_level(const ScoreArgs& a, const SeqGeom& g, int32_t lev, bool staged,
+                                            const float* aff, int32_t kp, SelectShared& sm) {
+  Level L;
+  L.staged = staged;
+  L.slot = lev;
+  if (lev == 0) {
+    L.off = a.max_pages + a.c_cap;
+    L.n = g.n_g;
+    L.fanout = 0;
+    L.parent = nullptr;
+  } else if (lev == 1) {
+    L.off = a.max_pages;
+    L.n = g.n_c;
+    L.fanout = a.cpg;
+    L.parent = sm.kept_grid;
+  } else {
+    L.off = 0;
+    L.n = g.n_p;
+    L.fanout = a.hier ? a.ppc : 0;
+    L.parent = sm.kept_chunk;
+  }
+  L.aff = aff + L.off;
+  L.n_par = kp;
+  return L;
+}
+
+__device__ __forceinline__ void clear_select_state(const ScoreArgs& a, const SeqGeom& g, SelectShared& sm) {
   const int tid = threadIdx.x;
-  const int32_t s = blockIdx.x;
-  const float* aff = a.aff + (int64_t)s * a.rows_per_seq;
-  const SeqGeom g = seq_geom(a, s, false);  // issued before the staging loads
-  const bool staged = a.rows_per_seq <= kLdsRows;
-  if (staged) stage_rows(sm.aff, aff, (int32_t)a.rows_per_seq);
   if (tid < 4) sm.cnt[tid] = 0;
   if (a.hier) {
     for (int32_t w = tid; w < (g.n_g + 31) / 32; w += kSelThreads) sm.kept_grid[w] = 0u;
     for (int32_t w = tid; w < (g.n_c + 31) / 32; w += kSelThreads) sm.kept_chunk[w] = 0u;
   }
-  __syncthreads();
-  // Levels run as one loop so a single copy of the level code is fetched
-  // (a lone work-group per compute unit starts with a cold instruction cache).
-  int32_t kp = 0;
-  const int32_t first = a.hier ? 0 : 2;
-  for (int32_t lev = first; lev < 3; ++lev) {
-    Level L;
-    L.staged = staged;
-    L.slot = lev;
-    if (lev == 0) {  // grids: every row is a candidate
-      L.off = a.max_pages + a.c_cap;
-      L.n = g.n_g;
-      L.fanout = 0;
-      L.parent = nullptr;
-    } else if (lev == 1) {  // chunks of kept grids
-      L.off = a.max_pages;
-      L.n = g.n_c;
-      L.fanout = a.cpg;
-      L.parent = sm.kept_grid;
-    } else {  // pages of kept chunks, or every page when flat
-      L.off = 0;
-      L.n = g.n_p;
-      L.fanout = a.hier ? a.ppc : 0;
-      L.parent = sm.kept_chunk;
-    }
-    L.aff = aff + L.off;
-    L.n_par = kp;
-    const int32_t k = lev == 0 ? a.k_g : (lev == 1 ? a.k_c : a.k_p);
-    kp = select_level(L, k, sm);
-    if (lev < 2) keep_parents(sm, kp, lev == 0 ? sm.kept_grid : sm.kept_chunk);
-  }
+}
+
+__device__ __forceinline__ void write_selection(const ScoreArgs& a, const SelectShared& sm, int32_t s, int32_t kp) {
+  const int tid = threadIdx.x;
   for (int32_t i = tid; i < a.k_p; i += kSelThreads) {
     int32_t idx = -1;
     float sc = 0.f;
@@ -504,11 +500,97 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(ScoreArgs a) {
   if (tid == 0 && a.cnt_out) a.cnt_out[s] = kp;
 }
 
+__global__ __launch_bounds__(kSelThreads) void select_kernel(ScoreArgs a) {
+  __shared__ SelectShared sm;
+  const int32_t s = blockIdx.x;
+  const float* aff = a.aff + (int64_t)s * a.rows_per_seq;
+  const SeqGeom g = seq_geom(a, s, false);  // issued before the staging loads
+  const bool staged = a.rows_per_seq <= kLdsRows;
+  if (staged) stage_rows(sm.aff, aff, (int32_t)a.rows_per_seq);
+  clear_select_state(a, g, sm);
+  __syncthreads();
+  // Levels run as one loop so a single copy of the level code is fetched
+  // (a lone work-group per compute unit starts with a cold instruction cache).
+  int32_t kp = 0;
+  for (int32_t lev = a.hier ? 0 : 2; lev < 3; ++lev) {
+    const Level L = make_level(a, g, lev, staged, aff, kp, sm);
+    kp = select_level(L, lev == 0 ? a.k_g : (lev == 1 ? a.k_c : a.k_p), sm);
+    if (lev < 2) keep_parents(sm, kp, lev == 0 ? sm.kept_grid : sm.kept_chunk);
+  }
+  write_selection(a, sm, s, kp);
+}
+
 // (1 + cos) / 2 clamped to [0, 1]; NaN and -0 become +0.
 __device__ __forceinline__ float affinity_of(float dot, float nr, float sqrt_na, float na) {
   const float c = (nr > 0.f && na > 0.f) ? dot / (sqrtf(nr) * sqrt_na) : 0.f;
   const float v = 0.5f * (1.0f + c);
   return v > 0.f ? (v < 1.f ? v : 1.f) : 0.f;
+}
+
+// The anchor as held by one lane of an LPR-lane row group: float4 pieces
+// lg, lg + LPR, ... of the row, plus the squared norm (every lane of the
+// group holds the full sum after a fixed butterfly).
+template <int LPR, int NQ>
+struct AnchorRegs {
+  f32x4 av[NQ];
+  float na, sqrt_na;
+};
+
+template <int LPR, int NQ>
+__device__ __forceinline__ AnchorRegs<LPR, NQ> load_anchor(const ScoreArgs& a, int32_t s, int32_t lg) {
+  AnchorRegs<LPR, NQ> r;
+  const int32_t Q = a.D >> 2;
+  const f32x4* anc = reinterpret_cast<const f32x4*>(a.anchors + (int64_t)s * a.D);
+  r.na = 0.f;
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int32_t qi = lg + LPR * j;
+    r.av[j] = qi < Q ? anc[qi] : f32x4{0.f, 0.f, 0.f, 0.f};
+    r.na = fmaf(r.av[j].x, r.av[j].x, r.na);
+    r.na = fmaf(r.av[j].y, r.av[j].y, r.na);
+    r.na = fmaf(r.av[j].z, r.av[j].z, r.na);
+    r.na = fmaf(r.av[j].w, r.av[j].w, r.na);
+  }
+#pragma unroll
+  for (int o = 1; o < LPR; o <<= 1) r.na += __shfl_xor(r.na, o);
+  r.sqrt_na = sqrtf(r.na);
+  return r;
+}
+
+// Loads this lane's pieces of one row (unconditional, from a clamped
+// in-bounds address; pieces past head_dim read as zero).
+template <int LPR, int NQ>
+__device__ __forceinline__ void load_row(const f32x4* rowp, int32_t lg, int32_t Q, f32x4 (&x)[NQ]) {
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int32_t qi = lg + LPR * j;
+    const f32x4 t = load_row4(rowp + min(qi, Q - 1));
+    x[j] = qi < Q ? t : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Affinity of one row from its loaded pieces: fixed FMA order per lane,
+// fixed butterfly over the group, so every caller gets the same bits.
+template <int LPR, int NQ>
+__device__ __forceinline__ float row_affinity(const f32x4 (&x)[NQ], const AnchorRegs<LPR, NQ>& A) {
+  float dot = 0.f, nr = 0.f;
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    dot = fmaf(x[j].x, A.av[j].x, dot);
+    dot = fmaf(x[j].y, A.av[j].y, dot);
+    dot = fmaf(x[j].z, A.av[j].z, dot);
+    dot = fmaf(x[j].w, A.av[j].w, dot);
+    nr = fmaf(x[j].x, x[j].x, nr);
+    nr = fmaf(x[j].y, x[j].y, nr);
+    nr = fmaf(x[j].z, x[j].z, nr);
+    nr = fmaf(x[j].w, x[j].w, nr);
+  }
+#pragma unroll
+  for (int o = 1; o < LPR; o <<= 1) {
+    dot += __shfl_xor(dot, o);
+    nr += __shfl_xor(nr, o);
+  }
+  return affinity_of(dot, nr, A.sqrt_na, A.na);
 }
 
 template <int LPR, int NQ, int R>
@@ -525,77 +607,110 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   const int32_t Q = a.D >> 2;
   const f32x4* seq = reinterpret_cast<const f32x4*>(a.lvl + (int64_t)s * a.rows_per_seq * a.D);
   float* aff = a.aff + (int64_t)s * a.rows_per_seq;
-
   const int32_t grp = tid / LPR, lg = tid % LPR;
-  f32x4 av[NQ];
-  float na = 0.f;
-  const f32x4* anc = reinterpret_cast<const f32x4*>(a.anchors + (int64_t)s * a.D);
-#pragma unroll
-  for (int j = 0; j < NQ; ++j) {
-    const int32_t qi = lg + LPR * j;
-    av[j] = qi < Q ? anc[qi] : f32x4{0.f, 0.f, 0.f, 0.f};
-    na = fmaf(av[j].x, av[j].x, na);
-    na = fmaf(av[j].y, av[j].y, na);
-    na = fmaf(av[j].z, av[j].z, na);
-    na = fmaf(av[j].w, av[j].w, na);
-  }
-#pragma unroll
-  for (int o = 1; o < LPR; o <<= 1) na += __shfl_xor(na, o);
-  const float sqrt_na = sqrtf(na);
+  const AnchorRegs<LPR, NQ> A = load_anchor<LPR, NQ>(a, s, lg);
 
   for (int32_t v = v0 + grp; v < v1; v += NG * R) {
     f32x4 x[R][NQ];
     int64_t row[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
+      // a row past the tile is replaced by row 0 (loaded, never written back)
       const int32_t vr = v + NG * r;
       const bool ok = vr < v1;
       row[r] = !ok ? 0
                : vr < g.n_p ? vr
                : vr < g.n_p + g.n_c ? (int64_t)a.max_pages + (vr - g.n_p)
                                     : (int64_t)a.max_pages + a.c_cap + (vr - g.n_p - g.n_c);
-#pragma unroll
-      for (int j = 0; j < NQ; ++j) {
-        // unconditional load from a clamped, in-bounds address (row 0 stands
-        // in for a row past the tile, which is never written back)
-        const int32_t qi = lg + LPR * j;
-        const f32x4 t = load_row4(seq + row[r] * Q + min(qi, Q - 1));
-        x[r][j] = qi < Q ? t : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      load_row<LPR, NQ>(seq + row[r] * Q, lg, Q, x[r]);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float dot = 0.f, nr = 0.f;
-#pragma unroll
-      for (int j = 0; j < NQ; ++j) {
-        dot = fmaf(x[r][j].x, av[j].x, dot);
-        dot = fmaf(x[r][j].y, av[j].y, dot);
-        dot = fmaf(x[r][j].z, av[j].z, dot);
-        dot = fmaf(x[r][j].w, av[j].w, dot);
-        nr = fmaf(x[r][j].x, x[r][j].x, nr);
-        nr = fmaf(x[r][j].y, x[r][j].y, nr);
-        nr = fmaf(x[r][j].z, x[r][j].z, nr);
-        nr = fmaf(x[r][j].w, x[r][j].w, nr);
-      }
-#pragma unroll
-      for (int o = 1; o < LPR; o <<= 1) {
-        dot += __shfl_xor(dot, o);
-        nr += __shfl_xor(nr, o);
-      }
-      if (lg == 0 && v + NG * r < v1) aff[row[r]] = affinity_of(dot, nr, sqrt_na, na);
+      const float v_aff = row_affinity<LPR, NQ>(x[r], A);
+      if (lg == 0 && v + NG * r < v1) aff[row[r]] = v_aff;
     }
   }
 }
 
+// Lazy hierarchical scoring: one work-group per sequence scores the grids,
+// selects, scores only the chunks of kept grids, selects, scores only the
+// pages of kept chunks and selects (the page's coarse-to-fine order).  Rows
+// under unkept parents are never read; their score is +0 by definition, so
+// the selection equals the one over every row.  Scored affinities land in
+// LDS when the sequence's rows fit, else in `a.aff`; when `lazy_out` is set
+// they are also written there (other rows untouched).
+template <int LPR, int NQ, int R>
+__global__ __launch_bounds__(kSelThreads) void lazy_kernel(ScoreArgs a, float* lazy_out) {
+  __shared__ SelectShared sm;
+  constexpr int NG = kSelThreads / LPR;
+  const int tid = threadIdx.x;
+  const int32_t s = blockIdx.x;
+  const SeqGeom g = seq_geom(a, s, tid == 0);
+  const int32_t Q = a.D >> 2;
+  const f32x4* seq = reinterpret_cast<const f32x4*>(a.lvl + (int64_t)s * a.rows_per_seq * a.D);
+  float* aff = a.aff + (int64_t)s * a.rows_per_seq;
+  float* out = lazy_out ? lazy_out + (int64_t)s * a.rows_per_seq : nullptr;
+  const bool staged = a.rows_per_seq <= kLdsRows;
+  const int32_t grp = tid / LPR, lg = tid % LPR;
+  const AnchorRegs<LPR, NQ> A = load_anchor<LPR, NQ>(a, s, lg);
+  clear_select_state(a, g, sm);
+  __syncthreads();
+  int32_t kp = 0;
+  for (int32_t lev = 0; lev < 3; ++lev) {
+    const Level L = make_level(a, g, lev, staged, aff, kp, sm);
+    const int32_t m = L.fanout ? L.n_par * L.fanout : L.n;
+    for (int32_t c0 = grp; c0 < m; c0 += NG * R) {
+      f32x4 x[R][NQ];
+      int32_t e[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int32_t c = c0 + NG * r;
+        e[r] = c < m ? cand32(L, sm, c) : -1;
+        load_row<LPR, NQ>(seq + (int64_t)(L.off + (e[r] >= 0 ? e[r] : 0)) * Q, lg, Q, x[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float v_aff = row_affinity<LPR, NQ>(x[r], A);
+        if (lg == 0 && e[r] >= 0) {
+          if (staged) sm.aff[L.off + e[r]] = v_aff;
+          else aff[L.off + e[r]] = v_aff;
+          if (out) out[L.off + e[r]] = v_aff;
+        }
+      }
+    }
+    __syncthreads();
+    kp = select_level(L, lev == 0 ? a.k_g : (lev == 1 ? a.k_c : a.k_p), sm);
+    if (lev < 2) keep_parents(sm, kp, lev == 0 ? sm.kept_grid : sm.kept_chunk);
+  }
+  write_selection(a, sm, s, kp);
+}
+
 template <int NQ>
-hipError_t launch_nq(const ScoreArgs& a, hipStream_t st) {
+hipError_t launch_nq(const ScoreArgs& a, bool lazy, float* lazy_out, hipStream_t st) {
   constexpr int R = NQ >= KKA_SCORE_LOADS ? 1 : KKA_SCORE_LOADS / NQ;
+  if (lazy) {
+    constexpr int RL = NQ >= 16 ? 1 : 16 / NQ;  // 16 row loads in flight per lane
+    hipLaunchKernelGGL((lazy_kernel<KKA_SCORE_LPR, NQ, RL>), dim3((unsigned)a.S), dim3(kSelThreads), 0, st, a,
+                       lazy_out);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((int64_t)a.S * a.tiles_per_seq));
   hipLaunchKernelGGL((score_kernel<KKA_SCORE_LPR, NQ, R>), grid, dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.S), dim3(kSelThreads), 0, st, a);
   return hipGetLastError();
+}
+
+hipError_t dispatch(const ScoreArgs& a, bool lazy, float* lazy_out, hipStream_t st) {
+  if (a.S <= 0) return hipSuccess;
+  const int32_t nq = (a.D / 4 + KKA_SCORE_LPR - 1) / KKA_SCORE_LPR;
+  if (nq <= 1) return launch_nq<1>(a, lazy, lazy_out, st);
+  if (nq <= 2) return launch_nq<2>(a, lazy, lazy_out, st);
+  if (nq <= 4) return launch_nq<4>(a, lazy, lazy_out, st);
+  if (nq <= 8) return launch_nq<8>(a, lazy, lazy_out, st);
+  if (nq <= 16) return launch_nq<16>(a, lazy, lazy_out, st);
+  return launch_nq<32>(a, lazy, lazy_out, st);
 }
 
 }  // namespace
@@ -609,15 +724,10 @@ int32_t score_rows_per_tile(int32_t D) {
   return (256 / KKA_SCORE_LPR) * R * KKA_SCORE_PASSES;
 }
 
-hipError_t launch_score_topk(const ScoreArgs& a, hipStream_t st) {
-  if (a.S <= 0) return hipSuccess;
-  const int32_t nq = (a.D / 4 + KKA_SCORE_LPR - 1) / KKA_SCORE_LPR;
-  if (nq <= 1) return launch_nq<1>(a, st);
-  if (nq <= 2) return launch_nq<2>(a, st);
-  if (nq <= 4) return launch_nq<4>(a, st);
-  if (nq <= 8) return launch_nq<8>(a, st);
-  if (nq <= 16) return launch_nq<16>(a, st);
-  return launch_nq<32>(a, st);
+hipError_t launch_score_topk(const ScoreArgs& a, hipStream_t st) { return dispatch(a, false, nullptr, st); }
+
+hipError_t launch_score_topk_lazy(const ScoreArgs& a, float* lazy_out, hipStream_t st) {
+  return dispatch(a, true, lazy_out, st);
 }
 
 }  // namespace kka

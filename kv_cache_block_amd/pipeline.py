@@ -69,12 +69,13 @@ class Selector:
     def levels(self, n_pages: torch.Tensor, first_dirty_page: Optional[torch.Tensor] = None, stream=None):
         kka_build_levels(self.lay, self.level, n_pages, first_dirty_page, stream=stream)
 
-    def score(self, n_pages: torch.Tensor, anchors: Optional[torch.Tensor] = None, stream=None):
+    def score(self, n_pages: torch.Tensor, anchors: Optional[torch.Tensor] = None, stream=None, lazy: bool = False):
+        """Affinity + top-K; lazy=True scores only children of kept parents."""
         kka_score_topk(self.lay, self.level, n_pages, self.anchors if anchors is None else anchors,
                        k_page=self.sel["k_page"], k_grid=self.sel.get("k_grid", 0),
                        k_chunk=self.sel.get("k_chunk", 0), page_idx_out=self.page_idx,
                        page_score_out=self.page_score, n_selected_out=self.n_selected,
-                       affinity_out=self.affinity, workspace=self.ws_score, stream=stream)
+                       affinity_out=self.affinity, workspace=self.ws_score, stream=stream, lazy=lazy)
 
     def step(self, n_pages: torch.Tensor, stream=None):
         """Whole path over the batch: pool, anchor, levels, score + top-K."""

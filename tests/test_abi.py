@@ -138,8 +138,12 @@ def test_level_rows_and_score_validation(L):
     assert L.kka_level_rows(ctypes.byref(flat)) == 1025
     for bad in (kka.c_level_layout(1, 100, 12, 1, 16, 16), kka.c_level_layout(1, 100, 128, 1, 0, 16),
                 kka.c_level_layout(1, 16 * 16385, 128, 1, 16, 16), kka.c_level_layout(1, 100, 1024, 1, 16, 17),
-                kka.c_level_layout(-1, 100, 128, 0, 16, 16)):
+                kka.c_level_layout(-1, 100, 128, 0, 16, 16), kka.c_level_layout(1, (1 << 30) + 1, 128, 0, 16, 16),
+                kka.c_level_layout(1, 1 << 30, 128, 1, (1 << 29) + 1, 16)):
         assert L.kka_level_rows(ctypes.byref(bad)) == -1
+    # page counts up to 2^30, also once rounded up to whole chunks
+    assert L.kka_level_rows(ctypes.byref(kka.c_level_layout(1, 1 << 30, 128, 0, 16, 16))) == 1 << 30
+    assert L.kka_level_rows(ctypes.byref(kka.c_level_layout(1, 1 << 30, 128, 1, 1 << 16, 16))) == (1 << 30) + 16384 + 1024
     sel = kka.c_select(4, 16, 64)
     ws = L.kka_score_topk_workspace(ctypes.byref(lay), ctypes.byref(sel), 0)
     assert ws >= 64 * 8736 * 4  # scratch affinities
@@ -159,6 +163,19 @@ def test_level_rows_and_score_validation(L):
     assert score(kka.c_level_layout(1, 100, 12, 1, 16, 16), sel) == 2
     assert L.kka_build_levels(ctypes.byref(kka.c_level_layout(1, 100, 12, 1, 16, 16)), FAKE, FAKE, None,
                               None) == 2
+    # the lazy entry point validates exactly like kka_score_topk
+    def lazy(lay_, sel_, lvl=FAKE, npg=FAKE, anc=FAKE, idx=FAKE, w=FAKE, wb=ws):
+        return L.kka_score_topk_lazy(ctypes.byref(lay_), lvl, npg, anc, ctypes.byref(sel_), None, idx, None, None,
+                                     w, wb, None)
+
+    assert lazy(lay, kka.c_select(4, 16, 1025)) == 2
+    assert lazy(lay, kka.c_select(4, -1, 64)) == 2
+    assert lazy(lay, sel, npg=None) == 1
+    assert lazy(lay, sel, lvl=FAKE_ODD) == 3
+    assert lazy(lay, sel, wb=ws - 4) == 4
+    assert lazy(flat, kka.c_select(0, 0, 1025)) == 2
+    assert lazy(kka.c_level_layout(0, 100, 128, 1, 16, 16), sel, lvl=None, npg=None, anc=None, idx=None,
+                w=None, wb=0) == 0
     assert L.kka_build_levels(ctypes.byref(lay), None, FAKE, None, None) == 1
     assert L.kka_build_levels(ctypes.byref(lay), FAKE_ODD, FAKE, None, None) == 3
 
