@@ -60,8 +60,9 @@ def lib():
         L.oracle_build_levels.argtypes = [vp, i32, i32, i32, i32, vp, vp]
         L.oracle_affinity.argtypes = [vp, i64, i32, vp, vp]
         L.oracle_select.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]
+        L.oracle_stability.argtypes = [vp, i32, i64, i32, ctypes.c_float, vp, vp]
         for f in (L.oracle_head_weights, L.oracle_pool_block, L.oracle_pool_anchor, L.oracle_build_levels,
-                  L.oracle_affinity, L.oracle_select):
+                  L.oracle_affinity, L.oracle_select, L.oracle_stability):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -170,6 +171,23 @@ def select(aff_pages, aff_chunks=None, aff_grids=None, *, hierarchical: int, k_g
                                int(hierarchical), k_grid, k_chunk, k_page, _p(idx), _p(sc), _p(cnt)), "select")
     c = int(cnt[0])
     return idx[:c].copy(), sc[:c].copy()
+
+
+def stability(aff_hist, window: int, theta: float):
+    """(score fp32 [n], window bits uint32 [n]) of n blocks from their
+    affinities over the steps so far (aff_hist [n_steps][n], oldest first;
+    a step before a block existed carries an affinity <= theta).
+    Pinned: the page's worked values (golden W3), closed forms."""
+    a = np.ascontiguousarray(aff_hist, dtype=np.float32)
+    if a.ndim != 2:
+        raise ValueError("aff_hist must be [n_steps][n]")
+    n_steps, n = a.shape
+    score = np.zeros(n, dtype=np.float32)
+    bits = np.zeros(n, dtype=np.uint32) if window <= 32 else None
+    _check(lib().oracle_stability(_p(a) if a.size else None, n_steps, n, window, float(theta),
+                                  _p(score) if n else None, _p(bits) if (bits is not None and n) else None),
+           "stability")
+    return score, bits
 
 
 # --------------------------------------------------------------- pipelines

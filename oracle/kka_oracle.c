@@ -306,3 +306,35 @@ int oracle_select(const float* aff_pages, const float* aff_chunks, const float* 
   free(sc);
   return 0;
 }
+
+/*
+ * Stability score (section 5.3 "stability filtering"): over the last W
+ * decode steps, the fraction of steps in which a block's affinity was high.
+ * The page gives the window W (usually 20), the per-step threshold theta
+ * (usually 0.5) and two worked values; its formula was lost in extraction.
+ * Readings: a step is high when aff > theta (strict); a step before the
+ * first one, or before the block existed (the caller passes an affinity at
+ * or below theta for it), is not high; the score is count / W from the
+ * first step on (fp64 division rounded once to fp32).
+ * aff_hist: [n_steps][n] affinities of n blocks, oldest step first.
+ * bits_out (optional, W <= 32): the same window as a word, bit i set when
+ * the step i steps before the newest was high.
+ */
+int oracle_stability(const float* aff_hist, int32_t n_steps, int64_t n, int32_t W, float theta, float* score_out,
+                     uint32_t* bits_out) {
+  if (n_steps < 0 || n < 0 || W < 1 || (bits_out && W > 32) || (n > 0 && (!score_out || (n_steps > 0 && !aff_hist))))
+    return 1;
+  int32_t first = n_steps > W ? n_steps - W : 0; /* oldest step still in the window */
+  for (int64_t b = 0; b < n; ++b) {
+    int32_t count = 0;
+    uint32_t bits = 0u;
+    for (int32_t t = first; t < n_steps; ++t) {
+      int high = (double)aff_hist[(int64_t)t * n + b] > (double)theta;
+      count += high;
+      if (high) bits |= 1u << (n_steps - 1 - t);
+    }
+    score_out[b] = (float)((double)count / (double)W);
+    if (bits_out) bits_out[b] = bits;
+  }
+  return 0;
+}

@@ -501,3 +501,74 @@ def test_recovery_config4():
         r = oracle.score_select(v.vb[s], v.anchors[s], v.select)
         assert len(r["idx"]) == 64
         assert (v.page_topic[s][r["idx"]] == v.anchor_topic[s]).all()
+
+
+# ------------------------------------------------------------ stability filter (section 5.3)
+
+def test_w3_stability_example():
+    """The page's two worked values (1/20 = 0.05 for a single spike, 1.0 for
+    twenty steps above 0.6) and three blocks worked by hand."""
+    g = json.load(open(os.path.join(GOLDEN, "w3_stability.json")))
+    for blk in g["blocks"]:
+        hist = np.asarray(blk["steps"], np.float32)[:, None]
+        score, bits = oracle.stability(hist, g["window"], g["theta"])
+        assert score[0] == np.float32(blk["expected_score"]), blk["name"]
+        assert int(bits[0]) == blk["expected_bits"], blk["name"]
+
+
+def test_stability_closed_forms():
+    W = 20
+    # fewer steps than the window: the missing steps count as not high
+    hist = np.full((7, 1), 0.9, np.float32)
+    assert oracle.stability(hist, W, 0.5)[0][0] == np.float32(7 / 20)
+    # W = 1 sees only the newest step
+    hist = np.array([[0.9], [0.9], [0.1]], np.float32)
+    assert oracle.stability(hist, 1, 0.5)[0][0] == 0.0
+    assert oracle.stability(hist[:2], 1, 0.5)[0][0] == 1.0
+    # a full 32-step window of high steps fills the word
+    score, bits = oracle.stability(np.full((40, 3), 0.75, np.float32), 32, 0.5)
+    assert (score == 1.0).all() and (bits == 0xFFFFFFFF).all()
+    # no steps yet
+    score, bits = oracle.stability(np.zeros((0, 4), np.float32), 20, 0.5)
+    assert (score == 0).all() and (bits == 0).all()
+
+
+def test_stability_matches_box_filter():
+    """Every prefix of a random history against a numpy box filter (a
+    length-W convolution of the high-step indicator) divided by W."""
+    rng = np.random.default_rng(31)
+    n_steps, n = 45, 9
+    for W, theta in ((20, 0.5), (1, 0.5), (32, 0.3), (7, 0.65)):
+        hist = rng.uniform(0, 1, (n_steps, n)).astype(np.float32)
+        high = (hist > np.float32(theta)).astype(np.int64)
+        for t in range(n_steps + 1):
+            score, bits = oracle.stability(hist[:t], W, theta)
+            if t == 0:
+                assert (score == 0).all()
+                continue
+            windowed = np.stack([np.convolve(high[:t, b], np.ones(W, np.int64))[t - 1] for b in range(n)])
+            np.testing.assert_array_equal(score, (windowed / W).astype(np.float32))
+            # bit i of the word is the step i before the newest
+            for i in range(min(W, t)):
+                np.testing.assert_array_equal((bits >> np.uint32(i)) & np.uint32(1), high[t - 1 - i])
+
+
+def test_stability_shift_invariant_and_threshold_monotone():
+    """One more step shifts the window word left by one and brings in the new
+    step's bit; raising theta never raises a score."""
+    rng = np.random.default_rng(32)
+    hist = rng.uniform(0, 1, (30, 50)).astype(np.float32)
+    W = 20
+    mask = np.uint32((1 << W) - 1)
+    for t in range(1, 30):
+        _, before = oracle.stability(hist[:t], W, 0.5)
+        _, after = oracle.stability(hist[:t + 1], W, 0.5)
+        new = (hist[t] > np.float32(0.5)).astype(np.uint32)
+        np.testing.assert_array_equal(after, ((before << np.uint32(1)) | new) & mask)
+    prev = None
+    for theta in (0.0, 0.25, 0.5, 0.75, 1.0):
+        score, _ = oracle.stability(hist, W, theta)
+        if prev is not None:
+            assert (score <= prev).all()
+        prev = score
+    assert (oracle.stability(hist, W, 1.0)[0] == 0).all()  # affinities never exceed 1
