@@ -208,6 +208,20 @@ def run(args):
     n_g4 = -(-n_c4 // 16)
     c4_lazy_rows = lazy_rows(n_g4, v.select)
 
+    # single pass with the stability filter fused in (window 20, theta 0.5)
+    hist4 = torch.zeros((S, NP), dtype=torch.int32, device=dev)
+    stab4 = torch.zeros((S, NP), dtype=torch.float32, device=dev)
+
+    def stable4(i):
+        kka.kka_score_topk_stable(lay4, levels[i % n_sets], npg4, anchors, history=hist4, stability_out=stab4,
+                                  window=20, theta=0.5, k_page=kp4, k_grid=v.select["k_grid"],
+                                  k_chunk=v.select["k_chunk"], page_idx_out=idx4, page_score_out=sc4,
+                                  n_selected_out=cnt4, affinity_out=affs[i % n_sets], workspace=ws4)
+
+    c4_stable_us = time_calls(stable4, args.steps, max(3, args.warmup), stream)
+    if not np.array_equal(idx4.cpu().numpy(), got):
+        raise RuntimeError("scoring with the stability filter selected different pages (serving batch)")
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -251,6 +265,7 @@ def run(args):
         "lazy_rows_scored_per_seq": c3_lazy_rows,
         "serving_lazy_score_topk_us_per_step": round(c4_lazy_us, 2),
         "serving_lazy_rows_scored_per_seq": c4_lazy_rows,
+        "serving_stable_score_topk_us_per_step": round(c4_stable_us, 2),
         "serving_topic_recovered_seqs": recovered,
         "roofline": {
             "bound": "hbm",

@@ -249,6 +249,48 @@ KKA_API kka_status kka_score_topk(const kka_level_layout* lay, const float* leve
 KKA_API size_t kka_score_topk_workspace(const kka_level_layout* lay, const kka_select* sel, int32_t with_affinity_out);
 
 /*
+ * Stability filter state (page section 5.3): per page, a word holding the
+ * last `window` steps, bit i set when the page's affinity i steps before the
+ * newest was above `theta`.  stability score = set bits / window.
+ *
+ * history    device [num_seqs][max_pages] uint32, caller-owned, in/out;
+ *            word of page p of sequence s at s * max_pages + p.  Zero-fill
+ *            it for a new sequence or a new page (no steps seen yet).
+ *            Only words of present pages (p < n_pages[s]) are touched.
+ * score_out  device [num_seqs][max_pages] fp32, same indexing, or NULL.
+ * window     number of steps, 1..32 (the page uses 20).
+ * theta      per-step threshold, finite (the page uses 0.5); a step counts
+ *            when the affinity is strictly above it.
+ * Readings where the page is silent: the strict comparison; steps before
+ * the first (or before the page existed) count as not high, so the score
+ * is set bits / window from the first step on; the affinity is the page's
+ * own, before any hierarchical masking.
+ */
+typedef struct kka_stability {
+  uint32_t* history;
+  float* score_out;
+  int32_t window;
+  float theta;
+} kka_stability;
+
+/*
+ * kka_score_topk_stable -- kka_score_topk with the stability filter fused
+ * into the scoring pass: every present page's window word shifts by one
+ * step and takes this step's bit (one 4-byte read and write per page, plus
+ * the 4-byte score when score_out is set).  Selection is unchanged (the
+ * page leaves the trigger threshold on the score to the caller, who reads
+ * score_out).  Other arguments, rules and workspace as kka_score_topk.
+ * Errors: stab NULL or history NULL (with num_seqs > 0 and max_pages > 0)
+ * -> KKA_ERR_NULL; window outside 1..32 or theta not finite -> KKA_ERR_SHAPE;
+ * history or score_out not 4-byte aligned -> KKA_ERR_ALIGN.
+ */
+KKA_API kka_status kka_score_topk_stable(const kka_level_layout* lay, const float* level_buf, const int32_t* n_pages,
+                                         const float* anchors, const kka_select* sel, const kka_stability* stab,
+                                         float* affinity_out, int32_t* page_idx_out, float* page_score_out,
+                                         int32_t* n_selected_out, void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
+/*
  * kka_score_topk_lazy -- the same selection, scored coarse to fine (page
  * section 5.1: chunks are scored only inside kept grids, pages only inside
  * surviving chunks).  One work-group per sequence scores the grids, keeps

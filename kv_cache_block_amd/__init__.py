@@ -10,8 +10,9 @@ raises.
 
 Entry points keep the C names: :func:`kka_pool_blocks`,
 :func:`kka_pool_anchor`, :func:`kka_build_levels`, :func:`kka_score_topk`,
-:func:`kka_score_topk_lazy`, :func:`kka_device_error` (plus the ``*_workspace``
-size queries).
+:func:`kka_score_topk_lazy`, :func:`kka_score_topk_stable` (through
+:func:`kka_score_topk` with ``history=``), :func:`kka_device_error` (plus the
+``*_workspace`` size queries).
 """
 from __future__ import annotations
 
@@ -40,7 +41,7 @@ _STATUS = {0: "ok", 1: "KKA_ERR_NULL", 2: "KKA_ERR_SHAPE", 3: "KKA_ERR_ALIGN", 4
 ENTRY_POINTS = (
     "kka_pool_blocks", "kka_pool_blocks_workspace", "kka_pool_anchor", "kka_pool_anchor_workspace",
     "kka_level_rows", "kka_build_levels", "kka_score_topk", "kka_score_topk_workspace", "kka_score_topk_lazy",
-    "kka_device_error",
+    "kka_score_topk_stable", "kka_device_error",
     "kka_status_string", "kka_version",
 )
 
@@ -79,6 +80,11 @@ class c_select(ctypes.Structure):
     _fields_ = [("k_grid", ctypes.c_int32), ("k_chunk", ctypes.c_int32), ("k_page", ctypes.c_int32)]
 
 
+class c_stability(ctypes.Structure):
+    _fields_ = [("history", ctypes.c_void_p), ("score_out", ctypes.c_void_p), ("window", ctypes.c_int32),
+                ("theta", ctypes.c_float)]
+
+
 _lib = None
 
 
@@ -101,9 +107,12 @@ def lib() -> ctypes.CDLL:
         L.kka_score_topk.argtypes = [P(c_level_layout), vp, vp, vp, P(c_select), vp, vp, vp, vp, vp, sz, vp]
         L.kka_score_topk_workspace.argtypes = [P(c_level_layout), P(c_select), i32]
         L.kka_score_topk_lazy.argtypes = [P(c_level_layout), vp, vp, vp, P(c_select), vp, vp, vp, vp, vp, sz, vp]
+        L.kka_score_topk_stable.argtypes = [P(c_level_layout), vp, vp, vp, P(c_select), P(c_stability), vp, vp, vp,
+                                            vp, vp, sz, vp]
         L.kka_device_error.argtypes = [vp]
         L.kka_status_string.argtypes = [ctypes.c_int]
-        for f in ("kka_pool_blocks", "kka_pool_anchor", "kka_build_levels", "kka_score_topk", "kka_score_topk_lazy"):
+        for f in ("kka_pool_blocks", "kka_pool_anchor", "kka_build_levels", "kka_score_topk", "kka_score_topk_lazy",
+                  "kka_score_topk_stable"):
             getattr(L, f).restype = ctypes.c_int
         for f in ("kka_pool_blocks_workspace", "kka_pool_anchor_workspace", "kka_score_topk_workspace"):
             getattr(L, f).restype = sz
@@ -305,9 +314,12 @@ def kka_score_topk(lay: LevelLayout, level_buf: torch.Tensor, n_pages: torch.Ten
                    k_page: int, k_grid: int = 0, k_chunk: int = 0, page_idx_out: torch.Tensor,
                    page_score_out: Optional[torch.Tensor] = None, n_selected_out: Optional[torch.Tensor] = None,
                    affinity_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                   stream=None, lazy: bool = False):
-    """Affinities of every level row and the top-k pages of each sequence
-    (lazy=True: kka_score_topk_lazy, scoring only children of kept parents)."""
+                   stream=None, lazy: bool = False, history: Optional[torch.Tensor] = None,
+                   stability_out: Optional[torch.Tensor] = None, window: int = 20, theta: float = 0.5):
+    """Affinities of every level row and the top-k pages of each sequence.
+    lazy=True: kka_score_topk_lazy (scores only children of kept parents).
+    history given: kka_score_topk_stable (uint32 [S][max_pages] window words
+    updated in place; stability scores into stability_out when given)."""
     S, D = lay.num_seqs, lay.head_dim
     lp = _dev(level_buf, "level_buf", torch.float32, min_numel=S * lay.rows_per_seq * D)
     npp = _dev(n_pages, "n_pages", torch.int32, min_numel=S)
@@ -319,6 +331,16 @@ def kka_score_topk(lay: LevelLayout, level_buf: torch.Tensor, n_pages: torch.Ten
     need = kka_score_topk_workspace(lay, affinity_out is not None)
     wp, wbytes, keep = _ws(workspace, need, level_buf.device)
     sel = c_select(int(k_grid), int(k_chunk), int(k_page))
+    if history is not None:
+        if lazy:
+            raise ValueError("the stability filter needs every page scored: it runs with the single pass only")
+        n_words = S * lay.max_pages
+        hp = _dev(history, "history", (torch.int32, torch.uint32), min_numel=n_words)
+        so = _dev(stability_out, "stability_out", torch.float32, min_numel=n_words, allow_none=True)
+        stab = c_stability(hp.value, None if so is None else so.value, int(window), float(theta))
+        _check(lib().kka_score_topk_stable(ctypes.byref(lay.c), lp, npp, anc, ctypes.byref(sel), ctypes.byref(stab),
+                                           aff, idx, sc, cnt, wp, wbytes, _stream(stream)), "kka_score_topk_stable")
+        return keep
     fn = lib().kka_score_topk_lazy if lazy else lib().kka_score_topk
     _check(fn(ctypes.byref(lay.c), lp, npp, anc, ctypes.byref(sel), aff, idx, sc, cnt, wp, wbytes, _stream(stream)),
            "kka_score_topk_lazy" if lazy else "kka_score_topk")
@@ -341,3 +363,9 @@ def kka_device_error(stream=None) -> int:
 
 def version() -> int:
     return int(lib().kka_version())
+
+
+def kka_score_topk_stable(lay: LevelLayout, level_buf: torch.Tensor, n_pages: torch.Tensor, anchors: torch.Tensor,
+                          *, history: torch.Tensor, **kw):
+    """kka_score_topk_stable: kka_score_topk plus the fused stability update."""
+    return kka_score_topk(lay, level_buf, n_pages, anchors, history=history, **kw)

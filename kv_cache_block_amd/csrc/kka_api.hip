@@ -3,6 +3,8 @@
 // rejected call has no effect on the device.
 #include <mutex>
 
+#include <cmath>
+
 #include "kka_internal.h"
 
 namespace kka {
@@ -344,6 +346,32 @@ kka_status kka_score_topk(const kka_level_layout* lay, const float* level_buf, c
   const kka_status st = prepare_score(lay, level_buf, n_pages, anchors, sel, affinity_out, page_idx_out,
                                       page_score_out, n_selected_out, workspace, workspace_bytes, need, a);
   if (st != KKA_OK || lay->num_seqs == 0) return st;
+  return launched(launch_score_topk(a, static_cast<hipStream_t>(stream)));
+}
+
+kka_status kka_score_topk_stable(const kka_level_layout* lay, const float* level_buf, const int32_t* n_pages,
+                                 const float* anchors, const kka_select* sel, const kka_stability* stab,
+                                 float* affinity_out, int32_t* page_idx_out, float* page_score_out,
+                                 int32_t* n_selected_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!stab || !lay) return KKA_ERR_NULL;
+  if (stab->window < 1 || stab->window > 32 || !std::isfinite(stab->theta)) return KKA_ERR_SHAPE;
+  const bool words = lay->num_seqs > 0 && lay->max_pages > 0;
+  if (words && !stab->history) return KKA_ERR_NULL;
+  if (words &&
+      ((reinterpret_cast<uintptr_t>(stab->history) & 3u) || (reinterpret_cast<uintptr_t>(stab->score_out) & 3u)))
+    return KKA_ERR_ALIGN;
+  ScoreArgs a;
+  const size_t need = kka_score_topk_workspace(lay, sel, affinity_out != nullptr);
+  const kka_status st = prepare_score(lay, level_buf, n_pages, anchors, sel, affinity_out, page_idx_out,
+                                      page_score_out, n_selected_out, workspace, workspace_bytes, need, a);
+  if (st != KKA_OK || lay->num_seqs == 0) return st;
+  if (words) {
+    a.hist = stab->history;
+    a.stab_out = stab->score_out;
+    a.stab_w = stab->window;
+    a.stab_mask = stab->window == 32 ? 0xFFFFFFFFu : ((1u << stab->window) - 1u);
+    a.theta = stab->theta;
+  }
   return launched(launch_score_topk(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -114,6 +114,12 @@ struct ScoreArgs {
   int32_t* cnt_out;
   int32_t tiles_per_seq, rows_per_tile;
   uint32_t* err;
+  // stability filter (page rows only; hist == nullptr: off)
+  uint32_t* hist;        // window words, hist + s * max_pages + page
+  float* stab_out;       // stability scores, same indexing (may be null)
+  uint32_t stab_mask;    // low `stab_w` bits set
+  int32_t stab_w;
+  float theta;
 };
 
 // ---------------------------------------------------------------- helpers

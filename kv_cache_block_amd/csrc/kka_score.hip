@@ -593,7 +593,17 @@ __device__ __forceinline__ float row_affinity(const f32x4 (&x)[NQ], const Anchor
   return affinity_of(dot, nr, A.sqrt_na, A.na);
 }
 
-template <int LPR, int NQ, int R>
+// Stability window of one page after this step (section 5.3): the word
+// shifts by one step and takes the new step's bit (affinity above theta);
+// the score is the fraction of set bits over the window length.
+__device__ __forceinline__ void stability_step(const ScoreArgs& a, uint32_t h, float v_aff, uint32_t* hist,
+                                               float* stab) {
+  const uint32_t nh = ((h << 1) | (v_aff > a.theta ? 1u : 0u)) & a.stab_mask;
+  *hist = nh;
+  if (stab) *stab = (float)__popc(nh) / (float)a.stab_w;
+}
+
+template <int LPR, int NQ, int R, bool STAB>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   constexpr int NG = 256 / LPR;  // row groups per work-group
   const int tid = threadIdx.x;
@@ -610,9 +620,13 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   const int32_t grp = tid / LPR, lg = tid % LPR;
   const AnchorRegs<LPR, NQ> A = load_anchor<LPR, NQ>(a, s, lg);
 
+  uint32_t* hist = STAB ? a.hist + (int64_t)s * a.max_pages : nullptr;
+  float* stab = STAB && a.stab_out ? a.stab_out + (int64_t)s * a.max_pages : nullptr;
+
   for (int32_t v = v0 + grp; v < v1; v += NG * R) {
     f32x4 x[R][NQ];
     int64_t row[R];
+    uint32_t h[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       // a row past the tile is replaced by row 0 (loaded, never written back)
@@ -623,11 +637,19 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
                : vr < g.n_p + g.n_c ? (int64_t)a.max_pages + (vr - g.n_p)
                                     : (int64_t)a.max_pages + a.c_cap + (vr - g.n_p - g.n_c);
       load_row<LPR, NQ>(seq + row[r] * Q, lg, Q, x[r]);
+      // page rows also load their window word (others load word 0: max_pages >= 1 here)
+      if constexpr (STAB) h[r] = hist[ok && vr < g.n_p ? vr : 0];
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float v_aff = row_affinity<LPR, NQ>(x[r], A);
-      if (lg == 0 && v + NG * r < v1) aff[row[r]] = v_aff;
+      const int32_t vr = v + NG * r;
+      if (lg == 0 && vr < v1) {
+        aff[row[r]] = v_aff;
+        if constexpr (STAB) {
+          if (vr < g.n_p) stability_step(a, h[r], v_aff, hist + vr, stab ? stab + vr : nullptr);
+        }
+      }
     }
   }
 }
@@ -695,7 +717,10 @@ hipError_t launch_nq(const ScoreArgs& a, bool lazy, float* lazy_out, hipStream_t
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((int64_t)a.S * a.tiles_per_seq));
-  hipLaunchKernelGGL((score_kernel<KKA_SCORE_LPR, NQ, R>), grid, dim3(256), 0, st, a);
+  if (a.hist)
+    hipLaunchKernelGGL((score_kernel<KKA_SCORE_LPR, NQ, R, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((score_kernel<KKA_SCORE_LPR, NQ, R, false>), grid, dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.S), dim3(kSelThreads), 0, st, a);

@@ -25,7 +25,7 @@ class Selector:
     """
 
     def __init__(self, kp: KPool, seqs: Seqs, select: dict, max_pages: int, window: int, mode: int = WEIGHT_UNIFORM,
-                 keep_affinity: bool = True, device="cuda"):
+                 keep_affinity: bool = True, device="cuda", stability_window: int = 0, stability_theta: float = 0.5):
         self.kp, self.seqs, self.sel, self.window, self.mode = kp, seqs, dict(select), window, mode
         S = seqs.num_seqs
         self.lay = LevelLayout(S, max_pages, kp.head_dim, bool(select["hierarchical"]),
@@ -43,6 +43,12 @@ class Selector:
         self.ws_pool = new_workspace(kka_pool_blocks_workspace(kp, seqs, mode), device)
         self.ws_anchor = new_workspace(kka_pool_anchor_workspace(kp, seqs, window), device)
         self.ws_score = new_workspace(kka_score_topk_workspace(self.lay, keep_affinity), device)
+        # stability filter state (section 5.3): window words and scores per page
+        self.stability_window, self.stability_theta = stability_window, stability_theta
+        self.history = self.stability = None
+        if stability_window:
+            self.history = torch.zeros((S, max_pages), dtype=torch.int32, device=device)
+            self.stability = torch.zeros((S, max_pages), dtype=torch.float32, device=device)
 
     @property
     def anchor_weights(self) -> Optional[torch.Tensor]:
@@ -70,12 +76,18 @@ class Selector:
         kka_build_levels(self.lay, self.level, n_pages, first_dirty_page, stream=stream)
 
     def score(self, n_pages: torch.Tensor, anchors: Optional[torch.Tensor] = None, stream=None, lazy: bool = False):
-        """Affinity + top-K; lazy=True scores only children of kept parents."""
+        """Affinity + top-K; lazy=True scores only children of kept parents.
+        With a stability window the single pass also advances every page's
+        window word and stability score."""
+        stab = {}
+        if getattr(self, "history", None) is not None and not lazy:
+            stab = dict(history=self.history, stability_out=self.stability, window=self.stability_window,
+                        theta=self.stability_theta)
         kka_score_topk(self.lay, self.level, n_pages, self.anchors if anchors is None else anchors,
                        k_page=self.sel["k_page"], k_grid=self.sel.get("k_grid", 0),
                        k_chunk=self.sel.get("k_chunk", 0), page_idx_out=self.page_idx,
                        page_score_out=self.page_score, n_selected_out=self.n_selected,
-                       affinity_out=self.affinity, workspace=self.ws_score, stream=stream, lazy=lazy)
+                       affinity_out=self.affinity, workspace=self.ws_score, stream=stream, lazy=lazy, **stab)
 
     def step(self, n_pages: torch.Tensor, stream=None):
         """Whole path over the batch: pool, anchor, levels, score + top-K."""

@@ -176,6 +176,24 @@ def test_level_rows_and_score_validation(L):
     assert lazy(flat, kka.c_select(0, 0, 1025)) == 2
     assert lazy(kka.c_level_layout(0, 100, 128, 1, 16, 16), sel, lvl=None, npg=None, anc=None, idx=None,
                 w=None, wb=0) == 0
+    # the stability variant: kka_score_topk's rules plus its own
+    def stable(st, lay_=lay, sel_=sel, anc=FAKE):
+        return L.kka_score_topk_stable(ctypes.byref(lay_), FAKE, FAKE, anc, ctypes.byref(sel_),
+                                       None if st is None else ctypes.byref(st), None, FAKE, None, None, FAKE, ws,
+                                       None)
+
+    st = lambda h=FAKE, so=None, W=20, th=0.5: kka.c_stability(h, so, W, th)
+    assert stable(None) == 1
+    assert stable(st(W=0)) == 2
+    assert stable(st(W=33)) == 2
+    assert stable(st(th=float("nan"))) == 2
+    assert stable(st(th=float("inf"))) == 2
+    assert stable(st(h=None)) == 1
+    assert stable(st(h=FAKE + 2)) == 3
+    assert stable(st(so=FAKE + 1)) == 3
+    assert stable(st(), sel_=kka.c_select(4, 16, 1025)) == 2
+    assert stable(st(), anc=FAKE_ODD) == 3
+    assert stable(st(), lay_=kka.c_level_layout(0, 100, 128, 1, 16, 16)) == 0
     assert L.kka_build_levels(ctypes.byref(lay), None, FAKE, None, None) == 1
     assert L.kka_build_levels(ctypes.byref(lay), FAKE_ODD, FAKE, None, None) == 3
 
