@@ -149,6 +149,42 @@ def run(args):
         raise RuntimeError("lazy scoring selected different pages than the full pass")
     c3_lazy_rows = lazy_rows(n_g, w.select)
 
+    # ---------------------------------------------------------------- pool-on-write decode step
+    # 64 sequences of the same 7B key shape, each owning 128 blocks of this
+    # pool; every step appends one token per sequence (its keys stored into
+    # the pool, its block's vector brought up to date).
+    S_w, nb_w = 64, 128
+    len_w = torch.full((S_w,), 1990, dtype=torch.int32, device=dev)
+    offs_w = torch.arange(0, (S_w + 1) * nb_w, nb_w, dtype=torch.int32, device=dev)
+    seqs_w = kka.Seqs(len_w, offs_w, torch.from_numpy(w.block_table[:S_w * nb_w].copy()).to(dev), S_w * nb_w)
+    vb_w = torch.zeros((S_w, nb_w, w.D), dtype=torch.float32, device=dev)
+    run_w = torch.zeros((S_w, w.D), dtype=torch.float32, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    new_k = (torch.randn((S_w, w.L, w.H, w.D), generator=g, device=dev)).to(torch.bfloat16)
+    kka.kka_pool_on_write(kp, seqs_w, vb_w, run_w, new_k=new_k, seed=True, vb_seq_stride=nb_w)
+
+    def write_step(i):
+        len_w.add_(1)
+        kka.kka_pool_on_write(kp, seqs_w, vb_w, run_w, new_k=new_k, vb_seq_stride=nb_w)
+
+    # time only the library launch: the length update sits outside the events
+    n_w = min(args.steps, 2040 - 1991 - max(3, args.warmup))
+    for _ in range(max(3, args.warmup)):
+        write_step(0)
+    torch.cuda.synchronize()
+    ev_w = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_w)]
+    for i in range(n_w):
+        len_w.add_(1)
+        ev_w[i][0].record(stream)
+        kka.kka_pool_on_write(kp, seqs_w, vb_w, run_w, new_k=new_k, vb_seq_stride=nb_w)
+        ev_w[i][1].record(stream)
+    torch.cuda.synchronize()
+    write_us = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in ev_w]))
+    write_bytes = S_w * (2 * w.L * w.H * w.D * 2 + 3 * w.D * 4)
+    if kka.kka_device_error() != 0:
+        raise RuntimeError("device error flag raised by pool-on-write")
+
     del sel, k, kp
     torch.cuda.empty_cache()
 
@@ -266,6 +302,10 @@ def run(args):
         "serving_lazy_score_topk_us_per_step": round(c4_lazy_us, 2),
         "serving_lazy_rows_scored_per_seq": c4_lazy_rows,
         "serving_stable_score_topk_us_per_step": round(c4_stable_us, 2),
+        "pool_on_write_us_per_step": round(write_us, 2),
+        "pool_on_write_workload": "64 sequences x 7B key shape, one token appended per sequence (keys stored into "
+                                  "the paged pool, open block's vector updated)",
+        "pool_on_write_algorithmic_bytes": write_bytes,
         "serving_topic_recovered_seqs": recovered,
         "roofline": {
             "bound": "hbm",

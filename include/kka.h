@@ -163,6 +163,45 @@ KKA_API kka_status kka_pool_anchor(const kka_kpool* kp, const kka_seqs* seqs, in
 KKA_API size_t kka_pool_anchor_workspace(const kka_kpool* kp, const kka_seqs* seqs, int32_t window);
 
 /*
+ * kka_pool_on_write -- keep block vectors current as keys are written (page
+ * section 2.2 step 1 and section 5.2 step 2: v_b is taken from the keys as
+ * k_proj produces them and stored).  One call per decode step in which
+ * every sequence gained one token: sequence s now holds seq_len[s] tokens
+ * and its newest token t = seq_len[s] - 1 sits in logical block
+ * j = t / block_size at slot t % block_size (the block table must already
+ * list that block).
+ *
+ * new_k          device [num_seqs][num_layers][num_kv_heads][head_dim] bf16
+ *                bits, 16-byte aligned: the new token's keys; they are
+ *                stored into the pool at (layer, block_table[j], slot, head),
+ *                so kp->k must then be writable memory (the const in
+ *                kka_kpool says only that the other entry points never
+ *                write it).  NULL: the keys are already in the pool and are
+ *                only read.
+ * mode           KKA_WEIGHT_UNIFORM (mean over tokens, layers and heads) or
+ *                KKA_WEIGHT_GIVEN (head_weight [num_seqs][L*H], frozen).
+ * running        device [num_seqs][head_dim] fp32, caller-owned state: the
+ *                open block's key sum (uniform) or weighted key sum (given).
+ * seed           0: `running` holds the open block's earlier tokens (a token
+ *                at slot 0 starts a new sum); 1: rebuild it from the pool's
+ *                tokens 0..slot-1 of the open block (e.g. after a prefill,
+ *                or when the state is not known).
+ * vb_out         receives the open block's vector, at row
+ *                s * vb_seq_stride + j (vb_seq_stride > 0) or at the global
+ *                logical block id (vb_seq_stride == 0); 16-byte aligned.
+ * The vector equals the block's mean over its tokens so far, as
+ * kka_pool_blocks computes it, up to fp32 summation order.  Sequences with
+ * seq_len 0 are skipped; a seq_len beyond the sequence's blocks, a bad
+ * physical block or a row past vb_seq_stride raises the device flag.
+ * Errors: KKA_ERR_NULL (kp, seqs, running, vb_out, head_weight in given
+ * mode), KKA_ERR_SHAPE (mode VARIANCE or unknown, vb_seq_stride < 0,
+ * block_size * L * H >= 2^30), KKA_ERR_ALIGN (new_k, vb_out).  One launch.
+ */
+KKA_API kka_status kka_pool_on_write(const kka_kpool* kp, const kka_seqs* seqs, const uint16_t* new_k, int32_t mode,
+                                     const float* head_weight, float* running, int32_t seed, float* vb_out,
+                                     int64_t vb_seq_stride, void* stream);
+
+/*
  * Level buffer geometry (page section 5.1).  Each sequence owns
  * rows_per_seq = kka_level_rows() consecutive rows of head_dim fp32:
  *   pages  rows [0, n_p)                   -- the block vectors v_b

@@ -9,7 +9,7 @@ status.  There is no CPU fallback: without the built library every call
 raises.
 
 Entry points keep the C names: :func:`kka_pool_blocks`,
-:func:`kka_pool_anchor`, :func:`kka_build_levels`, :func:`kka_score_topk`,
+:func:`kka_pool_anchor`, :func:`kka_pool_on_write`, :func:`kka_build_levels`, :func:`kka_score_topk`,
 :func:`kka_score_topk_lazy`, :func:`kka_score_topk_stable` (through
 :func:`kka_score_topk` with ``history=``), :func:`kka_device_error` (plus the
 ``*_workspace`` size queries).
@@ -39,7 +39,7 @@ _STATUS = {0: "ok", 1: "KKA_ERR_NULL", 2: "KKA_ERR_SHAPE", 3: "KKA_ERR_ALIGN", 4
            5: "KKA_ERR_DEVICE"}
 
 ENTRY_POINTS = (
-    "kka_pool_blocks", "kka_pool_blocks_workspace", "kka_pool_anchor", "kka_pool_anchor_workspace",
+    "kka_pool_blocks", "kka_pool_blocks_workspace", "kka_pool_anchor", "kka_pool_anchor_workspace", "kka_pool_on_write",
     "kka_level_rows", "kka_build_levels", "kka_score_topk", "kka_score_topk_workspace", "kka_score_topk_lazy",
     "kka_score_topk_stable", "kka_device_error",
     "kka_status_string", "kka_version",
@@ -102,6 +102,7 @@ def lib() -> ctypes.CDLL:
         L.kka_pool_blocks_workspace.argtypes = [P(c_kpool), P(c_seqs), vp, i32, i32]
         L.kka_pool_anchor.argtypes = [P(c_kpool), P(c_seqs), i32, vp, vp, vp, sz, vp]
         L.kka_pool_anchor_workspace.argtypes = [P(c_kpool), P(c_seqs), i32]
+        L.kka_pool_on_write.argtypes = [P(c_kpool), P(c_seqs), vp, i32, vp, vp, i32, vp, i64, vp]
         L.kka_level_rows.argtypes = [P(c_level_layout)]
         L.kka_build_levels.argtypes = [P(c_level_layout), vp, vp, vp, vp]
         L.kka_score_topk.argtypes = [P(c_level_layout), vp, vp, vp, P(c_select), vp, vp, vp, vp, vp, sz, vp]
@@ -112,7 +113,7 @@ def lib() -> ctypes.CDLL:
         L.kka_device_error.argtypes = [vp]
         L.kka_status_string.argtypes = [ctypes.c_int]
         for f in ("kka_pool_blocks", "kka_pool_anchor", "kka_build_levels", "kka_score_topk", "kka_score_topk_lazy",
-                  "kka_score_topk_stable"):
+                  "kka_score_topk_stable", "kka_pool_on_write"):
             getattr(L, f).restype = ctypes.c_int
         for f in ("kka_pool_blocks_workspace", "kka_pool_anchor_workspace", "kka_score_topk_workspace"):
             getattr(L, f).restype = sz
@@ -293,6 +294,25 @@ def kka_pool_anchor(kp: KPool, seqs: Seqs, window: int, anchor_out: torch.Tensor
     _check(lib().kka_pool_anchor(ctypes.byref(kp.c), ctypes.byref(seqs.c), int(window), hw, ap, wp, wbytes,
                                  _stream(stream)), "kka_pool_anchor")
     return keep
+
+
+def kka_pool_on_write(kp: KPool, seqs: Seqs, vb_out: torch.Tensor, running: torch.Tensor, *,
+                      new_k: Optional[torch.Tensor] = None, mode: int = WEIGHT_UNIFORM,
+                      head_weight: Optional[torch.Tensor] = None, seed: bool = False, vb_seq_stride: int = 0,
+                      stream=None):
+    """One decode step of pool-on-write: each sequence's newest token
+    (seq_len[s] - 1) is stored from new_k [S][L][H][D] (bf16 bits) into the
+    pool, or read from it when new_k is None, and its block's vector is
+    brought up to date from the running sums [S][D] (seed=True rebuilds
+    them from the pool)."""
+    S, D, LH = seqs.num_seqs, kp.head_dim, kp.num_layers * kp.num_kv_heads
+    nk = _dev(new_k, "new_k", _KEY_DTYPES, min_numel=S * LH * D, allow_none=True)
+    hw = _dev(head_weight, "head_weight", torch.float32, min_numel=S * LH, allow_none=mode != WEIGHT_GIVEN)
+    rp = _dev(running, "running", torch.float32, min_numel=S * D)
+    rows = S * vb_seq_stride if vb_seq_stride else seqs.total_blocks
+    vp_ = _dev(vb_out, "vb_out", torch.float32, min_numel=rows * D)
+    _check(lib().kka_pool_on_write(ctypes.byref(kp.c), ctypes.byref(seqs.c), nk, int(mode), hw, rp,
+                                   1 if seed else 0, vp_, int(vb_seq_stride), _stream(stream)), "kka_pool_on_write")
 
 
 def kka_build_levels(lay: LevelLayout, level_buf: torch.Tensor, n_pages: torch.Tensor,

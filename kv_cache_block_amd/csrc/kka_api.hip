@@ -204,6 +204,49 @@ kka_status kka_pool_blocks(const kka_kpool* kp, const kka_seqs* seqs, const int3
   return launched(launch_pool(a, mode, s));
 }
 
+kka_status kka_pool_on_write(const kka_kpool* kp, const kka_seqs* seqs, const uint16_t* new_k, int32_t mode,
+                             const float* head_weight, float* running, int32_t seed, float* vb_out,
+                             int64_t vb_seq_stride, void* stream) {
+  kka_status st = check_kpool(kp);
+  if (st != KKA_OK) return st;
+  if ((st = check_seqs(seqs)) != KKA_OK) return st;
+  if (mode != KKA_WEIGHT_UNIFORM && mode != KKA_WEIGHT_GIVEN) return KKA_ERR_SHAPE;
+  if (vb_seq_stride < 0) return KKA_ERR_SHAPE;
+  if ((int64_t)kp->block_size * kp->num_layers * kp->num_kv_heads >= ((int64_t)1 << 30)) return KKA_ERR_SHAPE;
+  if (seqs->num_seqs == 0) return KKA_OK;
+  if (!running || !vb_out || (mode == KKA_WEIGHT_GIVEN && !head_weight)) return KKA_ERR_NULL;
+  if ((new_k && !aligned16(new_k)) || !aligned16(vb_out)) return KKA_ERR_ALIGN;
+  uint32_t* err = device_error_word();
+  if (!err) return KKA_ERR_DEVICE;
+  (void)hipGetLastError();
+  WriteArgs a{};
+  a.k_new = new_k;
+  a.k = const_cast<uint16_t*>(kp->k);  // written only when new_k is given (documented)
+  a.sL = kp->stride_layer;
+  a.sB = kp->stride_block;
+  a.sT = kp->stride_token;
+  a.sH = kp->stride_head;
+  a.L = kp->num_layers;
+  a.H = kp->num_kv_heads;
+  a.D = kp->head_dim;
+  a.B = kp->block_size;
+  a.P = kp->num_phys_blocks;
+  a.S = seqs->num_seqs;
+  a.seq_len = seqs->seq_len;
+  a.offs = seqs->block_offsets;
+  a.table = seqs->block_table;
+  a.weights = mode == KKA_WEIGHT_GIVEN ? head_weight : nullptr;
+  a.running = running;
+  a.out = vb_out;
+  a.vb_stride = vb_seq_stride;
+  a.seed = seed ? 1 : 0;
+  a.q8 = kp->head_dim / 8;
+  a.m = a.q8 >= 256 ? 1 : 256 / a.q8;
+  a.nt = a.q8 * a.m;
+  a.err = err;
+  return launched(launch_pool_on_write(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t kka_pool_anchor_workspace(const kka_kpool* kp, const kka_seqs* seqs, int32_t window) {
   (void)window;
   if (check_kpool(kp) != KKA_OK || check_seqs(seqs) != KKA_OK) return 0;

@@ -92,6 +92,26 @@ struct WeightArgs {
   uint32_t* err;
 };
 
+// Pool-on-write: one new token per sequence.
+struct WriteArgs {
+  const uint16_t* k_new;  // [S][L][H][D] new keys, or null (already in the pool)
+  uint16_t* k;            // the pool; the new keys are stored into it
+  int64_t sL, sB, sT, sH;
+  int32_t L, H, D, B;
+  int64_t P;
+  int32_t S;
+  const int32_t* seq_len;
+  const int32_t* offs;
+  const int32_t* table;
+  const float* weights;   // [S][L*H] frozen head weights, or null (uniform)
+  float* running;         // [S][D] the open block's key sum
+  float* out;             // v_b rows
+  int64_t vb_stride;      // rows per sequence in `out`, 0 = row is the global block id
+  int32_t seed;           // 1: rebuild the running sum from the pool
+  int32_t q8, m, nt;      // D/8 threads per key row, m rows in flight, nt = q8 * m
+  uint32_t* err;
+};
+
 struct LevelArgs {
   float* lvl;
   int64_t rows_per_seq;
@@ -149,6 +169,7 @@ hipError_t launch_head_weights(const WeightArgs& w, hipStream_t st);          //
 hipError_t launch_pool_combine(const PoolArgs& a, const float* w, hipStream_t st);  // variance pass 3
 hipError_t launch_anchor(const PoolArgs& a, hipStream_t st);
 hipError_t launch_levels(const LevelArgs& a, hipStream_t st);
+hipError_t launch_pool_on_write(const WriteArgs& a, hipStream_t st);
 hipError_t launch_score_topk(const ScoreArgs& a, hipStream_t st);
 // Lazy hierarchical variant: one work-group per sequence; scored affinities
 // also go to lazy_out when it is set (a.aff is scratch for long sequences).

@@ -13,7 +13,7 @@ import torch
 
 from . import (WEIGHT_GIVEN, WEIGHT_UNIFORM, WEIGHT_VARIANCE, KPool, LevelLayout, Seqs, kka_build_levels,
                kka_pool_anchor, kka_pool_anchor_workspace, kka_pool_blocks, kka_pool_blocks_workspace,
-               kka_score_topk, kka_score_topk_workspace, new_workspace)
+               kka_pool_on_write, kka_score_topk, kka_score_topk_workspace, new_workspace)
 
 
 class Selector:
@@ -67,6 +67,19 @@ class Selector:
             workspace = new_workspace(kka_pool_blocks_workspace(self.kp, self.seqs, mode, blocks), self.level.device)
         kka_pool_blocks(self.kp, self.seqs, self.level, mode=mode, head_weight=self.head_weight, blocks=blocks,
                         vb_seq_stride=self.lay.rows_per_seq, workspace=workspace, stream=stream)
+
+    def append(self, new_k: Optional[torch.Tensor] = None, seed: bool = False, stream=None):
+        """Pool-on-write for one decode step (seq_len already counts the new
+        token of each sequence): stores new_k into the pool when given and
+        brings the open block's page row up to date."""
+        if getattr(self, "running", None) is None:
+            self.running = torch.zeros((self.seqs.num_seqs, self.kp.head_dim), dtype=torch.float32,
+                                       device=self.level.device)
+            seed = True
+        mode = WEIGHT_GIVEN if self.mode != WEIGHT_UNIFORM else WEIGHT_UNIFORM
+        kka_pool_on_write(self.kp, self.seqs, self.level, self.running, new_k=new_k, mode=mode,
+                          head_weight=self.head_weight, seed=seed, vb_seq_stride=self.lay.rows_per_seq,
+                          stream=stream)
 
     def anchor(self, stream=None):
         kka_pool_anchor(self.kp, self.seqs, self.window, self.anchors, head_weight=self.head_weight,

@@ -198,6 +198,26 @@ def test_level_rows_and_score_validation(L):
     assert L.kka_build_levels(ctypes.byref(lay), FAKE_ODD, FAKE, None, None) == 3
 
 
+def test_pool_on_write_validation(L):
+    kp, sq = kpool(), seqs()
+
+    def f(kp_=kp, sq_=sq, nk=FAKE, mode=0, hw=None, run=FAKE, out=FAKE, stride=0):
+        return L.kka_pool_on_write(ctypes.byref(kp_), ctypes.byref(sq_), nk, mode, hw, run, 0, out, stride, None)
+
+    assert f(mode=1) == 2            # variance weights are computed by kka_pool_blocks, then frozen
+    assert f(mode=7) == 2
+    assert f(mode=2) == 1            # given weights need head_weight
+    assert f(run=None) == 1
+    assert f(out=None) == 1
+    assert f(out=FAKE_ODD) == 3
+    assert f(nk=FAKE_ODD) == 3
+    assert f(stride=-1) == 2
+    assert f(kp_=kpool(head_dim=12)) == 2
+    assert f(kp_=kpool(block_size=1 << 20, num_layers=64, num_kv_heads=16)) == 2
+    assert f(sq_=seqs(num_seqs=0, total_blocks=0), run=None, out=None) == 0
+    assert L.kka_pool_on_write(None, ctypes.byref(sq), FAKE, 0, None, FAKE, 0, FAKE, 0, None) == 1
+
+
 def test_anchor_validation(L):
     kp, sq = kpool(), seqs()
     f = lambda kp_, sq_, W=16, out=FAKE, ws=FAKE, wb=1 << 20: L.kka_pool_anchor(
