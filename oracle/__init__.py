@@ -61,8 +61,9 @@ def lib():
         L.oracle_affinity.argtypes = [vp, i64, i32, vp, vp]
         L.oracle_select.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]
         L.oracle_stability.argtypes = [vp, i32, i64, i32, ctypes.c_float, vp, vp]
+        L.oracle_attention_blocks.argtypes = [ctypes.POINTER(_KPool), vp, i32, i32, vp, ctypes.c_double, vp]
         for f in (L.oracle_head_weights, L.oracle_pool_block, L.oracle_pool_anchor, L.oracle_build_levels,
-                  L.oracle_affinity, L.oracle_select, L.oracle_stability):
+                  L.oracle_affinity, L.oracle_select, L.oracle_stability, L.oracle_attention_blocks):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -188,6 +189,30 @@ def stability(aff_hist, window: int, theta: float):
                                   _p(score) if n else None, _p(bits) if (bits is not None and n) else None),
            "stability")
     return score, bits
+
+
+def attention_blocks(kp: KPool, table: np.ndarray, T: int, q: np.ndarray, scale: float) -> np.ndarray:
+    """Attention mass per block [ceil(T/B)] of one decode query q [L][Hq][D],
+    averaged over layers and query heads (GQA: head hq reads KV head
+    hq // (Hq / H)).  Pinned: uniform cases, a two-token closed form, shift
+    invariance, unit total mass, the GQA head mapping."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    L, Hq, D = q.shape
+    if L != kp.L or D != kp.D:
+        raise ValueError("query shape does not match the pool")
+    table = np.ascontiguousarray(table, dtype=np.int32)
+    nb = -(-T // kp.B)
+    out = np.zeros(max(1, nb), dtype=np.float32)
+    _check(lib().oracle_attention_blocks(ctypes.byref(kp._s), _p(table), int(T), Hq, _p(q), float(scale), _p(out)),
+           "attention_blocks")
+    return out[:nb]
+
+
+def overlap(a, b, k: int) -> float:
+    """|top-k set a  intersect  top-k set b| / k (the overlap rate the page reports)."""
+    if k <= 0:
+        return 0.0
+    return len(set(np.asarray(a)[:k].tolist()) & set(np.asarray(b)[:k].tolist())) / k
 
 
 # --------------------------------------------------------------- pipelines

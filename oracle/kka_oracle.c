@@ -338,3 +338,44 @@ int oracle_stability(const float* aff_hist, int32_t n_steps, int64_t n, int32_t 
   }
   return 0;
 }
+
+/*
+ * Attention mass per block for one decode query (section 3.3 "experimental
+ * validation": the reference selection is the top-K blocks by real
+ * attention, QK^T averaged over every layer and head).  Readings: the
+ * attention of query head hq in layer l is softmax over the sequence's T
+ * tokens of scale * (q[l][hq] . k[l][t][h]) with KV head h = hq / (Hq / H)
+ * (consecutive query heads share a KV head); the probabilities are averaged
+ * over the L * Hq (layer, query head) pairs and summed over each block's
+ * tokens.  Softmax is taken with the maximum subtracted, in double.
+ * q: [L][Hq][D] fp32.  out: ceil(T / B) block scores (fp32, rounded once).
+ */
+int oracle_attention_blocks(const oracle_kpool* kp, const int32_t* table, int32_t T, int32_t Hq, const float* q,
+                            double scale, float* out) {
+  if (!kpool_ok(kp) || T < 0 || Hq < kp->H || Hq % kp->H != 0 || !q || (T > 0 && (!table || !out))) return 1;
+  const int32_t G = Hq / kp->H;
+  const int32_t nb = (T + kp->B - 1) / kp->B;
+  double* logit = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+  double* acc = (double*)calloc((size_t)(nb > 0 ? nb : 1), sizeof(double));
+  for (int32_t l = 0; l < kp->L; ++l) {
+    for (int32_t hq = 0; hq < Hq; ++hq) {
+      const int32_t h = hq / G;
+      const float* qv = q + ((int64_t)l * Hq + hq) * kp->D;
+      double mx = -INFINITY;
+      for (int32_t t = 0; t < T; ++t) {
+        const uint16_t* kr = key_row(kp, l, table[t / kp->B], t % kp->B, h);
+        double dot = 0.0;
+        for (int32_t d = 0; d < kp->D; ++d) dot += (double)qv[d] * bf16_value(kr[d]);
+        logit[t] = scale * dot;
+        if (logit[t] > mx) mx = logit[t];
+      }
+      double z = 0.0;
+      for (int32_t t = 0; t < T; ++t) z += exp(logit[t] - mx);
+      for (int32_t t = 0; t < T; ++t) acc[t / kp->B] += exp(logit[t] - mx) / z;
+    }
+  }
+  for (int32_t b = 0; b < nb; ++b) out[b] = (float)(acc[b] / ((double)kp->L * Hq));
+  free(logit);
+  free(acc);
+  return 0;
+}

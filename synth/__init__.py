@@ -39,6 +39,7 @@ TAG_HEAD_VAR = 17
 TAG_VB = 18
 TAG_ANCHOR = 19
 TAG_RUN_POS = 20
+TAG_QUERY = 21
 
 
 def build(force: bool = True) -> str:
@@ -302,7 +303,28 @@ def planted_kpool(name: str, *, L: int, H: int, D: int, B: int, n_blocks: int, n
                   seed=seed)
     w.extra["anchor_run"] = anchor_run
     w.extra["run_len"] = run_len
+    w.extra["n_topics"] = n_topics
     return w
+
+
+def planted_queries(w: KWorkload, n_q_heads: int, amp: float, noise: float, seed: int = 0,
+                    topic: Optional[int] = None) -> np.ndarray:
+    """Decode-step queries [L][n_q_heads][D] (fp32) for a planted workload:
+    query head hq of layer l points along the planted direction of `topic`
+    (default: the anchor topic) for KV head hq // (n_q_heads / H), scaled by
+    amp, plus N(0, noise) per element.  Grouped query heads share their KV
+    head's direction.  Only random numbers and the workload's own planted
+    directions; no attention arithmetic."""
+    L, H, D = w.L, w.H, w.D
+    if n_q_heads % H:
+        raise ValueError("n_q_heads must be a multiple of the KV heads")
+    G = n_q_heads // H
+    n_topics = w.extra["n_topics"]
+    t = int(w.anchor_topic[0]) if topic is None else int(topic)
+    dirs = unit_dirs(w.seed, TAG_TOPIC_DIR, n_topics * L * H, D).reshape(n_topics, L, H, D)
+    q = amp * np.repeat(dirs[t], G, axis=1)  # [L][Hq][D]
+    q = q + normal(seed, TAG_QUERY, L * n_q_heads * D, 0.0, noise).reshape(L, n_q_heads, D)
+    return np.ascontiguousarray(q, dtype=np.float32)
 
 
 def config1(seed: int = 0) -> KWorkload:

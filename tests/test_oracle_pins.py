@@ -572,3 +572,102 @@ def test_stability_shift_invariant_and_threshold_monotone():
             assert (score <= prev).all()
         prev = score
     assert (oracle.stability(hist, W, 1.0)[0] == 0).all()  # affinities never exceed 1
+
+
+# ------------------------------------------------------------ attention mass per block (section 3.3)
+
+def _kp_const(L, H, D, B, P, fill):
+    keys = np.zeros((L, P, B, H, D), np.float32)
+    keys[...] = fill
+    return kp_from_f32(keys)
+
+
+def test_attention_uniform_cases():
+    """Equal logits give every token 1/T, so a block holds n_b / T: constant
+    keys, a zero query, and scale 0 all reduce to that."""
+    L, H, D, B, P, T = 2, 2, 16, 4, 5, 18
+    rng = np.random.default_rng(60)
+    table = np.array([3, 0, 4, 1, 2], np.int32)
+    expect = np.array([4, 4, 4, 4, 2], np.float64) / T
+    kp = _kp_const(L, H, D, B, P, 0.75)
+    q = rng.standard_normal((L, 4, D)).astype(np.float32)
+    np.testing.assert_allclose(oracle.attention_blocks(kp, table, T, q, 0.25), expect, rtol=0, atol=1e-7)
+    kp2 = kp_from_f32(rand_keys(rng, L, P, B, H, D))
+    np.testing.assert_allclose(oracle.attention_blocks(kp2, table, T, np.zeros_like(q), 0.25), expect, atol=1e-7)
+    np.testing.assert_allclose(oracle.attention_blocks(kp2, table, T, q, 0.0), expect, atol=1e-7)
+
+
+def test_attention_two_token_closed_form():
+    """Two tokens, one head: p0 = 1 / (1 + exp(scale * (b - a)))."""
+    D = 8
+    keys = np.zeros((1, 2, 1, 1, D), np.float32)
+    a, b = 1.5, -0.75
+    keys[0, 0, 0, 0, 0] = a
+    keys[0, 1, 0, 0, 0] = b
+    kp = kp_from_f32(keys)
+    q = np.zeros((1, 1, D), np.float32)
+    q[0, 0, 0] = 1.0
+    for scale in (0.1, 1.0, 3.0):
+        got = oracle.attention_blocks(kp, np.array([0, 1], np.int32), 2, q, scale)
+        p0 = 1.0 / (1.0 + math.exp(scale * (b - a)))
+        np.testing.assert_allclose(got, [p0, 1.0 - p0], rtol=1e-7, atol=0)
+
+
+def test_attention_shift_invariance_and_unit_mass():
+    """Adding one vector to every key of a (layer, KV head) shifts all its
+    logits equally and leaves the softmax unchanged; the block masses sum
+    to 1."""
+    rng = np.random.default_rng(61)
+    L, H, D, B, P, T = 2, 2, 16, 4, 6, 22
+    base = np.round(rng.standard_normal((L, P, B, H, D)) * 4).astype(np.float32)  # small integers: exact in bf16
+    shift = np.round(rng.standard_normal((L, 1, 1, H, D)) * 3).astype(np.float32)
+    table = np.array([5, 2, 0, 4, 1, 3], np.int32)
+    q = (rng.standard_normal((L, 4, D)) * 0.3).astype(np.float32)
+    a = oracle.attention_blocks(kp_from_f32(base), table, T, q, 0.5)
+    b = oracle.attention_blocks(kp_from_f32(base + shift), table, T, q, 0.5)
+    np.testing.assert_allclose(b, a, rtol=1e-6, atol=1e-9)
+    assert abs(float(np.sum(a, dtype=np.float64)) - 1.0) < 1e-6
+
+
+def test_attention_gqa_head_mapping():
+    """Query heads 0-1 read KV head 0 and heads 2-3 read KV head 1 (four
+    query heads over two KV heads).  KV head 0 matches the query only at
+    token 0, KV head 1 only at token 1; with only query head 1 non-zero and
+    a large scale, query head 1 puts all its mass on token 0 and the other
+    three spread evenly: block 0 holds (1 + 3/T) / 4."""
+    D, T = 8, 4
+    keys = np.zeros((1, T, 1, 2, D), np.float32)
+    keys[0, 0, 0, 0, 0] = 1.0
+    keys[0, 1, 0, 1, 0] = 1.0
+    kp = kp_from_f32(keys)
+    q = np.zeros((1, 4, D), np.float32)
+    q[0, 1, 0] = 1.0
+    got = oracle.attention_blocks(kp, np.arange(T, dtype=np.int32), T, q, 200.0)
+    expect = np.array([1 + 3 / T, 3 / T, 3 / T, 3 / T]) / 4
+    np.testing.assert_allclose(got, expect, rtol=0, atol=1e-7)
+
+
+def test_attention_matches_scipy_softmax():
+    """Random pool through a table against scipy's softmax of numpy dot
+    products, averaged over heads and summed per block."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(62)
+    L, H, Hq, D, B, P, T = 3, 2, 6, 32, 5, 9, 41
+    keys = rand_keys(rng, L, P, B, H, D)
+    table = synth.permutation(63, 1, P)[: -(-T // B)].astype(np.int32)
+    q = rng.standard_normal((L, Hq, D)).astype(np.float32)
+    got = oracle.attention_blocks(kp_from_f32(keys), table, T, q, 1 / math.sqrt(D))
+    tok = np.stack([keys[:, table[t // B], t % B] for t in range(T)], axis=1).astype(np.float64)  # [L][T][H][D]
+    mass = np.zeros(T)
+    for l in range(L):
+        for hq in range(Hq):
+            mass += softmax(tok[l, :, hq // (Hq // H)] @ q[l, hq].astype(np.float64) / math.sqrt(D))
+    mass /= L * Hq
+    expect = np.array([mass[b * B:(b + 1) * B].sum() for b in range(-(-T // B))])
+    np.testing.assert_allclose(got, expect, rtol=1e-6, atol=1e-9)
+
+
+def test_overlap_rate():
+    assert oracle.overlap([3, 1, 2, 9], [2, 3, 4, 5], 4) == 0.5
+    assert oracle.overlap([1, 2], [2, 1], 2) == 1.0
+    assert oracle.overlap([], [], 0) == 0.0

@@ -70,3 +70,16 @@ def test_config5_ragged_state():
     assert sorted(after["block_table"].tolist()) == list(range(w.P))
     v = w.extra["head_var"]
     assert v.min() >= 0.1 and v.max() <= 4.0
+
+
+def test_planted_queries_share_their_kv_head_direction():
+    w = synth.config1(0)
+    q = synth.planted_queries(w, 14, 8.0, 0.0)
+    assert q.shape == (24, 14, 64)
+    np.testing.assert_allclose(np.linalg.norm(q, axis=2), 8.0, rtol=1e-5)
+    for g in range(7):  # query heads 0-6 read KV head 0, 7-13 read KV head 1
+        np.testing.assert_array_equal(q[:, g], q[:, 0])
+        np.testing.assert_array_equal(q[:, 7 + g], q[:, 7])
+    assert np.abs(q[:, 0] - q[:, 7]).max() > 0.1
+    noisy = synth.planted_queries(w, 14, 8.0, 0.5, seed=3)
+    assert 0.4 < float((noisy - q).std()) < 0.6
