@@ -202,6 +202,43 @@ KKA_API kka_status kka_pool_on_write(const kka_kpool* kp, const kka_seqs* seqs, 
                                      int64_t vb_seq_stride, void* stream);
 
 /*
+ * kka_attention_topk -- the reference selection the page compares with
+ * (section 3.3): for one decode query per sequence, the attention mass of
+ * every block, QK^T softmax averaged over every layer and query head, and
+ * the top-k blocks by that mass.  Query head hq of layer l uses KV head
+ * hq / (num_q_heads / num_kv_heads); its attention is softmax over the
+ * sequence's seq_len[s] tokens of scale * (q . k); a block's score is the
+ * sum over its tokens, averaged over the L * num_q_heads (layer, query head)
+ * pairs, so a sequence's scores sum to 1.
+ *
+ * queries          device [num_seqs][L][num_q_heads][head_dim] fp32,
+ *                  16-byte aligned.
+ * block_score_out  device [num_seqs][out_seq_stride] fp32, 16-byte aligned:
+ *                  block j of sequence s (j < its listed blocks) at
+ *                  s * out_seq_stride + j; blocks without tokens score 0.
+ * k, idx_out, score_out, n_selected_out
+ *                  top-k logical block indices per sequence by (score
+ *                  descending, index ascending) over the blocks holding
+ *                  tokens, as in kka_score_topk's flat mode ([num_seqs][k];
+ *                  k = 0 skips the selection).
+ * workspace        >= kka_attention_topk_workspace() bytes, 16-byte aligned.
+ * Rules: num_q_heads a multiple of num_kv_heads with at most 8 query heads
+ * per KV head; head_dim a power of two <= 512 with
+ * (head_dim / 8) * num_kv_heads <= 256; num_q_heads * (block_size + 1)
+ * <= 15360 (one block's logits must fit in LDS); scale finite; k in 0..1024;
+ * out_seq_stride >= 1.  Device-side problems (offsets, block table,
+ * seq_len beyond the listed blocks, blocks past out_seq_stride) raise the
+ * device flag and are skipped.  Several launches on `stream`.
+ */
+KKA_API kka_status kka_attention_topk(const kka_kpool* kp, const kka_seqs* seqs, const float* queries,
+                                      int32_t num_q_heads, float scale, int32_t k, float* block_score_out,
+                                      int64_t out_seq_stride, int32_t* idx_out, float* score_out,
+                                      int32_t* n_selected_out, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+KKA_API size_t kka_attention_topk_workspace(const kka_kpool* kp, const kka_seqs* seqs, int32_t num_q_heads);
+
+/*
  * Level buffer geometry (page section 5.1).  Each sequence owns
  * rows_per_seq = kka_level_rows() consecutive rows of head_dim fp32:
  *   pages  rows [0, n_p)                   -- the block vectors v_b

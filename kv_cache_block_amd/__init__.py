@@ -41,7 +41,7 @@ _STATUS = {0: "ok", 1: "KKA_ERR_NULL", 2: "KKA_ERR_SHAPE", 3: "KKA_ERR_ALIGN", 4
 ENTRY_POINTS = (
     "kka_pool_blocks", "kka_pool_blocks_workspace", "kka_pool_anchor", "kka_pool_anchor_workspace", "kka_pool_on_write",
     "kka_level_rows", "kka_build_levels", "kka_score_topk", "kka_score_topk_workspace", "kka_score_topk_lazy",
-    "kka_score_topk_stable", "kka_device_error",
+    "kka_score_topk_stable", "kka_attention_topk", "kka_attention_topk_workspace", "kka_device_error",
     "kka_status_string", "kka_version",
 )
 
@@ -103,6 +103,9 @@ def lib() -> ctypes.CDLL:
         L.kka_pool_anchor.argtypes = [P(c_kpool), P(c_seqs), i32, vp, vp, vp, sz, vp]
         L.kka_pool_anchor_workspace.argtypes = [P(c_kpool), P(c_seqs), i32]
         L.kka_pool_on_write.argtypes = [P(c_kpool), P(c_seqs), vp, i32, vp, vp, i32, vp, i64, vp]
+        L.kka_attention_topk.argtypes = [P(c_kpool), P(c_seqs), vp, i32, ctypes.c_float, i32, vp, i64, vp, vp, vp,
+                                         vp, sz, vp]
+        L.kka_attention_topk_workspace.argtypes = [P(c_kpool), P(c_seqs), i32]
         L.kka_level_rows.argtypes = [P(c_level_layout)]
         L.kka_build_levels.argtypes = [P(c_level_layout), vp, vp, vp, vp]
         L.kka_score_topk.argtypes = [P(c_level_layout), vp, vp, vp, P(c_select), vp, vp, vp, vp, vp, sz, vp]
@@ -113,9 +116,10 @@ def lib() -> ctypes.CDLL:
         L.kka_device_error.argtypes = [vp]
         L.kka_status_string.argtypes = [ctypes.c_int]
         for f in ("kka_pool_blocks", "kka_pool_anchor", "kka_build_levels", "kka_score_topk", "kka_score_topk_lazy",
-                  "kka_score_topk_stable", "kka_pool_on_write"):
+                  "kka_score_topk_stable", "kka_pool_on_write", "kka_attention_topk"):
             getattr(L, f).restype = ctypes.c_int
-        for f in ("kka_pool_blocks_workspace", "kka_pool_anchor_workspace", "kka_score_topk_workspace"):
+        for f in ("kka_pool_blocks_workspace", "kka_pool_anchor_workspace", "kka_score_topk_workspace",
+                  "kka_attention_topk_workspace"):
             getattr(L, f).restype = sz
         L.kka_level_rows.restype = i64
         L.kka_device_error.restype = i32
@@ -313,6 +317,33 @@ def kka_pool_on_write(kp: KPool, seqs: Seqs, vb_out: torch.Tensor, running: torc
     vp_ = _dev(vb_out, "vb_out", torch.float32, min_numel=rows * D)
     _check(lib().kka_pool_on_write(ctypes.byref(kp.c), ctypes.byref(seqs.c), nk, int(mode), hw, rp,
                                    1 if seed else 0, vp_, int(vb_seq_stride), _stream(stream)), "kka_pool_on_write")
+
+
+def kka_attention_topk_workspace(kp: KPool, seqs: Seqs, num_q_heads: int) -> int:
+    return int(lib().kka_attention_topk_workspace(ctypes.byref(kp.c), ctypes.byref(seqs.c), int(num_q_heads)))
+
+
+def kka_attention_topk(kp: KPool, seqs: Seqs, queries: torch.Tensor, num_q_heads: int, block_score_out: torch.Tensor,
+                       out_seq_stride: int, *, scale: Optional[float] = None, k: int = 0,
+                       idx_out: Optional[torch.Tensor] = None, score_out: Optional[torch.Tensor] = None,
+                       n_selected_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       stream=None):
+    """Attention mass per block for one decode query per sequence
+    (queries [S][L][Hq][D] fp32), averaged over layers and query heads, and
+    the top-k blocks by it (the page's reference selection)."""
+    S, L, D = seqs.num_seqs, kp.num_layers, kp.head_dim
+    qp = _dev(queries, "queries", torch.float32, min_numel=S * L * num_q_heads * D)
+    op = _dev(block_score_out, "block_score_out", torch.float32, min_numel=S * out_seq_stride)
+    ip = _dev(idx_out, "idx_out", torch.int32, min_numel=S * k, allow_none=k == 0)
+    sp = _dev(score_out, "score_out", torch.float32, min_numel=S * k, allow_none=True)
+    cp = _dev(n_selected_out, "n_selected_out", torch.int32, min_numel=S, allow_none=True)
+    need = kka_attention_topk_workspace(kp, seqs, num_q_heads)
+    wp, wbytes, keep = _ws(workspace, need, block_score_out.device)
+    sc = (1.0 / D ** 0.5) if scale is None else float(scale)
+    _check(lib().kka_attention_topk(ctypes.byref(kp.c), ctypes.byref(seqs.c), qp, int(num_q_heads), sc, int(k), op,
+                                    int(out_seq_stride), ip, sp, cp, wp, wbytes, _stream(stream)),
+           "kka_attention_topk")
+    return keep
 
 
 def kka_build_levels(lay: LevelLayout, level_buf: torch.Tensor, n_pages: torch.Tensor,

@@ -247,6 +247,136 @@ kka_status kka_pool_on_write(const kka_kpool* kp, const kka_seqs* seqs, const ui
   return launched(launch_pool_on_write(a, static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Geometry and workspace layout of the attention reference.
+struct AttnPlan {
+  int32_t G = 0, TB = 0, TT = 0, max_tiles = 0, n_chunks = 0;
+  size_t tile_offs = 0, n_blocks = 0, m_tile = 0, z_tile = 0, e_blk = 0, M = 0, Z = 0, partial = 0, total = 0;
+};
+
+kka_status attn_plan(const kka_kpool* kp, const kka_seqs* sq, int32_t Hq, AttnPlan& p) {
+  kka_status st = check_kpool(kp);
+  if (st != KKA_OK) return st;
+  if ((st = check_seqs(sq)) != KKA_OK) return st;
+  const int32_t H = kp->num_kv_heads, D = kp->head_dim, B = kp->block_size, L = kp->num_layers;
+  if (Hq < H || Hq % H != 0 || Hq / H > 8) return KKA_ERR_SHAPE;
+  const int32_t q8 = D / 8;
+  if (D > 512 || (q8 & (q8 - 1)) != 0 || (int64_t)q8 * H > 256) return KKA_ERR_SHAPE;
+  p.G = Hq / H;
+  p.TB = attention_tile_blocks(B, H, p.G);
+  if (p.TB < 1) return KKA_ERR_SHAPE;  // one block's logits do not fit in LDS
+  p.TT = p.TB * B;
+  const int64_t tiles = ((int64_t)sq->total_blocks + p.TB - 1) / p.TB + sq->num_seqs;
+  const int64_t LHq = (int64_t)L * Hq;
+  if (tiles > 0x7fffffffLL || LHq * tiles > ((int64_t)1 << 40)) return KKA_ERR_SHAPE;
+  p.max_tiles = (int32_t)tiles;
+  p.n_chunks = (int32_t)((LHq + attention_chunk_heads() - 1) / attention_chunk_heads());
+  const size_t S = (size_t)sq->num_seqs, tb = (size_t)sq->total_blocks;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  p.tile_offs = take((S + 1) * sizeof(int32_t));
+  p.n_blocks = take(S * sizeof(int32_t));
+  p.m_tile = take((size_t)LHq * tiles * sizeof(float));
+  p.z_tile = take((size_t)LHq * tiles * sizeof(float));
+  p.e_blk = take((size_t)LHq * tb * sizeof(float));
+  p.M = take(S * LHq * sizeof(float));
+  p.Z = take(S * LHq * sizeof(float));
+  p.partial = take((size_t)p.n_chunks * tb * sizeof(float));
+  p.total = off;
+  return KKA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kka_attention_topk_workspace(const kka_kpool* kp, const kka_seqs* seqs, int32_t num_q_heads) {
+  AttnPlan p;
+  if (attn_plan(kp, seqs, num_q_heads, p) != KKA_OK) return 0;
+  return p.total;
+}
+
+kka_status kka_attention_topk(const kka_kpool* kp, const kka_seqs* seqs, const float* queries, int32_t num_q_heads,
+                              float scale, int32_t k, float* block_score_out, int64_t out_seq_stride,
+                              int32_t* idx_out, float* score_out, int32_t* n_selected_out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  AttnPlan p;
+  kka_status st = attn_plan(kp, seqs, num_q_heads, p);
+  if (st != KKA_OK) return st;
+  if (!std::isfinite(scale) || k < 0 || k > kMaxK || out_seq_stride < 1 || out_seq_stride > 0x7fffffffLL)
+    return KKA_ERR_SHAPE;
+  if (seqs->num_seqs == 0) return KKA_OK;
+  if (!queries || !block_score_out || (k > 0 && !idx_out)) return KKA_ERR_NULL;
+  if (!aligned16(queries) || !aligned16(block_score_out)) return KKA_ERR_ALIGN;
+  if (!workspace || workspace_bytes < p.total) return KKA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KKA_ERR_ALIGN;
+  uint32_t* err = device_error_word();
+  if (!err) return KKA_ERR_DEVICE;
+  (void)hipGetLastError();
+  char* ws = static_cast<char*>(workspace);
+  AttnArgs a{};
+  a.k = kp->k;
+  a.sL = kp->stride_layer;
+  a.sB = kp->stride_block;
+  a.sT = kp->stride_token;
+  a.sH = kp->stride_head;
+  a.L = kp->num_layers;
+  a.H = kp->num_kv_heads;
+  a.D = kp->head_dim;
+  a.B = kp->block_size;
+  a.P = kp->num_phys_blocks;
+  a.S = seqs->num_seqs;
+  a.total_blocks = seqs->total_blocks;
+  a.seq_len = seqs->seq_len;
+  a.offs = seqs->block_offsets;
+  a.table = seqs->block_table;
+  a.q = queries;
+  a.Hq = num_q_heads;
+  a.G = p.G;
+  a.scale = scale;
+  a.TB = p.TB;
+  a.TT = p.TT;
+  a.max_tiles = p.max_tiles;
+  a.n_chunks = p.n_chunks;
+  a.tile_offs = reinterpret_cast<int32_t*>(ws + p.tile_offs);
+  a.n_blocks = reinterpret_cast<int32_t*>(ws + p.n_blocks);
+  a.m_tile = reinterpret_cast<float*>(ws + p.m_tile);
+  a.z_tile = reinterpret_cast<float*>(ws + p.z_tile);
+  a.e_blk = reinterpret_cast<float*>(ws + p.e_blk);
+  a.M = reinterpret_cast<float*>(ws + p.M);
+  a.Z = reinterpret_cast<float*>(ws + p.Z);
+  a.partial = reinterpret_cast<float*>(ws + p.partial);
+  a.out = block_score_out;
+  a.out_stride = out_seq_stride;
+  a.err = err;
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_attention_blocks(a, strm);
+  if (e != hipSuccess || k == 0) return launched(e);
+  // flat top-k over the block scores (non-negative by construction)
+  ScoreArgs sa{};
+  sa.aff = block_score_out;
+  sa.rows_per_seq = out_seq_stride;
+  sa.S = a.S;
+  sa.max_pages = (int32_t)out_seq_stride;
+  sa.D = a.D;
+  sa.hier = 0;
+  sa.ppc = sa.cpg = 1;
+  sa.n_pages = a.n_blocks;
+  sa.k_p = k;
+  sa.idx_out = idx_out;
+  sa.score_out = score_out;
+  sa.cnt_out = n_selected_out;
+  sa.err = err;
+  return launched(launch_select(sa, strm));
+}
+
 size_t kka_pool_anchor_workspace(const kka_kpool* kp, const kka_seqs* seqs, int32_t window) {
   (void)window;
   if (check_kpool(kp) != KKA_OK || check_seqs(seqs) != KKA_OK) return 0;

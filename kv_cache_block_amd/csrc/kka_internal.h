@@ -112,6 +112,35 @@ struct WriteArgs {
   uint32_t* err;
 };
 
+// Attention mass per block (one decode query per sequence).
+struct AttnArgs {
+  const uint16_t* k;
+  int64_t sL, sB, sT, sH;
+  int32_t L, H, D, B;
+  int64_t P;
+  int32_t S, total_blocks;
+  const int32_t* seq_len;
+  const int32_t* offs;
+  const int32_t* table;
+  const float* q;        // [S][L][Hq][D]
+  int32_t Hq, G;         // query heads, query heads per KV head
+  float scale;
+  int32_t TB, TT;        // blocks and tokens per tile
+  int32_t max_tiles;     // grid bound on tiles
+  int32_t n_chunks;      // head chunks of the block-mass pass
+  int32_t* tile_offs;    // [S+1] first tile of each sequence
+  int32_t* n_blocks;     // [S] blocks holding tokens (selection candidates)
+  float* m_tile;         // [L*Hq][max_tiles] tile maximum logit, then the tile's factor
+  float* z_tile;         // [L*Hq][max_tiles] tile sum of exp(logit - max)
+  float* e_blk;          // [L*Hq][total_blocks] block sum of exp(logit - tile max)
+  float* M;              // [S][L*Hq] sequence maximum logit
+  float* Z;              // [S][L*Hq] softmax normaliser
+  float* partial;        // [n_chunks][total_blocks] block mass per head chunk
+  float* out;            // block scores, out + s * out_stride + j
+  int64_t out_stride;
+  uint32_t* err;
+};
+
 struct LevelArgs {
   float* lvl;
   int64_t rows_per_seq;
@@ -170,10 +199,15 @@ hipError_t launch_pool_combine(const PoolArgs& a, const float* w, hipStream_t st
 hipError_t launch_anchor(const PoolArgs& a, hipStream_t st);
 hipError_t launch_levels(const LevelArgs& a, hipStream_t st);
 hipError_t launch_pool_on_write(const WriteArgs& a, hipStream_t st);
+hipError_t launch_attention_blocks(const AttnArgs& a, hipStream_t st);
+int32_t attention_chunk_heads();  // (layer, query head) pairs per block-mass chunk
+int32_t attention_tile_blocks(int32_t B, int32_t H, int32_t G);  // blocks per tile, 0 = too large
 hipError_t launch_score_topk(const ScoreArgs& a, hipStream_t st);
 // Lazy hierarchical variant: one work-group per sequence; scored affinities
 // also go to lazy_out when it is set (a.aff is scratch for long sequences).
 hipError_t launch_score_topk_lazy(const ScoreArgs& a, float* lazy_out, hipStream_t st);
 int32_t score_rows_per_tile(int32_t D);  // rows one score work-group covers
+// Selection only, over scores already in a.aff (non-negative, not NaN).
+hipError_t launch_select(const ScoreArgs& a, hipStream_t st);
 
 }  // namespace kka

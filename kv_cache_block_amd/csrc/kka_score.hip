@@ -751,6 +751,12 @@ int32_t score_rows_per_tile(int32_t D) {
 
 hipError_t launch_score_topk(const ScoreArgs& a, hipStream_t st) { return dispatch(a, false, nullptr, st); }
 
+hipError_t launch_select(const ScoreArgs& a, hipStream_t st) {
+  if (a.S <= 0) return hipSuccess;
+  hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.S), dim3(kSelThreads), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_score_topk_lazy(const ScoreArgs& a, float* lazy_out, hipStream_t st) {
   return dispatch(a, true, lazy_out, st);
 }

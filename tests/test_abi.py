@@ -218,6 +218,32 @@ def test_pool_on_write_validation(L):
     assert L.kka_pool_on_write(None, ctypes.byref(sq), FAKE, 0, None, FAKE, 0, FAKE, 0, None) == 1
 
 
+def test_attention_topk_validation(L):
+    kp, sq = kpool(), seqs()  # 28 layers, 4 KV heads, head_dim 128, blocks of 16
+    ws = L.kka_attention_topk_workspace(ctypes.byref(kp), ctypes.byref(sq), 28)
+    # block partials and tile max/sum of 28 x 28 (layer, query head) pairs
+    assert ws >= 784 * 64 * 4 + 2 * 784 * 4
+
+    def f(kp_=kp, sq_=sq, q=FAKE, hq=28, scale=0.1, k=8, out=FAKE, stride=64, idx=FAKE, w=FAKE, wb=ws):
+        return L.kka_attention_topk(ctypes.byref(kp_), ctypes.byref(sq_), q, hq, scale, k, out, stride, idx, None,
+                                    None, w, wb, None)
+
+    assert f(hq=6) == 2                 # not a multiple of the KV heads
+    assert f(hq=36) == 2                # 9 query heads per KV head
+    assert f(kp_=kpool(head_dim=96)) == 2
+    assert f(kp_=kpool(head_dim=1024, num_kv_heads=1)) == 2
+    assert f(scale=float("nan")) == 2
+    assert f(k=1025) == 2
+    assert f(stride=0) == 2
+    assert f(q=None) == 1
+    assert f(idx=None) == 1
+    assert f(out=FAKE_ODD) == 3
+    assert f(w=None) == 4
+    assert f(wb=ws - 1) == 4
+    assert f(sq_=seqs(num_seqs=0, total_blocks=0), q=None, out=None, idx=None, w=None, wb=0) == 0
+    assert L.kka_attention_topk_workspace(ctypes.byref(kp), ctypes.byref(sq), 6) == 0
+
+
 def test_anchor_validation(L):
     kp, sq = kpool(), seqs()
     f = lambda kp_, sq_, W=16, out=FAKE, ws=FAKE, wb=1 << 20: L.kka_pool_anchor(
