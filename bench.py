@@ -378,13 +378,24 @@ def quality_overlaps(args, dev):
         a_idx = aidx[0].cpu().numpy()
         topic = w.block_topic[0]
         entry = {"k": kq, "attention_topic_share": float((topic[a_idx] == w.anchor_topic[0]).mean())}
+        # also at k = the number of planted anchor-topic blocks, where both
+        # methods should pick exactly the relevant set
+        kt = int((topic == w.anchor_topic[0]).sum())
+        aidx_t = torch.zeros((1, kt), dtype=torch.int32, device=dev)
+        kka.kka_attention_topk(kp, seqs, q, Hq, att, w.total_blocks, k=kt, idx_out=aidx_t)
+        a_idx_t = aidx_t[0].cpu().numpy()
+        entry["k_topic"] = kt
         npg = torch.tensor([w.total_blocks], dtype=torch.int32, device=dev)
         for mode_name, mode in (("uniform", kka.WEIGHT_UNIFORM), ("variance", kka.WEIGHT_VARIANCE)):
             sel = Selector(kp, seqs, w.select, max_pages=w.total_blocks, window=w.window, mode=mode, device=dev)
             sel.step(npg)
             s_idx = sel.page_idx[0, :kq].cpu().numpy()
+            sel_t = Selector(kp, seqs, dict(w.select, k_page=kt), max_pages=w.total_blocks, window=w.window,
+                             mode=mode, device=dev)
+            sel_t.step(npg)
             entry[mode_name] = {"overlap": overlap(s_idx, a_idx, kq),
-                                "topic_share": float((topic[s_idx] == w.anchor_topic[0]).mean())}
+                                "topic_share": float((topic[s_idx] == w.anchor_topic[0]).mean()),
+                                "overlap_at_k_topic": overlap(sel_t.page_idx[0, :kt].cpu().numpy(), a_idx_t, kt)}
         torch.cuda.synchronize()
         res[name] = entry
         del k, kp, seqs

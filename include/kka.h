@@ -222,10 +222,13 @@ KKA_API kka_status kka_pool_on_write(const kka_kpool* kp, const kka_seqs* seqs, 
  *                  tokens, as in kka_score_topk's flat mode ([num_seqs][k];
  *                  k = 0 skips the selection).
  * workspace        >= kka_attention_topk_workspace() bytes, 16-byte aligned.
- * Rules: num_q_heads a multiple of num_kv_heads with at most 8 query heads
- * per KV head; head_dim a power of two <= 512 with
- * (head_dim / 8) * num_kv_heads <= 256; num_q_heads * (block_size + 1)
- * <= 15360 (one block's logits must fit in LDS); scale finite; k in 0..1024;
+ * Rules: num_q_heads a multiple of num_kv_heads (G = num_q_heads /
+ * num_kv_heads).  Matrix-core path: head_dim in {32, 64, 128, 256},
+ * G <= 16 and block_size dividing 16 or a multiple of 16.  Otherwise the
+ * vector path: G <= 8, head_dim a power of two <= 512 with
+ * (head_dim / 8) * num_kv_heads <= 256 and num_q_heads * (block_size + 1)
+ * <= 15360 (one block's logits must fit in LDS).  Both: scale finite, the
+ * queries finite; k in 0..1024;
  * out_seq_stride >= 1.  Device-side problems (offsets, block table,
  * seq_len beyond the listed blocks, blocks past out_seq_stride) raise the
  * device flag and are skipped.  Several launches on `stream`.

@@ -253,8 +253,9 @@ namespace {
 
 // Geometry and workspace layout of the attention reference.
 struct AttnPlan {
-  int32_t G = 0, TB = 0, TT = 0, max_tiles = 0, n_chunks = 0;
-  size_t tile_offs = 0, n_blocks = 0, m_tile = 0, z_tile = 0, e_blk = 0, M = 0, Z = 0, partial = 0, total = 0;
+  int32_t G = 0, TB = 0, TT = 0, max_tiles = 0, n_chunks = 0, U = 0, UPB = 0;
+  bool mfma = false;
+  size_t tile_offs = 0, n_blocks = 0, um = 0, ue = 0, M = 0, Z = 0, partial = 0, total = 0;
 };
 
 kka_status attn_plan(const kka_kpool* kp, const kka_seqs* sq, int32_t Hq, AttnPlan& p) {
@@ -262,16 +263,22 @@ kka_status attn_plan(const kka_kpool* kp, const kka_seqs* sq, int32_t Hq, AttnPl
   if (st != KKA_OK) return st;
   if ((st = check_seqs(sq)) != KKA_OK) return st;
   const int32_t H = kp->num_kv_heads, D = kp->head_dim, B = kp->block_size, L = kp->num_layers;
-  if (Hq < H || Hq % H != 0 || Hq / H > 8) return KKA_ERR_SHAPE;
-  const int32_t q8 = D / 8;
-  if (D > 512 || (q8 & (q8 - 1)) != 0 || (int64_t)q8 * H > 256) return KKA_ERR_SHAPE;
+  if (Hq < H || Hq % H != 0) return KKA_ERR_SHAPE;
   p.G = Hq / H;
-  p.TB = attention_tile_blocks(B, H, p.G);
+  p.mfma = attention_mfma_ok(D, p.G, B);
+  if (!p.mfma) {  // vector kernel: query group in registers, D/8 lanes per key row
+    const int32_t q8 = D / 8;
+    if (p.G > 8 || D > 512 || (q8 & (q8 - 1)) != 0 || (int64_t)q8 * H > 256) return KKA_ERR_SHAPE;
+  }
+  p.TB = attention_tile_blocks(B, H, p.G, p.mfma);
   if (p.TB < 1) return KKA_ERR_SHAPE;  // one block's logits do not fit in LDS
   p.TT = p.TB * B;
+  p.U = p.mfma && B > 16 ? 16 : B;
+  p.UPB = B / p.U;
   const int64_t tiles = ((int64_t)sq->total_blocks + p.TB - 1) / p.TB + sq->num_seqs;
   const int64_t LHq = (int64_t)L * Hq;
-  if (tiles > 0x7fffffffLL || LHq * tiles > ((int64_t)1 << 40)) return KKA_ERR_SHAPE;
+  const int64_t units = (int64_t)sq->total_blocks * p.UPB;
+  if (tiles > 0x7fffffffLL || units > 0x7fffffffLL || LHq * units > ((int64_t)1 << 40)) return KKA_ERR_SHAPE;
   p.max_tiles = (int32_t)tiles;
   p.n_chunks = (int32_t)((LHq + attention_chunk_heads() - 1) / attention_chunk_heads());
   const size_t S = (size_t)sq->num_seqs, tb = (size_t)sq->total_blocks;
@@ -283,9 +290,8 @@ kka_status attn_plan(const kka_kpool* kp, const kka_seqs* sq, int32_t Hq, AttnPl
   };
   p.tile_offs = take((S + 1) * sizeof(int32_t));
   p.n_blocks = take(S * sizeof(int32_t));
-  p.m_tile = take((size_t)LHq * tiles * sizeof(float));
-  p.z_tile = take((size_t)LHq * tiles * sizeof(float));
-  p.e_blk = take((size_t)LHq * tb * sizeof(float));
+  p.um = take((size_t)LHq * units * sizeof(float));
+  p.ue = take((size_t)LHq * units * sizeof(float));
   p.M = take(S * LHq * sizeof(float));
   p.Z = take(S * LHq * sizeof(float));
   p.partial = take((size_t)p.n_chunks * tb * sizeof(float));
@@ -345,11 +351,13 @@ kka_status kka_attention_topk(const kka_kpool* kp, const kka_seqs* seqs, const f
   a.TT = p.TT;
   a.max_tiles = p.max_tiles;
   a.n_chunks = p.n_chunks;
+  a.U = p.U;
+  a.UPB = p.UPB;
+  a.mfma = p.mfma ? 1 : 0;
   a.tile_offs = reinterpret_cast<int32_t*>(ws + p.tile_offs);
   a.n_blocks = reinterpret_cast<int32_t*>(ws + p.n_blocks);
-  a.m_tile = reinterpret_cast<float*>(ws + p.m_tile);
-  a.z_tile = reinterpret_cast<float*>(ws + p.z_tile);
-  a.e_blk = reinterpret_cast<float*>(ws + p.e_blk);
+  a.um = reinterpret_cast<float*>(ws + p.um);
+  a.ue = reinterpret_cast<float*>(ws + p.ue);
   a.M = reinterpret_cast<float*>(ws + p.M);
   a.Z = reinterpret_cast<float*>(ws + p.Z);
   a.partial = reinterpret_cast<float*>(ws + p.partial);

@@ -42,7 +42,15 @@ constexpr int kChunkHeads = 32;  // (layer, query head) pairs per block-mass chu
 #define KKA_ATTN_ROWS 8
 #endif
 constexpr int kRowUnroll = KKA_ATTN_ROWS;  // key rows per batch
-constexpr int kMaxTB = 256;      // blocks per tile
+constexpr int kMaxTB = 256;      // blocks per vector-kernel tile
+#ifndef KKA_ATTN_BUFS
+#define KKA_ATTN_BUFS 3
+#endif
+#ifndef KKA_ATTN_MFMA_TOKENS
+#define KKA_ATTN_MFMA_TOKENS 512
+#endif
+constexpr int kMfmaBufs = KKA_ATTN_BUFS;           // key chunks in flight per wave
+constexpr int kMfmaTileTokens = KKA_ATTN_MFMA_TOKENS;  // tokens per matrix-core tile (>= its blocks)
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v, float identity) {
@@ -83,16 +91,40 @@ __device__ __forceinline__ float group_allsum_t(float v) {
   return v;
 }
 
-// The same for a group width known only at run time (uniform).
-__device__ __forceinline__ float group_sum_rt(float v, int32_t n) {
+// The same butterfly with the maximum.
+template <int N>
+__device__ __forceinline__ float group_allmax_t(float v) {
+  if constexpr (N >= 2) v = fmaxf(v, dpp_f<0xB1>(v, -INFINITY));
+  if constexpr (N >= 4) v = fmaxf(v, dpp_f<0x4E>(v, -INFINITY));
+  if constexpr (N >= 8) v = fmaxf(v, dpp_f<0x141>(v, -INFINITY));
+  if constexpr (N >= 16) v = fmaxf(v, dpp_f<0x128>(v, -INFINITY));
+  if constexpr (N >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+  if constexpr (N >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+// Group widths known only at run time (uniform; a power of two <= 64).
+__device__ __forceinline__ float group_allsum_rt(float v, int32_t n) {
   switch (n) {
     case 1: return v;
-    case 2: return group_sum_t<2>(v);
-    case 4: return group_sum_t<4>(v);
-    case 8: return group_sum_t<8>(v);
-    case 16: return group_sum_t<16>(v);
-    case 32: return group_sum_t<32>(v);
-    default: return group_sum_t<64>(v);
+    case 2: return group_allsum_t<2>(v);
+    case 4: return group_allsum_t<4>(v);
+    case 8: return group_allsum_t<8>(v);
+    case 16: return group_allsum_t<16>(v);
+    case 32: return group_allsum_t<32>(v);
+    default: return group_allsum_t<64>(v);
+  }
+}
+
+__device__ __forceinline__ float group_allmax_rt(float v, int32_t n) {
+  switch (n) {
+    case 1: return v;
+    case 2: return group_allmax_t<2>(v);
+    case 4: return group_allmax_t<4>(v);
+    case 8: return group_allmax_t<8>(v);
+    case 16: return group_allmax_t<16>(v);
+    case 32: return group_allmax_t<32>(v);
+    default: return group_allmax_t<64>(v);
   }
 }
 
@@ -304,106 +336,263 @@ __global__ __launch_bounds__(kAttnThreads) void attn_logits_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // one wave per query head: tile maximum, each block's exp sum, tile sum
+  // one wave per query head: each block's maximum logit and its sum of
+  // exp(logit - maximum) (a unit is a block on this path)
   const int wave = tid >> 6, lane = tid & 63;
   const int32_t ntok = nblk * a.B;
   // tiles of whole 64-token segments whose blocks tile each segment: block
   // j of segment i = lanes [j*B, (j+1)*B) of token index 64 i + lane
   const bool aligned = a.TT % 64 == 0 && 64 % a.B == 0;
   const int32_t nseg = a.TT / 64;
+  const int64_t nunits = (int64_t)a.total_blocks * a.UPB;
   for (int32_t hq = wave; hq < a.Hq; hq += kAttnThreads / 64) {
     const float* row = lg + hq * ldw;
-    const int64_t lhq = (int64_t)l * a.Hq + hq;
-    float* eb = a.e_blk + lhq * a.total_blocks + o0 + j0;
-    float mx, ztot;
+    const int64_t base = ((int64_t)l * a.Hq + hq) * nunits + o0 + j0;
     if (aligned) {
-      float xm = -INFINITY;
-      for (int32_t i = 0; i < nseg; ++i) {
-        const int32_t t = 64 * i + lane;
-        xm = fmaxf(xm, t < ntok ? row[t] : -INFINITY);
-      }
-      mx = wave_max(xm);
-      float zl = 0.f;
       for (int32_t i = 0; i < nseg; ++i) {
         const int32_t t = 64 * i + lane;
         const float x = t < ntok ? row[t] : -INFINITY;
-        const float ex = x == -INFINITY ? 0.f : expf(x - mx);
-        const float bs = group_sum_rt(ex, a.B);
-        if (lane % a.B == 0 && t / a.B < nblk) eb[t / a.B] = bs;
-        zl += ex;
+        const float gm = group_allmax_rt(x, a.B);
+        const float ex = x == -INFINITY ? 0.f : expf(x - gm);
+        const float gs = group_allsum_rt(ex, a.B);
+        if (lane % a.B == 0 && t < ntok) {
+          a.um[base + t / a.B] = gm;
+          a.ue[base + t / a.B] = gs;
+        }
       }
-      ztot = wave_sum(zl);
     } else {
-      float xm = -INFINITY;
-      for (int32_t t = lane; t < ntok; t += 64) xm = fmaxf(xm, row[t]);
-      mx = wave_max(xm);
-      ztot = 0.f;
       for (int32_t jb = 0; jb < nblk; ++jb) {
+        float xm = -INFINITY;
+        for (int32_t t = jb * a.B + lane; t < (jb + 1) * a.B; t += 64) xm = fmaxf(xm, row[t]);
+        const float gm = wave_max(xm);
         float e = 0.f;
         for (int32_t t = jb * a.B + lane; t < (jb + 1) * a.B; t += 64) {
           const float x = row[t];
-          e += x == -INFINITY ? 0.f : expf(x - mx);
+          e += x == -INFINITY ? 0.f : expf(x - gm);
         }
         e = wave_sum(e);
-        if (lane == 0) eb[jb] = e;
-        ztot += e;
+        if (lane == 0) {
+          a.um[base + jb] = gm;
+          a.ue[base + jb] = e;
+        }
       }
-    }
-    if (lane == 0) {
-      a.m_tile[lhq * a.max_tiles + tile] = mx;
-      a.z_tile[lhq * a.max_tiles + tile] = ztot;
     }
   }
 }
 
-// Softmax maximum and normaliser of every (sequence, layer, query head) from
-// its tiles (one pass, running maximum), then each tile's factor
-// exp(tile max - maximum) / normaliser, written over the tile maximum.
-__global__ __launch_bounds__(kAttnThreads) void attn_norm_kernel(AttnArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int32_t LHq = a.L * a.Hq;
-  const int64_t pair = (int64_t)blockIdx.x * (kAttnThreads / 64) + wave;
-  if (pair >= (int64_t)a.S * LHq) return;
-  const int32_t s = (int32_t)(pair / LHq);
-  const int32_t lhq = (int32_t)(pair - (int64_t)s * LHq);
-  const int32_t t0 = a.tile_offs[s], t1 = a.tile_offs[s + 1];
-  float* mt = a.m_tile + (int64_t)lhq * a.max_tiles;
-  const float* zt = a.z_tile + (int64_t)lhq * a.max_tiles;
-  constexpr int U = 8;
-  float m_l = -INFINITY, z_l = 0.f;
-  for (int32_t t = t0 + lane; t < t1; t += 64 * U) {
-    float mv[U], zv[U];
+// ------------------------------------------------------------ matrix-core logits
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Round to nearest even bf16 (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Eight fp32 values as three bf16 vectors whose sum equals them to about
+// 2^-24 relative: each part is the bf16 rounding of what the earlier parts
+// left (every remainder is exact in fp32).  A bf16 part times a bf16 key is
+// exact in fp32, so the three products carry fp32 accuracy into the
+// matrix cores' fp32 accumulation.
+__device__ __forceinline__ void split3(const float (&x)[8], bf16x8& p1, bf16x8& p2, bf16x8& p3) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int32_t tu = t + 64 * u < t1 ? t + 64 * u : t;
-      mv[u] = t + 64 * u < t1 ? mt[tu] : -INFINITY;
-      zv[u] = zt[tu];
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t h1 = bf16_bits_rne(x[i]);
+    const float r1 = x[i] - __uint_as_float(h1 << 16);
+    const uint32_t h2 = bf16_bits_rne(r1);
+    const float r2 = r1 - __uint_as_float(h2 << 16);
+    const uint32_t h3 = bf16_bits_rne(r2);
+    p1[i] = __builtin_bit_cast(__bf16, (uint16_t)h1);
+    p2[i] = __builtin_bit_cast(__bf16, (uint16_t)h2);
+    p3[i] = __builtin_bit_cast(__bf16, (uint16_t)h3);
+  }
+}
+
+// KS = head_dim / 32.  A wave takes one KV head at a time and 16-token
+// chunks of the tile: v_mfma_f32_16x16x32_bf16 with the head's (up to 16)
+// queries as A (lane l: query l % 16, dims 8 (l / 16) + 32 ks) and the
+// chunk's keys as B (lane l: token l % 16, the same dims), so each lane
+// loads 16 bytes of key per k-step; the result gives lane l the logits of
+// queries 4 (l / 16) + r for token l % 16.  Units of U <= 16 tokens are
+// aligned lane groups of a 16-lane row, reduced with DPP butterflies.
+template <int KS, int U>
+__global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a) {
+  __shared__ int64_t phys[kMfmaTileTokens];  // physical block of each tile block, -1 if invalid
+  const int tid = threadIdx.x;
+  const int32_t tile = blockIdx.x;
+  const int32_t l = blockIdx.y;
+  if (tile >= a.tile_offs[a.S]) return;
+  int32_t lo = 0, hi = a.S - 1;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (a.tile_offs[mid] <= tile) lo = mid;
+    else hi = mid - 1;
+  }
+  const int32_t s = lo;
+  const int32_t j0 = (tile - a.tile_offs[s]) * a.TB;
+  const int32_t o0 = a.offs[s];
+  const int32_t nb_s = seq_blocks(a, s, false);
+  const int32_t nblk = min(a.TB, nb_s - j0);
+  if (nblk <= 0) return;  // uniform over the group
+  const int64_t T = min((int64_t)max(a.seq_len[s], 0), (int64_t)nb_s * a.B);
+  for (int32_t jb = tid; jb < nblk; jb += kAttnThreads) {
+    const int64_t p = a.table[o0 + j0 + jb];
+    const bool ok = p >= 0 && p < a.P;
+    if (!ok && l == 0) raise_err(a.err, KKA_DEVERR_BLOCK_TABLE);
+    phys[jb] = ok ? p : -1;
+  }
+  __syncthreads();
+
+  const int wave = tid >> 6, lane = tid & 63;
+  const int32_t n = lane & 15, quad = lane >> 4;
+  const int32_t wph = a.H >= 4 ? 1 : 4 / a.H;  // waves per head
+  const int32_t hstep = 4 / wph;
+  const int32_t ntok = nblk * a.B;
+  const int32_t nch = (ntok + 15) / 16;
+  const int64_t nunits = (int64_t)a.total_blocks * a.UPB;
+  const int64_t unit0 = ((int64_t)o0 + j0) * a.UPB;
+  for (int32_t h = wave / wph; h < a.H; h += hstep) {
+    bf16x8 q1[KS], q2[KS], q3[KS];
+    {
+      const bool qrow = n < a.G;
+      const float* qb =
+          a.q + (((int64_t)s * a.L + l) * a.Hq + (int64_t)h * a.G + (qrow ? n : 0)) * a.D + 8 * quad;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        float x[8];
+        float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
+        if (qrow) {
+          x0 = *reinterpret_cast<const float4*>(qb + 32 * ks);
+          x1 = *reinterpret_cast<const float4*>(qb + 32 * ks + 4);
+        }
+        x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+        x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+        split3(x, q1[ks], q2[ks], q3[ks]);
+      }
     }
+    const uint16_t* kh = a.k + (int64_t)l * a.sL + (int64_t)h * a.sH + 8 * quad;
+    // Issues the key loads of chunk c (all of them before any use).  A key
+    // column outside the tile loads the tile's first row and is masked.
+    auto load = [&](int32_t c, bf16x8 (&kv)[KS], bool& ok, int32_t& tl) {
+      tl = 16 * c + n;
+      const bool in_tile = tl < ntok;
+      const int32_t jb = in_tile ? tl / a.B : 0;
+      const int32_t st = in_tile ? tl - jb * a.B : 0;
+      const int64_t p = phys[jb];
+      ok = in_tile && p >= 0 && (int64_t)(j0 + jb) * a.B + st < T;
+      if (!in_tile) tl = -1;
+      const uint16_t* kr = kh + (p >= 0 ? p : 0) * a.sB + (int64_t)st * a.sT;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (mv[u] == -INFINITY) continue;
-      if (mv[u] > m_l) {
-        z_l = z_l * expf(m_l - mv[u]) + zv[u];
-        m_l = mv[u];
-      } else {
-        z_l += zv[u] * expf(mv[u] - m_l);
+      for (int ks = 0; ks < KS; ++ks) kv[ks] = *reinterpret_cast<const bf16x8*>(kr + 32 * ks);
+    };
+    // Logits of one chunk on the matrix cores, then each unit's maximum
+    // and exp sum from the accumulator lanes.
+    auto process = [&](const bf16x8 (&kv)[KS], bool ok, int32_t tl) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q1[ks], kv[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q2[ks], kv[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q3[ks], kv[ks], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int32_t m = 4 * quad + r;  // query within the head's group
+        const float x = ok && m < a.G ? acc[r] * a.scale : -INFINITY;
+        const float gm = group_allmax_t<U>(x);
+        const float ex = x == -INFINITY ? 0.f : expf(x - gm);
+        const float gs = group_allsum_t<U>(ex);
+        if (m < a.G && tl >= 0 && n % U == 0) {
+          const int64_t at = ((int64_t)l * a.Hq + (int64_t)h * a.G + m) * nunits + unit0 + tl / U;
+          a.um[at] = gm;
+          a.ue[at] = gs;
+        }
+      }
+    };
+    // kMfmaBufs chunks in flight: while one computes, the next ones load
+    bf16x8 kbuf[kMfmaBufs][KS];
+    bool okb[kMfmaBufs];
+    int32_t tlb[kMfmaBufs];
+    const int32_t c0 = wave % wph;
+#pragma unroll
+    for (int b = 0; b < kMfmaBufs - 1; ++b) {
+      okb[b] = false;
+      tlb[b] = -1;
+      if (c0 + b * wph < nch) load(c0 + b * wph, kbuf[b], okb[b], tlb[b]);
+    }
+    for (int32_t c = c0; c < nch; c += kMfmaBufs * wph) {
+#pragma unroll
+      for (int b = 0; b < kMfmaBufs; ++b) {
+        const int32_t cc = c + b * wph;
+        if (cc < nch) {
+          const int32_t cn = cc + (kMfmaBufs - 1) * wph;
+          const int bn = (b + kMfmaBufs - 1) % kMfmaBufs;
+          if (cn < nch) load(cn, kbuf[bn], okb[bn], tlb[bn]);
+          __builtin_amdgcn_sched_barrier(0);
+          process(kbuf[b], okb[b], tlb[b]);
+        }
       }
     }
   }
-  const float M = wave_max(m_l);
-  const float Z = wave_sum(m_l == -INFINITY ? 0.f : z_l * expf(m_l - M));
-  if (lane == 0) {
-    a.M[pair] = M;
-    a.Z[pair] = Z;
+}
+
+// Softmax maximum and normaliser of one (sequence, layer, query head) over
+// its units: M = max of the unit maxima, Z = sum of unit sums rescaled to M.
+__global__ __launch_bounds__(kAttnThreads) void attn_norm_kernel(AttnArgs a) {
+  __shared__ float red[kAttnThreads / 64];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int32_t LHq = a.L * a.Hq;
+  const int64_t pair = blockIdx.x;
+  const int32_t s = (int32_t)(pair / LHq);
+  const int32_t lhq = (int32_t)(pair - (int64_t)s * LHq);
+  const int64_t nu = (int64_t)seq_blocks(a, s, false) * a.UPB;
+  const int64_t u0 = nu > 0 ? (int64_t)a.offs[s] * a.UPB : 0;
+  const int64_t nunits = (int64_t)a.total_blocks * a.UPB;
+  const float* um = a.um + (int64_t)lhq * nunits + u0;
+  const float* ue = a.ue + (int64_t)lhq * nunits + u0;
+  constexpr int U = 8;
+  float mx = -INFINITY;
+  for (int64_t i = tid; i < nu; i += (int64_t)U * kAttnThreads) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = i + u * kAttnThreads < nu ? um[i + u * kAttnThreads] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mx = fmaxf(mx, v[u]);
   }
-  for (int32_t t = t0 + lane; t < t1; t += 64) {
-    const float m_t = mt[t];
-    mt[t] = (m_t == -INFINITY || !(Z > 0.f)) ? 0.f : expf(m_t - M) / Z;
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float z = 0.f;
+  if (mx != -INFINITY) {
+    for (int64_t i = tid; i < nu; i += (int64_t)U * kAttnThreads) {
+      float mv[U], ev[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool in = i + u * kAttnThreads < nu;
+        const int64_t iu = in ? i + u * kAttnThreads : i;
+        mv[u] = in ? um[iu] : -INFINITY;
+        ev[u] = ue[iu];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) z += mv[u] == -INFINITY ? 0.f : ev[u] * expf(mv[u] - mx);
+    }
+  }
+  z = wave_sum(z);
+  if (lane == 0) red[wave] = z;
+  __syncthreads();
+  if (tid == 0) {
+    a.M[pair] = mx;
+    a.Z[pair] = (red[0] + red[1]) + (red[2] + red[3]);
   }
 }
 
 // Normalised mass of every block over one chunk of (layer, query head)
-// pairs: the block's exp sum times its tile's factor.
+// pairs: the sum over its units of unit sum * exp(unit max - M) / Z.
 __global__ __launch_bounds__(kAttnThreads) void attn_mass_kernel(AttnArgs a) {
   const int64_t b = (int64_t)blockIdx.x * kAttnThreads + threadIdx.x;
   const int32_t c = blockIdx.y;
@@ -412,25 +601,23 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mass_kernel(AttnArgs a) {
   const int32_t j = (int32_t)b - a.offs[s];
   bool ok = j >= 0 && j < a.n_blocks[s];
   const int32_t tile = ok ? a.tile_offs[s] + j / a.TB : 0;
-  ok = ok && tile < a.tile_offs[s + 1];
+  ok = ok && tile < a.tile_offs[s + 1];  // the tile was computed
   float mass = 0.f;
   if (ok) {
     const int32_t LHq = a.L * a.Hq;
-    const int32_t h0 = c * kChunkHeads;
-    const int32_t nh = min(LHq, h0 + kChunkHeads) - h0;
-    const float* e = a.e_blk + (int64_t)h0 * a.total_blocks + b;
-    const float* f = a.m_tile + (int64_t)h0 * a.max_tiles + tile;
-    constexpr int U = 8;
-    for (int32_t i = 0; i < nh; i += U) {
-      float ev[U], fv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int32_t iu = i + u < nh ? i + u : i;
-        ev[u] = e[(int64_t)iu * a.total_blocks];
-        fv[u] = i + u < nh ? f[(int64_t)iu * a.max_tiles] : 0.f;
+    const int32_t h1 = min(LHq, (c + 1) * kChunkHeads);
+    const int64_t nunits = (int64_t)a.total_blocks * a.UPB;
+    for (int32_t lhq = c * kChunkHeads; lhq < h1; ++lhq) {
+      const float z = a.Z[(int64_t)s * LHq + lhq];
+      if (!(z > 0.f)) continue;
+      const float M = a.M[(int64_t)s * LHq + lhq];
+      const int64_t at = (int64_t)lhq * nunits + b * a.UPB;
+      float part = 0.f;
+      for (int32_t v = 0; v < a.UPB; ++v) {
+        const float m = a.um[at + v];
+        part += m == -INFINITY ? 0.f : a.ue[at + v] * expf(m - M);
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u) mass = fmaf(ev[u], fv[u], mass);
+      mass += part / z;
     }
   }
   a.partial[(int64_t)c * a.total_blocks + b] = mass;
@@ -447,6 +634,18 @@ __global__ __launch_bounds__(kAttnThreads) void attn_finish_kernel(AttnArgs a) {
   if (j < a.n_blocks[s])
     for (int32_t c = 0; c < a.n_chunks; ++c) sum += a.partial[(int64_t)c * a.total_blocks + b];
   a.out[(int64_t)s * a.out_stride + j] = sum / (float)(a.L * a.Hq);
+}
+
+template <int KS>
+hipError_t launch_mfma_ks(const AttnArgs& a, dim3 grid, hipStream_t st) {
+  switch (a.U) {
+    case 1: hipLaunchKernelGGL((attn_mfma_kernel<KS, 1>), grid, dim3(kAttnThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((attn_mfma_kernel<KS, 2>), grid, dim3(kAttnThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((attn_mfma_kernel<KS, 4>), grid, dim3(kAttnThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((attn_mfma_kernel<KS, 8>), grid, dim3(kAttnThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((attn_mfma_kernel<KS, 16>), grid, dim3(kAttnThreads), 0, st, a); break;
+  }
+  return hipGetLastError();
 }
 
 template <int Q8>
@@ -471,8 +670,16 @@ hipError_t launch_attention_blocks(const AttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(attn_tiles_kernel, dim3(1), dim3(1024), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.total_blocks <= 0) return e;
-  const size_t lds = sizeof(float) * (size_t)a.Hq * (a.TT + 1);
   const dim3 grid((unsigned)a.max_tiles, (unsigned)a.L);
+  if (a.mfma) {
+    switch (a.D >> 5) {
+      case 1: e = launch_mfma_ks<1>(a, grid, st); break;
+      case 2: e = launch_mfma_ks<2>(a, grid, st); break;
+      case 4: e = launch_mfma_ks<4>(a, grid, st); break;
+      default: e = launch_mfma_ks<8>(a, grid, st); break;
+    }
+  } else {
+  const size_t lds = sizeof(float) * (size_t)a.Hq * (a.TT + 1);
   switch (a.D >> 3) {
     case 1: e = launch_logits_q8<1>(a, grid, lds, st); break;
     case 2: e = launch_logits_q8<2>(a, grid, lds, st); break;
@@ -482,9 +689,10 @@ hipError_t launch_attention_blocks(const AttnArgs& a, hipStream_t st) {
     case 32: e = launch_logits_q8<32>(a, grid, lds, st); break;
     default: e = launch_logits_q8<64>(a, grid, lds, st); break;
   }
+  }
   if (e != hipSuccess) return e;
   const int64_t pairs = (int64_t)a.S * a.L * a.Hq;
-  hipLaunchKernelGGL(attn_norm_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(kAttnThreads), 0, st, a);
+  hipLaunchKernelGGL(attn_norm_kernel, dim3((unsigned)pairs), dim3(kAttnThreads), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned nbx = (unsigned)((a.total_blocks + kAttnThreads - 1) / kAttnThreads);
   hipLaunchKernelGGL(attn_mass_kernel, dim3(nbx, (unsigned)a.n_chunks), dim3(kAttnThreads), 0, st, a);
@@ -495,10 +703,15 @@ hipError_t launch_attention_blocks(const AttnArgs& a, hipStream_t st) {
 
 int32_t attention_chunk_heads() { return kChunkHeads; }
 
+bool attention_mfma_ok(int32_t D, int32_t G, int32_t B) {
+  return (D == 32 || D == 64 || D == 128 || D == 256) && G >= 1 && G <= 16 && (16 % B == 0 || B % 16 == 0);
+}
+
 // Blocks per tile: about 256 tokens, whole 64-token segments when the block
 // size divides 64, and the tile's logits (H * G rows of tokens + 1 floats)
 // within 60 KB of LDS.  0 when even one block does not fit.
-int32_t attention_tile_blocks(int32_t B, int32_t H, int32_t G) {
+int32_t attention_tile_blocks(int32_t B, int32_t H, int32_t G, bool mfma) {
+  if (mfma) return B >= kMfmaTileTokens ? 1 : kMfmaTileTokens / B;  // logits stay in registers
   const int64_t cap = 15360 / ((int64_t)H * G) - 1;  // tokens
   if (64 % B == 0) {
     int64_t tt = 256;

@@ -128,11 +128,12 @@ struct AttnArgs {
   int32_t TB, TT;        // blocks and tokens per tile
   int32_t max_tiles;     // grid bound on tiles
   int32_t n_chunks;      // head chunks of the block-mass pass
+  int32_t U, UPB;        // tokens per unit (a block or 16 tokens), units per block
+  int32_t mfma;          // 1: matrix-core logits kernel, 0: vector kernel
   int32_t* tile_offs;    // [S+1] first tile of each sequence
   int32_t* n_blocks;     // [S] blocks holding tokens (selection candidates)
-  float* m_tile;         // [L*Hq][max_tiles] tile maximum logit, then the tile's factor
-  float* z_tile;         // [L*Hq][max_tiles] tile sum of exp(logit - max)
-  float* e_blk;          // [L*Hq][total_blocks] block sum of exp(logit - tile max)
+  float* um;             // [L*Hq][total_blocks*UPB] unit maximum logit (-inf: no token)
+  float* ue;             // [L*Hq][total_blocks*UPB] unit sum of exp(logit - unit max)
   float* M;              // [S][L*Hq] sequence maximum logit
   float* Z;              // [S][L*Hq] softmax normaliser
   float* partial;        // [n_chunks][total_blocks] block mass per head chunk
@@ -201,7 +202,8 @@ hipError_t launch_levels(const LevelArgs& a, hipStream_t st);
 hipError_t launch_pool_on_write(const WriteArgs& a, hipStream_t st);
 hipError_t launch_attention_blocks(const AttnArgs& a, hipStream_t st);
 int32_t attention_chunk_heads();  // (layer, query head) pairs per block-mass chunk
-int32_t attention_tile_blocks(int32_t B, int32_t H, int32_t G);  // blocks per tile, 0 = too large
+int32_t attention_tile_blocks(int32_t B, int32_t H, int32_t G, bool mfma);  // blocks per tile, 0 = too large
+bool attention_mfma_ok(int32_t D, int32_t G, int32_t B);  // matrix-core logits apply
 hipError_t launch_score_topk(const ScoreArgs& a, hipStream_t st);
 // Lazy hierarchical variant: one work-group per sequence; scored affinities
 // also go to lazy_out when it is set (a.aff is scratch for long sequences).

@@ -229,7 +229,8 @@ def test_attention_topk_validation(L):
                                     None, w, wb, None)
 
     assert f(hq=6) == 2                 # not a multiple of the KV heads
-    assert f(hq=36) == 2                # 9 query heads per KV head
+    assert f(hq=68) == 2                # 17 query heads per KV head
+    assert f(kp_=kpool(head_dim=96), hq=40) == 2  # vector path: 10 query heads per KV head
     assert f(kp_=kpool(head_dim=96)) == 2
     assert f(kp_=kpool(head_dim=1024, num_kv_heads=1)) == 2
     assert f(scale=float("nan")) == 2

@@ -6,7 +6,10 @@ Block scores against the oracle (fp64 softmax, rounded once) within
 rtol 2e-5 + atol 1e-7: fp32 logits carry a relative error of a few ulp of
 |logit|, which exp turns into the same relative error of the mass.  The
 top-k against the oracle's selection on the GPU's own scores, bit-exact.
-At 128K tokens with all 28 layers the oracle is too slow, so that case is
+Both logit kernels are covered: the matrix-core one (head_dim 32-256, up to
+16 query heads per KV head, blocks dividing or divisible by 16) and the
+vector one (everything else).  At 128K tokens with all 28 layers the
+oracle is too slow, so that case is
 checked through properties that hold at any size (unit total mass,
 non-negative scores, selection on the GPU's scores, planted-topic blocks on
 top) plus full parity of the same 131072-token sequence at 4 layers.
@@ -73,7 +76,8 @@ def check(w, q, Hq, k, scale, out, idx, sc, cnt, tag, seqs_to_check=None):
 
 
 @pytest.mark.parametrize("D,B,H,Hq", [(64, 16, 2, 14), (128, 5, 4, 28), (8, 1, 1, 8), (32, 128, 2, 2),
-                                      (512, 16, 1, 4), (128, 64, 4, 4)])
+                                      (512, 16, 1, 4), (128, 64, 4, 4), (128, 16, 2, 32), (64, 8, 1, 12),
+                                      (256, 4, 3, 9), (16, 32, 4, 8), (128, 48, 8, 8)])
 def test_attention_matches_oracle_ragged(D, B, H, Hq):
     say(f"attention ragged D={D} B={B} H={H} Hq={Hq}")
     lengths = [0, 1, 37, 300, B * 3]
