@@ -21,6 +21,7 @@ namespace {
 constexpr int kWriteThreads = 256;
 constexpr int kWriteUnroll = 8;
 constexpr int kMaxLH = 4096;
+constexpr int kMaxD = 1024;
 
 template <bool GIVEN>
 __global__ __launch_bounds__(kWriteThreads) void write_pool_kernel(WriteArgs a) {
@@ -28,6 +29,27 @@ __global__ __launch_bounds__(kWriteThreads) void write_pool_kernel(WriteArgs a) 
   __shared__ float wsh[GIVEN ? kMaxLH : 1];
   const int tid = threadIdx.x;
   const int32_t s = blockIdx.x;
+  const int32_t LH = a.L * a.H;
+  const int32_t dg = tid % a.q8;
+  const int32_t r0 = tid / a.q8;
+  const bool active = tid < a.nt;
+  // Loads whose addresses depend only on the sequence go first, so they
+  // overlap the metadata reads below: the first rows of the new token's
+  // keys (a step without seeding reads nothing else) and the running sums.
+  const uint16_t* knew = a.k_new ? a.k_new + (int64_t)s * LH * a.D + dg * 8 : nullptr;
+  const bool pre_ok = knew && !a.seed && active;
+  u32x4 pre[kWriteUnroll];
+#pragma unroll
+  for (int u = 0; u < kWriteUnroll; ++u) {
+    const int32_t rr = r0 + u * a.m < LH ? r0 + u * a.m : min(r0, LH - 1);
+    pre[u] = pre_ok ? *reinterpret_cast<const u32x4*>(knew + (int64_t)rr * a.D) : u32x4{0u, 0u, 0u, 0u};
+  }
+  float rp[kMaxD / kWriteThreads];
+#pragma unroll
+  for (int i = 0; i < kMaxD / kWriteThreads; ++i) {
+    const int32_t d = tid + i * kWriteThreads;
+    rp[i] = !a.seed && d < a.D ? a.running[(int64_t)s * a.D + d] : 0.f;
+  }
   const int32_t T = a.seq_len[s];
   // every thread takes the same exits, so the barriers below stay uniform
   if (T <= 0) {
@@ -56,7 +78,6 @@ __global__ __launch_bounds__(kWriteThreads) void write_pool_kernel(WriteArgs a) 
     }
     row_out = (int64_t)s * a.vb_stride + j;
   }
-  const int32_t LH = a.L * a.H;
   if (GIVEN) {
     for (int32_t x = tid; x < LH; x += kWriteThreads) wsh[x] = a.weights[(int64_t)s * LH + x];
     __syncthreads();
@@ -64,11 +85,8 @@ __global__ __launch_bounds__(kWriteThreads) void write_pool_kernel(WriteArgs a) 
 
   const int32_t t0 = a.seed ? 0 : slot;
   const int32_t n_rows = (slot - t0 + 1) * LH;
-  const int32_t dg = tid % a.q8;
-  const int32_t r0 = tid / a.q8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (tid < a.nt) {
-    const uint16_t* knew = a.k_new ? a.k_new + (int64_t)s * LH * a.D + dg * 8 : nullptr;
+  if (active) {
     uint16_t* kp = a.k + p * a.sB + dg * 8;
     for (int32_t r = r0; r < n_rows; r += kWriteUnroll * a.m) {
       u32x4 v[kWriteUnroll];
@@ -83,7 +101,8 @@ __global__ __launch_bounds__(kWriteThreads) void write_pool_kernel(WriteArgs a) 
         const int32_t h = lh - l * a.H;
         uint16_t* dst = kp + (int64_t)l * a.sL + (int64_t)ti * a.sT + (int64_t)h * a.sH;
         if (knew && ti == slot) {
-          v[u] = *reinterpret_cast<const u32x4*>(knew + (int64_t)lh * a.D);
+          // the first batch of a step without seeding was loaded at entry
+          v[u] = pre_ok && r == r0 ? pre[u] : *reinterpret_cast<const u32x4*>(knew + (int64_t)lh * a.D);
           *reinterpret_cast<u32x4*>(dst) = v[u];  // the cache write (idempotent for repeats)
         } else {
           v[u] = *reinterpret_cast<const u32x4*>(dst);
@@ -113,15 +132,18 @@ __global__ __launch_bounds__(kWriteThreads) void write_pool_kernel(WriteArgs a) 
   }
   __syncthreads();
   const float denom = GIVEN ? (float)(slot + 1) : (float)((int64_t)(slot + 1) * LH);
-  for (int32_t d = tid; d < a.D; d += kWriteThreads) {
-    // lanes sharing the 16-byte column of d are dg + r * q8, r < m
-    const int32_t base = ((d >> 3) << 3) + (d & 7);
-    float sum = 0.f;
-    for (int32_t r = 0; r < a.m; ++r) sum += red[base + r * a.q8 * 8];
-    float* run = a.running + (int64_t)s * a.D + d;
-    const float total = (a.seed || slot == 0) ? sum : *run + sum;
-    *run = total;
-    a.out[row_out * a.D + d] = total / denom;
+#pragma unroll
+  for (int i = 0; i < kMaxD / kWriteThreads; ++i) {
+    const int32_t d = tid + i * kWriteThreads;
+    if (d < a.D) {
+      // lanes sharing the 16-byte column of d are dg + r * q8, r < m
+      const int32_t base = ((d >> 3) << 3) + (d & 7);
+      float sum = 0.f;
+      for (int32_t r = 0; r < a.m; ++r) sum += red[base + r * a.q8 * 8];
+      const float total = (a.seed || slot == 0) ? sum : rp[i] + sum;
+      a.running[(int64_t)s * a.D + d] = total;
+      a.out[row_out * a.D + d] = total / denom;
+    }
   }
 }
 
