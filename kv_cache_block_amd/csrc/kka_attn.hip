@@ -605,19 +605,30 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mass_kernel(AttnArgs a) {
   float mass = 0.f;
   if (ok) {
     const int32_t LHq = a.L * a.Hq;
-    const int32_t h1 = min(LHq, (c + 1) * kChunkHeads);
+    const int32_t h0 = c * kChunkHeads;
+    const int32_t nh = min(LHq, h0 + kChunkHeads) - h0;
     const int64_t nunits = (int64_t)a.total_blocks * a.UPB;
-    for (int32_t lhq = c * kChunkHeads; lhq < h1; ++lhq) {
-      const float z = a.Z[(int64_t)s * LHq + lhq];
-      if (!(z > 0.f)) continue;
-      const float M = a.M[(int64_t)s * LHq + lhq];
-      const int64_t at = (int64_t)lhq * nunits + b * a.UPB;
-      float part = 0.f;
-      for (int32_t v = 0; v < a.UPB; ++v) {
-        const float m = a.um[at + v];
-        part += m == -INFINITY ? 0.f : a.ue[at + v] * expf(m - M);
+    constexpr int V = 8;  // (layer, query head) pairs whose loads are in flight together
+    for (int32_t i = 0; i < nh; i += V) {
+      float z[V], M[V];
+#pragma unroll
+      for (int u = 0; u < V; ++u) {
+        const int64_t at = (int64_t)s * LHq + h0 + min(i + u, nh - 1);
+        z[u] = a.Z[at];
+        M[u] = a.M[at];
       }
-      mass += part / z;
+      for (int32_t v = 0; v < a.UPB; ++v) {
+        float m[V], e[V];
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+          const int64_t at = (int64_t)(h0 + min(i + u, nh - 1)) * nunits + b * a.UPB + v;
+          m[u] = a.um[at];
+          e[u] = a.ue[at];
+        }
+#pragma unroll
+        for (int u = 0; u < V; ++u)
+          if (i + u < nh && z[u] > 0.f && m[u] != -INFINITY) mass += e[u] * expf(m[u] - M[u]) / z[u];
+      }
     }
   }
   a.partial[(int64_t)c * a.total_blocks + b] = mass;
@@ -631,8 +642,17 @@ __global__ __launch_bounds__(kAttnThreads) void attn_finish_kernel(AttnArgs a) {
   const int32_t j = (int32_t)b - a.offs[s];
   if (j < 0 || j >= a.out_stride || (int64_t)a.offs[s] + j >= a.offs[s + 1]) return;
   float sum = 0.f;
-  if (j < a.n_blocks[s])
-    for (int32_t c = 0; c < a.n_chunks; ++c) sum += a.partial[(int64_t)c * a.total_blocks + b];
+  if (j < a.n_blocks[s]) {
+    constexpr int V = 8;
+    for (int32_t c = 0; c < a.n_chunks; c += V) {
+      float pv[V];
+#pragma unroll
+      for (int u = 0; u < V; ++u) pv[u] = a.partial[(int64_t)min(c + u, a.n_chunks - 1) * a.total_blocks + b];
+#pragma unroll
+      for (int u = 0; u < V; ++u)
+        if (c + u < a.n_chunks) sum += pv[u];
+    }
+  }
   a.out[(int64_t)s * a.out_stride + j] = sum / (float)(a.L * a.Hq);
 }
 

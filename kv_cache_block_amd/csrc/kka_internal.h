@@ -13,8 +13,12 @@ namespace kka {
 // Largest block size any pool kernel is launched with (one thread per 16-byte
 // chunk of a token's H*D key row, H*D/8 <= 1024).
 constexpr int kMaxPoolThreads = 1024;
-// Target work-groups for one pooling launch: 256 CUs x 8 resident groups.
-constexpr int kPoolTargetGroups = 2048;
+// Target work-groups for one pooling launch (blocks are split over layers
+// until there are about this many groups).
+#ifndef KKA_POOL_TARGET_GROUPS
+#define KKA_POOL_TARGET_GROUPS 2048
+#endif
+constexpr int kPoolTargetGroups = KKA_POOL_TARGET_GROUPS;
 // Largest k at any selection level.
 constexpr int kMaxK = 1024;
 // Largest number of parents whose keep flags one selecting group tracks.
