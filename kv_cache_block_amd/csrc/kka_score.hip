@@ -310,14 +310,35 @@ __device__ __forceinline__ int32_t group_sum(int32_t v, int32_t n) {
   return v;
 }
 
+// Rank of key x of the run at g0 among NG sorted runs of 64: its rank r in
+// its own run plus, for every other run, how many of its keys exceed x
+// (binary search; the searches of different runs are independent).
+template <int NG>
+__device__ __forceinline__ int32_t merged_rank(const uint64_t* runs, int32_t g0, uint64_t x, int32_t r) {
+  int32_t pos[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) pos[g] = 0;
+#pragma unroll
+  for (int step = 32; step > 0; step >>= 1) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      if ((g << 6) != g0 && runs[(g << 6) + pos[g] + step - 1] > x) pos[g] += step;
+  }
+  int32_t R = r;
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+    if ((g << 6) != g0) R += (pos[g] == 63 && runs[(g << 6) + 63] > x) ? 64 : pos[g];
+  return R;
+}
+
 // Keeps the top min(k, n) elements of a level, sorted, in sm.buf.
 // Levels with at most kSelThreads candidates: candidate keys go to LDS in
 // groups of 64 (slots past the candidates hold distinct keys below every
 // real one); all threads rank every key within its group, tpc lanes per key
-// each comparing a strided share; each group is written back as a strictly
-// descending run; a key's rank in the level is its rank in its group plus,
-// for every other group, how many keys of that run exceed it (binary
-// search).  Keys without a positive score rank below all positive ones and
+// each comparing a strided share; with one group that rank is final,
+// otherwise each group is written back as a strictly descending run and a
+// key's rank in the level is its rank in its group plus, for every other
+// group, how many keys of that run exceed it (binary search).  Keys without a positive score rank below all positive ones and
 // are never kept here (the zero fill handles them).
 __device__ int32_t select_level(const Level& L, int32_t k, SelectShared& sm) {
   const int32_t k_eff = k < L.n ? k : L.n;
@@ -360,23 +381,27 @@ __device__ int32_t select_level(const Level& L, int32_t k, SelectShared& sm) {
     for (int u = 0; u < 8; ++u) r += (int32_t)(j + u * tpc < 64 && y[u] > x);
   }
   r = group_sum(r, tpc);
+  if (n_grp == 1) {
+    // one group: the rank in it is the rank in the level
+    if (active && q == 0 && (x >> 32) != 0ull && r < k_eff) sm.buf[r] = x;
+    __syncthreads();
+    if (P < k_eff) fill_zeros(L, sm, P, k_eff);
+    return k_eff;
+  }
   if (active && q == 0) runs[g0 + r] = x;
   __syncthreads();
   // phase C: rank in the level, positive keys only
   if (active && q == 0 && (x >> 32) != 0ull) {
-    int32_t R = r;
-    int32_t pos[kSelThreads / 64];
-#pragma unroll
-    for (int g = 0; g < kSelThreads / 64; ++g) pos[g] = 0;
-#pragma unroll
-    for (int step = 32; step > 0; step >>= 1) {
-#pragma unroll
-      for (int g = 0; g < kSelThreads / 64; ++g)
-        if (g < n_grp && (g << 6) != g0 && runs[(g << 6) + pos[g] + step - 1] > x) pos[g] += step;
+    int32_t R;
+    switch (n_grp) {
+      case 2: R = merged_rank<2>(runs, g0, x, r); break;
+      case 3: R = merged_rank<3>(runs, g0, x, r); break;
+      case 4: R = merged_rank<4>(runs, g0, x, r); break;
+      case 5: R = merged_rank<5>(runs, g0, x, r); break;
+      case 6: R = merged_rank<6>(runs, g0, x, r); break;
+      case 7: R = merged_rank<7>(runs, g0, x, r); break;
+      default: R = merged_rank<8>(runs, g0, x, r); break;
     }
-#pragma unroll
-    for (int g = 0; g < kSelThreads / 64; ++g)
-      if (g < n_grp && (g << 6) != g0) R += (pos[g] == 63 && runs[(g << 6) + 63] > x) ? 64 : pos[g];
     if (R < k_eff) sm.buf[R] = x;
   }
   __syncthreads();
