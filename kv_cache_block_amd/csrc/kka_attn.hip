@@ -35,13 +35,7 @@ namespace {
 
 constexpr int kAttnThreads = 256;
 constexpr int kChunkHeads = 32;  // (layer, query head) pairs per block-mass chunk
-#ifndef KKA_ATTN_PIPELINE
-#define KKA_ATTN_PIPELINE 0
-#endif
-#ifndef KKA_ATTN_ROWS
-#define KKA_ATTN_ROWS 8
-#endif
-constexpr int kRowUnroll = KKA_ATTN_ROWS;  // key rows per batch
+constexpr int kRowUnroll = 8;    // key rows in flight per lane (vector kernel)
 constexpr int kMaxTB = 256;      // blocks per vector-kernel tile
 #ifndef KKA_ATTN_BUFS
 #define KKA_ATTN_BUFS 3
@@ -196,6 +190,48 @@ __global__ __launch_bounds__(1024) void attn_tiles_kernel(AttnArgs a) {
   }
 }
 
+// The tile a work-group of a logits kernel takes: its sequence, first
+// block j0 (within the sequence), block count, the sequence's first global
+// block o0 and its token count T clamped to its blocks.  valid is false
+// for groups past the last tile (the grid is an upper bound) -- the same for
+// every thread of the group.
+struct Tile {
+  bool valid;
+  int32_t s, j0, o0, nblk;
+  int64_t T;
+};
+
+__device__ __forceinline__ Tile find_tile(const AttnArgs& a, int32_t tile) {
+  Tile t{};
+  t.valid = false;
+  if (tile >= a.tile_offs[a.S]) return t;
+  int32_t lo = 0, hi = a.S - 1;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (a.tile_offs[mid] <= tile) lo = mid;
+    else hi = mid - 1;
+  }
+  t.s = lo;
+  t.j0 = (tile - a.tile_offs[t.s]) * a.TB;
+  t.o0 = a.offs[t.s];
+  const int32_t nb_s = seq_blocks(a, t.s, false);
+  t.nblk = min(a.TB, nb_s - t.j0);
+  t.T = min((int64_t)max(a.seq_len[t.s], 0), (int64_t)nb_s * a.B);
+  t.valid = t.nblk > 0;
+  return t;
+}
+
+// Physical block of each of the tile's blocks into phys[] (-1 if invalid;
+// raises the flag once, from the first layer).
+__device__ __forceinline__ void load_tile_table(const AttnArgs& a, const Tile& t, int32_t l, int64_t* phys) {
+  for (int32_t jb = threadIdx.x; jb < t.nblk; jb += kAttnThreads) {
+    const int64_t p = a.table[t.o0 + t.j0 + jb];
+    const bool ok = p >= 0 && p < a.P;
+    if (!ok && l == 0) raise_err(a.err, KKA_DEVERR_BLOCK_TABLE);
+    phys[jb] = ok ? p : -1;
+  }
+}
+
 // Q8 = head_dim / 8 lanes per key row; GQ = query heads per KV head.
 template <int Q8, int GQ>
 __global__ __launch_bounds__(kAttnThreads) void attn_logits_kernel(AttnArgs a) {
@@ -204,20 +240,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_logits_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int32_t tile = blockIdx.x;
   const int32_t l = blockIdx.y;
-  if (tile >= a.tile_offs[a.S]) return;
-  int32_t lo = 0, hi = a.S - 1;
-  while (lo < hi) {
-    const int32_t mid = (lo + hi + 1) >> 1;
-    if (a.tile_offs[mid] <= tile) lo = mid;
-    else hi = mid - 1;
-  }
-  const int32_t s = lo;
-  const int32_t j0 = (tile - a.tile_offs[s]) * a.TB;
-  const int32_t o0 = a.offs[s];
-  const int32_t nb_s = seq_blocks(a, s, false);
-  const int32_t nblk = min(a.TB, nb_s - j0);
-  if (nblk <= 0) return;  // uniform over the group
-  const int64_t T = min((int64_t)max(a.seq_len[s], 0), (int64_t)nb_s * a.B);
+  const Tile tt = find_tile(a, tile);
+  if (!tt.valid) return;  // uniform over the group
+  const int32_t s = tt.s, j0 = tt.j0, o0 = tt.o0, nblk = tt.nblk;
+  const int64_t T = tt.T;
 
   constexpr int kSlots = kAttnThreads / Q8;
   const int32_t m = (kSlots / a.H) * a.H;  // rows in flight, a multiple of H
@@ -240,12 +266,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_logits_kernel(AttnArgs a) {
       qr[g][4] = x1.x; qr[g][5] = x1.y; qr[g][6] = x1.z; qr[g][7] = x1.w;
     }
   }
-  for (int32_t jb = tid; jb < nblk; jb += kAttnThreads) {
-    const int64_t p = a.table[o0 + j0 + jb];
-    const bool ok = p >= 0 && p < a.P;
-    if (!ok && l == 0) raise_err(a.err, KKA_DEVERR_BLOCK_TABLE);
-    phys[jb] = ok ? p : -1;
-  }
+  load_tile_table(a, tt, l, phys);
   __syncthreads();
 
   if (slot < m) {
@@ -259,9 +280,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_logits_kernel(AttnArgs a) {
     int32_t jb = tl / a.B, st = tl - (tl / a.B) * a.B;
     const int32_t n_it = ((ntok + dtl - 1) / dtl + kRowUnroll - 1) / kRowUnroll;  // uniform
 
-    u32x4 va[kRowUnroll], vb[kRowUnroll];
-    bool oka[kRowUnroll], okb[kRowUnroll];
-    int32_t ta[kRowUnroll], tb[kRowUnroll];
+    u32x4 va[kRowUnroll];
+    bool oka[kRowUnroll];
+    int32_t ta[kRowUnroll];
     // Issues one batch of row loads.  A row outside the tile loads the
     // tile's first row (in bounds) and is never stored.
     auto issue = [&](u32x4 (&v)[kRowUnroll], bool (&ok)[kRowUnroll], int32_t (&t)[kRowUnroll]) {
@@ -313,26 +334,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_logits_kernel(AttnArgs a) {
         }
       }
     };
-#if KKA_ATTN_PIPELINE
-    // two batches in flight: the next batch loads while this one computes
-    if (n_it > 0) issue(va, oka, ta);
-    for (int32_t it = 0; it < n_it; it += 2) {
-      if (it + 1 < n_it) issue(vb, okb, tb);
-      compute(va, oka, ta);
-      if (it + 1 < n_it) {
-        if (it + 2 < n_it) issue(va, oka, ta);
-        compute(vb, okb, tb);
-      }
-    }
-#else
-    (void)vb;
-    (void)okb;
-    (void)tb;
     for (int32_t it = 0; it < n_it; ++it) {
       issue(va, oka, ta);
       compute(va, oka, ta);
     }
-#endif
   }
   __syncthreads();
 
@@ -423,26 +428,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int32_t tile = blockIdx.x;
   const int32_t l = blockIdx.y;
-  if (tile >= a.tile_offs[a.S]) return;
-  int32_t lo = 0, hi = a.S - 1;
-  while (lo < hi) {
-    const int32_t mid = (lo + hi + 1) >> 1;
-    if (a.tile_offs[mid] <= tile) lo = mid;
-    else hi = mid - 1;
-  }
-  const int32_t s = lo;
-  const int32_t j0 = (tile - a.tile_offs[s]) * a.TB;
-  const int32_t o0 = a.offs[s];
-  const int32_t nb_s = seq_blocks(a, s, false);
-  const int32_t nblk = min(a.TB, nb_s - j0);
-  if (nblk <= 0) return;  // uniform over the group
-  const int64_t T = min((int64_t)max(a.seq_len[s], 0), (int64_t)nb_s * a.B);
-  for (int32_t jb = tid; jb < nblk; jb += kAttnThreads) {
-    const int64_t p = a.table[o0 + j0 + jb];
-    const bool ok = p >= 0 && p < a.P;
-    if (!ok && l == 0) raise_err(a.err, KKA_DEVERR_BLOCK_TABLE);
-    phys[jb] = ok ? p : -1;
-  }
+  const Tile tt = find_tile(a, tile);
+  if (!tt.valid) return;  // uniform over the group
+  const int32_t s = tt.s, j0 = tt.j0, o0 = tt.o0, nblk = tt.nblk;
+  const int64_t T = tt.T;
+  load_tile_table(a, tt, l, phys);
   __syncthreads();
 
   const int wave = tid >> 6, lane = tid & 63;
