@@ -11,7 +11,12 @@
  * cosine of anchor and block vector mapped to [0, 1] (section 2.2 step 3,
  * section 3.2) and the top-K are kept (section 5.2 step 4), optionally
  * through the Grid -> Chunk -> Page hierarchy scored in one pass with
- * parent masks (section 5.1).
+ * parent masks (section 5.1).  Further entry points: the same selection
+ * scored coarse to fine (kka_score_topk_lazy, section 5.1), the stability
+ * filter fused into the scoring pass (kka_score_topk_stable, section 5.3),
+ * block vectors kept current as keys are written (kka_pool_on_write,
+ * section 5.2 step 2), and the attention-mass reference the page compares
+ * its selection with (kka_attention_topk, section 3.3).
  *
  * Conventions shared by every entry point
  *  - Pointers named "device" are HIP device pointers; structs and scalars
