@@ -319,11 +319,20 @@ typedef struct kka_select {
  *                past the kept count hold 0
  * n_selected_out device [num_seqs] int32 kept count, or NULL
  * workspace      device, 16-byte aligned, >= kka_score_topk_workspace()
- *                bytes: scratch affinities when affinity_out is NULL (size 0
- *                and may be NULL otherwise).  Calls that run concurrently
- *                must not share a workspace.
- * Runs as two launches on `stream`: the scoring pass over every row, then
- * one selecting work-group per sequence.
+ *                bytes (0, and NULL allowed, only when num_seqs is 0): one
+ *                uint32 tile counter per sequence (the first 4 * num_seqs
+ *                bytes, rounded up to 256), then scratch affinities when
+ *                affinity_out is NULL.  The counters must be zero before the
+ *                first call that uses the workspace (allocate it
+ *                zero-filled); every call leaves them zero.  Calls that run
+ *                concurrently must not share a workspace.
+ * Work-groups score tiles of rows spread over the chip.  When every tile
+ * of the batch fits on the chip at once, the call is one launch on
+ * `stream`: the work-group that completes a sequence's last tile selects
+ * that sequence (affinities pass between work-groups through device-scope
+ * stores and loads).  Larger batches run as two launches: the scoring
+ * pass, then one selecting work-group per sequence.  Results are the same
+ * either way.
  */
 KKA_API kka_status kka_score_topk(const kka_level_layout* lay, const float* level_buf, const int32_t* n_pages,
                           const float* anchors, const kka_select* sel, float* affinity_out, int32_t* page_idx_out,
@@ -386,8 +395,9 @@ KKA_API kka_status kka_score_topk_stable(const kka_level_layout* lay, const floa
  * given) receives only the rows actually scored, bit-identical to
  * kka_score_topk's values for those rows; other rows are left untouched.
  * Arguments, rules and workspace are those of kka_score_topk (the same
- * kka_score_topk_workspace() size suffices).  A flat layout has no parents:
- * the call is then kka_score_topk.  One launch on `stream`.
+ * kka_score_topk_workspace() size suffices; the tile counters are not
+ * touched).  A flat layout has no parents: the call is then
+ * kka_score_topk.  One launch on `stream`.
  */
 KKA_API kka_status kka_score_topk_lazy(const kka_level_layout* lay, const float* level_buf, const int32_t* n_pages,
                                        const float* anchors, const kka_select* sel, float* affinity_out,

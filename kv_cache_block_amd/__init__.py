@@ -244,11 +244,14 @@ def new_workspace(nbytes: int, device="cuda") -> Optional[torch.Tensor]:
     return torch.zeros(int(nbytes), dtype=torch.uint8, device=device)
 
 
-def _ws(ws: Optional[torch.Tensor], need: int, device) -> tuple:
+def _ws(ws: Optional[torch.Tensor], need: int, device, stream=None) -> tuple:
     if need <= 0 and ws is None:
         return None, 0, None
     if ws is None:
         ws = new_workspace(need, device)
+        if stream is not None:
+            # zero-filled on torch's current stream; the call runs on `stream`
+            torch.cuda.current_stream(ws.device).synchronize()
     if ws.numel() * ws.element_size() < need:
         raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, needs {need}")
     return _dev(ws, "workspace"), ws.numel() * ws.element_size(), ws
@@ -275,7 +278,7 @@ def kka_pool_blocks(kp: KPool, seqs: Seqs, vb_out: torch.Tensor, mode: int = WEI
     hw = _dev(head_weight, "head_weight", torch.float32, min_numel=S * kp.num_layers * kp.num_kv_heads,
               allow_none=mode == WEIGHT_UNIFORM)
     need = kka_pool_blocks_workspace(kp, seqs, mode, blocks)
-    wp, wbytes, keep = _ws(workspace, need, vb_out.device if vb_out is not None else "cuda")
+    wp, wbytes, keep = _ws(workspace, need, vb_out.device if vb_out is not None else "cuda", stream)
     _check(lib().kka_pool_blocks(ctypes.byref(kp.c), ctypes.byref(seqs.c), bp, nb, int(mode), hw, outp,
                                  int(vb_seq_stride), wp, wbytes, _stream(stream)), "kka_pool_blocks")
     return keep
@@ -294,7 +297,7 @@ def kka_pool_anchor(kp: KPool, seqs: Seqs, window: int, anchor_out: torch.Tensor
     hw = _dev(head_weight, "head_weight", torch.float32, min_numel=S * kp.num_layers * kp.num_kv_heads,
               allow_none=True)
     need = kka_pool_anchor_workspace(kp, seqs, window)
-    wp, wbytes, keep = _ws(workspace, need, anchor_out.device)
+    wp, wbytes, keep = _ws(workspace, need, anchor_out.device, stream)
     _check(lib().kka_pool_anchor(ctypes.byref(kp.c), ctypes.byref(seqs.c), int(window), hw, ap, wp, wbytes,
                                  _stream(stream)), "kka_pool_anchor")
     return keep
@@ -338,7 +341,7 @@ def kka_attention_topk(kp: KPool, seqs: Seqs, queries: torch.Tensor, num_q_heads
     sp = _dev(score_out, "score_out", torch.float32, min_numel=S * k, allow_none=True)
     cp = _dev(n_selected_out, "n_selected_out", torch.int32, min_numel=S, allow_none=True)
     need = kka_attention_topk_workspace(kp, seqs, num_q_heads)
-    wp, wbytes, keep = _ws(workspace, need, block_score_out.device)
+    wp, wbytes, keep = _ws(workspace, need, block_score_out.device, stream)
     sc = (1.0 / D ** 0.5) if scale is None else float(scale)
     _check(lib().kka_attention_topk(ctypes.byref(kp.c), ctypes.byref(seqs.c), qp, int(num_q_heads), sc, int(k), op,
                                     int(out_seq_stride), ip, sp, cp, wp, wbytes, _stream(stream)),
@@ -380,7 +383,7 @@ def kka_score_topk(lay: LevelLayout, level_buf: torch.Tensor, n_pages: torch.Ten
     cnt = _dev(n_selected_out, "n_selected_out", torch.int32, min_numel=S, allow_none=True)
     aff = _dev(affinity_out, "affinity_out", torch.float32, min_numel=S * lay.rows_per_seq, allow_none=True)
     need = kka_score_topk_workspace(lay, affinity_out is not None)
-    wp, wbytes, keep = _ws(workspace, need, level_buf.device)
+    wp, wbytes, keep = _ws(workspace, need, level_buf.device, stream)
     sel = c_select(int(k_grid), int(k_chunk), int(k_page))
     if history is not None:
         if lazy:

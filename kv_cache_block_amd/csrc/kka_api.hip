@@ -33,6 +33,9 @@ uint32_t* device_error_word() {
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Scoring workspace head: one tile counter per sequence.
+inline size_t score_counter_bytes(int32_t S) { return S > 0 ? align256((size_t)S * sizeof(uint32_t)) : 0; }
+
 kka_status check_kpool(const kka_kpool* kp) {
   if (!kp || !kp->k) return KKA_ERR_NULL;
   if (kp->num_layers < 1 || kp->num_kv_heads < 1 || kp->block_size < 1 || kp->num_phys_blocks < 1)
@@ -458,7 +461,8 @@ size_t kka_score_topk_workspace(const kka_level_layout* lay, const kka_select* s
   (void)sel;
   LevelGeom g;
   if (!level_geom(lay, g)) return 0;
-  return with_affinity_out ? 0 : align256((size_t)lay->num_seqs * (size_t)g.rows * sizeof(float));
+  return score_counter_bytes(lay->num_seqs) +
+         (with_affinity_out ? 0 : align256((size_t)lay->num_seqs * (size_t)g.rows * sizeof(float)));
 }
 
 }  // extern "C"
@@ -499,7 +503,10 @@ kka_status prepare_score(const kka_level_layout* lay, const float* level_buf, co
   a.c_cap = g.c_cap;
   a.n_pages = n_pages;
   a.anchors = anchors;
-  a.aff = affinity_out ? affinity_out : static_cast<float*>(workspace);
+  // workspace: per-sequence tile counters, then scratch affinities
+  a.done = static_cast<uint32_t*>(workspace);
+  a.aff = affinity_out ? affinity_out
+                       : reinterpret_cast<float*>(static_cast<char*>(workspace) + score_counter_bytes(a.S));
   a.k_g = lay->hierarchical ? sel->k_grid : 0;
   a.k_c = lay->hierarchical ? sel->k_chunk : 0;
   a.k_p = sel->k_page;

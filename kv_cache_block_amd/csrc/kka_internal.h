@@ -167,6 +167,7 @@ struct ScoreArgs {
   float* score_out;
   int32_t* cnt_out;
   int32_t tiles_per_seq, rows_per_tile;
+  uint32_t* done;        // per-sequence count of finished scoring tiles (zero between calls)
   uint32_t* err;
   // stability filter (page rows only; hist == nullptr: off)
   uint32_t* hist;        // window words, hist + s * max_pages + page

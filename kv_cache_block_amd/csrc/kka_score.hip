@@ -6,25 +6,28 @@
 // single pass, children of unselected parents masked to zero) and section
 // 5.2 step 4 (keep the K highest-affinity blocks).
 //
-// score_kernel: a batched GEMV with one right-hand side per sequence, bound
-// by HBM bandwidth.  Each sequence's present rows are cut into tiles spread
+// Scoring: a batched GEMV with one right-hand side per sequence, bound by
+// HBM bandwidth.  Each sequence's present rows are cut into tiles spread
 // over the whole chip; in a tile, 8 lanes share one row (each lane reads
 // 16-byte pieces 128 bytes apart, so 8 lanes read whole 128-byte lines) and
 // every lane keeps 8 non-temporal loads in flight (rows are read once per
 // step; a serving batch's level rows exceed the last-level cache anyway).
 // Dot product and row norm are reduced over the 8 lanes with a fixed
-// butterfly.  No cross-group communication: the kernel boundary publishes
-// the affinities.
+// butterfly.
 //
-// select_kernel: one work-group per sequence, written for latency: the
-// sequence's whole affinity row block is staged into LDS in one round of
-// loads, then each level is selected from LDS: candidates (children of kept
-// parents, or every row) with a positive score are compacted with wave
-// ballots; up to 512 of them are ranked directly (rank = number of larger
-// keys, so rank < k places the element at its final position); larger sets
-// use an MSB-first radix select.  Keys are (affinity bits << 32 | ~index):
-// unique, and larger means higher score then lower index.  When fewer than
-// k candidates score above zero, the lowest-index rows scoring exactly 0
+// Selection, written for latency: for batches whose tiles all fit on the
+// chip at once, the work-group that finishes a sequence's last scoring
+// tile (a per-sequence counter) selects that sequence in the same launch
+// (score_select_kernel); larger batches run the lighter score_kernel and
+// then select_kernel, one work-group per sequence.  The sequence's whole
+// affinity row block is staged into LDS in one round of loads, then each
+// level is selected from LDS: candidates (children of kept parents, or
+// every row) with a positive score are compacted with wave ballots; up to
+// 512 of them are ranked directly (rank = number of larger keys, so rank <
+// k places the element at its final position); larger sets use an
+// MSB-first radix select.  Keys are (affinity bits << 32 | ~index): unique,
+// and larger means higher score then lower index.  When fewer than k
+// candidates score above zero, the lowest-index rows scoring exactly 0
 // (masked or zero affinity) fill the remaining slots in index order.
 #include "kka_internal.h"
 
@@ -47,10 +50,7 @@ constexpr int kBitmapWords = kMaxParents / 32;
 #ifndef KKA_SCORE_PASSES
 #define KKA_SCORE_PASSES 1
 #endif
-// lanes sharing one row, and whether row loads bypass cache allocation
-#ifndef KKA_SCORE_LPR
-#define KKA_SCORE_LPR 8
-#endif
+// whether row loads bypass cache allocation
 #ifndef KKA_SCORE_NT
 #define KKA_SCORE_NT 1
 #endif
@@ -77,40 +77,63 @@ struct SelectShared {
   uint32_t digit, above, bucket;
   int32_t cnt[4];
   int32_t wave_tot[kSelThreads / 64];
+  uint32_t last;  // this work-group finished its sequence's scoring
 };
 
 struct Level {
   const float* aff;        // global scores: element e at aff[e] (used when not staged)
   int32_t off;             // row offset of element 0 in the staged LDS copy
-  bool staged;             // read scores from sm.aff[off + e]
   int32_t n;               // elements in the level
   int32_t fanout;          // children per parent; 0 = no parent level (all live)
+  int32_t shift;           // log2(fanout) when fanout is a power of two, else -1
   int32_t n_par;           // kept parents listed in plist (fanout > 0)
   const uint32_t* parent;  // keep flags of the parent level (fanout > 0)
   int32_t slot;            // counter of sm.cnt this level uses
 };
 
+// Affinities cross work-groups inside one launch (scoring tiles on any
+// XCD, the selecting work-group on another), and each XCD has its own L2:
+// they are stored and loaded with device-scope atomics, which write
+// through and read past the non-coherent L2, instead of paying a
+// device-scope fence (a whole-L2 write-back) per tile.
+__device__ __forceinline__ void store_aff(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_aff(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Score bits of element e: from the LDS copy (STG) or from global memory.
+// The two sources are separate instantiations so that LDS reads compile to
+// LDS instructions rather than generic-address loads.
+template <bool STG>
 __device__ __forceinline__ uint32_t aff_key(const Level& L, const SelectShared& sm, int32_t e) {
-  return __float_as_uint(L.staged ? sm.aff[L.off + e] : L.aff[e]);
+  if constexpr (STG) return __float_as_uint(sm.aff[L.off + e]);
+  else return __float_as_uint(load_aff(L.aff + e));
+}
+
+// Parent slot of child c (a shift for power-of-two fan-outs).
+__device__ __forceinline__ int32_t parent_of(const Level& L, int32_t c) {
+  return L.shift >= 0 ? (c >> L.shift) : c / L.fanout;
 }
 
 __device__ __forceinline__ bool is_live(const Level& L, int32_t e) {
   if (L.fanout == 0) return true;
-  const int32_t p = e / L.fanout;
+  const int32_t p = parent_of(L, e);
   return (L.parent[p >> 5] >> (p & 31)) & 1u;
 }
 
 // Candidate c -> element index (or -1 when past the level's end).
 __device__ __forceinline__ int32_t cand(const Level& L, const SelectShared& sm, int64_t c) {
   if (L.fanout == 0) return (int32_t)c;
-  const int32_t pi = (int32_t)(c / L.fanout);
+  const int32_t pi = L.shift >= 0 ? (int32_t)(c >> L.shift) : (int32_t)(c / L.fanout);
   const int32_t e = sm.plist[pi] * L.fanout + (int32_t)(c - (int64_t)pi * L.fanout);
   return e < L.n ? e : -1;
 }
 
 __device__ __forceinline__ int32_t cand32(const Level& L, const SelectShared& sm, int32_t c) {
   if (L.fanout == 0) return c;
-  const int32_t pi = c / L.fanout;
+  const int32_t pi = parent_of(L, c);
   const int32_t e = sm.plist[pi] * L.fanout + (c - pi * L.fanout);
   return e < L.n ? e : -1;
 }
@@ -171,6 +194,7 @@ __device__ void sort_desc(SelectShared& sm, int32_t n) {
 
 // Radix select over every positive candidate (re-enumerated each pass), for
 // candidate sets too large to rank; leaves the top k_eff sorted in sm.buf.
+template <bool STG>
 __device__ void radix_top(const Level& L, int64_t m, int32_t k_eff, SelectShared& sm) {
   const int tid = threadIdx.x;
   uint64_t prefix = 0, mask = 0;
@@ -181,7 +205,7 @@ __device__ void radix_top(const Level& L, int64_t m, int32_t k_eff, SelectShared
     for (int64_t c = tid; c < m; c += kSelThreads) {
       const int32_t e = cand(L, sm, c);
       if (e < 0) continue;
-      const uint32_t key = aff_key(L, sm, e);
+      const uint32_t key = aff_key<STG>(L, sm, e);
       if (key == 0u) continue;
       const uint64_t comp = composite(key, e);
       if ((comp & mask) == prefix) atomicAdd(&sm.hist[(uint32_t)(comp >> shift) & 255u], 1u);
@@ -201,7 +225,7 @@ __device__ void radix_top(const Level& L, int64_t m, int32_t k_eff, SelectShared
   for (int64_t c = tid; c < m; c += kSelThreads) {
     const int32_t e = cand(L, sm, c);
     if (e < 0) continue;
-    const uint32_t key = aff_key(L, sm, e);
+    const uint32_t key = aff_key<STG>(L, sm, e);
     if (key == 0u) continue;
     const uint64_t comp = composite(key, e);
     if (comp >= prefix) {
@@ -216,6 +240,7 @@ __device__ void radix_top(const Level& L, int64_t m, int32_t k_eff, SelectShared
 // When only P < k_eff candidates score above zero, the lowest-index rows
 // scoring exactly 0 (masked, or live with zero affinity) take slots
 // P .. k_eff-1 of sm.buf in index order.
+template <bool STG>
 __device__ void fill_zeros(const Level& L, SelectShared& sm, int32_t P, int32_t k_eff) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -224,7 +249,7 @@ __device__ void fill_zeros(const Level& L, SelectShared& sm, int32_t P, int32_t 
   int32_t found = 0;
   for (int32_t e0 = 0; e0 < L.n && found < need; e0 += kSelThreads) {
     const int32_t e = e0 + tid;
-    const bool zero = e < L.n && (!is_live(L, e) || aff_key(L, sm, e) == 0u);
+    const bool zero = e < L.n && (!is_live(L, e) || aff_key<STG>(L, sm, e) == 0u);
     const uint64_t bal = __ballot(zero);
     if (lane == 0) sm.wave_tot[wave] = (int32_t)__popcll(bal);
     __syncthreads();
@@ -242,6 +267,7 @@ __device__ void fill_zeros(const Level& L, SelectShared& sm, int32_t P, int32_t 
 
 // Keeps the top min(k, n) elements of a level with more candidates than
 // threads, sorted, in sm.buf.  sm.cnt[L.slot] must be zero on entry.
+template <bool STG>
 __device__ int32_t select_level_big(const Level& L, int32_t k, SelectShared& sm) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -254,7 +280,7 @@ __device__ int32_t select_level_big(const Level& L, int32_t k, SelectShared& sm)
   for (int64_t c0 = 0; c0 < m; c0 += kSelThreads) {
     const int64_t c = c0 + tid;
     const int32_t e = c < m ? cand(L, sm, c) : -1;
-    const uint32_t key = e >= 0 ? aff_key(L, sm, e) : 0u;
+    const uint32_t key = e >= 0 ? aff_key<STG>(L, sm, e) : 0u;
     const bool pos = key != 0u;
     const uint64_t bal = __ballot(pos);
     int32_t base = 0;
@@ -269,7 +295,7 @@ __device__ int32_t select_level_big(const Level& L, int32_t k, SelectShared& sm)
     // too many to rank: radix select the top k_eff, or (when k_eff is larger
     // still) all P positive candidates, sorted; zeros fill the rest below
     const int32_t take = P >= k_eff ? k_eff : P;
-    radix_top(L, m, take, sm);
+    radix_top<STG>(L, m, take, sm);
     if (P >= k_eff) return k_eff;
   } else {
     // rank the positive candidates: rank r goes to slot r when r < k_eff.
@@ -297,7 +323,7 @@ __device__ int32_t select_level_big(const Level& L, int32_t k, SelectShared& sm)
     __syncthreads();
     if (P >= k_eff) return k_eff;
   }
-  fill_zeros(L, sm, P, k_eff);
+  fill_zeros<STG>(L, sm, P, k_eff);
   return k_eff;
 }
 
@@ -331,82 +357,97 @@ __device__ __forceinline__ int32_t merged_rank(const uint64_t* runs, int32_t g0,
   return R;
 }
 
-// Keeps the top min(k, n) elements of a level, sorted, in sm.buf.
-// Levels with at most kSelThreads candidates: candidate keys go to LDS in
-// groups of 64 (slots past the candidates hold distinct keys below every
-// real one); all threads rank every key within its group, tpc lanes per key
-// each comparing a strided share; with one group that rank is final,
-// otherwise each group is written back as a strictly descending run and a
-// key's rank in the level is its rank in its group plus, for every other
-// group, how many keys of that run exceed it (binary search).  Keys without a positive score rank below all positive ones and
+// Lanes that share one key when NG groups of 64 keys are ranked by
+// kSelThreads threads: the largest power of two up to 8 that fits.
+constexpr int rank_tpc(int ng) {
+  int t = 1;
+  while (t < 8 && ng * 64 * t * 2 <= kSelThreads) t <<= 1;
+  return t;
+}
+
+// Keeps the top k_eff of a level's m <= NG * 64 candidates, sorted, in
+// sm.buf.  Candidate keys go to LDS in NG groups of 64 (slots past the
+// candidates hold distinct keys below every real one); TPC lanes rank each
+// key within its group, each comparing a fixed strided share; with one group
+// that rank is final, otherwise each group is written back as a strictly
+// descending run and a key's rank in the level is its rank in its group
+// plus, for every other group, how many keys of that run exceed it (binary
+// search).  Keys without a positive score rank below all positive ones and
 // are never kept here (the zero fill handles them).
-__device__ int32_t select_level(const Level& L, int32_t k, SelectShared& sm) {
-  const int32_t k_eff = k < L.n ? k : L.n;
-  if (k_eff <= 0) return 0;
-  const int64_t m64 = L.fanout ? (int64_t)L.n_par * L.fanout : (int64_t)L.n;
-  if (m64 > kSelThreads) return select_level_big(L, k, sm);
-  const int32_t m = (int32_t)m64;
+template <bool STG, int NG>
+__device__ int32_t select_small(const Level& L, int32_t m, int32_t k_eff, SelectShared& sm) {
+  constexpr int TPC = rank_tpc(NG);
+  static_assert(NG * 64 * TPC <= kSelThreads && 64 % (8 * TPC) == 0, "rank layout");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int32_t n_grp = (m + 63) >> 6;
-  uint64_t* keys = sm.ck;    // [n_grp * 64] candidate keys by candidate index
-  uint64_t* runs = sm.run;   // [n_grp * 64] the same keys, each group sorted
+  uint64_t* keys = sm.ck;    // [NG * 64] candidate keys by candidate index
+  uint64_t* runs = sm.run;   // [NG * 64] the same keys, each group sorted
   // phase A: candidate keys
   {
     const int32_t e = tid < m ? cand32(L, sm, tid) : -1;
-    const uint32_t key = e >= 0 ? aff_key(L, sm, e) : 0u;
-    if (tid < (n_grp << 6)) keys[tid] = e >= 0 ? composite(key, e) : (uint64_t)tid;
+    const uint32_t key = e >= 0 ? aff_key<STG>(L, sm, e) : 0u;
+    if (tid < NG * 64) keys[tid] = e >= 0 ? composite(key, e) : (uint64_t)tid;
     const uint64_t bal = __ballot(key != 0u);
     if (lane == 0) sm.wave_tot[wave] = (int32_t)__popcll(bal);
   }
   __syncthreads();
   int32_t P = 0;
   for (int w = 0; w < kSelThreads / 64; ++w) P += sm.wave_tot[w];
-  // phase B: rank within the group, tpc lanes per key (the largest power of
-  // two with n_grp * 64 * tpc <= kSelThreads); threads past the last group
-  // only read
-  int32_t tpc = 1;
-  while (tpc < 8 && (n_grp << 6) * tpc * 2 <= kSelThreads) tpc <<= 1;
-  const int32_t i = tid / tpc, q = tid - i * tpc;
-  const bool active = i < (n_grp << 6);
+  // phase B: rank within the group.  Active threads form whole waves
+  // (NG * 64 * TPC is a multiple of 64), and a wave's 64 / TPC keys lie in
+  // one group, so the group base is uniform over the wave.
+  const int32_t i = tid / TPC, q = tid % TPC;
+  const bool active = i < NG * 64;
   const int32_t ic = active ? i : 0;
-  const int32_t g0 = (ic >> 6) << 6;
+  const int32_t g0 = __builtin_amdgcn_readfirstlane((ic >> 6) << 6);
   const uint64_t x = keys[ic];
   int32_t r = 0;
-  for (int32_t j = q; j < 64; j += 8 * tpc) {
+#pragma unroll
+  for (int j = 0; j < 64 / TPC; j += 8) {
     uint64_t y[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) y[u] = keys[g0 + min(j + u * tpc, 63)];
+    for (int u = 0; u < 8; ++u) y[u] = keys[g0 + q + (j + u) * TPC];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) r += (int32_t)(j + u * tpc < 64 && y[u] > x);
+    for (int u = 0; u < 8; ++u) r += (int32_t)(y[u] > x);
   }
-  r = group_sum(r, tpc);
-  if (n_grp == 1) {
+  r = group_sum(r, TPC);
+  if constexpr (NG == 1) {
     // one group: the rank in it is the rank in the level
     if (active && q == 0 && (x >> 32) != 0ull && r < k_eff) sm.buf[r] = x;
     __syncthreads();
-    if (P < k_eff) fill_zeros(L, sm, P, k_eff);
-    return k_eff;
-  }
-  if (active && q == 0) runs[g0 + r] = x;
-  __syncthreads();
-  // phase C: rank in the level, positive keys only
-  if (active && q == 0 && (x >> 32) != 0ull) {
-    int32_t R;
-    switch (n_grp) {
-      case 2: R = merged_rank<2>(runs, g0, x, r); break;
-      case 3: R = merged_rank<3>(runs, g0, x, r); break;
-      case 4: R = merged_rank<4>(runs, g0, x, r); break;
-      case 5: R = merged_rank<5>(runs, g0, x, r); break;
-      case 6: R = merged_rank<6>(runs, g0, x, r); break;
-      case 7: R = merged_rank<7>(runs, g0, x, r); break;
-      default: R = merged_rank<8>(runs, g0, x, r); break;
+  } else {
+    if (active && q == 0) runs[g0 + r] = x;
+    __syncthreads();
+    // phase C: rank in the level, positive keys only
+    if (active && q == 0 && (x >> 32) != 0ull) {
+      const int32_t R = merged_rank<NG>(runs, g0, x, r);
+      if (R < k_eff) sm.buf[R] = x;
     }
-    if (R < k_eff) sm.buf[R] = x;
+    __syncthreads();
   }
-  __syncthreads();
-  if (P < k_eff) fill_zeros(L, sm, P, k_eff);
+  if (P < k_eff) fill_zeros<STG>(L, sm, P, k_eff);
   return k_eff;
+}
+
+// Picks the group count: the smallest NG with m <= NG * 64.
+template <bool STG, int NG>
+__device__ __forceinline__ int32_t select_small_ng(const Level& L, int32_t m, int32_t k_eff, SelectShared& sm) {
+  if constexpr (NG * 64 < kSelThreads) {
+    if (m > NG * 64) return select_small_ng<STG, NG + 1>(L, m, k_eff, sm);
+  }
+  return select_small<STG, NG>(L, m, k_eff, sm);
+}
+
+// Keeps the top min(k, n) elements of a level, sorted, in sm.buf: levels
+// with at most kSelThreads candidates are ranked, larger ones compacted and
+// ranked or radix-selected.
+template <bool STG>
+__device__ int32_t select_level(const Level& L, int32_t k, SelectShared& sm) {
+  const int32_t k_eff = k < L.n ? k : L.n;
+  if (k_eff <= 0) return 0;
+  const int64_t m64 = L.fanout ? (int64_t)L.n_par * L.fanout : (int64_t)L.n;
+  if (m64 > kSelThreads) return select_level_big<STG>(L, k, sm);
+  return select_small_ng<STG, 1>(L, (int32_t)m64, k_eff, sm);
 }
 
 // Records the kept elements of a level (sm.buf[0, k_eff)) as the parents of
@@ -439,45 +480,28 @@ __device__ __forceinline__ SeqGeom seq_geom(const ScoreArgs& a, int32_t s, bool 
 }
 
 // Copies a sequence's whole affinity row block src[0, n) (n <= kLdsRows)
-// into LDS with one round of loads, every load issued before the first
-// store; 16-byte pieces when src is 16-byte aligned.  Rows that are not
-// present are copied too and never read.
-__device__ void stage_rows(float* dst, const float* src, int32_t n) {
-  constexpr int U = (kLdsRows / 4 + kSelThreads - 1) / kSelThreads;
+// into LDS with one round of device-scope loads, every load issued before
+// the first store.  Rows that are not present are copied too and never
+// read.
+__device__ __forceinline__ void stage_rows(float* dst, const float* src, int32_t n) {
+  constexpr int U = (kLdsRows + kSelThreads - 1) / kSelThreads;
   const int tid = threadIdx.x;
-  int32_t done = 0;
-  if ((((uintptr_t)src) & 15u) == 0) {
-    const int32_t n4 = n >> 2;
-    const float4* s4 = reinterpret_cast<const float4*>(src);
-    float4* d4 = reinterpret_cast<float4*>(dst);
-    if (n4 > 0) {
-      // Clamped indices make every load and store unconditional, so all U
-      // loads are in flight before the first store; the clamped copies write
-      // the value the last slot holds anyway.
-      float4 t[U];
+  if (n <= 0) return;
+  // Clamped indices make every load and store unconditional; the clamped
+  // copies write the value the last slot holds anyway.
+  float t[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) t[u] = s4[min(u * kSelThreads + tid, n4 - 1)];
+  for (int u = 0; u < U; ++u) t[u] = load_aff(src + min(u * kSelThreads + tid, n - 1));
 #pragma unroll
-      for (int u = 0; u < U; ++u) d4[min(u * kSelThreads + tid, n4 - 1)] = t[u];
-    }
-    done = n4 << 2;
-  }
-  for (int32_t r0 = done; r0 < n; r0 += 8 * kSelThreads) {
-    float t[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) t[u] = src[min(r0 + u * kSelThreads + tid, n - 1)];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) dst[min(r0 + u * kSelThreads + tid, n - 1)] = t[u];
-  }
+  for (int u = 0; u < U; ++u) dst[min(u * kSelThreads + tid, n - 1)] = t[u];
 }
 
 // Level `lev` (0 grids, 1 chunks of kept grids, 2 pages of kept chunks or
 // every page when flat) of sequence geometry g; kp = kept count of the
 // level above.
-__device__ __forceinline__ Level make_level(const ScoreArgs& a, const SeqGeom& g, int32_t lev, bool staged,
-                                            const float* aff, int32_t kp, SelectShared& sm) {
+__device__ __forceinline__ Level make_level(const ScoreArgs& a, const SeqGeom& g, int32_t lev, const float* aff,
+                                            int32_t kp, SelectShared& sm) {
   Level L;
-  L.staged = staged;
   L.slot = lev;
   if (lev == 0) {
     L.off = a.max_pages + a.c_cap;
@@ -497,6 +521,7 @@ __device__ __forceinline__ Level make_level(const ScoreArgs& a, const SeqGeom& g
   }
   L.aff = aff + L.off;
   L.n_par = kp;
+  L.shift = (L.fanout > 0 && (L.fanout & (L.fanout - 1)) == 0) ? __builtin_ctz((unsigned)L.fanout) : -1;
   return L;
 }
 
@@ -525,24 +550,35 @@ __device__ __forceinline__ void write_selection(const ScoreArgs& a, const Select
   if (tid == 0 && a.cnt_out) a.cnt_out[s] = kp;
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(ScoreArgs a) {
-  __shared__ SelectShared sm;
-  const int32_t s = blockIdx.x;
+// Selects grids, chunks of kept grids and pages of kept chunks (pages only
+// when flat); returns the kept page count.
+template <bool STG>
+__device__ __forceinline__ int32_t select_levels(const ScoreArgs& a, const SeqGeom& g, const float* aff, SelectShared& sm) {
+  int32_t kp = 0;
+  for (int32_t lev = a.hier ? 0 : 2; lev < 3; ++lev) {
+    const Level L = make_level(a, g, lev, aff, kp, sm);
+    kp = select_level<STG>(L, lev == 0 ? a.k_g : (lev == 1 ? a.k_c : a.k_p), sm);
+    if (lev < 2) keep_parents(sm, kp, lev == 0 ? sm.kept_grid : sm.kept_chunk);
+  }
+  return kp;
+}
+
+// Selection of sequence s from its affinity rows in a.aff, by the whole
+// work-group.
+__device__ __forceinline__ void select_sequence(const ScoreArgs& a, int32_t s, SelectShared& sm) {
   const float* aff = a.aff + (int64_t)s * a.rows_per_seq;
   const SeqGeom g = seq_geom(a, s, false);  // issued before the staging loads
   const bool staged = a.rows_per_seq <= kLdsRows;
   if (staged) stage_rows(sm.aff, aff, (int32_t)a.rows_per_seq);
   clear_select_state(a, g, sm);
   __syncthreads();
-  // Levels run as one loop so a single copy of the level code is fetched
-  // (a lone work-group per compute unit starts with a cold instruction cache).
-  int32_t kp = 0;
-  for (int32_t lev = a.hier ? 0 : 2; lev < 3; ++lev) {
-    const Level L = make_level(a, g, lev, staged, aff, kp, sm);
-    kp = select_level(L, lev == 0 ? a.k_g : (lev == 1 ? a.k_c : a.k_p), sm);
-    if (lev < 2) keep_parents(sm, kp, lev == 0 ? sm.kept_grid : sm.kept_chunk);
-  }
+  const int32_t kp = staged ? select_levels<true>(a, g, aff, sm) : select_levels<false>(a, g, aff, sm);
   write_selection(a, sm, s, kp);
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(ScoreArgs a) {
+  __shared__ SelectShared sm;
+  select_sequence(a, blockIdx.x, sm);
 }
 
 // (1 + cos) / 2 clamped to [0, 1]; NaN and -0 become +0.
@@ -628,6 +664,10 @@ __device__ __forceinline__ void stability_step(const ScoreArgs& a, uint32_t h, f
   if (stab) *stab = (float)__popc(nh) / (float)a.stab_w;
 }
 
+// Scoring pass for batches too large for one wave of fused work-groups:
+// 256-thread work-groups without LDS (more of them resident per compute
+// unit), each scoring one tile; the kernel boundary publishes the
+// affinities to the selection launch that follows.
 template <int LPR, int NQ, int R, bool STAB>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   constexpr int NG = 256 / LPR;  // row groups per work-group
@@ -679,32 +719,100 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   }
 }
 
+// Scoring tile, then selection: every work-group scores one tile of one
+// sequence's rows; the work-group that finishes a sequence's last tile (a
+// per-sequence counter, incremented once each tile's device-scope
+// affinity stores have completed) selects that sequence.  Other sequences'
+// tiles keep streaming meanwhile, and the selection needs no second launch.
+template <int LPR, int NQ, int R, bool STAB>
+__global__ __launch_bounds__(kSelThreads) void score_select_kernel(ScoreArgs a) {
+  __shared__ SelectShared sm;
+  constexpr int NG = kSelThreads / LPR;  // row groups per work-group
+  const int tid = threadIdx.x;
+  const int32_t s = blockIdx.x / a.tiles_per_seq;
+  const int32_t tile = blockIdx.x - s * a.tiles_per_seq;
+  const SeqGeom g = seq_geom(a, s, tid == 0 && tile == 0);
+  const int32_t nv = g.n_p + g.n_c + g.n_g;
+  const int32_t v0 = tile * a.rows_per_tile;
+  const int32_t v1 = min(nv, v0 + a.rows_per_tile);
+  const int32_t Q = a.D >> 2;
+  const f32x4* seq = reinterpret_cast<const f32x4*>(a.lvl + (int64_t)s * a.rows_per_seq * a.D);
+  float* aff = a.aff + (int64_t)s * a.rows_per_seq;
+  const int32_t grp = tid / LPR, lg = tid % LPR;
+
+  if (v0 < v1) {
+    const AnchorRegs<LPR, NQ> A = load_anchor<LPR, NQ>(a, s, lg);
+    uint32_t* hist = STAB ? a.hist + (int64_t)s * a.max_pages : nullptr;
+    float* stab = STAB && a.stab_out ? a.stab_out + (int64_t)s * a.max_pages : nullptr;
+    for (int32_t v = v0 + grp; v < v1; v += NG * R) {
+      f32x4 x[R][NQ];
+      int64_t row[R];
+      uint32_t h[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        // a row past the tile is replaced by row 0 (loaded, never written back)
+        const int32_t vr = v + NG * r;
+        const bool ok = vr < v1;
+        row[r] = !ok ? 0
+                 : vr < g.n_p ? vr
+                 : vr < g.n_p + g.n_c ? (int64_t)a.max_pages + (vr - g.n_p)
+                                      : (int64_t)a.max_pages + a.c_cap + (vr - g.n_p - g.n_c);
+        load_row<LPR, NQ>(seq + row[r] * Q, lg, Q, x[r]);
+        // page rows also load their window word (others load word 0: max_pages >= 1 here)
+        if constexpr (STAB) h[r] = hist[ok && vr < g.n_p ? vr : 0];
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float v_aff = row_affinity<LPR, NQ>(x[r], A);
+        const int32_t vr = v + NG * r;
+        if (lg == 0 && vr < v1) {
+          sm.aff[vr - v0] = v_aff;
+          if constexpr (STAB) {
+            if (vr < g.n_p) stability_step(a, h[r], v_aff, hist + vr, stab ? stab + vr : nullptr);
+          }
+        }
+      }
+    }
+  }
+  // The tile's affinities leave in whole lines: consecutive rows of a level
+  // are consecutive in memory, so consecutive lanes write consecutive words.
+  __syncthreads();
+  for (int32_t i = tid; i < v1 - v0; i += kSelThreads) {
+    const int32_t vr = v0 + i;
+    const int64_t row = vr < g.n_p ? vr
+                        : vr < g.n_p + g.n_c ? (int64_t)a.max_pages + (vr - g.n_p)
+                                             : (int64_t)a.max_pages + a.c_cap + (vr - g.n_p - g.n_c);
+    store_aff(aff + row, sm.aff[i]);
+  }
+  // Every tile of the launch counts, scored or empty: once all of this
+  // work-group's affinity stores have completed (written through), one
+  // device-scope increment; atomicInc wraps the counter back to 0 on the
+  // last tile, leaving it ready for the next call.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) sm.last = atomicInc(a.done + s, (unsigned)(a.tiles_per_seq - 1)) == (unsigned)(a.tiles_per_seq - 1);
+  __syncthreads();
+  if (!sm.last) return;
+  select_sequence(a, s, sm);
+}
+
 // Lazy hierarchical scoring: one work-group per sequence scores the grids,
 // selects, scores only the chunks of kept grids, selects, scores only the
 // pages of kept chunks and selects (the page's coarse-to-fine order).  Rows
 // under unkept parents are never read; their score is +0 by definition, so
 // the selection equals the one over every row.  Scored affinities land in
-// LDS when the sequence's rows fit, else in `a.aff`; when `lazy_out` is set
-// they are also written there (other rows untouched).
-template <int LPR, int NQ, int R>
-__global__ __launch_bounds__(kSelThreads) void lazy_kernel(ScoreArgs a, float* lazy_out) {
-  __shared__ SelectShared sm;
+// LDS when the sequence's rows fit (STG), else in `a.aff`; when `lazy_out`
+// is set they are also written there (other rows untouched).
+template <bool STG, int LPR, int NQ, int R>
+__device__ __forceinline__ int32_t lazy_levels(const ScoreArgs& a, const SeqGeom& g, const f32x4* seq, float* aff, float* out,
+                               const AnchorRegs<LPR, NQ>& A, SelectShared& sm) {
   constexpr int NG = kSelThreads / LPR;
   const int tid = threadIdx.x;
-  const int32_t s = blockIdx.x;
-  const SeqGeom g = seq_geom(a, s, tid == 0);
-  const int32_t Q = a.D >> 2;
-  const f32x4* seq = reinterpret_cast<const f32x4*>(a.lvl + (int64_t)s * a.rows_per_seq * a.D);
-  float* aff = a.aff + (int64_t)s * a.rows_per_seq;
-  float* out = lazy_out ? lazy_out + (int64_t)s * a.rows_per_seq : nullptr;
-  const bool staged = a.rows_per_seq <= kLdsRows;
   const int32_t grp = tid / LPR, lg = tid % LPR;
-  const AnchorRegs<LPR, NQ> A = load_anchor<LPR, NQ>(a, s, lg);
-  clear_select_state(a, g, sm);
-  __syncthreads();
+  const int32_t Q = a.D >> 2;
   int32_t kp = 0;
   for (int32_t lev = 0; lev < 3; ++lev) {
-    const Level L = make_level(a, g, lev, staged, aff, kp, sm);
+    const Level L = make_level(a, g, lev, aff, kp, sm);
     const int32_t m = L.fanout ? L.n_par * L.fanout : L.n;
     for (int32_t c0 = grp; c0 < m; c0 += NG * R) {
       f32x4 x[R][NQ];
@@ -719,34 +827,87 @@ __global__ __launch_bounds__(kSelThreads) void lazy_kernel(ScoreArgs a, float* l
       for (int r = 0; r < R; ++r) {
         const float v_aff = row_affinity<LPR, NQ>(x[r], A);
         if (lg == 0 && e[r] >= 0) {
-          if (staged) sm.aff[L.off + e[r]] = v_aff;
-          else aff[L.off + e[r]] = v_aff;
+          if constexpr (STG) sm.aff[L.off + e[r]] = v_aff;
+          else store_aff(aff + L.off + e[r], v_aff);
           if (out) out[L.off + e[r]] = v_aff;
         }
       }
     }
     __syncthreads();
-    kp = select_level(L, lev == 0 ? a.k_g : (lev == 1 ? a.k_c : a.k_p), sm);
+    kp = select_level<STG>(L, lev == 0 ? a.k_g : (lev == 1 ? a.k_c : a.k_p), sm);
     if (lev < 2) keep_parents(sm, kp, lev == 0 ? sm.kept_grid : sm.kept_chunk);
   }
+  return kp;
+}
+
+template <int LPR, int NQ, int R>
+__global__ __launch_bounds__(kSelThreads) void lazy_kernel(ScoreArgs a, float* lazy_out) {
+  __shared__ SelectShared sm;
+  const int tid = threadIdx.x;
+  const int32_t s = blockIdx.x;
+  const SeqGeom g = seq_geom(a, s, tid == 0);
+  const f32x4* seq = reinterpret_cast<const f32x4*>(a.lvl + (int64_t)s * a.rows_per_seq * a.D);
+  float* aff = a.aff + (int64_t)s * a.rows_per_seq;
+  float* out = lazy_out ? lazy_out + (int64_t)s * a.rows_per_seq : nullptr;
+  const AnchorRegs<LPR, NQ> A = load_anchor<LPR, NQ>(a, s, tid % LPR);
+  clear_select_state(a, g, sm);
+  __syncthreads();
+  const int32_t kp = a.rows_per_seq <= kLdsRows ? lazy_levels<true, LPR, NQ, R>(a, g, seq, aff, out, A, sm)
+                                                : lazy_levels<false, LPR, NQ, R>(a, g, seq, aff, out, A, sm);
   write_selection(a, sm, s, kp);
 }
 
-template <int NQ>
-hipError_t launch_nq(const ScoreArgs& a, bool lazy, float* lazy_out, hipStream_t st) {
+// Lanes sharing one row: 8 (whole 128-byte lines per row group), 16 above
+// head_dim 512 so that a lane's row and anchor pieces stay in registers.
+constexpr int32_t score_lpr(int32_t D) { return D / 4 > 8 * 16 ? 16 : 8; }
+
+// Compute units of the current device (cached per device).
+int32_t device_cus() {
+  static int32_t cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <int LPR, int NQ>
+hipError_t launch_nq(const ScoreArgs& a0, bool lazy, float* lazy_out, hipStream_t st) {
   constexpr int R = NQ >= KKA_SCORE_LOADS ? 1 : KKA_SCORE_LOADS / NQ;
   if (lazy) {
     constexpr int RL = NQ >= 16 ? 1 : 16 / NQ;  // 16 row loads in flight per lane
-    hipLaunchKernelGGL((lazy_kernel<KKA_SCORE_LPR, NQ, RL>), dim3((unsigned)a.S), dim3(kSelThreads), 0, st, a,
-                       lazy_out);
+    hipLaunchKernelGGL((lazy_kernel<LPR, NQ, RL>), dim3((unsigned)a0.S), dim3(kSelThreads), 0, st, a0, lazy_out);
     return hipGetLastError();
   }
+  // Latency-bound batches (one wave of fused work-groups, two per compute
+  // unit, covers every tile) score and select in one launch; larger ones
+  // stream the rows with the lighter scoring kernel and select after it.
+  ScoreArgs a = a0;
+  constexpr int32_t kFusedRows = (kSelThreads / LPR) * R * KKA_SCORE_PASSES;
+  constexpr int32_t kPlainRows = (256 / LPR) * R * KKA_SCORE_PASSES;
+  const int64_t fused_tiles = (a.rows_per_seq + kFusedRows - 1) / kFusedRows;
+  if ((int64_t)a.S * fused_tiles <= 2 * (int64_t)device_cus()) {
+    a.rows_per_tile = kFusedRows;
+    a.tiles_per_seq = (int32_t)(fused_tiles > 0 ? fused_tiles : 1);
+    const dim3 grid((unsigned)((int64_t)a.S * a.tiles_per_seq));
+    if (a.hist)
+      hipLaunchKernelGGL((score_select_kernel<LPR, NQ, R, true>), grid, dim3(kSelThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((score_select_kernel<LPR, NQ, R, false>), grid, dim3(kSelThreads), 0, st, a);
+    return hipGetLastError();
+  }
+  const int64_t tiles = (a.rows_per_seq + kPlainRows - 1) / kPlainRows;
+  a.rows_per_tile = kPlainRows;
+  a.tiles_per_seq = (int32_t)(tiles > 0 ? tiles : 1);
   const dim3 grid((unsigned)((int64_t)a.S * a.tiles_per_seq));
   if (a.hist)
-    hipLaunchKernelGGL((score_kernel<KKA_SCORE_LPR, NQ, R, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((score_kernel<LPR, NQ, R, true>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((score_kernel<KKA_SCORE_LPR, NQ, R, false>), grid, dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
+    hipLaunchKernelGGL((score_kernel<LPR, NQ, R, false>), grid, dim3(256), 0, st, a);
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.S), dim3(kSelThreads), 0, st, a);
   return hipGetLastError();
@@ -754,24 +915,29 @@ hipError_t launch_nq(const ScoreArgs& a, bool lazy, float* lazy_out, hipStream_t
 
 hipError_t dispatch(const ScoreArgs& a, bool lazy, float* lazy_out, hipStream_t st) {
   if (a.S <= 0) return hipSuccess;
-  const int32_t nq = (a.D / 4 + KKA_SCORE_LPR - 1) / KKA_SCORE_LPR;
-  if (nq <= 1) return launch_nq<1>(a, lazy, lazy_out, st);
-  if (nq <= 2) return launch_nq<2>(a, lazy, lazy_out, st);
-  if (nq <= 4) return launch_nq<4>(a, lazy, lazy_out, st);
-  if (nq <= 8) return launch_nq<8>(a, lazy, lazy_out, st);
-  if (nq <= 16) return launch_nq<16>(a, lazy, lazy_out, st);
-  return launch_nq<32>(a, lazy, lazy_out, st);
+  if (score_lpr(a.D) == 16) return launch_nq<16, 16>(a, lazy, lazy_out, st);  // head_dim 516..1024
+  const int32_t nq = (a.D / 4 + 7) / 8;
+  if (nq <= 1) return launch_nq<8, 1>(a, lazy, lazy_out, st);
+  if (nq <= 2) return launch_nq<8, 2>(a, lazy, lazy_out, st);
+  if (nq <= 4) return launch_nq<8, 4>(a, lazy, lazy_out, st);
+  if (nq <= 8) return launch_nq<8, 8>(a, lazy, lazy_out, st);
+  return launch_nq<8, 16>(a, lazy, lazy_out, st);
 }
 
 }  // namespace
 
-// Rows one scoring work-group covers for a given head_dim.
+// A tile's affinities are gathered in the selection's LDS row buffer.
+static_assert((kSelThreads / 8) * KKA_SCORE_LOADS * KKA_SCORE_PASSES <= kLdsRows, "tile rows exceed LDS");
+
+// Rows the smaller (256-thread) scoring work-group covers for a given
+// head_dim: the launch sizes its tiles from this or twice this.
 int32_t score_rows_per_tile(int32_t D) {
-  const int32_t nq = (D / 4 + KKA_SCORE_LPR - 1) / KKA_SCORE_LPR;
+  const int32_t lpr = score_lpr(D);
+  const int32_t nq = (D / 4 + lpr - 1) / lpr;
   int32_t NQ = 1;
   while (NQ < nq) NQ <<= 1;
   const int32_t R = NQ >= KKA_SCORE_LOADS ? 1 : KKA_SCORE_LOADS / NQ;
-  return (256 / KKA_SCORE_LPR) * R * KKA_SCORE_PASSES;
+  return (256 / lpr) * R * KKA_SCORE_PASSES;
 }
 
 hipError_t launch_score_topk(const ScoreArgs& a, hipStream_t st) { return dispatch(a, false, nullptr, st); }

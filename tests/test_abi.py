@@ -146,8 +146,10 @@ def test_level_rows_and_score_validation(L):
     assert L.kka_level_rows(ctypes.byref(kka.c_level_layout(1, 1 << 30, 128, 1, 1 << 16, 16))) == (1 << 30) + 16384 + 1024
     sel = kka.c_select(4, 16, 64)
     ws = L.kka_score_topk_workspace(ctypes.byref(lay), ctypes.byref(sel), 0)
-    assert ws >= 64 * 8736 * 4  # scratch affinities
-    assert L.kka_score_topk_workspace(ctypes.byref(lay), ctypes.byref(sel), 1) == 0
+    assert ws >= 256 + 64 * 8736 * 4  # per-sequence tile counters, then scratch affinities
+    assert L.kka_score_topk_workspace(ctypes.byref(lay), ctypes.byref(sel), 1) == 256  # counters only
+    assert L.kka_score_topk_workspace(ctypes.byref(kka.c_level_layout(0, 100, 128, 1, 16, 16)),
+                                      ctypes.byref(sel), 1) == 0
 
     def score(lay_, sel_, lvl=FAKE, npg=FAKE, anc=FAKE, idx=FAKE, w=FAKE, wb=ws):
         return L.kka_score_topk(ctypes.byref(lay_), lvl, npg, anc, ctypes.byref(sel_), None, idx, None, None, w,

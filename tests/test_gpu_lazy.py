@@ -15,10 +15,11 @@ import pytest
 import torch
 
 import kv_cache_block_amd as kka
+import oracle
 import synth
 from kv_cache_block_amd.pipeline import Selector
 
-from gpu_harness import check_selection, run_selector, say
+from gpu_harness import ATOL, check_selection, run_selector, say
 
 pytestmark = pytest.mark.gpu
 
@@ -155,14 +156,30 @@ def test_lazy_equals_full_rows_beyond_lds(cfg):
     compare(lay, cfg, npg.cpu().numpy(), full2, lazy2, with_affinity=False, tag="long")
 
 
-@pytest.mark.parametrize("D", [8, 24, 256, 1024])
+@pytest.mark.parametrize("D", [8, 24, 256, 520, 1024])
 def test_lazy_equals_full_head_dims(D):
+    """Both passes at head dims that take every lane layout (8 lanes per row
+    up to 512, 16 above); the full pass also against the oracle."""
     cfg = dict(hierarchical=1, k_grid=3, k_chunk=9, k_page=33, pages_per_chunk=8, chunks_per_grid=4)
     say(f"lazy head_dim {D}")
     lengths = [400, 129, 64]
     lay, level, npg, anchors = random_levels(23, 3, 400, D, cfg, lengths)
     full, lazy = score_both(lay, level, npg, anchors, cfg)
     compare(lay, cfg, npg.cpu().numpy(), full, lazy, tag=f"D={D}")
+    lv, an = level.cpu().numpy(), anchors.cpu().numpy()
+    for s, n_p in enumerate(lengths):
+        n_c = -(-n_p // 8)
+        n_g = -(-n_c // 4)
+        rows = np.concatenate([np.arange(n_p), lay.chunk_row0 + np.arange(n_c), lay.grid_row0 + np.arange(n_g)])
+        np.testing.assert_allclose(full["aff"][s][rows], oracle.affinity(lv[s][rows], an[s]), atol=ATOL, rtol=0,
+                                   err_msg=f"D={D} s={s}")
+        a = full["aff"][s]
+        ridx, rsc = oracle.select(a[:n_p], a[lay.chunk_row0:lay.chunk_row0 + n_c],
+                                  a[lay.grid_row0:lay.grid_row0 + n_g], hierarchical=1, k_grid=3, k_chunk=9,
+                                  k_page=33, pages_per_chunk=8, chunks_per_grid=4)
+        assert full["cnt"][s] == len(ridx)
+        np.testing.assert_array_equal(full["idx"][s][:len(ridx)], ridx)
+        np.testing.assert_array_equal(full["sc"][s][:len(ridx)].view(np.uint32), rsc.view(np.uint32))
 
 
 def test_lazy_exact_ties():

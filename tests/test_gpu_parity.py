@@ -524,3 +524,61 @@ def test_ragged_variance_batch_full_size_and_decode_step():
         tab = oracle.seq_table(after["block_offsets"], after["block_table"], s)
         a = oracle.pool_anchor(okp, tab, int(after["seq_len"][s]), w.window, wf[s])
         np.testing.assert_allclose(sel.anchors[s].cpu().numpy(), a, atol=ATOL, rtol=0)
+
+
+@pytest.mark.parametrize("case", [
+    dict(hierarchical=1, k_grid=2, k_chunk=3, k_page=5, pages_per_chunk=4, chunks_per_grid=3),
+    dict(hierarchical=1, k_grid=1, k_chunk=1, k_page=40, pages_per_chunk=4, chunks_per_grid=3),  # zero fill
+    dict(hierarchical=1, k_grid=0, k_chunk=2, k_page=6, pages_per_chunk=2, chunks_per_grid=2),   # all masked
+    dict(hierarchical=0, k_grid=0, k_chunk=0, k_page=9, pages_per_chunk=16, chunks_per_grid=16),
+])
+@pytest.mark.parametrize("S", [5, 600])
+def test_selection_both_launch_shapes(case, S):
+    """Few sequences score and select in one launch; 600 short sequences
+    (more tiles than fit on the chip at once) take the scoring launch and
+    then the selection launch.  Both against the oracle, on the same rules."""
+    say(f"launch shapes S={S} {case}")
+    max_pages, D = 60, 8
+    lay = kka.LevelLayout(S, max_pages, D, bool(case["hierarchical"]), case["pages_per_chunk"],
+                          case["chunks_per_grid"])
+    rng = np.random.default_rng(31 + S)
+    lvl = np.zeros((S, lay.rows_per_seq, D), np.float32)
+    lvl[:, :max_pages] = rng.standard_normal((S, max_pages, D), dtype=np.float32)
+    n_pages = rng.integers(0, max_pages + 1, S).astype(np.int32)
+    level = torch.from_numpy(lvl).cuda()
+    npg = torch.from_numpy(n_pages).cuda()
+    kka.kka_build_levels(lay, level, npg)
+    anchors = torch.from_numpy(rng.standard_normal((S, D), dtype=np.float32)).cuda()
+    K = max(1, case["k_page"])
+    idx = torch.full((S, K), -9, dtype=torch.int32, device="cuda")
+    sc = torch.full((S, K), 7.0, dtype=torch.float32, device="cuda")
+    cnt = torch.full((S,), -9, dtype=torch.int32, device="cuda")
+    aff = torch.zeros((S, lay.rows_per_seq), dtype=torch.float32, device="cuda")
+    ws = kka.new_workspace(kka.kka_score_topk_workspace(lay, True))
+    for _ in range(2):  # the tile counters are left ready for the next call
+        kka.kka_score_topk(lay, level, npg, anchors, k_page=case["k_page"], k_grid=case["k_grid"],
+                           k_chunk=case["k_chunk"], page_idx_out=idx, page_score_out=sc, n_selected_out=cnt,
+                           affinity_out=aff, workspace=ws)
+        torch.cuda.synchronize()
+        lv, an, af = level.cpu().numpy(), anchors.cpu().numpy(), aff.cpu().numpy()
+        gi, gs, gc = idx.cpu().numpy(), sc.cpu().numpy(), cnt.cpu().numpy()
+        for s in range(S):
+            n_p = int(n_pages[s])
+            if case["hierarchical"]:
+                n_c = -(-n_p // case["pages_per_chunk"])
+                n_g = -(-n_c // case["chunks_per_grid"])
+                rows = np.concatenate([np.arange(n_p), lay.chunk_row0 + np.arange(n_c),
+                                       lay.grid_row0 + np.arange(n_g)]).astype(np.int64)
+                a_c = af[s, lay.chunk_row0:lay.chunk_row0 + n_c]
+                a_g = af[s, lay.grid_row0:lay.grid_row0 + n_g]
+            else:
+                rows, a_c, a_g = np.arange(n_p), None, None
+            if len(rows):
+                np.testing.assert_allclose(af[s, rows], oracle.affinity(lv[s, rows], an[s]), atol=ATOL, rtol=0,
+                                           err_msg=f"S={S} s={s}")
+            ridx, rsc = oracle.select(af[s, :n_p], a_c, a_g, **case)
+            assert gc[s] == len(ridx), f"S={S} s={s}"
+            np.testing.assert_array_equal(gi[s, :len(ridx)], ridx, err_msg=f"S={S} s={s}")
+            np.testing.assert_array_equal(gs[s, :len(ridx)].view(np.uint32), rsc.view(np.uint32))
+            if case["k_page"] > len(ridx):
+                assert (gi[s, len(ridx):case["k_page"]] == -1).all()
