@@ -68,7 +68,10 @@ __device__ __forceinline__ f32x4 load_row4(const f32x4* p) {
 struct SelectShared {
   float aff[kLdsRows];
   uint64_t ck[kRankMax];
-  uint64_t run[kSelThreads];
+  union {
+    uint64_t run[kSelThreads];            // sorted groups (levels of 65-512 candidates)
+    int32_t part[kSelThreads / 64][64];   // per-wave counts (levels of up to 64)
+  };
   uint64_t buf[kMaxK];
   uint32_t kept_grid[kBitmapWords];   // grids kept (parents of chunks)
   uint32_t kept_chunk[kBitmapWords];  // chunks kept (parents of pages)
@@ -336,24 +339,33 @@ __device__ __forceinline__ int32_t group_sum(int32_t v, int32_t n) {
   return v;
 }
 
-// Rank of key x of the run at g0 among NG sorted runs of 64: its rank r in
-// its own run plus, for every other run, how many of its keys exceed x
-// (binary search; the searches of different runs are independent).
+// Rank of key x of the run at g0 among NG strictly descending runs of 64:
+// its rank r in its own run plus, for every other run, how many of its keys
+// exceed x.  That count comes from two rounds of independent LDS reads: the
+// run's 8 block-end pivots (every eighth key; the same addresses for the
+// whole wave) give the block, then the block's 8 keys give the position.
+// g0 is uniform over the wave.
 template <int NG>
 __device__ __forceinline__ int32_t merged_rank(const uint64_t* runs, int32_t g0, uint64_t x, int32_t r) {
-  int32_t pos[NG];
+  int32_t c[NG];
 #pragma unroll
-  for (int g = 0; g < NG; ++g) pos[g] = 0;
+  for (int g = 0; g < NG; ++g) {
+    c[g] = 0;
+    if ((g << 6) == g0) continue;
 #pragma unroll
-  for (int step = 32; step > 0; step >>= 1) {
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
-      if ((g << 6) != g0 && runs[(g << 6) + pos[g] + step - 1] > x) pos[g] += step;
+    for (int p = 0; p < 8; ++p) c[g] += (int32_t)(runs[(g << 6) + 8 * p + 7] > x);
   }
   int32_t R = r;
 #pragma unroll
-  for (int g = 0; g < NG; ++g)
-    if ((g << 6) != g0) R += (pos[g] == 63 && runs[(g << 6) + 63] > x) ? 64 : pos[g];
+  for (int g = 0; g < NG; ++g) {
+    if ((g << 6) == g0) continue;
+    // keys 0 .. 8c-1 exceed x; the block of 8 at 8c holds the boundary
+    const uint64_t* blk = runs + (g << 6) + 8 * (c[g] < 8 ? c[g] : 7);
+    int32_t f = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f += (int32_t)(blk[i] > x);
+    R += c[g] == 8 ? 64 : 8 * c[g] + f;
+  }
   return R;
 }
 
@@ -365,19 +377,19 @@ constexpr int rank_tpc(int ng) {
   return t;
 }
 
-// Keeps the top k_eff of a level's m <= NG * 64 candidates, sorted, in
-// sm.buf.  Candidate keys go to LDS in NG groups of 64 (slots past the
+// Keeps the top k_eff of a level's 64 < m <= NG * 64 candidates, sorted,
+// in sm.buf.  Candidate keys go to LDS in NG groups of 64 (slots past the
 // candidates hold distinct keys below every real one); TPC lanes rank each
-// key within its group, each comparing a fixed strided share; with one group
-// that rank is final, otherwise each group is written back as a strictly
-// descending run and a key's rank in the level is its rank in its group
-// plus, for every other group, how many keys of that run exceed it (binary
-// search).  Keys without a positive score rank below all positive ones and
-// are never kept here (the zero fill handles them).
+// key within its group, each comparing a fixed strided share; each group is
+// written back as a strictly descending run and a key's rank in the level
+// is its rank in its group plus, for every other group, how many keys of
+// that run exceed it (binary search).  Keys without a positive score rank
+// below all positive ones and are never kept here (the zero fill handles
+// them).
 template <bool STG, int NG>
 __device__ int32_t select_small(const Level& L, int32_t m, int32_t k_eff, SelectShared& sm) {
   constexpr int TPC = rank_tpc(NG);
-  static_assert(NG * 64 * TPC <= kSelThreads && 64 % (8 * TPC) == 0, "rank layout");
+  static_assert(NG >= 2 && NG * 64 * TPC <= kSelThreads && 64 % (8 * TPC) == 0, "rank layout");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   uint64_t* keys = sm.ck;    // [NG * 64] candidate keys by candidate index
@@ -411,25 +423,59 @@ __device__ int32_t select_small(const Level& L, int32_t m, int32_t k_eff, Select
     for (int u = 0; u < 8; ++u) r += (int32_t)(y[u] > x);
   }
   r = group_sum(r, TPC);
-  if constexpr (NG == 1) {
-    // one group: the rank in it is the rank in the level
-    if (active && q == 0 && (x >> 32) != 0ull && r < k_eff) sm.buf[r] = x;
-    __syncthreads();
-  } else {
-    if (active && q == 0) runs[g0 + r] = x;
-    __syncthreads();
-    // phase C: rank in the level, positive keys only
-    if (active && q == 0 && (x >> 32) != 0ull) {
-      const int32_t R = merged_rank<NG>(runs, g0, x, r);
-      if (R < k_eff) sm.buf[R] = x;
-    }
-    __syncthreads();
+  if (active && q == 0) runs[g0 + r] = x;
+  __syncthreads();
+  // phase C: rank in the level, positive keys only
+  if (active && q == 0 && (x >> 32) != 0ull) {
+    const int32_t R = merged_rank<NG>(runs, g0, x, r);
+    if (R < k_eff) sm.buf[R] = x;
   }
+  __syncthreads();
   if (P < k_eff) fill_zeros<STG>(L, sm, P, k_eff);
   return k_eff;
 }
 
-// Picks the group count: the smallest NG with m <= NG * 64.
+// Keeps the top k_eff of a level of at most 64 candidates, sorted, in
+// sm.buf.  Every wave builds all the candidate keys in registers (lane =
+// candidate; lanes past the candidates hold distinct keys below every real
+// one) and counts, for each lane, how many keys of its share of the lanes
+// exceed that lane's key, reading them with register broadcasts; the waves'
+// counts are summed through LDS.  A key's total count is its rank.
+template <bool STG>
+__device__ int32_t select_one_group(const Level& L, int32_t m, int32_t k_eff, SelectShared& sm) {
+  constexpr int W = kSelThreads / 64;  // waves
+  constexpr int J = 64 / W;            // lanes each wave compares against
+  static_assert(W * J == 64, "wave layout");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t e = lane < m ? cand32(L, sm, lane) : -1;
+  const uint32_t key = e >= 0 ? aff_key<STG>(L, sm, e) : 0u;
+  const uint64_t x = e >= 0 ? composite(key, e) : (uint64_t)lane;
+  const int32_t P = (int32_t)__popcll(__ballot(key != 0u));
+  const uint32_t xlo = (uint32_t)x, xhi = (uint32_t)(x >> 32);
+  int32_t c = 0;
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj) {
+    const int j = wave * J + jj;
+    const uint64_t y = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)xhi, j) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)xlo, j);
+    c += (int32_t)(y > x);
+  }
+  sm.part[wave][lane] = c;
+  __syncthreads();
+  if (wave == 0) {
+    int32_t r = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) r += sm.part[w][lane];
+    if (xhi != 0u && r < k_eff) sm.buf[r] = x;
+  }
+  __syncthreads();
+  if (P < k_eff) fill_zeros<STG>(L, sm, P, k_eff);
+  return k_eff;
+}
+
+// Picks the group count: the smallest NG >= 2 with m <= NG * 64.
 template <bool STG, int NG>
 __device__ __forceinline__ int32_t select_small_ng(const Level& L, int32_t m, int32_t k_eff, SelectShared& sm) {
   if constexpr (NG * 64 < kSelThreads) {
@@ -447,7 +493,8 @@ __device__ int32_t select_level(const Level& L, int32_t k, SelectShared& sm) {
   if (k_eff <= 0) return 0;
   const int64_t m64 = L.fanout ? (int64_t)L.n_par * L.fanout : (int64_t)L.n;
   if (m64 > kSelThreads) return select_level_big<STG>(L, k, sm);
-  return select_small_ng<STG, 1>(L, (int32_t)m64, k_eff, sm);
+  if (m64 <= 64) return select_one_group<STG>(L, (int32_t)m64, k_eff, sm);
+  return select_small_ng<STG, 2>(L, (int32_t)m64, k_eff, sm);
 }
 
 // Records the kept elements of a level (sm.buf[0, k_eff)) as the parents of
