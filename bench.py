@@ -306,6 +306,7 @@ def run(args):
         "kpool_us": round(pool_us, 2),
         "kpool_algorithmic_bytes": b_pool,
         "score_topk_us_per_step": round(c3_score_us, 2),
+        "score_topk_launches": "one (score_select_kernel): the batch's tiles fit on the chip at once",
         "serving_score_topk_us_per_step": round(c4_us, 2),
         "serving_score_topk_GBps": round(c4_gbps, 2),
         "serving_score_topk_frac_of_peak": round(c4_gbps / PEAK_HBM_GBPS, 4),
@@ -339,7 +340,7 @@ def run(args):
         },
         "roofline_serving_score": {
             "bound": "hbm",
-            "kernel": "score_topk_kernel (kka_score_topk)",
+            "kernel": "kka_score_topk: score_kernel then select_kernel (whole call, event-timed)",
             "achieved": round(c4_gbps, 2),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
