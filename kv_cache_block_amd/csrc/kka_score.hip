@@ -10,8 +10,10 @@
 // HBM bandwidth.  Each sequence's present rows are cut into tiles spread
 // over the whole chip; in a tile, 8 lanes share one row (each lane reads
 // 16-byte pieces 128 bytes apart, so 8 lanes read whole 128-byte lines) and
-// every lane keeps 8 non-temporal loads in flight (rows are read once per
-// step; a serving batch's level rows exceed the last-level cache anyway).
+// every lane keeps 4 non-temporal loads in flight per pass over its tile
+// (few registers, so eight waves per SIMD stay resident; rows are read once
+// per step, and a serving batch's level rows exceed the last-level cache
+// anyway); the fused kernel issues all 8 of a lane's loads in one pass.
 // Dot product and row norm are reduced over the 8 lanes with a fixed
 // butterfly.
 //
@@ -45,10 +47,10 @@ constexpr int kBitmapWords = kMaxParents / 32;
 // float4 row loads each lane keeps in flight in the scoring pass, and how
 // many passes of the row-groups one scoring work-group makes.
 #ifndef KKA_SCORE_LOADS
-#define KKA_SCORE_LOADS 8
+#define KKA_SCORE_LOADS 4
 #endif
 #ifndef KKA_SCORE_PASSES
-#define KKA_SCORE_PASSES 1
+#define KKA_SCORE_PASSES 2
 #endif
 // whether row loads bypass cache allocation
 #ifndef KKA_SCORE_NT
@@ -932,8 +934,11 @@ hipError_t launch_nq(const ScoreArgs& a0, bool lazy, float* lazy_out, hipStream_
   // Latency-bound batches (one wave of fused work-groups, two per compute
   // unit, covers every tile) score and select in one launch; larger ones
   // stream the rows with the lighter scoring kernel and select after it.
+  // The fused kernel is latency-bound: all of a lane's row loads go out in
+  // one pass over its tile (one HBM round trip).
+  constexpr int RF = NQ >= KKA_SCORE_LOADS * KKA_SCORE_PASSES ? 1 : KKA_SCORE_LOADS * KKA_SCORE_PASSES / NQ;
   ScoreArgs a = a0;
-  constexpr int32_t kFusedRows = (kSelThreads / LPR) * R * KKA_SCORE_PASSES;
+  constexpr int32_t kFusedRows = (kSelThreads / LPR) * RF;
   constexpr int32_t kPlainRows = (256 / LPR) * R * KKA_SCORE_PASSES;
   const int64_t fused_tiles = (a.rows_per_seq + kFusedRows - 1) / kFusedRows;
   if ((int64_t)a.S * fused_tiles <= 2 * (int64_t)device_cus()) {
@@ -941,9 +946,9 @@ hipError_t launch_nq(const ScoreArgs& a0, bool lazy, float* lazy_out, hipStream_
     a.tiles_per_seq = (int32_t)(fused_tiles > 0 ? fused_tiles : 1);
     const dim3 grid((unsigned)((int64_t)a.S * a.tiles_per_seq));
     if (a.hist)
-      hipLaunchKernelGGL((score_select_kernel<LPR, NQ, R, true>), grid, dim3(kSelThreads), 0, st, a);
+      hipLaunchKernelGGL((score_select_kernel<LPR, NQ, RF, true>), grid, dim3(kSelThreads), 0, st, a);
     else
-      hipLaunchKernelGGL((score_select_kernel<LPR, NQ, R, false>), grid, dim3(kSelThreads), 0, st, a);
+      hipLaunchKernelGGL((score_select_kernel<LPR, NQ, RF, false>), grid, dim3(kSelThreads), 0, st, a);
     return hipGetLastError();
   }
   const int64_t tiles = (a.rows_per_seq + kPlainRows - 1) / kPlainRows;
