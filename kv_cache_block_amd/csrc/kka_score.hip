@@ -31,6 +31,8 @@
 // and larger means higher score then lower index.  When fewer than k
 // candidates score above zero, the lowest-index rows scoring exactly 0
 // (masked or zero affinity) fill the remaining slots in index order.
+#include <atomic>
+
 #include "kka_internal.h"
 
 namespace kka {
@@ -910,17 +912,20 @@ __global__ __launch_bounds__(kSelThreads) void lazy_kernel(ScoreArgs a, float* l
 // head_dim 512 so that a lane's row and anchor pieces stay in registers.
 constexpr int32_t score_lpr(int32_t D) { return D / 4 > 8 * 16 ? 16 : 8; }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; callers on
+// several host threads may fill an entry at once with the same value).
 int32_t device_cus() {
-  static int32_t cus[64];
+  static std::atomic<int32_t> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cus[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
+  int32_t n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    int q = 0;
+    if (hipDeviceGetAttribute(&q, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || q <= 0) q = 256;
+    n = q;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 template <int LPR, int NQ>
