@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0
 METRIC = "K-pool HBM GB/s (% peak); score+top-K µs/decode step, 7B shape @128K ctx"
 COUNTERS = os.path.join(ROOT, "profiles", "kpool_7b_128k_hbm_counters.json")
+SCORE_COUNTERS = os.path.join(ROOT, "profiles", "score_topk_64seq_decode_hbm_counters.json")
 
 
 def kernel_source_hash(name: str) -> str:
@@ -50,6 +51,35 @@ def kpool_bytes(w) -> int:
 
 def score_bytes(S, rows, D, k_page) -> int:
     return S * rows * D * 4 + S * D * 4 + S * rows * 4 + S * k_page * 8
+
+
+def score_traffic_from_counters():
+    """HBM bytes per serving-batch kka_score_topk call (scoring launch plus
+    selection launch) from the committed counter runs, if they were taken on
+    the current scoring source; else None."""
+    try:
+        with open(SCORE_COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha256_16") != kernel_source_hash("kka_score.hip"):
+        return None
+    return c.get("traffic_bytes_per_call")
+
+
+def host_info() -> dict:
+    """CPU model and the cores this process may use."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"cpu_model": model, "usable_cores": usable, "os_cpu_count": os.cpu_count()}
 
 
 def traffic_from_counters(algo_bytes_unused=None):
@@ -120,6 +150,8 @@ def run(args):
     score_ms = [e[2].elapsed_time(e[3]) for e in events]
     pool_us = 1e3 * float(np.mean(pool_ms))
     c3_score_us = 1e3 * float(np.mean(score_ms))
+    pool_med_us = 1e3 * float(np.median(pool_ms))
+    c3_score_med_us = 1e3 * float(np.median(score_ms))
 
     n_p = w.total_blocks
     n_c = -(-n_p // w.select["pages_per_chunk"])
@@ -235,7 +267,11 @@ def run(args):
         score4(i)
         ev4[i][1].record(stream)
     torch.cuda.synchronize()
-    c4_us = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in ev4]))
+    c4_ms = [e[0].elapsed_time(e[1]) for e in ev4]
+    c4_us = 1e3 * float(np.mean(c4_ms))
+    c4_med_us = 1e3 * float(np.median(c4_ms))
+    # the same calls on one buffer set: the level rows stay in the last-level cache
+    c4_warm_us = time_calls(lambda i: score4(0), args.steps, args.warmup, stream)
     rows4 = lay4.rows_per_seq
     b4 = score_bytes(S, rows4, D, kp4)
     c4_gbps = b4 / (c4_us * 1e-6) / 1e9
@@ -304,10 +340,14 @@ def run(args):
         "kpool_GBps": round(kpool_gbps, 2),
         "kpool_frac_of_peak": round(kpool_gbps / PEAK_HBM_GBPS, 4),
         "kpool_us": round(pool_us, 2),
+        "kpool_median_us": round(pool_med_us, 2),
         "kpool_algorithmic_bytes": b_pool,
         "score_topk_us_per_step": round(c3_score_us, 2),
+        "score_topk_median_us": round(c3_score_med_us, 2),
         "score_topk_launches": "one (score_select_kernel): the batch's tiles fit on the chip at once",
         "serving_score_topk_us_per_step": round(c4_us, 2),
+        "serving_score_topk_median_us": round(c4_med_us, 2),
+        "serving_score_topk_warm_cache_us": round(c4_warm_us, 2),
         "serving_score_topk_GBps": round(c4_gbps, 2),
         "serving_score_topk_frac_of_peak": round(c4_gbps / PEAK_HBM_GBPS, 4),
         "serving_workload": "64 sequences x 8192 fp32 block vectors (D=128) + 512 chunk + 32 grid rows each, "
@@ -345,6 +385,7 @@ def run(args):
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(c4_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": score_traffic_from_counters(),
         },
         "cpu_baseline": cpu,
         "generation_s": round(gen_s, 2),
@@ -455,7 +496,7 @@ def cpu_baseline(w, step_bytes, seconds):
     return {"value": round(gbps, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} whole step(s) of the same 131072-token workload ({reps * step_bytes / 1e9:.2f} GB "
                       f"of algorithmic bytes) in {el:.1f} s on one host core",
-            "ms_per_step": round(el * 1e3 / reps, 1)}
+            "ms_per_step": round(el * 1e3 / reps, 1), "host": host_info()}
 
 
 def profile_pass(args):
@@ -486,8 +527,31 @@ def profile_pass(args):
     for _ in range(3):
         sel.step(npg)
     torch.cuda.synchronize()
+    del sel, kp, k
+    torch.cuda.empty_cache()
+    # the serving decode step: 64 sequences, scoring launch then selection launch
+    v = synth.config4(args.seed)
+    S, NP, D = v.vb.shape
+    lay4 = kka.LevelLayout(S, NP, D, True, 16, 16)
+    npg4 = torch.full((S,), NP, dtype=torch.int32, device=dev)
+    lvl4 = lay4.new_buffer(dev)
+    lvl4[:, :NP] = torch.from_numpy(v.vb).to(dev)
+    kka.kka_build_levels(lay4, lvl4, npg4)
+    anchors = torch.from_numpy(v.anchors).to(dev)
+    idx4 = torch.zeros((S, v.select["k_page"]), dtype=torch.int32, device=dev)
+    sc4 = torch.zeros((S, v.select["k_page"]), dtype=torch.float32, device=dev)
+    aff4 = torch.zeros((S, lay4.rows_per_seq), dtype=torch.float32, device=dev)
+    ws4 = kka.new_workspace(kka.kka_score_topk_workspace(lay4, True), dev)
+    for _ in range(3):
+        kka.kka_score_topk(lay4, lvl4, npg4, anchors, k_page=v.select["k_page"], k_grid=v.select["k_grid"],
+                           k_chunk=v.select["k_chunk"], page_idx_out=idx4, page_score_out=sc4, affinity_out=aff4,
+                           workspace=ws4)
+    torch.cuda.synchronize()
     print(json.dumps({"profile_pass": "done", "copy_bytes": (1 << 28) * 4, "kpool_algorithmic_bytes":
-                      kpool_bytes(w), "kernel_source_sha256_16": kernel_source_hash("kka_pool.hip")}), flush=True)
+                      kpool_bytes(w), "serving_score_algorithmic_bytes": score_bytes(S, lay4.rows_per_seq, D,
+                                                                                     v.select["k_page"]),
+                      "kernel_source_sha256_16": kernel_source_hash("kka_pool.hip"),
+                      "score_source_sha256_16": kernel_source_hash("kka_score.hip")}), flush=True)
 
 
 def _short(name: str) -> str:
@@ -495,11 +559,13 @@ def _short(name: str) -> str:
     return name.split("(kka::")[0] if "(kka::" in name else name[:60]
 
 
-def write_counter_summary(fetch_csv: str, write_csv: str, out_json: str, command: str):
-    """Per-dispatch HBM bytes of the K-pool kernel from two rocprofv3 --pmc
-    runs of --profile-pass (FETCH_SIZE, then WRITE_SIZE, in KiB), each scaled
-    by what the same counter reads for the plain 1 GiB device copy that the
-    profile pass runs first (known bytes: 1 GiB read and 1 GiB written)."""
+def write_counter_summary(fetch_csv: str, write_csv: str, out_dir: str, command: str):
+    """Per-dispatch HBM bytes of the K-pool kernel and of the serving-batch
+    scoring call (scoring launch plus selection launch) from two rocprofv3
+    --pmc runs of --profile-pass (FETCH_SIZE, then WRITE_SIZE, in KiB), each
+    scaled by what the same counter reads for the plain 1 GiB device copy that
+    the profile pass runs first (known bytes: 1 GiB read and 1 GiB written).
+    Writes the two summaries into out_dir."""
     import csv
     import statistics
 
@@ -542,10 +608,36 @@ def write_counter_summary(fetch_csv: str, write_csv: str, out_json: str, command
         "per_kernel": kernels,
         "commands": command,
     }
-    with open(out_json, "w") as fh:
+    with open(os.path.join(out_dir, os.path.basename(COUNTERS)), "w") as fh:
         json.dump(summary, fh, indent=1)
     print(json.dumps({"traffic_bytes_per_launch": summary["traffic_bytes_per_launch"],
                       "fetch_factor": summary["fetch_factor"], "write_factor": summary["write_factor"]}))
+    # serving batch: the 64-sequence scoring launch and the selection launch after it
+    sk = [k for k in f if "score_kernel" in k[0]]
+    sl = [k for k in f if "select_kernel" in k[0] and int(k[1]) == 64 * 512]
+    if sk and sl:
+        parts = {}
+        for k in (sk[0], sl[0]):
+            parts[_short(k[0])] = {"fetch_bytes": round(statistics.mean(f[k]) * 1024.0 * fetch_factor),
+                                   "write_bytes": round(statistics.mean(w[k]) * 1024.0 * write_factor),
+                                   "dispatches": len(f[k])}
+        call = sum(v["fetch_bytes"] + v["write_bytes"] for v in parts.values())
+        algo = 288563200
+        score = {
+            "call": "kka_score_topk on the serving batch: score_kernel then select_kernel",
+            "workload": "64 sequences x 8192 fp32 block vectors (D = 128) + 512 chunk + 32 grid rows, top 4/16/64",
+            "kernel_source_sha256_16": kernel_source_hash("kka_score.hip"),
+            "fetch_factor": round(fetch_factor, 5),
+            "write_factor": round(write_factor, 5),
+            "traffic_bytes_per_call": call,
+            "score_algorithmic_bytes": algo,
+            "traffic_over_algorithmic": round(call / algo, 5),
+            "per_kernel": parts,
+            "commands": command,
+        }
+        with open(os.path.join(out_dir, os.path.basename(SCORE_COUNTERS)), "w") as fh:
+            json.dump(score, fh, indent=1)
+        print(json.dumps({"traffic_bytes_per_call": call, "over_algorithmic": score["traffic_over_algorithmic"]}))
 
 
 def write_stats_summary(stats_csv: str, out_md: str, title: str, command: str = ""):
@@ -586,7 +678,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true", help="short run for rocprofv3 counter passes")
-    ap.add_argument("--write-counter-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
+    ap.add_argument("--write-counter-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_DIR"),
                     help="summarise two rocprofv3 --pmc runs of --profile-pass (no GPU needed)")
     ap.add_argument("--write-stats-summary", nargs=3, metavar=("STATS_CSV", "OUT_MD", "TITLE"),
                     help="summarise a rocprofv3 --kernel-trace --stats run (no GPU needed)")
