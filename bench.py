@@ -306,6 +306,10 @@ def run(args):
     if not np.array_equal(idx4.cpu().numpy(), got):
         raise RuntimeError("scoring with the stability filter selected different pages (serving batch)")
 
+    del levels, affs, ws4, hist4, stab4
+    torch.cuda.empty_cache()
+    others = reported_configs(args, dev, stream)
+
     quality = quality_overlaps(args, dev)
     quality["7B_128K_b16_uniform_hier_top64"] = {"overlap": c3_overlap}
 
@@ -368,6 +372,7 @@ def run(args):
                                         "averaged over layers and heads per block, top-64",
         "attention_reference_algorithmic_bytes": attn_bytes,
         "qk_overlap": quality,
+        "reported_configs": others,
         "serving_topic_recovered_seqs": recovered,
         "roofline": {
             "bound": "hbm",
@@ -464,6 +469,97 @@ def time_calls(fn, steps, warmup, stream):
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     return 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+
+
+def reported_configs(args, dev, stream):
+    """K-pool GB/s of the 0.5B and 7B/32K workloads, and for the ragged
+    variance-weighted batch the weighted K-pool GB/s (one-pass algorithmic
+    bytes) and one decode step (re-pool of each sequence's newest block with
+    the frozen weights, anchor, score, flat top-48).  Reported, not gated.
+    Each timed call follows an untimed 1 GiB write, so no input is served
+    from the last-level cache."""
+    import numpy as np
+    import torch
+
+    import kv_cache_block_amd as kka
+    import synth
+    from kv_cache_block_amd.pipeline import Selector
+
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def cold_us(fn, steps):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for i in range(steps):
+            flush.zero_()
+            ev[i][0].record(stream)
+            fn()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        t = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
+        return float(np.mean(t)), float(np.median(t))
+
+    def upload(w):
+        k = torch.from_numpy(w.k.reshape(-1).view(np.int16)).to(dev)
+        kp = kka.KPool(k, w.L, w.H, w.D, w.B, w.P)
+        seqs = kka.Seqs(torch.from_numpy(w.seq_len).to(dev), torch.from_numpy(w.block_offsets).to(dev),
+                        torch.from_numpy(w.block_table).to(dev), w.total_blocks)
+        return k, kp, seqs
+
+    out = {}
+    for name, w in (("0.5B_4K_b16", synth.config1(args.seed)), ("7B_32K_b128", synth.config2(args.seed))):
+        k, kp, seqs = upload(w)
+        sel = Selector(kp, seqs, w.select, max_pages=w.total_blocks, window=w.window, device=dev)
+        for _ in range(args.warmup):
+            sel.pool()
+        mean_us, med_us = cold_us(sel.pool, args.steps)
+        b = kpool_bytes(w)
+        out[name] = {"kpool_us": round(mean_us, 2), "kpool_median_us": round(med_us, 2),
+                     "kpool_algorithmic_bytes": b, "kpool_GBps": round(b / (mean_us * 1e-6) / 1e9, 2),
+                     "kpool_frac_of_peak": round(b / (mean_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+        del sel, kp, seqs, k
+    torch.cuda.empty_cache()
+
+    w = synth.config5(args.seed)
+    after = w.extra["after"]
+    k, kp, seqs = upload(w)
+    max_pages = int(np.max(np.diff(after["block_offsets"])))
+    sel = Selector(kp, seqs, w.select, max_pages=max_pages, window=w.window, mode=kka.WEIGHT_VARIANCE, device=dev)
+    steps5 = max(5, args.steps // 5)
+    for _ in range(2):
+        sel.pool()
+    pool_mean, pool_med = cold_us(sel.pool, steps5)
+    b5 = kpool_bytes(w)
+    npg = torch.from_numpy(np.diff(w.block_offsets).astype(np.int32)).to(dev)
+    sel.anchor()
+    sel.score(npg)
+    # the decode step: one token more per sequence, newest block re-pooled with the frozen weights
+    sel.seqs = kka.Seqs(torch.from_numpy(after["seq_len"]).to(dev), torch.from_numpy(after["block_offsets"]).to(dev),
+                        torch.from_numpy(after["block_table"]).to(dev), int(after["block_offsets"][-1]))
+    newest = torch.from_numpy((after["block_offsets"][1:] - 1).astype(np.int32)).to(dev)
+    npg_after = torch.from_numpy(np.diff(after["block_offsets"]).astype(np.int32)).to(dev)
+    ws_re = kka.new_workspace(kka.kka_pool_blocks_workspace(kp, sel.seqs, kka.WEIGHT_GIVEN, newest), dev)
+
+    def decode():
+        sel.repool(newest, workspace=ws_re)
+        sel.anchor()
+        sel.score(npg_after)
+
+    for _ in range(args.warmup):
+        decode()
+    dec_mean, dec_med = cold_us(decode, args.steps)
+    if kka.kka_device_error() != 0:
+        raise RuntimeError("device error flag raised on the ragged batch")
+    out["ragged32_b64_variance"] = {
+        "sequences": int(w.S), "tokens": int(w.seq_len.sum()), "blocks": int(w.total_blocks),
+        "weighted_kpool_us": round(pool_mean, 2), "weighted_kpool_median_us": round(pool_med, 2),
+        "kpool_algorithmic_bytes": b5, "weighted_kpool_GBps": round(b5 / (pool_mean * 1e-6) / 1e9, 2),
+        "weighted_kpool_frac_of_peak": round(b5 / (pool_mean * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        "decode_step_us": round(dec_mean, 2), "decode_step_median_us": round(dec_med, 2),
+        "decode_step": "re-pool the newest block of each sequence (frozen weights) + anchor + score + flat top-48",
+    }
+    del sel, kp, seqs, k, flush
+    torch.cuda.empty_cache()
+    return out
 
 
 def lazy_rows(n_g, select):

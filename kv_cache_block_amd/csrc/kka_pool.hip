@@ -220,10 +220,15 @@ __global__ __launch_bounds__(256) void pool_finish_kernel(PoolArgs a) {
 // ------------------------------------------------- variance weights, 3 passes
 
 // Pass 1: per block and (layer, head): token sums s1[b][l][h][:] and the sum
-// of squares q[b][l][h], one streaming pass over the keys.
+// of squares q[b][l][h], one streaming pass over the keys.  A thread owns one
+// 16-byte column (8 dims of one head) of one layer and walks all of the
+// block's tokens, kUnroll loads in flight, so its 8 token sums need no
+// reduction across threads and are stored from registers.  The m row slots
+// of a group take m layers at a time; only the sums of squares of a head's
+// D/8 columns are added through LDS, once per round of layers.
 template <int MAXT>
 __global__ __launch_bounds__(MAXT) void pool_stats_kernel(PoolArgs a) {
-  __shared__ float red[MAXT * 9];
+  __shared__ float redq[MAXT];
   const int tid = threadIdx.x;
   const int32_t item = blockIdx.x / a.n_split;
   const int32_t j = blockIdx.x - item * a.n_split;
@@ -232,64 +237,60 @@ __global__ __launch_bounds__(MAXT) void pool_stats_kernel(PoolArgs a) {
   const int32_t q = tid % a.ps.rg;
   const int32_t h = q / DG;
   const int32_t dg = q - h * DG;
-  const int32_t toff = tid / a.ps.rg;
+  const int32_t slot = tid / a.ps.rg;
   const int32_t l0 = j * a.lps;
   const int32_t l1 = min(a.L, l0 + a.lps);
-  const int32_t n_tok = it.n_b > toff ? (it.n_b - toff + a.ps.m - 1) / a.ps.m : 0;
-  const int64_t step_t = (int64_t)a.ps.m * a.sT;
-  float* redq = red + MAXT * 8;
+  const int32_t n_tok = it.n_b;
 
-  for (int32_t l = l0; l < l1; ++l) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float sq = 0.f;
-    const uint16_t* tp = a.k + (int64_t)l * a.sL + it.p * a.sB + (int64_t)h * a.sH + (int64_t)dg * 8 +
-                         (int64_t)toff * a.sT;
-    int32_t ti = 0;
-    for (; ti + kUnroll <= n_tok; ti += kUnroll) {
-      u32x4 v[kUnroll];
+  for (int32_t lr = l0; lr < l1; lr += a.ps.m) {
+    const int32_t l = lr + slot;
+    if (l < l1) {
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      float sq = 0.f;
+      const uint16_t* tp = a.k + (int64_t)l * a.sL + it.p * a.sB + (int64_t)h * a.sH + (int64_t)dg * 8;
+      int32_t ti = 0;
+      for (; ti + kUnroll <= n_tok; ti += kUnroll) {
+        u32x4 v[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) v[u] = load16(tp + (int64_t)(ti + u) * step_t);
+        for (int u = 0; u < kUnroll; ++u) v[u] = load16(tp + (int64_t)(ti + u) * a.sT);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float x0 = bf16_lo(v[u][c]), x1 = bf16_hi(v[u][c]);
+            acc[2 * c] += x0;
+            acc[2 * c + 1] += x1;
+            sq = fmaf(x0, x0, sq);
+            sq = fmaf(x1, x1, sq);
+          }
+        }
+      }
+      for (; ti < n_tok; ++ti) {
+        const u32x4 v = load16(tp + (int64_t)ti * a.sT);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const float x0 = bf16_lo(v[u][c]), x1 = bf16_hi(v[u][c]);
+          const float x0 = bf16_lo(v[c]), x1 = bf16_hi(v[c]);
           acc[2 * c] += x0;
           acc[2 * c + 1] += x1;
           sq = fmaf(x0, x0, sq);
           sq = fmaf(x1, x1, sq);
         }
       }
+      float4* dst = reinterpret_cast<float4*>(a.partial + (((int64_t)item * a.L + l) * a.H) * a.D + (int64_t)q * 8);
+      dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      redq[tid] = sq;
     }
-    for (; ti < n_tok; ++ti) {
-      const u32x4 v = load16(tp + (int64_t)ti * step_t);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float x0 = bf16_lo(v[c]), x1 = bf16_hi(v[c]);
-        acc[2 * c] += x0;
-        acc[2 * c + 1] += x1;
-        sq = fmaf(x0, x0, sq);
-        sq = fmaf(x1, x1, sq);
-      }
-    }
-    stash8(red, tid, acc);
-    redq[tid] = sq;
     __syncthreads();
-    const int64_t lh_row = ((int64_t)item * a.L + l) * a.H;  // (item, l, h=0)
-    if (tid < a.ps.rg) {
-      float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int32_t r = 0; r < a.ps.m; ++r)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s8[e] += red[(tid + r * a.ps.rg) * 8 + e];
-      float4* dst = reinterpret_cast<float4*>(a.partial + lh_row * a.D + (int64_t)tid * 8);
-      dst[0] = make_float4(s8[0], s8[1], s8[2], s8[3]);
-      dst[1] = make_float4(s8[4], s8[5], s8[6], s8[7]);
-    }
-    if (tid < a.H) {
-      float s = 0.f;
-      for (int32_t r = 0; r < a.ps.m; ++r)
-        for (int32_t x = 0; x < DG; ++x) s += redq[r * a.ps.rg + tid * DG + x];
-      a.stats_q[lh_row + tid] = s;
+    // sum of squares per (layer, head) of this round, columns in order
+    if (tid < a.ps.m * a.H) {
+      const int32_t sl = tid / a.H, hh = tid - sl * a.H;
+      const int32_t ll = lr + sl;
+      if (ll < l1) {
+        float s = 0.f;
+        for (int32_t x = 0; x < DG; ++x) s += redq[sl * a.ps.rg + hh * DG + x];
+        a.stats_q[((int64_t)item * a.L + ll) * a.H + hh] = s;
+      }
     }
     __syncthreads();
   }
@@ -297,8 +298,15 @@ __global__ __launch_bounds__(MAXT) void pool_stats_kernel(PoolArgs a) {
 
 // Pass 2: one group per (sequence, head): temporal variance of the head,
 //   var = ( sum_tau |x_tau|^2 / T  -  sum_d (sum_tau x_tau,d / T)^2 ) / D,
-// from the pass-1 sums, combined in fp64.
+// from the pass-1 sums, combined in fp64.  For head_dim <= 256 the group
+// splits into 256 / D lane groups of D lanes, group g summing blocks
+// g, g + ng, ... with kVarUnroll independent loads in flight; the groups'
+// sums are then added in group order (a fixed order, so the result is
+// reproducible).
+constexpr int kVarUnroll = 4;
+
 __global__ __launch_bounds__(256) void head_var_kernel(WeightArgs w) {
+  __shared__ double part[256];
   __shared__ double r1[256];
   __shared__ double r2[256];
   const int tid = threadIdx.x;
@@ -308,12 +316,47 @@ __global__ __launch_bounds__(256) void head_var_kernel(WeightArgs w) {
   const int32_t b1 = min(max(w.offs[s + 1], 0), w.total_blocks);
   const int32_t b0 = min(max(w.offs[s], 0), b1);
   const int64_t T = w.seq_len[s] > 0 ? w.seq_len[s] : 0;
+  const int64_t bstride = (int64_t)w.LH * w.D;  // floats from one block's sums to the next block's
+  const float* base = w.s1 + (int64_t)lh * w.D;
   double m2 = 0.0;
-  for (int32_t d = tid; d < w.D; d += 256) {
-    double s1 = 0.0;
-    for (int32_t b = b0; b < b1; ++b) s1 += (double)w.s1[((int64_t)b * w.LH + lh) * w.D + d];
-    const double mean = T > 0 ? s1 / (double)T : 0.0;
-    m2 += mean * mean;
+  if (w.D <= 256) {
+    const int32_t ng = 256 / w.D;
+    const int32_t g = tid / w.D, d = tid - g * w.D;
+    double acc = 0.0;
+    if (g < ng) {
+      int32_t b = b0 + g;
+      for (; b + (kVarUnroll - 1) * ng < b1; b += kVarUnroll * ng) {
+        float x[kVarUnroll];
+#pragma unroll
+        for (int u = 0; u < kVarUnroll; ++u) x[u] = base[(int64_t)(b + u * ng) * bstride + d];
+#pragma unroll
+        for (int u = 0; u < kVarUnroll; ++u) acc += (double)x[u];
+      }
+      for (; b < b1; b += ng) acc += (double)base[(int64_t)b * bstride + d];
+    }
+    part[tid] = acc;
+    __syncthreads();
+    if (tid < w.D) {
+      double s1 = 0.0;
+      for (int32_t q = 0; q < ng; ++q) s1 += part[q * w.D + tid];
+      const double mean = T > 0 ? s1 / (double)T : 0.0;
+      m2 = mean * mean;
+    }
+  } else {
+    for (int32_t d = tid; d < w.D; d += 256) {
+      double acc = 0.0;
+      int32_t b = b0;
+      for (; b + kVarUnroll - 1 < b1; b += kVarUnroll) {
+        float x[kVarUnroll];
+#pragma unroll
+        for (int u = 0; u < kVarUnroll; ++u) x[u] = base[(int64_t)(b + u) * bstride + d];
+#pragma unroll
+        for (int u = 0; u < kVarUnroll; ++u) acc += (double)x[u];
+      }
+      for (; b < b1; ++b) acc += (double)base[(int64_t)b * bstride + d];
+      const double mean = T > 0 ? acc / (double)T : 0.0;
+      m2 += mean * mean;
+    }
   }
   double qs = 0.0;
   for (int32_t b = b0 + tid; b < b1; b += 256) qs += (double)w.q[(int64_t)b * w.LH + lh];
@@ -359,11 +402,19 @@ __global__ __launch_bounds__(256) void pool_combine_kernel(PoolArgs a, const flo
   if (it.row < 0) return;
   const int32_t LH = a.L * a.H;
   for (int32_t d = threadIdx.x; d < a.D; d += blockDim.x) {
-    float acc = 0.f;
+    // four accumulators (heads lh = 0, 1, 2, 3 mod 4), added in a fixed
+    // order, so the loads and FMAs of four heads overlap
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
     const float* src = a.partial + (int64_t)item * LH * a.D + d;
     const float* wr = wts + (int64_t)it.s * LH;
-    for (int32_t lh = 0; lh < LH; ++lh) acc = fmaf(wr[lh], src[(int64_t)lh * a.D], acc);
-    a.out[it.row * a.D + d] = it.n_b > 0 ? acc / (float)it.n_b : 0.f;
+    int32_t lh = 0;
+    for (; lh + 3 < LH; lh += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] = fmaf(wr[lh + u], src[(int64_t)(lh + u) * a.D], acc[u]);
+    }
+    for (; lh < LH; ++lh) acc[lh & 3] = fmaf(wr[lh], src[(int64_t)lh * a.D], acc[lh & 3]);
+    const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    a.out[it.row * a.D + d] = it.n_b > 0 ? sum / (float)it.n_b : 0.f;
   }
 }
 
