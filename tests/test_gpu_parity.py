@@ -582,3 +582,56 @@ def test_selection_both_launch_shapes(case, S):
             np.testing.assert_array_equal(gs[s, :len(ridx)].view(np.uint32), rsc.view(np.uint32))
             if case["k_page"] > len(ridx):
                 assert (gi[s, len(ridx):case["k_page"]] == -1).all()
+
+
+@pytest.mark.parametrize("case,S,max_pages", [
+    (dict(hierarchical=1, k_grid=3, k_chunk=12, k_page=70, pages_per_chunk=16, chunks_per_grid=16), 1, 12000),
+    (dict(hierarchical=0, k_grid=0, k_chunk=0, k_page=100, pages_per_chunk=16, chunks_per_grid=16), 2, 10000),
+])
+def test_one_launch_selection_beyond_lds_rows(case, S, max_pages):
+    """Few sequences whose rows exceed what the selecting work-group stages in
+    LDS: scoring and selection still share one launch, and the selection
+    reads the affinities from memory.  Against the oracle."""
+    say(f"one launch beyond LDS rows S={S} max_pages={max_pages}")
+    D = 16
+    lay = kka.LevelLayout(S, max_pages, D, bool(case["hierarchical"]), case["pages_per_chunk"],
+                          case["chunks_per_grid"])
+    assert lay.rows_per_seq > 9216
+    rng = np.random.default_rng(41)
+    lvl = np.zeros((S, lay.rows_per_seq, D), np.float32)
+    lvl[:, :max_pages] = rng.standard_normal((S, max_pages, D), dtype=np.float32)
+    n_pages = np.array([max_pages - 7 * s for s in range(S)], np.int32)
+    level = torch.from_numpy(lvl).cuda()
+    npg = torch.from_numpy(n_pages).cuda()
+    kka.kka_build_levels(lay, level, npg)
+    anchors = torch.from_numpy(rng.standard_normal((S, D), dtype=np.float32)).cuda()
+    K = case["k_page"]
+    idx = torch.full((S, K), -9, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((S, K), dtype=torch.float32, device="cuda")
+    cnt = torch.zeros((S,), dtype=torch.int32, device="cuda")
+    for with_aff in (True, False):
+        aff = torch.zeros((S, lay.rows_per_seq), dtype=torch.float32, device="cuda") if with_aff else None
+        kka.kka_score_topk(lay, level, npg, anchors, k_page=K, k_grid=case["k_grid"], k_chunk=case["k_chunk"],
+                           page_idx_out=idx, page_score_out=sc, n_selected_out=cnt, affinity_out=aff)
+        torch.cuda.synchronize()
+        if with_aff:
+            af = aff.cpu().numpy()
+            ref_idx = idx.cpu().numpy().copy()
+        lv, an = level.cpu().numpy(), anchors.cpu().numpy()
+        gi, gs, gc = idx.cpu().numpy(), sc.cpu().numpy(), cnt.cpu().numpy()
+        for s in range(S):
+            n_p = int(n_pages[s])
+            if case["hierarchical"]:
+                n_c = -(-n_p // case["pages_per_chunk"])
+                n_g = -(-n_c // case["chunks_per_grid"])
+                rows = np.concatenate([np.arange(n_p), lay.chunk_row0 + np.arange(n_c), lay.grid_row0 + np.arange(n_g)])
+                a_c, a_g = af[s, lay.chunk_row0:lay.chunk_row0 + n_c], af[s, lay.grid_row0:lay.grid_row0 + n_g]
+            else:
+                rows, a_c, a_g = np.arange(n_p), None, None
+            np.testing.assert_allclose(af[s, rows], oracle.affinity(lv[s, rows], an[s]), atol=ATOL, rtol=0)
+            ridx, rsc = oracle.select(af[s, :n_p], a_c, a_g, **case)
+            assert gc[s] == len(ridx)
+            np.testing.assert_array_equal(gi[s, :len(ridx)], ridx, err_msg=f"s={s} with_aff={with_aff}")
+            np.testing.assert_array_equal(gs[s, :len(ridx)].view(np.uint32), rsc.view(np.uint32))
+        if not with_aff:
+            np.testing.assert_array_equal(gi, ref_idx)  # scratch affinities in the workspace: same selection
