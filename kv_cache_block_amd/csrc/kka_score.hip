@@ -8,29 +8,31 @@
 //
 // Scoring: a batched GEMV with one right-hand side per sequence, bound by
 // HBM bandwidth.  Each sequence's present rows are cut into tiles spread
-// over the whole chip; in a tile, 8 lanes share one row (each lane reads
-// 16-byte pieces 128 bytes apart, so 8 lanes read whole 128-byte lines) and
-// every lane keeps 4 non-temporal loads in flight per pass over its tile
-// (few registers, so eight waves per SIMD stay resident; rows are read once
-// per step, and a serving batch's level rows exceed the last-level cache
-// anyway); the fused kernel issues all 8 of a lane's loads in one pass.
-// Dot product and row norm are reduced over the 8 lanes with a fixed
-// butterfly.
+// over the whole chip; in a tile, 8 lanes share one row (16 above head_dim
+// 512; each lane reads 16-byte pieces 128 bytes apart, so 8 lanes read
+// whole 128-byte lines) and every lane keeps 4 non-temporal loads in flight
+// per pass over its tile (few registers, so eight waves per SIMD stay
+// resident; rows are read once per step, and a serving batch's level rows
+// exceed the last-level cache anyway); the fused kernel issues all 8 of a
+// lane's loads in one pass.  Dot product and row norm are reduced over the
+// row's lanes with a fixed butterfly.
 //
 // Selection, written for latency: for batches whose tiles all fit on the
 // chip at once, the work-group that finishes a sequence's last scoring
 // tile (a per-sequence counter) selects that sequence in the same launch
 // (score_select_kernel); larger batches run the lighter score_kernel and
-// then select_kernel, one work-group per sequence.  The sequence's whole
-// affinity row block is staged into LDS in one round of loads, then each
-// level is selected from LDS: candidates (children of kept parents, or
-// every row) with a positive score are compacted with wave ballots; up to
-// 512 of them are ranked directly (rank = number of larger keys, so rank <
-// k places the element at its final position); larger sets use an
-// MSB-first radix select.  Keys are (affinity bits << 32 | ~index): unique,
-// and larger means higher score then lower index.  When fewer than k
-// candidates score above zero, the lowest-index rows scoring exactly 0
-// (masked or zero affinity) fill the remaining slots in index order.
+// then select_kernel, one work-group per sequence.  The sequence's
+// affinity rows are staged into LDS in one round of loads (sequences of
+// more than kLdsRows rows are selected from memory), then each level is
+// selected: up to 64 candidates (children of kept parents, or every row)
+// are ranked from registers, up to 512 in LDS groups of 64 that are ranked
+// and merged, larger sets are compacted with wave ballots and ranked or
+// radix-selected (MSB first).  A rank is the number of larger keys, so rank
+// < k places the element at its final position.  Keys are (affinity bits
+// << 32 | ~index): unique, and larger means higher score then lower index.
+// When fewer than k candidates score above zero, the lowest-index rows
+// scoring exactly 0 (masked or zero affinity) fill the remaining slots in
+// index order.
 #include <atomic>
 
 #include "kka_internal.h"
@@ -387,7 +389,7 @@ constexpr int rank_tpc(int ng) {
 // key within its group, each comparing a fixed strided share; each group is
 // written back as a strictly descending run and a key's rank in the level
 // is its rank in its group plus, for every other group, how many keys of
-// that run exceed it (binary search).  Keys without a positive score rank
+// that run exceed it (merged_rank).  Keys without a positive score rank
 // below all positive ones and are never kept here (the zero fill handles
 // them).
 template <bool STG, int NG>
