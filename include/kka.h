@@ -68,6 +68,8 @@ typedef enum kka_status {
 #define KKA_DEVERR_ROW 4u         /* a block's index in its sequence >= vb_seq_stride      */
 #define KKA_DEVERR_PAGES 8u       /* n_pages[s] < 0 or > max_pages                         */
 #define KKA_DEVERR_OFFSETS 16u    /* block_offsets not nondecreasing / total mismatch      */
+#define KKA_DEVERR_WORKSPACE 32u  /* a scoring workspace's tile counter was not zero at a   */
+                                  /* one-launch kka_score_topk call (see its workspace)    */
 
 /*
  * Paged key pool.  Element (layer l, physical block p, token slot t,
@@ -324,7 +326,10 @@ typedef struct kka_select {
  *                bytes, rounded up to 256), then scratch affinities when
  *                affinity_out is NULL.  The counters must be zero before the
  *                first call that uses the workspace (allocate it
- *                zero-filled); every call leaves them zero.  Calls that run
+ *                zero-filled); every call leaves them zero.  A counter found
+ *                at or above the sequence's tile count raises
+ *                KKA_DEVERR_WORKSPACE, and that sequence's selection is then
+ *                not valid (re-zero the counters).  Calls that run
  *                concurrently must not share a workspace.
  * Work-groups score tiles of rows spread over the chip.  When every tile
  * of the batch fits on the chip at once, the call is one launch on

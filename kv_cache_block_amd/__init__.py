@@ -34,6 +34,7 @@ DEVERR_SEQ_LEN = 2
 DEVERR_ROW = 4
 DEVERR_PAGES = 8
 DEVERR_OFFSETS = 16
+DEVERR_WORKSPACE = 32
 
 _STATUS = {0: "ok", 1: "KKA_ERR_NULL", 2: "KKA_ERR_SHAPE", 3: "KKA_ERR_ALIGN", 4: "KKA_ERR_WORKSPACE",
            5: "KKA_ERR_DEVICE"}

@@ -843,7 +843,12 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(ScoreArgs a) 
   // last tile, leaving it ready for the next call.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) sm.last = atomicInc(a.done + s, (unsigned)(a.tiles_per_seq - 1)) == (unsigned)(a.tiles_per_seq - 1);
+  if (tid == 0) {
+    const unsigned top = (unsigned)(a.tiles_per_seq - 1);
+    const unsigned old = atomicInc(a.done + s, top);
+    if (old > top) raise_err(a.err, KKA_DEVERR_WORKSPACE);  // counters not zeroed before the call
+    sm.last = old == top;
+  }
   __syncthreads();
   if (!sm.last) return;
   select_sequence(a, s, sm);

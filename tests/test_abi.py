@@ -33,6 +33,17 @@ def declared():
     return re.findall(r"KKA_API\s+[\w\s\*]+?\b(kka_\w+)\s*\(", text)
 
 
+def test_binding_constants_match_header():
+    """Device error bits, weight modes and status codes: the binding's
+    values are the header's."""
+    text = open(HEADER).read()
+    bits = dict(re.findall(r"#define KKA_DEVERR_(\w+) (\d+)u", text))
+    assert bits and {k: int(v) for k, v in bits.items()} == \
+        {k[len("DEVERR_"):]: getattr(kka, k) for k in dir(kka) if k.startswith("DEVERR_")}
+    modes = dict(re.findall(r"KKA_WEIGHT_(\w+) = (\d+)", text))
+    assert modes and all(getattr(kka, "WEIGHT_" + k) == int(v) for k, v in modes.items())
+
+
 def test_header_declares_all_entry_points():
     names = declared()
     assert sorted(names) == sorted(kka.ENTRY_POINTS)

@@ -635,3 +635,22 @@ def test_one_launch_selection_beyond_lds_rows(case, S, max_pages):
             np.testing.assert_array_equal(gs[s, :len(ridx)].view(np.uint32), rsc.view(np.uint32))
         if not with_aff:
             np.testing.assert_array_equal(gi, ref_idx)  # scratch affinities in the workspace: same selection
+
+
+def test_unzeroed_score_workspace_raises_flag():
+    """A scoring workspace whose tile counters hold garbage: the one-launch
+    call raises the workspace flag (the kernel still completes); after the
+    counters are re-zeroed the same call selects as the oracle does."""
+    say("score workspace garbage counters")
+    case = dict(hierarchical=1, k_grid=2, k_chunk=3, k_page=5, pages_per_chunk=4, chunks_per_grid=3)
+    w = ragged_workload(12, 3, 2, 2, 64, 4, 100, 800, select=case)
+    sel, npg = run_selector(w)
+    sel.ws_score.fill_(0xFF)
+    sel.score(npg)
+    assert kka.kka_device_error() & kka.DEVERR_WORKSPACE
+    sel.ws_score.zero_()
+    sel.score(npg)
+    torch.cuda.synchronize()
+    assert kka.kka_device_error() == 0
+    for s in range(w.S):
+        check_selection(sel, s, int(npg[s]))
