@@ -278,6 +278,8 @@ def run(args):
     # every sequence must select its planted topic
     got = idx4.cpu().numpy()
     recovered = int(sum((v.page_topic[s][got[s]] == v.anchor_topic[s]).all() for s in range(S)))
+    if recovered != S:
+        raise RuntimeError(f"serving selection lost the planted topic in {S - recovered} of {S} sequences")
 
     # lazy (coarse-to-fine) scoring of the same batch: same selection, fewer rows read
     def lazy4(i):
