@@ -201,14 +201,83 @@ __device__ void sort_desc(SelectShared& sm, int32_t n) {
   }
 }
 
+// Sorts sm.buf[0, n) in descending order for n <= 64 distinct keys that
+// all lie above 2^32 (positive scores): every wave holds the n keys (lane =
+// key) and counts, for each, how many keys of its share of the lanes are
+// larger, reading them with lane broadcasts; the counts are summed through
+// LDS and give each key's slot.
+__device__ void sort_desc_small(SelectShared& sm, int32_t n) {
+  constexpr int W = kSelThreads / 64;
+  constexpr int J = 64 / W;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint64_t x = lane < n ? sm.buf[lane] : (uint64_t)lane;  // padding below every real key
+  const uint32_t xlo = (uint32_t)x, xhi = (uint32_t)(x >> 32);
+  int32_t c = 0;
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj) {
+    const int j = wave * J + jj;
+    const uint64_t y = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)xhi, j) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)xlo, j);
+    c += (int32_t)(y > x);
+  }
+  sm.part[wave][lane] = c;
+  __syncthreads();
+  if (wave == 0) {
+    int32_t r = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) r += sm.part[w][lane];
+    if (lane < n) sm.ck[r] = x;
+  }
+  __syncthreads();
+  if (tid < n) sm.buf[tid] = sm.ck[tid];
+  __syncthreads();
+}
+
 // Radix select over every positive candidate (re-enumerated each pass), for
 // candidate sets too large to rank; leaves the top k_eff sorted in sm.buf.
+// Bytes that every positive key shares (scores of one sequence often agree
+// in their leading bits) are fixed up front from an AND / OR reduction, so
+// the digit passes start at the first byte that tells keys apart.
 template <bool STG>
 __device__ void radix_top(const Level& L, int64_t m, int32_t k_eff, SelectShared& sm) {
+  constexpr int W = kSelThreads / 64;
   const int tid = threadIdx.x;
-  uint64_t prefix = 0, mask = 0;
+  uint64_t all_and = ~0ull, any_or = 0ull;
+  for (int64_t c = tid; c < m; c += kSelThreads) {
+    const int32_t e = cand(L, sm, c);
+    if (e < 0) continue;
+    const uint32_t key = aff_key<STG>(L, sm, e);
+    if (key == 0u) continue;
+    const uint64_t comp = composite(key, e);
+    all_and &= comp;
+    any_or |= comp;
+  }
+  for (int o = 1; o < 64; o <<= 1) {
+    all_and &= __shfl_xor(all_and, o, 64);
+    any_or |= __shfl_xor(any_or, o, 64);
+  }
+  if ((tid & 63) == 0) {
+    sm.ck[tid >> 6] = all_and;
+    sm.ck[W + (tid >> 6)] = any_or;
+  }
+  __syncthreads();
+  for (int w = 0; w < W; ++w) {
+    all_and &= sm.ck[w];
+    any_or |= sm.ck[W + w];
+  }
+  // keys are distinct, so some bit differs: digits of up to 8 bits start at
+  // the highest differing bit and go down (a byte-aligned first digit would
+  // put scores on either side of 0.5, which differ in the exponent's last
+  // bit, into two bins and serialise the LDS atomics on them)
+  const int hb = 63 - __clzll((long long)(all_and ^ any_or));
+  uint64_t mask = hb >= 63 ? 0ull : ~((2ull << hb) - 1ull);
+  uint64_t prefix = any_or & mask;
   int32_t kk = k_eff;
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  for (int top = hb; top >= 0;) {
+    const int sh = top >= 7 ? top - 7 : 0;
+    const uint32_t dmask = (2u << (top - sh)) - 1u;
     for (int b = tid; b < 256; b += kSelThreads) sm.hist[b] = 0u;
     __syncthreads();
     for (int64_t c = tid; c < m; c += kSelThreads) {
@@ -217,17 +286,18 @@ __device__ void radix_top(const Level& L, int64_t m, int32_t k_eff, SelectShared
       const uint32_t key = aff_key<STG>(L, sm, e);
       if (key == 0u) continue;
       const uint64_t comp = composite(key, e);
-      if ((comp & mask) == prefix) atomicAdd(&sm.hist[(uint32_t)(comp >> shift) & 255u], 1u);
+      if ((comp & mask) == prefix) atomicAdd(&sm.hist[(uint32_t)(comp >> sh) & dmask], 1u);
     }
     __syncthreads();
     if (tid < 64) pick_digit(sm, kk);
     __syncthreads();
-    prefix |= (uint64_t)sm.digit << shift;
-    mask |= (uint64_t)255u << shift;
+    prefix |= (uint64_t)sm.digit << sh;
+    mask |= (uint64_t)dmask << sh;
     kk -= (int32_t)sm.above;
     const bool done = sm.bucket == (uint32_t)kk;
     __syncthreads();
     if (done) break;
+    top = sh - 1;
   }
   if (tid == 0) sm.cnt[3] = 0;
   __syncthreads();
@@ -243,7 +313,8 @@ __device__ void radix_top(const Level& L, int64_t m, int32_t k_eff, SelectShared
     }
   }
   __syncthreads();
-  sort_desc(sm, k_eff);
+  if (k_eff <= 64) sort_desc_small(sm, k_eff);
+  else sort_desc(sm, k_eff);
 }
 
 // When only P < k_eff candidates score above zero, the lowest-index rows
@@ -274,6 +345,144 @@ __device__ void fill_zeros(const Level& L, SelectShared& sm, int32_t P, int32_t 
   }
 }
 
+// Ranks the P <= kRankMax compacted positive keys sm.ck[0, P): rank r goes
+// to sm.buf[r] when r < k_eff.  tpc consecutive lanes share a key, each
+// counting a strided part with 8 LDS reads in flight.
+__device__ void rank_compacted(SelectShared& sm, int32_t P, int32_t k_eff) {
+  const int tid = threadIdx.x;
+  int32_t tpc = 1;
+  while (tpc < 16 && P * tpc * 2 <= kSelThreads) tpc <<= 1;
+  for (int32_t t0 = 0; t0 < P * tpc; t0 += kSelThreads) {
+    const int32_t t = t0 + tid;
+    const int32_t i = t / tpc, q = t - i * tpc;
+    const uint64_t x = i < P ? sm.ck[i] : ~0ull;
+    int32_t r = 0;
+    int32_t j = q;
+    for (; j + 7 * tpc < P; j += 8 * tpc) {
+      uint64_t y[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) y[u] = sm.ck[j + u * tpc];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r += (int32_t)(y[u] > x);
+    }
+    for (; j < P; j += tpc) r += (int32_t)(sm.ck[j] > x);
+    for (int32_t o = 1; o < tpc; o <<= 1) r += __shfl_xor(r, o);
+    if (q == 0 && i < P && r < k_eff) sm.buf[r] = x;
+  }
+  __syncthreads();
+}
+
+// Rows each thread covers in the flat staged path (row r * kSelThreads + tid).
+constexpr int kKeysPerThread = (kLdsRows + kSelThreads - 1) / kSelThreads;
+
+// Top k_eff of a flat level of m <= kKeysPerThread * kSelThreads rows staged
+// in LDS, sorted, in sm.buf.  Every pass (positive count with the fixed
+// leading bits, the radix digits, the gather) reads a thread's rows
+// r * kSelThreads + tid straight from the LDS copy with all reads in
+// flight; up to kRankMax positive scores are compacted and ranked instead.
+__device__ int32_t select_flat_staged(const Level& L, int32_t m, int32_t k_eff, SelectShared& sm) {
+  constexpr int W = kSelThreads / 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const float* row = sm.aff + L.off;
+  const int nr = (m + kSelThreads - 1) / kSelThreads;  // row slots in use (<= kKeysPerThread)
+  auto key_at = [&](int r) -> uint32_t {
+    const int32_t e = r * kSelThreads + tid;
+    return e < m ? __float_as_uint(row[e]) : 0u;
+  };
+  uint64_t a_and = ~0ull, a_or = 0ull;
+  int32_t npos = 0;
+#pragma unroll 6
+  for (int r = 0; r < nr; ++r) {
+    const uint32_t kb = key_at(r);
+    if (kb != 0u) {
+      const uint64_t comp = composite(kb, r * kSelThreads + tid);
+      a_and &= comp;
+      a_or |= comp;
+      ++npos;
+    }
+  }
+  for (int o = 1; o < 64; o <<= 1) {
+    a_and &= __shfl_xor(a_and, o, 64);
+    a_or |= __shfl_xor(a_or, o, 64);
+    npos += __shfl_xor(npos, o, 64);
+  }
+  if (lane == 0) {
+    sm.ck[wave] = a_and;
+    sm.ck[W + wave] = a_or;
+    sm.wave_tot[wave] = npos;
+  }
+  __syncthreads();
+  int32_t P = 0;
+  for (int w = 0; w < W; ++w) {
+    a_and &= sm.ck[w];
+    a_or |= sm.ck[W + w];
+    P += sm.wave_tot[w];
+  }
+  __syncthreads();  // sm.ck and sm.wave_tot are reused below
+  if (P <= kRankMax) {
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    int32_t* cnt = &sm.cnt[L.slot];
+#pragma unroll 6
+    for (int r = 0; r < nr; ++r) {
+      const uint32_t kb = key_at(r);
+      const bool pos = kb != 0u;
+      const uint64_t bal = __ballot(pos);
+      int32_t base = 0;
+      if (lane == 0 && bal) base = atomicAdd(cnt, (int32_t)__popcll(bal));
+      base = __shfl(base, 0, 64);
+      if (pos) sm.ck[base + (int32_t)__popcll(bal & lt_mask)] = composite(kb, r * kSelThreads + tid);
+    }
+    __syncthreads();
+    rank_compacted(sm, P, k_eff);
+  } else {
+    // radix select of the top min(k_eff, P), as in radix_top
+    const int32_t take = P >= k_eff ? k_eff : P;
+    const int hb = 63 - __clzll((long long)(a_and ^ a_or));
+    uint64_t mask = hb >= 63 ? 0ull : ~((2ull << hb) - 1ull);
+    uint64_t prefix = a_or & mask;
+    int32_t kk = take;
+    for (int top = hb; top >= 0;) {
+      const int sh = top >= 7 ? top - 7 : 0;
+      const uint32_t dmask = (2u << (top - sh)) - 1u;
+      for (int b = tid; b < 256; b += kSelThreads) sm.hist[b] = 0u;
+      __syncthreads();
+#pragma unroll 6
+      for (int r = 0; r < nr; ++r) {
+        const uint32_t kb = key_at(r);
+        const uint64_t comp = composite(kb, r * kSelThreads + tid);
+        if (kb != 0u && (comp & mask) == prefix) atomicAdd(&sm.hist[(uint32_t)(comp >> sh) & dmask], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) pick_digit(sm, kk);
+      __syncthreads();
+      prefix |= (uint64_t)sm.digit << sh;
+      mask |= (uint64_t)dmask << sh;
+      kk -= (int32_t)sm.above;
+      const bool done = sm.bucket == (uint32_t)kk;
+      __syncthreads();
+      if (done) break;
+      top = sh - 1;
+    }
+    if (tid == 0) sm.cnt[3] = 0;
+    __syncthreads();
+#pragma unroll 6
+    for (int r = 0; r < nr; ++r) {
+      const uint32_t kb = key_at(r);
+      const uint64_t comp = composite(kb, r * kSelThreads + tid);
+      if (kb != 0u && comp >= prefix) {
+        const int32_t slot = atomicAdd(&sm.cnt[3], 1);
+        if (slot < take) sm.buf[slot] = comp;
+      }
+    }
+    __syncthreads();
+    if (take <= 64) sort_desc_small(sm, take);
+    else sort_desc(sm, take);
+  }
+  if (P < k_eff) fill_zeros<true>(L, sm, P, k_eff);
+  return k_eff;
+}
+
 // Keeps the top min(k, n) elements of a level with more candidates than
 // threads, sorted, in sm.buf.  sm.cnt[L.slot] must be zero on entry.
 template <bool STG>
@@ -284,6 +493,10 @@ __device__ int32_t select_level_big(const Level& L, int32_t k, SelectShared& sm)
   const int32_t k_eff = k < L.n ? k : L.n;
   if (k_eff <= 0) return 0;
   const int64_t m = L.fanout ? (int64_t)L.n_par * L.fanout : (int64_t)L.n;
+  if constexpr (STG) {
+    if (L.fanout == 0 && m <= (int64_t)kKeysPerThread * kSelThreads)
+      return select_flat_staged(L, (int32_t)m, k_eff, sm);
+  }
   int32_t* cnt = &sm.cnt[L.slot];
   // compact the candidates scoring above zero
   for (int64_t c0 = 0; c0 < m; c0 += kSelThreads) {
@@ -307,29 +520,8 @@ __device__ int32_t select_level_big(const Level& L, int32_t k, SelectShared& sm)
     radix_top<STG>(L, m, take, sm);
     if (P >= k_eff) return k_eff;
   } else {
-    // rank the positive candidates: rank r goes to slot r when r < k_eff.
-    // tpc consecutive lanes share a candidate, each counting a strided part
-    // with 8 LDS reads in flight.
-    int32_t tpc = 1;
-    while (tpc < 16 && P * tpc * 2 <= kSelThreads) tpc <<= 1;
-    for (int32_t t0 = 0; t0 < P * tpc; t0 += kSelThreads) {
-      const int32_t t = t0 + tid;
-      const int32_t i = t / tpc, q = t - i * tpc;
-      const uint64_t x = i < P ? sm.ck[i] : ~0ull;
-      int32_t r = 0;
-      int32_t j = q;
-      for (; j + 7 * tpc < P; j += 8 * tpc) {
-        uint64_t y[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) y[u] = sm.ck[j + u * tpc];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) r += (int32_t)(y[u] > x);
-      }
-      for (; j < P; j += tpc) r += (int32_t)(sm.ck[j] > x);
-      for (int32_t o = 1; o < tpc; o <<= 1) r += __shfl_xor(r, o);
-      if (q == 0 && i < P && r < k_eff) sm.buf[r] = x;
-    }
-    __syncthreads();
+    // rank the positive candidates: rank r goes to slot r when r < k_eff
+    rank_compacted(sm, P, k_eff);
     if (P >= k_eff) return k_eff;
   }
   fill_zeros<STG>(L, sm, P, k_eff);

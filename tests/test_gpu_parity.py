@@ -235,6 +235,9 @@ def test_levels_and_selection_match_oracle(case):
     dict(hierarchical=1, k_grid=6, k_chunk=20, k_page=200, pages_per_chunk=16, chunks_per_grid=8),  # 320 live
     dict(hierarchical=1, k_grid=7, k_chunk=28, k_page=500, pages_per_chunk=16, chunks_per_grid=8),  # 448 live
     dict(hierarchical=0, k_grid=0, k_chunk=0, k_page=77, pages_per_chunk=16, chunks_per_grid=16),
+    dict(hierarchical=0, k_grid=0, k_chunk=0, k_page=48, pages_per_chunk=16, chunks_per_grid=16),
+    dict(hierarchical=0, k_grid=0, k_chunk=0, k_page=64, pages_per_chunk=16, chunks_per_grid=16),
+    dict(hierarchical=0, k_grid=0, k_chunk=0, k_page=1, pages_per_chunk=16, chunks_per_grid=16),
 ])
 def test_selection_large_candidate_sets(case):
     """Levels with more candidates than the selecting group has threads
