@@ -102,9 +102,14 @@ struct Level {
 
 // Affinities cross work-groups inside one launch (scoring tiles on any
 // XCD, the selecting work-group on another), and each XCD has its own L2:
-// they are stored and loaded with device-scope atomics, which write
-// through and read past the non-coherent L2, instead of paying a
-// device-scope fence (a whole-L2 write-back) per tile.
+// they are stored and loaded with device-scope (relaxed) atomics, which
+// write through and read past the non-coherent L2, instead of paying a
+// device-scope release fence (a whole-L2 write-back) per tile.  The
+// handoff's order comes from the hardware rather than from release /
+// acquire: a tile waits for its stores to be acknowledged (vmcnt 0) before
+// its device-scope counter increment, and the selecting work-group issues
+// its device-scope loads only after its own increment has returned the
+// last count.
 __device__ __forceinline__ void store_aff(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
