@@ -657,3 +657,25 @@ def test_unzeroed_score_workspace_raises_flag():
     assert kka.kka_device_error() == 0
     for s in range(w.S):
         check_selection(sel, s, int(npg[s]))
+
+
+def test_concurrent_calls_on_two_streams_with_own_workspaces():
+    """Two one-launch score+top-K calls in flight at once on two streams
+    (default priority), each with its own workspace: both select as the
+    oracle does, repeatedly."""
+    say("concurrent score calls on two streams")
+    case = dict(hierarchical=1, k_grid=2, k_chunk=3, k_page=6, pages_per_chunk=4, chunks_per_grid=3)
+    w1 = ragged_workload(21, 3, 2, 2, 64, 4, 100, 900, select=case)
+    w2 = ragged_workload(22, 4, 2, 2, 64, 4, 100, 900, select=case)
+    sel1, npg1 = run_selector(w1)
+    sel2, npg2 = run_selector(w2)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(20):
+        sel1.score(npg1, stream=s1)
+        sel2.score(npg2, stream=s2)
+    torch.cuda.synchronize()
+    assert kka.kka_device_error() == 0
+    for sel, w, npg in ((sel1, w1, npg1), (sel2, w2, npg2)):
+        for s in range(w.S):
+            check_selection(sel, s, int(npg[s]))
