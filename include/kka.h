@@ -419,7 +419,13 @@ KKA_API int32_t kka_device_error(void* stream);
 /* Static description of a kka_status value. */
 KKA_API const char* kka_status_string(kka_status s);
 
-/* Library version as major*10000 + minor*100 + patch. */
+/* Version of this header as major*10000 + minor*100 + patch.  0.2.0: the
+ * kka_score_topk workspace holds per-sequence tile counters that must be
+ * zero at first use. */
+#define KKA_VERSION 200
+
+/* Version of the loaded library, same encoding (equals KKA_VERSION when the
+ * header and the library match). */
 KKA_API int32_t kka_version(void);
 
 #ifdef __cplusplus

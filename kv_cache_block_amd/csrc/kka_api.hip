@@ -604,6 +604,6 @@ const char* kka_status_string(kka_status s) {
   return "unknown status";
 }
 
-int32_t kka_version(void) { return 100; }
+int32_t kka_version(void) { return KKA_VERSION; }
 
 }  // extern "C"
