@@ -397,7 +397,6 @@ __device__ int32_t select_flat_staged(const Level& L, int32_t m, int32_t k_eff, 
   };
   uint64_t a_and = ~0ull, a_or = 0ull;
   int32_t npos = 0;
-#pragma unroll 6
   for (int r = 0; r < nr; ++r) {
     const uint32_t kb = key_at(r);
     if (kb != 0u) {
@@ -428,7 +427,6 @@ __device__ int32_t select_flat_staged(const Level& L, int32_t m, int32_t k_eff, 
   if (P <= kRankMax) {
     const uint64_t lt_mask = (1ull << lane) - 1ull;
     int32_t* cnt = &sm.cnt[L.slot];
-#pragma unroll 6
     for (int r = 0; r < nr; ++r) {
       const uint32_t kb = key_at(r);
       const bool pos = kb != 0u;
@@ -452,7 +450,6 @@ __device__ int32_t select_flat_staged(const Level& L, int32_t m, int32_t k_eff, 
       const uint32_t dmask = (2u << (top - sh)) - 1u;
       for (int b = tid; b < 256; b += kSelThreads) sm.hist[b] = 0u;
       __syncthreads();
-#pragma unroll 6
       for (int r = 0; r < nr; ++r) {
         const uint32_t kb = key_at(r);
         const uint64_t comp = composite(kb, r * kSelThreads + tid);
@@ -471,7 +468,6 @@ __device__ int32_t select_flat_staged(const Level& L, int32_t m, int32_t k_eff, 
     }
     if (tid == 0) sm.cnt[3] = 0;
     __syncthreads();
-#pragma unroll 6
     for (int r = 0; r < nr; ++r) {
       const uint32_t kb = key_at(r);
       const uint64_t comp = composite(kb, r * kSelThreads + tid);
