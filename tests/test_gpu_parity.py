@@ -679,3 +679,41 @@ def test_concurrent_calls_on_two_streams_with_own_workspaces():
     for sel, w, npg in ((sel1, w1, npg1), (sel2, w2, npg2)):
         for s in range(w.S):
             check_selection(sel, s, int(npg[s]))
+
+
+@pytest.mark.parametrize("K", [100, 400])
+def test_flat_selection_many_rows_few_positive(K):
+    """A flat level of 1000 pages of which 700 point exactly away from the
+    anchor (affinity exactly 0): more rows than the ranking path takes but
+    only 300 positive scores, so those are compacted and ranked; with k
+    above 300 the lowest-index zero rows fill the remaining slots."""
+    say(f"flat few positive K={K}")
+    S, NP, D = 2, 1000, 8
+    lay = kka.LevelLayout(S, NP, D, False, 16, 16)
+    rng = np.random.default_rng(61)
+    anc = np.zeros((S, D), np.float32)
+    anc[:, 0] = 1.0
+    lvl = np.zeros((S, lay.rows_per_seq, D), np.float32)
+    lvl[:, :NP] = rng.standard_normal((S, NP, D), dtype=np.float32)
+    for s in range(S):
+        neg = rng.permutation(NP)[:700]
+        lvl[s, neg] = 0.0
+        lvl[s, neg, 0] = -rng.uniform(0.5, 2.0, 700).astype(np.float32)  # cos = -1 exactly
+    level = torch.from_numpy(lvl).cuda()
+    npg = torch.full((S,), NP, dtype=torch.int32, device="cuda")
+    anchors = torch.from_numpy(anc).cuda()
+    idx = torch.full((S, K), -9, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((S, K), dtype=torch.float32, device="cuda")
+    cnt = torch.zeros((S,), dtype=torch.int32, device="cuda")
+    aff = torch.zeros((S, NP), dtype=torch.float32, device="cuda")
+    kka.kka_score_topk(lay, level, npg, anchors, k_page=K, page_idx_out=idx, page_score_out=sc,
+                       n_selected_out=cnt, affinity_out=aff)
+    torch.cuda.synchronize()
+    af = aff.cpu().numpy()
+    for s in range(S):
+        assert int((af[s] > 0).sum()) <= 300
+        np.testing.assert_allclose(af[s], oracle.affinity(lvl[s, :NP], anc[s]), atol=ATOL, rtol=0)
+        ridx, rsc = oracle.select(af[s], hierarchical=0, k_page=K)
+        assert int(cnt[s]) == len(ridx)
+        np.testing.assert_array_equal(idx[s].cpu().numpy()[:len(ridx)], ridx)
+        np.testing.assert_array_equal(sc[s].cpu().numpy()[:len(ridx)].view(np.uint32), rsc.view(np.uint32))
