@@ -62,6 +62,7 @@ constexpr int kBitmapWords = kMaxParents / 32;
 #endif
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 load_row4(const f32x4* p) {
 #if KKA_SCORE_NT
@@ -71,11 +72,18 @@ __device__ __forceinline__ f32x4 load_row4(const f32x4* p) {
 #endif
 }
 
+// Sorted groups of a level of 65-512 candidates: the keys, and every
+// eighth key of each group (the last key of each block of 8).
+struct SortedRuns {
+  alignas(16) uint64_t key[kSelThreads];
+  alignas(16) uint64_t piv[kSelThreads / 8];
+};
+
 struct SelectShared {
   float aff[kLdsRows];
-  uint64_t ck[kRankMax];
+  alignas(16) uint64_t ck[kRankMax];
   union {
-    uint64_t run[kSelThreads];            // sorted groups (levels of 65-512 candidates)
+    SortedRuns runs;                      // levels of 65-512 candidates
     int32_t part[kSelThreads / 64][64];   // per-wave counts (levels of up to 64)
   };
   uint64_t buf[kMaxK];
@@ -154,6 +162,31 @@ __device__ __forceinline__ int32_t cand32(const Level& L, const SelectShared& sm
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, int32_t e) {
   return ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)e);
+}
+
+// Puts key x in slot `slot` of the level's result; on a level that parents
+// the next one (`kept` set) its element also becomes parent `slot` of the
+// next level, with its keep flag set.
+__device__ __forceinline__ void put_kept(SelectShared& sm, int32_t slot, uint64_t x, uint32_t* kept) {
+  sm.buf[slot] = x;
+  if (kept) {
+    const int32_t e = (int32_t)(~(uint32_t)x);
+    sm.plist[slot] = e;
+    atomicOr(&kept[e >> 5], 1u << (e & 31));
+  }
+}
+
+// Records the kept elements of a level (sm.buf[0, k_eff)) as the parents of
+// the next level: their indices in plist and their bits in `kept` (clear on
+// entry).
+__device__ void keep_parents(SelectShared& sm, int32_t k_eff, uint32_t* kept) {
+  const int tid = threadIdx.x;
+  for (int32_t i = tid; i < k_eff; i += kSelThreads) {
+    const int32_t e = (int32_t)(~(uint32_t)sm.buf[i]);
+    sm.plist[i] = e;
+    atomicOr(&kept[e >> 5], 1u << (e & 31));
+  }
+  __syncthreads();
 }
 
 // Wave 0 finds the digit whose bucket holds the kk-th largest key.
@@ -324,9 +357,10 @@ __device__ void radix_top(const Level& L, int64_t m, int32_t k_eff, SelectShared
 
 // When only P < k_eff candidates score above zero, the lowest-index rows
 // scoring exactly 0 (masked, or live with zero affinity) take slots
-// P .. k_eff-1 of sm.buf in index order.
+// P .. k_eff-1 of sm.buf in index order (recorded as parents when `kept`
+// is set).
 template <bool STG>
-__device__ void fill_zeros(const Level& L, SelectShared& sm, int32_t P, int32_t k_eff) {
+__device__ void fill_zeros(const Level& L, SelectShared& sm, int32_t P, int32_t k_eff, uint32_t* kept) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
@@ -344,7 +378,7 @@ __device__ void fill_zeros(const Level& L, SelectShared& sm, int32_t P, int32_t 
       tot += sm.wave_tot[w];
     }
     const int32_t rank = found + before + (int32_t)__popcll(bal & lt_mask);
-    if (zero && rank < need) sm.buf[P + rank] = composite(0u, e);
+    if (zero && rank < need) put_kept(sm, P + rank, composite(0u, e), kept);
     found += tot;
     __syncthreads();
   }
@@ -480,14 +514,14 @@ __device__ int32_t select_flat_staged(const Level& L, int32_t m, int32_t k_eff, 
     if (take <= 64) sort_desc_small(sm, take);
     else sort_desc(sm, take);
   }
-  if (P < k_eff) fill_zeros<true>(L, sm, P, k_eff);
+  if (P < k_eff) fill_zeros<true>(L, sm, P, k_eff, nullptr);
   return k_eff;
 }
 
 // Keeps the top min(k, n) elements of a level with more candidates than
 // threads, sorted, in sm.buf.  sm.cnt[L.slot] must be zero on entry.
 template <bool STG>
-__device__ int32_t select_level_big(const Level& L, int32_t k, SelectShared& sm) {
+__device__ int32_t select_big_sorted(const Level& L, int32_t k, SelectShared& sm) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
@@ -525,7 +559,16 @@ __device__ int32_t select_level_big(const Level& L, int32_t k, SelectShared& sm)
     rank_compacted(sm, P, k_eff);
     if (P >= k_eff) return k_eff;
   }
-  fill_zeros<STG>(L, sm, P, k_eff);
+  fill_zeros<STG>(L, sm, P, k_eff, nullptr);
+  return k_eff;
+}
+
+// select_big_sorted, then (on a level that parents the next one) its
+// results recorded as parents.
+template <bool STG>
+__device__ int32_t select_level_big(const Level& L, int32_t k, SelectShared& sm, uint32_t* kept) {
+  const int32_t k_eff = select_big_sorted<STG>(L, k, sm);
+  if (kept) keep_parents(sm, k_eff, kept);
   return k_eff;
 }
 
@@ -538,34 +581,26 @@ __device__ __forceinline__ int32_t group_sum(int32_t v, int32_t n) {
   return v;
 }
 
-// Rank of key x of the run at g0 among NG strictly descending runs of 64:
-// its rank r in its own run plus, for every other run, how many of its keys
-// exceed x.  That count comes from two rounds of independent LDS reads: the
-// run's 8 block-end pivots (every eighth key; the same addresses for the
-// whole wave) give the block, then the block's 8 keys give the position.
-// g0 is uniform over the wave.
-template <int NG>
-__device__ __forceinline__ int32_t merged_rank(const uint64_t* runs, int32_t g0, uint64_t x, int32_t r) {
-  int32_t c[NG];
+// Keys of the strictly descending run g that exceed x, from two rounds of
+// 16-byte LDS reads: the run's 8 block-end keys give the number c of whole
+// blocks of 8 above x (the same addresses for every lane counting run g),
+// then the 8 keys of block c give the position inside it.
+__device__ __forceinline__ int32_t run_count_above(const SortedRuns& R, int32_t g, uint64_t x) {
+  const u64x2* pv = reinterpret_cast<const u64x2*>(R.piv + 8 * g);
+  int32_t c = 0;
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    c[g] = 0;
-    if ((g << 6) == g0) continue;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) c[g] += (int32_t)(runs[(g << 6) + 8 * p + 7] > x);
+  for (int p = 0; p < 4; ++p) {
+    const u64x2 v = pv[p];
+    c += (int32_t)(v.x > x) + (int32_t)(v.y > x);
   }
-  int32_t R = r;
+  const u64x2* bk = reinterpret_cast<const u64x2*>(R.key + 64 * g + 8 * (c < 8 ? c : 7));
+  int32_t f = 0;
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    if ((g << 6) == g0) continue;
-    // keys 0 .. 8c-1 exceed x; the block of 8 at 8c holds the boundary
-    const uint64_t* blk = runs + (g << 6) + 8 * (c[g] < 8 ? c[g] : 7);
-    int32_t f = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f += (int32_t)(blk[i] > x);
-    R += c[g] == 8 ? 64 : 8 * c[g] + f;
+  for (int p = 0; p < 4; ++p) {
+    const u64x2 v = bk[p];
+    f += (int32_t)(v.x > x) + (int32_t)(v.y > x);
   }
-  return R;
+  return c == 8 ? 64 : 8 * c + f;
 }
 
 // Lanes that share one key when NG groups of 64 keys are ranked by
@@ -579,20 +614,21 @@ constexpr int rank_tpc(int ng) {
 // Keeps the top k_eff of a level's 64 < m <= NG * 64 candidates, sorted,
 // in sm.buf.  Candidate keys go to LDS in NG groups of 64 (slots past the
 // candidates hold distinct keys below every real one); TPC lanes rank each
-// key within its group, each comparing a fixed strided share; each group is
-// written back as a strictly descending run and a key's rank in the level
-// is its rank in its group plus, for every other group, how many keys of
-// that run exceed it (merged_rank).  Keys without a positive score rank
-// below all positive ones and are never kept here (the zero fill handles
-// them).
+// key within its group, each comparing a contiguous share; each group is
+// written back as a strictly descending run (with its block-end keys) and
+// a key's rank in the level is the number of keys above it summed over all
+// runs, its own included (run_count_above), the runs split among its TPC
+// lanes.  Keys without a positive score rank below all positive ones and
+// are never kept here (the zero fill handles them).
 template <bool STG, int NG>
-__device__ int32_t select_small(const Level& L, int32_t m, int32_t k_eff, SelectShared& sm) {
+__device__ int32_t select_small(const Level& L, int32_t m, int32_t k_eff, SelectShared& sm, uint32_t* kept) {
   constexpr int TPC = rank_tpc(NG);
-  static_assert(NG >= 2 && NG * 64 * TPC <= kSelThreads && 64 % (8 * TPC) == 0, "rank layout");
+  constexpr int SPAN = 64 / TPC;            // keys of its group one lane compares
+  constexpr int RPL = (NG + TPC - 1) / TPC;  // runs one lane counts in
+  static_assert(NG >= 2 && NG * 64 * TPC <= kSelThreads && SPAN % 8 == 0, "rank layout");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  uint64_t* keys = sm.ck;    // [NG * 64] candidate keys by candidate index
-  uint64_t* runs = sm.run;   // [NG * 64] the same keys, each group sorted
+  uint64_t* keys = sm.ck;  // [NG * 64] candidate keys by candidate index
   // phase A: candidate keys
   {
     const int32_t e = tid < m ? cand32(L, sm, tid) : -1;
@@ -612,25 +648,36 @@ __device__ int32_t select_small(const Level& L, int32_t m, int32_t k_eff, Select
   const int32_t ic = active ? i : 0;
   const int32_t g0 = __builtin_amdgcn_readfirstlane((ic >> 6) << 6);
   const uint64_t x = keys[ic];
+  const u64x2* share = reinterpret_cast<const u64x2*>(keys + g0 + q * SPAN);
   int32_t r = 0;
 #pragma unroll
-  for (int j = 0; j < 64 / TPC; j += 8) {
-    uint64_t y[8];
+  for (int j = 0; j < SPAN / 2; j += 4) {
+    u64x2 y[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) y[u] = keys[g0 + q + (j + u) * TPC];
+    for (int u = 0; u < 4; ++u) y[u] = share[j + u];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) r += (int32_t)(y[u] > x);
+    for (int u = 0; u < 4; ++u) r += (int32_t)(y[u].x > x) + (int32_t)(y[u].y > x);
   }
   r = group_sum(r, TPC);
-  if (active && q == 0) runs[g0 + r] = x;
-  __syncthreads();
-  // phase C: rank in the level, positive keys only
-  if (active && q == 0 && (x >> 32) != 0ull) {
-    const int32_t R = merged_rank<NG>(runs, g0, x, r);
-    if (R < k_eff) sm.buf[R] = x;
+  if (active && q == 0) {
+    sm.runs.key[g0 + r] = x;
+    if ((r & 7) == 7) sm.runs.piv[(g0 >> 3) + (r >> 3)] = x;
   }
   __syncthreads();
-  if (P < k_eff) fill_zeros<STG>(L, sm, P, k_eff);
+  // phase C: rank in the level; lane q counts in runs q, q + TPC, ...
+  if (active) {
+    int32_t R = 0;
+#pragma unroll
+    for (int t = 0; t < RPL; ++t) {
+      const int32_t g = q + t * TPC;
+      const int32_t above = run_count_above(sm.runs, g < NG ? g : NG - 1, x);
+      R += g < NG ? above : 0;
+    }
+    R = group_sum(R, TPC);
+    if (q == 0 && (x >> 32) != 0ull && R < k_eff) put_kept(sm, R, x, kept);
+  }
+  __syncthreads();
+  if (P < k_eff) fill_zeros<STG>(L, sm, P, k_eff, kept);
   return k_eff;
 }
 
@@ -641,7 +688,7 @@ __device__ int32_t select_small(const Level& L, int32_t m, int32_t k_eff, Select
 // exceed that lane's key, reading them with register broadcasts; the waves'
 // counts are summed through LDS.  A key's total count is its rank.
 template <bool STG>
-__device__ int32_t select_one_group(const Level& L, int32_t m, int32_t k_eff, SelectShared& sm) {
+__device__ int32_t select_one_group(const Level& L, int32_t m, int32_t k_eff, SelectShared& sm, uint32_t* kept) {
   constexpr int W = kSelThreads / 64;  // waves
   constexpr int J = 64 / W;            // lanes each wave compares against
   static_assert(W * J == 64, "wave layout");
@@ -667,46 +714,37 @@ __device__ int32_t select_one_group(const Level& L, int32_t m, int32_t k_eff, Se
     int32_t r = 0;
 #pragma unroll
     for (int w = 0; w < W; ++w) r += sm.part[w][lane];
-    if (xhi != 0u && r < k_eff) sm.buf[r] = x;
+    if (xhi != 0u && r < k_eff) put_kept(sm, r, x, kept);
   }
   __syncthreads();
-  if (P < k_eff) fill_zeros<STG>(L, sm, P, k_eff);
+  if (P < k_eff) fill_zeros<STG>(L, sm, P, k_eff, kept);
   return k_eff;
 }
 
 // Picks the group count: the smallest NG >= 2 with m <= NG * 64.
 template <bool STG, int NG>
-__device__ __forceinline__ int32_t select_small_ng(const Level& L, int32_t m, int32_t k_eff, SelectShared& sm) {
+__device__ __forceinline__ int32_t select_small_ng(const Level& L, int32_t m, int32_t k_eff, SelectShared& sm,
+                                                   uint32_t* kept) {
   if constexpr (NG * 64 < kSelThreads) {
-    if (m > NG * 64) return select_small_ng<STG, NG + 1>(L, m, k_eff, sm);
+    if (m > NG * 64) return select_small_ng<STG, NG + 1>(L, m, k_eff, sm, kept);
   }
-  return select_small<STG, NG>(L, m, k_eff, sm);
+  return select_small<STG, NG>(L, m, k_eff, sm, kept);
 }
 
 // Keeps the top min(k, n) elements of a level, sorted, in sm.buf: levels
 // with at most kSelThreads candidates are ranked, larger ones compacted and
-// ranked or radix-selected.
+// ranked or radix-selected.  With `kept` set (a level that parents the next
+// one) the kept elements are also recorded as the next level's parents: in
+// plist, in rank order, and as bits of `kept` (clear on entry).  Everything
+// is visible to the whole work-group on return.
 template <bool STG>
-__device__ int32_t select_level(const Level& L, int32_t k, SelectShared& sm) {
+__device__ int32_t select_level(const Level& L, int32_t k, SelectShared& sm, uint32_t* kept) {
   const int32_t k_eff = k < L.n ? k : L.n;
   if (k_eff <= 0) return 0;
   const int64_t m64 = L.fanout ? (int64_t)L.n_par * L.fanout : (int64_t)L.n;
-  if (m64 > kSelThreads) return select_level_big<STG>(L, k, sm);
-  if (m64 <= 64) return select_one_group<STG>(L, (int32_t)m64, k_eff, sm);
-  return select_small_ng<STG, 2>(L, (int32_t)m64, k_eff, sm);
-}
-
-// Records the kept elements of a level (sm.buf[0, k_eff)) as the parents of
-// the next level: their indices in plist and their bits in `kept` (clear on
-// entry).
-__device__ void keep_parents(SelectShared& sm, int32_t k_eff, uint32_t* kept) {
-  const int tid = threadIdx.x;
-  for (int32_t i = tid; i < k_eff; i += kSelThreads) {
-    const int32_t e = (int32_t)(~(uint32_t)sm.buf[i]);
-    sm.plist[i] = e;
-    atomicOr(&kept[e >> 5], 1u << (e & 31));
-  }
-  __syncthreads();
+  if (m64 > kSelThreads) return select_level_big<STG>(L, k, sm, kept);
+  if (m64 <= 64) return select_one_group<STG>(L, (int32_t)m64, k_eff, sm, kept);
+  return select_small_ng<STG, 2>(L, (int32_t)m64, k_eff, sm, kept);
 }
 
 struct SeqGeom {
@@ -803,8 +841,8 @@ __device__ __forceinline__ int32_t select_levels(const ScoreArgs& a, const SeqGe
   int32_t kp = 0;
   for (int32_t lev = a.hier ? 0 : 2; lev < 3; ++lev) {
     const Level L = make_level(a, g, lev, aff, kp, sm);
-    kp = select_level<STG>(L, lev == 0 ? a.k_g : (lev == 1 ? a.k_c : a.k_p), sm);
-    if (lev < 2) keep_parents(sm, kp, lev == 0 ? sm.kept_grid : sm.kept_chunk);
+    kp = select_level<STG>(L, lev == 0 ? a.k_g : (lev == 1 ? a.k_c : a.k_p), sm,
+                           lev == 0 ? sm.kept_grid : (lev == 1 ? sm.kept_chunk : nullptr));
   }
   return kp;
 }
@@ -1085,8 +1123,8 @@ __device__ __forceinline__ int32_t lazy_levels(const ScoreArgs& a, const SeqGeom
       }
     }
     __syncthreads();
-    kp = select_level<STG>(L, lev == 0 ? a.k_g : (lev == 1 ? a.k_c : a.k_p), sm);
-    if (lev < 2) keep_parents(sm, kp, lev == 0 ? sm.kept_grid : sm.kept_chunk);
+    kp = select_level<STG>(L, lev == 0 ? a.k_g : (lev == 1 ? a.k_c : a.k_p), sm,
+                           lev == 0 ? sm.kept_grid : (lev == 1 ? sm.kept_chunk : nullptr));
   }
   return kp;
 }
