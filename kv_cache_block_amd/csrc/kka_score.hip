@@ -682,40 +682,39 @@ __device__ int32_t select_small(const Level& L, int32_t m, int32_t k_eff, Select
 }
 
 // Keeps the top k_eff of a level of at most 64 candidates, sorted, in
-// sm.buf.  Every wave builds all the candidate keys in registers (lane =
-// candidate; lanes past the candidates hold distinct keys below every real
-// one) and counts, for each lane, how many keys of its share of the lanes
-// exceed that lane's key, reading them with register broadcasts; the waves'
-// counts are summed through LDS.  A key's total count is its rank.
+// sm.buf.  Every wave builds the 64 candidate keys (lane = candidate; lanes
+// past the candidates hold distinct keys below every real one) and stores
+// them to a copy of its own in LDS; then each wave ranks its share of the
+// candidates: W lanes share a key, each counting the larger keys among a
+// contiguous share of the copy, and a DPP sum over the W lanes gives the
+// rank, which is the key's result slot.  One barrier per level.
 template <bool STG>
 __device__ int32_t select_one_group(const Level& L, int32_t m, int32_t k_eff, SelectShared& sm, uint32_t* kept) {
-  constexpr int W = kSelThreads / 64;  // waves
-  constexpr int J = 64 / W;            // lanes each wave compares against
-  static_assert(W * J == 64, "wave layout");
+  constexpr int W = kSelThreads / 64;  // waves = lanes per key
+  constexpr int CPW = 64 / W;          // keys each wave ranks = keys each lane compares
+  static_assert(W * CPW == 64 && W <= 8 && CPW % 4 == 0, "wave layout");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = tid >> 6;
   const int32_t e = lane < m ? cand32(L, sm, lane) : -1;
   const uint32_t key = e >= 0 ? aff_key<STG>(L, sm, e) : 0u;
-  const uint64_t x = e >= 0 ? composite(key, e) : (uint64_t)lane;
   const int32_t P = (int32_t)__popcll(__ballot(key != 0u));
-  const uint32_t xlo = (uint32_t)x, xhi = (uint32_t)(x >> 32);
-  int32_t c = 0;
+  uint64_t* copy = sm.ck + 64 * wave;
+  copy[lane] = e >= 0 ? composite(key, e) : (uint64_t)lane;
+  // lanes of this wave read each other's stores: wave-scope synchronisation
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint64_t x = copy[CPW * wave + lane / W];
+  const u64x2* share = reinterpret_cast<const u64x2*>(copy + CPW * (lane % W));
+  int32_t r = 0;
 #pragma unroll
-  for (int jj = 0; jj < J; ++jj) {
-    const int j = wave * J + jj;
-    const uint64_t y = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)xhi, j) << 32) |
-                       (uint32_t)__builtin_amdgcn_readlane((int)xlo, j);
-    c += (int32_t)(y > x);
+  for (int u = 0; u < CPW / 2; ++u) {
+    const u64x2 y = share[u];
+    r += (int32_t)(y.x > x) + (int32_t)(y.y > x);
   }
-  sm.part[wave][lane] = c;
-  __syncthreads();
-  if (wave == 0) {
-    int32_t r = 0;
-#pragma unroll
-    for (int w = 0; w < W; ++w) r += sm.part[w][lane];
-    if (xhi != 0u && r < k_eff) put_kept(sm, r, x, kept);
-  }
+  r = group_sum(r, W);
+  if (lane % W == 0 && (x >> 32) != 0ull && r < k_eff) put_kept(sm, r, x, kept);
   __syncthreads();
   if (P < k_eff) fill_zeros<STG>(L, sm, P, k_eff, kept);
   return k_eff;
@@ -1009,7 +1008,8 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 // affinity stores have completed) selects that sequence.  Other sequences'
 // tiles keep streaming meanwhile, and the selection needs no second launch.
 template <int LPR, int NQ, int R, bool STAB>
-__global__ __launch_bounds__(kSelThreads) void score_select_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(NQ * R <= 8 ? 4 : 1)))
+void score_select_kernel(ScoreArgs a) {
   __shared__ SelectShared sm;
   constexpr int NG = kSelThreads / LPR;  // row groups per work-group
   const int tid = threadIdx.x;
