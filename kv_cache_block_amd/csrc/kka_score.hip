@@ -612,14 +612,15 @@ constexpr int rank_tpc(int ng) {
 }
 
 // Keeps the top k_eff of a level's 64 < m <= NG * 64 candidates, sorted,
-// in sm.buf.  Candidate keys go to LDS in NG groups of 64 (slots past the
-// candidates hold distinct keys below every real one); TPC lanes rank each
-// key within its group, each comparing a contiguous share; each group is
-// written back as a strictly descending run (with its block-end keys) and
-// a key's rank in the level is the number of keys above it summed over all
-// runs, its own included (run_count_above), the runs split among its TPC
-// lanes.  Keys without a positive score rank below all positive ones and
-// are never kept here (the zero fill handles them).
+// in sm.buf.  The candidates form NG groups of 64 (slots past the
+// candidates hold distinct keys below every real one).  TPC waves rank a
+// group: each stores the group's keys to a copy of its own in LDS, and TPC
+// lanes rank each key within the group, each comparing a contiguous share.
+// Each group is written back as a strictly descending run (with its
+// block-end keys) and a key's rank in the level is the number of keys above
+// it summed over all runs, its own included (run_count_above), the runs
+// split among its TPC lanes.  Keys without a positive score rank below all
+// positive ones and are never kept here (the zero fill handles them).
 template <bool STG, int NG>
 __device__ int32_t select_small(const Level& L, int32_t m, int32_t k_eff, SelectShared& sm, uint32_t* kept) {
   constexpr int TPC = rank_tpc(NG);
@@ -628,50 +629,51 @@ __device__ int32_t select_small(const Level& L, int32_t m, int32_t k_eff, Select
   static_assert(NG >= 2 && NG * 64 * TPC <= kSelThreads && SPAN % 8 == 0, "rank layout");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  uint64_t* keys = sm.ck;  // [NG * 64] candidate keys by candidate index
-  // phase A: candidate keys
-  {
-    const int32_t e = tid < m ? cand32(L, sm, tid) : -1;
+  const int32_t g = wave / TPC;   // group this wave ranks
+  const bool active = g < NG;     // whole waves
+  const int32_t q = lane % TPC;   // this lane's share of its key's comparisons
+  uint64_t x = 0;
+  if (active) {
+    const int32_t c = 64 * g + lane;
+    const int32_t e = c < m ? cand32(L, sm, c) : -1;
     const uint32_t key = e >= 0 ? aff_key<STG>(L, sm, e) : 0u;
-    if (tid < NG * 64) keys[tid] = e >= 0 ? composite(key, e) : (uint64_t)tid;
     const uint64_t bal = __ballot(key != 0u);
-    if (lane == 0) sm.wave_tot[wave] = (int32_t)__popcll(bal);
+    if (lane == 0 && wave % TPC == 0) sm.wave_tot[g] = (int32_t)__popcll(bal);
+    uint64_t* copy = sm.ck + 64 * wave;
+    copy[lane] = e >= 0 ? composite(key, e) : (uint64_t)c;
+    // lanes of this wave read each other's stores: wave-scope synchronisation
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // the wave's 64 / TPC keys are consecutive in the group
+    x = copy[SPAN * (wave % TPC) + lane / TPC];
+    const u64x2* share = reinterpret_cast<const u64x2*>(copy + q * SPAN);
+    int32_t r = 0;
+#pragma unroll
+    for (int j = 0; j < SPAN / 2; j += 4) {
+      u64x2 y[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) y[u] = share[j + u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) r += (int32_t)(y[u].x > x) + (int32_t)(y[u].y > x);
+    }
+    r = group_sum(r, TPC);
+    if (q == 0) {
+      sm.runs.key[64 * g + r] = x;
+      if ((r & 7) == 7) sm.runs.piv[8 * g + (r >> 3)] = x;
+    }
   }
   __syncthreads();
   int32_t P = 0;
-  for (int w = 0; w < kSelThreads / 64; ++w) P += sm.wave_tot[w];
-  // phase B: rank within the group.  Active threads form whole waves
-  // (NG * 64 * TPC is a multiple of 64), and a wave's 64 / TPC keys lie in
-  // one group, so the group base is uniform over the wave.
-  const int32_t i = tid / TPC, q = tid % TPC;
-  const bool active = i < NG * 64;
-  const int32_t ic = active ? i : 0;
-  const int32_t g0 = __builtin_amdgcn_readfirstlane((ic >> 6) << 6);
-  const uint64_t x = keys[ic];
-  const u64x2* share = reinterpret_cast<const u64x2*>(keys + g0 + q * SPAN);
-  int32_t r = 0;
-#pragma unroll
-  for (int j = 0; j < SPAN / 2; j += 4) {
-    u64x2 y[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) y[u] = share[j + u];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) r += (int32_t)(y[u].x > x) + (int32_t)(y[u].y > x);
-  }
-  r = group_sum(r, TPC);
-  if (active && q == 0) {
-    sm.runs.key[g0 + r] = x;
-    if ((r & 7) == 7) sm.runs.piv[(g0 >> 3) + (r >> 3)] = x;
-  }
-  __syncthreads();
-  // phase C: rank in the level; lane q counts in runs q, q + TPC, ...
+  for (int w = 0; w < NG; ++w) P += sm.wave_tot[w];
+  // rank in the level; lane q counts in runs q, q + TPC, ...
   if (active) {
     int32_t R = 0;
 #pragma unroll
     for (int t = 0; t < RPL; ++t) {
-      const int32_t g = q + t * TPC;
-      const int32_t above = run_count_above(sm.runs, g < NG ? g : NG - 1, x);
-      R += g < NG ? above : 0;
+      const int32_t gg = q + t * TPC;
+      const int32_t above = run_count_above(sm.runs, gg < NG ? gg : NG - 1, x);
+      R += gg < NG ? above : 0;
     }
     R = group_sum(R, TPC);
     if (q == 0 && (x >> 32) != 0ull && R < k_eff) put_kept(sm, R, x, kept);
