@@ -25,8 +25,9 @@
 // affinity rows are staged into LDS in one round of loads (sequences of
 // more than kLdsRows rows are selected from memory), then each level is
 // selected: up to 64 candidates (children of kept parents, or every row)
-// are ranked from registers, up to 512 in LDS groups of 64 that are ranked
-// and merged, larger sets are compacted with wave ballots and ranked or
+// are ranked from per-wave LDS copies with one barrier, up to 512 in
+// groups of 64 that are ranked, written back as sorted runs and merged by
+// counting, larger sets are compacted with wave ballots and ranked or
 // radix-selected (MSB first).  A rank is the number of larger keys, so rank
 // < k places the element at its final position.  Keys are (affinity bits
 // << 32 | ~index): unique, and larger means higher score then lower index.
