@@ -717,3 +717,59 @@ def test_flat_selection_many_rows_few_positive(K):
         assert int(cnt[s]) == len(ridx)
         np.testing.assert_array_equal(idx[s].cpu().numpy()[:len(ridx)], ridx)
         np.testing.assert_array_equal(sc[s].cpu().numpy()[:len(ridx)].view(np.uint32), rsc.view(np.uint32))
+
+
+# page counts at the edges of the 65-512 candidate ranking path: 2 to 8
+# groups of 64, each group count with a ragged, a full and a just-started
+# last group
+GROUP_EDGES = [65, 100, 127, 128, 129, 191, 192, 193, 255, 256, 257, 319, 320, 321, 383, 384, 385, 447, 448,
+               449, 511, 512]
+
+
+@pytest.mark.parametrize("K", [1, 17, 64, 200])
+@pytest.mark.parametrize("reps", [1, 8])
+def test_flat_selection_group_edges(K, reps):
+    """Flat levels of 65-512 pages (every group count of the ranking path
+    and the edges between them) with exact ties, exact 0 and exact 0.5
+    affinities: integer-valued vectors, some exactly opposite the anchor,
+    some zero.  reps = 8 repeats the batch so that it takes the two-launch
+    path; bit-exact against the oracle's selection of the GPU's own
+    affinities."""
+    say(f"flat group edges K={K} reps={reps}")
+    base = len(GROUP_EDGES)
+    S, NP, D = base * reps, 512, 8
+    lay = kka.LevelLayout(S, NP, D, False, 16, 16)
+    rng = np.random.default_rng(71 + K)
+    anc = np.zeros((S, D), np.float32)
+    anc[:, 0] = 1.0
+    anc[:, 1] = 1.0
+    lvl = np.zeros((S, lay.rows_per_seq, D), np.float32)
+    lvl[:, :NP] = rng.integers(-1, 2, (S, NP, D)).astype(np.float32)
+    for s in range(S):
+        opp = rng.permutation(NP)[:NP // 3]
+        lvl[s, opp] = 0.0
+        lvl[s, opp, 0] = -1.0
+        lvl[s, opp, 1] = -1.0  # cos = -1 exactly: affinity 0
+        lvl[s, rng.permutation(NP)[:5]] = 0.0  # zero norm: affinity 0.5
+    n_pages = np.array([GROUP_EDGES[s % base] for s in range(S)], np.int32)
+    level = torch.from_numpy(lvl).cuda()
+    npg = torch.from_numpy(n_pages).cuda()
+    anchors = torch.from_numpy(anc).cuda()
+    idx = torch.full((S, K), -9, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((S, K), dtype=torch.float32, device="cuda")
+    cnt = torch.zeros((S,), dtype=torch.int32, device="cuda")
+    aff = torch.zeros((S, NP), dtype=torch.float32, device="cuda")
+    kka.kka_score_topk(lay, level, npg, anchors, k_page=K, page_idx_out=idx, page_score_out=sc,
+                       n_selected_out=cnt, affinity_out=aff)
+    torch.cuda.synchronize()
+    af = aff.cpu().numpy()
+    gi, gs = idx.cpu().numpy(), sc.cpu().numpy()
+    for s in range(S):
+        n = int(n_pages[s])
+        np.testing.assert_allclose(af[s, :n], oracle.affinity(lvl[s, :n], anc[s]), atol=ATOL, rtol=0)
+        ridx, rsc = oracle.select(af[s, :n], hierarchical=0, k_page=K)
+        assert int(cnt[s]) == len(ridx) == min(K, n)
+        np.testing.assert_array_equal(gi[s, :len(ridx)], ridx, err_msg=f"s={s} n={n}")
+        np.testing.assert_array_equal(gs[s, :len(ridx)].view(np.uint32), rsc.view(np.uint32))
+        if K > n:
+            assert (gi[s, n:] == -1).all()
