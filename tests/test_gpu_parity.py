@@ -719,18 +719,18 @@ def test_flat_selection_many_rows_few_positive(K):
         np.testing.assert_array_equal(sc[s].cpu().numpy()[:len(ridx)].view(np.uint32), rsc.view(np.uint32))
 
 
-# page counts at the edges of the 65-512 candidate ranking path: 2 to 8
-# groups of 64, each group count with a ragged, a full and a just-started
-# last group
-GROUP_EDGES = [65, 100, 127, 128, 129, 191, 192, 193, 255, 256, 257, 319, 320, 321, 383, 384, 385, 447, 448,
-               449, 511, 512]
+# page counts at the edges of the ranking paths: one group of up to 64, and
+# 2 to 8 groups of 64, each group count with a ragged, a full and a
+# just-started last group
+GROUP_EDGES = [1, 2, 7, 8, 9, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 191, 192, 193, 255, 256, 257, 319, 320,
+               321, 383, 384, 385, 447, 448, 449, 511, 512]
 
 
 @pytest.mark.parametrize("K", [1, 17, 64, 200])
 @pytest.mark.parametrize("reps", [1, 8])
 def test_flat_selection_group_edges(K, reps):
-    """Flat levels of 65-512 pages (every group count of the ranking path
-    and the edges between them) with exact ties, exact 0 and exact 0.5
+    """Flat levels of 1-512 pages (one group, every group count of the
+    ranking path and the edges between them) with exact ties, exact 0 and exact 0.5
     affinities: integer-valued vectors, some exactly opposite the anchor,
     some zero.  reps = 8 repeats the batch so that it takes the two-launch
     path; bit-exact against the oracle's selection of the GPU's own
