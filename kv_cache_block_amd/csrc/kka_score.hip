@@ -753,9 +753,10 @@ struct SeqGeom {
   int32_t n_p, n_c, n_g;
 };
 
-__device__ __forceinline__ SeqGeom seq_geom(const ScoreArgs& a, int32_t s, bool report) {
+// Level sizes of a sequence of n_p pages (the value read from a.n_pages).
+__device__ __forceinline__ SeqGeom geom_of(const ScoreArgs& a, int32_t n_p, bool report) {
   SeqGeom g;
-  g.n_p = a.n_pages[s];
+  g.n_p = n_p;
   if (g.n_p < 0 || g.n_p > a.max_pages) {
     if (report) raise_err(a.err, KKA_DEVERR_PAGES);
     g.n_p = g.n_p < 0 ? 0 : a.max_pages;
@@ -763,6 +764,10 @@ __device__ __forceinline__ SeqGeom seq_geom(const ScoreArgs& a, int32_t s, bool 
   g.n_c = a.hier ? (g.n_p + a.ppc - 1) / a.ppc : 0;
   g.n_g = a.hier ? (g.n_c + a.cpg - 1) / a.cpg : 0;
   return g;
+}
+
+__device__ __forceinline__ SeqGeom seq_geom(const ScoreArgs& a, int32_t s, bool report) {
+  return geom_of(a, a.n_pages[s], report);
 }
 
 // Copies a sequence's whole affinity row block src[0, n) (n <= kLdsRows)
@@ -1088,41 +1093,68 @@ void score_select_kernel(ScoreArgs a) {
   select_sequence(a, s, sm);
 }
 
+// Affinity v of element e of a level (lazy scoring) to LDS (STG) or to
+// `aff`, and to `out` when it is set.
+template <bool STG>
+__device__ __forceinline__ void lazy_put(const Level& L, int32_t e, float v, float* aff, float* out, SelectShared& sm) {
+  if constexpr (STG) sm.aff[L.off + e] = v;
+  else store_aff(aff + L.off + e, v);
+  if (out) out[L.off + e] = v;
+}
+
 // Lazy hierarchical scoring: one work-group per sequence scores the grids,
 // selects, scores only the chunks of kept grids, selects, scores only the
 // pages of kept chunks and selects (the page's coarse-to-fine order).  Rows
 // under unkept parents are never read; their score is +0 by definition, so
 // the selection equals the one over every row.  Scored affinities land in
 // LDS when the sequence's rows fit (STG), else in `a.aff`; when `lazy_out`
-// is set they are also written there (other rows untouched).
-template <bool STG, int LPR, int NQ, int R>
-__device__ __forceinline__ int32_t lazy_levels(const ScoreArgs& a, const SeqGeom& g, const f32x4* seq, float* aff, float* out,
-                               const AnchorRegs<LPR, NQ>& A, SelectShared& sm) {
+// is set they are also written there (other rows untouched).  With EARLY,
+// v0 holds the affinities of the first pass of rows of the first scored
+// level (grids, or the pages of a flat layout), scored by the caller (the
+// widest rows, 16 pieces per lane, keep the plain order: their registers
+// are full).
+template <bool STG, bool EARLY, int LPR, int NQ, int R>
+__device__ __forceinline__ int32_t lazy_levels(const ScoreArgs& a, const SeqGeom& g, const f32x4* seq, float* aff,
+                                               float* out, const AnchorRegs<LPR, NQ>& A, SelectShared& sm,
+                                               const float (&v0)[R]) {
   constexpr int NG = kSelThreads / LPR;
   const int tid = threadIdx.x;
   const int32_t grp = tid / LPR, lg = tid % LPR;
   const int32_t Q = a.D >> 2;
+  const int32_t lev0 = a.hier ? 0 : 2;
+  Level L = make_level(a, g, lev0, aff, 0, sm);
+  int32_t c_start = grp;
+  if constexpr (EARLY) {
+    // the first pass of the first level, from v0 (no parents: element = candidate)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int32_t c = grp + NG * r;
+      if (lg == 0 && c < L.n) lazy_put<STG>(L, c, v0[r], aff, out, sm);
+    }
+    c_start += NG * R;
+  }
   int32_t kp = 0;
-  for (int32_t lev = 0; lev < 3; ++lev) {
-    const Level L = make_level(a, g, lev, aff, kp, sm);
+  for (int32_t lev = lev0; lev < 3; ++lev) {
+    if (lev != lev0) {
+      L = make_level(a, g, lev, aff, kp, sm);
+      c_start = grp;
+    }
     const int32_t m = L.fanout ? L.n_par * L.fanout : L.n;
-    for (int32_t c0 = grp; c0 < m; c0 += NG * R) {
+    for (int32_t c0 = c_start; c0 < m; c0 += NG * R) {
       f32x4 x[R][NQ];
       int32_t e[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int32_t c = c0 + NG * r;
         e[r] = c < m ? cand32(L, sm, c) : -1;
+        // lanes past the candidates load row 0 (unconditional loads issue
+        // back to back; exec-masked ones measured 15 % slower on a batch)
         load_row<LPR, NQ>(seq + (int64_t)(L.off + (e[r] >= 0 ? e[r] : 0)) * Q, lg, Q, x[r]);
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const float v_aff = row_affinity<LPR, NQ>(x[r], A);
-        if (lg == 0 && e[r] >= 0) {
-          if constexpr (STG) sm.aff[L.off + e[r]] = v_aff;
-          else store_aff(aff + L.off + e[r], v_aff);
-          if (out) out[L.off + e[r]] = v_aff;
-        }
+        if (lg == 0 && e[r] >= 0) lazy_put<STG>(L, e[r], v_aff, aff, out, sm);
       }
     }
     __syncthreads();
@@ -1135,17 +1167,45 @@ __device__ __forceinline__ int32_t lazy_levels(const ScoreArgs& a, const SeqGeom
 template <int LPR, int NQ, int R>
 __global__ __launch_bounds__(kSelThreads) void lazy_kernel(ScoreArgs a, float* lazy_out) {
   __shared__ SelectShared sm;
+  constexpr int NG = kSelThreads / LPR;
   const int tid = threadIdx.x;
   const int32_t s = blockIdx.x;
-  const SeqGeom g = seq_geom(a, s, tid == 0);
+  const int32_t grp = tid / LPR, lg = tid % LPR;
+  const int32_t Q = a.D >> 2;
   const f32x4* seq = reinterpret_cast<const f32x4*>(a.lvl + (int64_t)s * a.rows_per_seq * a.D);
+  // The first scored level starts at a fixed row whatever the sequence's
+  // length, so its first pass of rows is requested together with the page
+  // count and the anchor, and scored as soon as they arrive; affinities of
+  // rows past the level's end (known from the page count) are dropped.
+  const int32_t n_p = a.n_pages[s];
+  const int32_t off0 = a.hier ? a.max_pages + a.c_cap : 0;
+  const int64_t cap0 = a.hier ? a.rows_per_seq - off0 : a.max_pages;
+  constexpr bool EARLY = NQ < 16;
+  float v0[R] = {};
+  if constexpr (EARLY) {
+    f32x4 x0[R][NQ];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int32_t c = grp + NG * r;
+      if (c < cap0) {
+        load_row<LPR, NQ>(seq + (int64_t)(off0 + c) * Q, lg, Q, x0[r]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) x0[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    const AnchorRegs<LPR, NQ> A0 = load_anchor<LPR, NQ>(a, s, lg);
+#pragma unroll
+    for (int r = 0; r < R; ++r) v0[r] = row_affinity<LPR, NQ>(x0[r], A0);
+  }
+  const AnchorRegs<LPR, NQ> A = load_anchor<LPR, NQ>(a, s, lg);
+  const SeqGeom g = geom_of(a, n_p, tid == 0);
   float* aff = a.aff + (int64_t)s * a.rows_per_seq;
   float* out = lazy_out ? lazy_out + (int64_t)s * a.rows_per_seq : nullptr;
-  const AnchorRegs<LPR, NQ> A = load_anchor<LPR, NQ>(a, s, tid % LPR);
   clear_select_state(a, g, sm);
   __syncthreads();
-  const int32_t kp = a.rows_per_seq <= kLdsRows ? lazy_levels<true, LPR, NQ, R>(a, g, seq, aff, out, A, sm)
-                                                : lazy_levels<false, LPR, NQ, R>(a, g, seq, aff, out, A, sm);
+  const int32_t kp = a.rows_per_seq <= kLdsRows ? lazy_levels<true, EARLY, LPR, NQ, R>(a, g, seq, aff, out, A, sm, v0)
+                                                : lazy_levels<false, EARLY, LPR, NQ, R>(a, g, seq, aff, out, A, sm, v0);
   write_selection(a, sm, s, kp);
 }
 
