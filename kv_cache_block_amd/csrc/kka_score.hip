@@ -82,10 +82,10 @@ struct SortedRuns {
 
 struct SelectShared {
   float aff[kLdsRows];
-  alignas(16) uint64_t ck[kRankMax];
+  alignas(16) uint64_t ck[kRankMax];   // compacted candidate keys, or 64 keys per wave (copies)
   union {
     SortedRuns runs;                      // levels of 65-512 candidates
-    int32_t part[kSelThreads / 64][64];   // per-wave counts (levels of up to 64)
+    int32_t part[kSelThreads / 64][64];   // per-wave counts (sorting up to 64 results)
   };
   uint64_t buf[kMaxK];
   uint32_t kept_grid[kBitmapWords];   // grids kept (parents of chunks)
