@@ -773,3 +773,45 @@ def test_flat_selection_group_edges(K, reps):
         np.testing.assert_array_equal(gs[s, :len(ridx)].view(np.uint32), rsc.view(np.uint32))
         if K > n:
             assert (gi[s, n:] == -1).all()
+
+
+@pytest.mark.parametrize("case", [
+    dict(hierarchical=1, k_grid=2, k_chunk=3, k_page=5, pages_per_chunk=4, chunks_per_grid=3),
+    dict(hierarchical=1, k_grid=5, k_chunk=8, k_page=20, pages_per_chunk=4, chunks_per_grid=3),
+])
+def test_parented_small_levels_many_sequences(case):
+    """A level of at most 64 candidates that both reads the parent list (its
+    candidates are children of kept parents) and rewrites it (its kept
+    elements parent the next level) must let every wave finish reading
+    before the list is rewritten.  4000 sequences of ragged lengths take the
+    selection launch (work-groups sharing a compute unit at different
+    phases), six calls, every sequence bit-exact against the oracle's
+    selection of the GPU's own affinities."""
+    say(f"parented small levels {case}")
+    S, max_pages, D = 4000, 60, 8
+    lay = kka.LevelLayout(S, max_pages, D, True, case["pages_per_chunk"], case["chunks_per_grid"])
+    rng = np.random.default_rng(83)
+    lvl = np.zeros((S, lay.rows_per_seq, D), np.float32)
+    lvl[:, :max_pages] = rng.standard_normal((S, max_pages, D), dtype=np.float32)
+    n_pages = rng.integers(1, max_pages + 1, S).astype(np.int32)
+    level = torch.from_numpy(lvl).cuda()
+    npg = torch.from_numpy(n_pages).cuda()
+    kka.kka_build_levels(lay, level, npg)
+    anchors = torch.from_numpy(rng.standard_normal((S, D), dtype=np.float32)).cuda()
+    K = case["k_page"]
+    idx = torch.full((S, K), -9, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((S, K), dtype=torch.float32, device="cuda")
+    aff = torch.zeros((S, lay.rows_per_seq), dtype=torch.float32, device="cuda")
+    for call in range(6):
+        kka.kka_score_topk(lay, level, npg, anchors, k_page=K, k_grid=case["k_grid"], k_chunk=case["k_chunk"],
+                           page_idx_out=idx, page_score_out=sc, affinity_out=aff)
+        torch.cuda.synchronize()
+        af, gi, gs = aff.cpu().numpy(), idx.cpu().numpy(), sc.cpu().numpy()
+        for s in range(S):
+            n_p = int(n_pages[s])
+            n_c = -(-n_p // case["pages_per_chunk"])
+            n_g = -(-n_c // case["chunks_per_grid"])
+            ridx, rsc = oracle.select(af[s, :n_p], af[s, lay.chunk_row0:lay.chunk_row0 + n_c],
+                                      af[s, lay.grid_row0:lay.grid_row0 + n_g], **case)
+            np.testing.assert_array_equal(gi[s, :len(ridx)], ridx, err_msg=f"call={call} s={s}")
+            np.testing.assert_array_equal(gs[s, :len(ridx)].view(np.uint32), rsc.view(np.uint32))
