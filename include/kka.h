@@ -68,8 +68,9 @@ typedef enum kka_status {
 #define KKA_DEVERR_ROW 4u         /* a block's index in its sequence >= vb_seq_stride      */
 #define KKA_DEVERR_PAGES 8u       /* n_pages[s] < 0 or > max_pages                         */
 #define KKA_DEVERR_OFFSETS 16u    /* block_offsets not nondecreasing / total mismatch      */
-#define KKA_DEVERR_WORKSPACE 32u  /* a scoring workspace's tile counter was not zero at a   */
-                                  /* one-launch kka_score_topk call (see its workspace)    */
+#define KKA_DEVERR_WORKSPACE 32u  /* a workspace's arrival counter was not zero when a     */
+                                  /* call used it (kka_score_topk, kka_pool_blocks,         */
+                                  /* kka_pool_anchor: see their workspace)                  */
 
 /*
  * Paged key pool.  Element (layer l, physical block p, token slot t,
@@ -144,7 +145,18 @@ typedef enum kka_weight_mode {
  *             sequence, e.g. the page rows of a level buffer) or to row b
  *             (vb_seq_stride == 0); a row is head_dim floats.
  * workspace   device, 16-byte aligned, >= kka_pool_blocks_workspace() bytes
- *             (may be NULL when that size is 0).
+ *             (may be NULL when that size is 0).  With fewer blocks than fill
+ *             the chip, a block's layers are split over several work-groups:
+ *             the workspace then starts with one uint32 arrival counter per
+ *             block (4 * blocks bytes, rounded up to 256), followed by the
+ *             shares' partial sums, and the work-group that finishes a
+ *             block's last share adds them (in split order) and writes v_b,
+ *             all in one launch.  The counters must be zero before the first
+ *             call that uses the workspace (allocate it zero-filled); every
+ *             call leaves them zero.  A counter found at or above the split
+ *             count raises KKA_DEVERR_WORKSPACE and that block's v_b is not
+ *             written (re-zero the counters).  Calls that run concurrently
+ *             must not share a workspace.
  */
 KKA_API kka_status kka_pool_blocks(const kka_kpool* kp, const kka_seqs* seqs, const int32_t* blocks, int32_t num_blocks,
                            int32_t mode, float* head_weight, float* vb_out, int64_t vb_seq_stride, void* workspace,
@@ -161,7 +173,10 @@ KKA_API size_t kka_pool_blocks_workspace(const kka_kpool* kp, const kka_seqs* se
  * head_weight device [num_seqs][L*H] or NULL for uniform pooling.
  * anchor_out  device [num_seqs][head_dim] fp32, 16-byte aligned; an empty
  *             window gives the zero vector.
- * workspace   >= kka_pool_anchor_workspace() bytes.
+ * workspace   >= kka_pool_anchor_workspace() bytes, 16-byte aligned (NULL
+ *             allowed when that size is 0); with a layer split, one uint32
+ *             arrival counter per sequence then the shares' partial sums,
+ *             with the same rules as kka_pool_blocks' workspace.
  * Rules: window >= 0.
  */
 KKA_API kka_status kka_pool_anchor(const kka_kpool* kp, const kka_seqs* seqs, int32_t window, const float* head_weight,
@@ -421,8 +436,10 @@ KKA_API const char* kka_status_string(kka_status s);
 
 /* Version of this header as major*10000 + minor*100 + patch.  0.2.0: the
  * kka_score_topk workspace holds per-sequence tile counters that must be
- * zero at first use. */
-#define KKA_VERSION 200
+ * zero at first use.  0.3.0: so do the kka_pool_blocks and kka_pool_anchor
+ * workspaces of layer-split launches (per-block / per-sequence arrival
+ * counters; the split shares are combined in the same launch). */
+#define KKA_VERSION 300
 
 /* Version of the loaded library, same encoding (equals KKA_VERSION when the
  * header and the library match). */

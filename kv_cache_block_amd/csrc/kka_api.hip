@@ -61,9 +61,12 @@ kka_status check_seqs(const kka_seqs* sq) {
   return KKA_OK;
 }
 
-// Byte layout of the pooling workspace.
+// Byte layout of the pooling workspace: layer-split pooling keeps one
+// arrival counter per item, then each (item, split)'s partial sums; variance
+// pooling keeps per-(block, layer, head) sums, sums of squares and fp64
+// per-(sequence, head) variances.
 struct PoolWs {
-  size_t partial = 0, q = 0, var = 0, total = 0;
+  size_t counters = 0, partial = 0, q = 0, var = 0, total = 0;
 };
 
 PoolWs pool_ws(const kka_kpool* kp, const kka_seqs* sq, int64_t items, int32_t mode) {
@@ -76,9 +79,12 @@ PoolWs pool_ws(const kka_kpool* kp, const kka_seqs* sq, int64_t items, int32_t m
     w.var = align256((size_t)sq->num_seqs * LH * sizeof(double));
   } else {
     const LayerSplit ls = layer_split(items, kp->num_layers);
-    if (ls.n_split > 1) w.partial = align256((size_t)items * ls.n_split * D * sizeof(float));
+    if (ls.n_split > 1) {
+      w.counters = align256((size_t)items * sizeof(uint32_t));
+      w.partial = align256((size_t)items * ls.n_split * D * sizeof(float));
+    }
   }
-  w.total = w.partial + w.q + w.var;
+  w.total = w.counters + w.partial + w.q + w.var;
   return w;
 }
 
@@ -202,7 +208,8 @@ kka_status kka_pool_blocks(const kka_kpool* kp, const kka_seqs* seqs, const int3
   const LayerSplit ls = layer_split(items, a.L);
   a.n_split = ls.n_split;
   a.lps = ls.lps;
-  a.partial = ls.n_split > 1 ? reinterpret_cast<float*>(wsb) : nullptr;
+  a.done = ls.n_split > 1 ? reinterpret_cast<uint32_t*>(wsb) : nullptr;
+  a.partial = ls.n_split > 1 ? reinterpret_cast<float*>(wsb + ws.counters) : nullptr;
   a.weights = mode == KKA_WEIGHT_GIVEN ? head_weight : nullptr;
   return launched(launch_pool(a, mode, s));
 }
@@ -388,11 +395,17 @@ kka_status kka_attention_topk(const kka_kpool* kp, const kka_seqs* seqs, const f
   return launched(launch_select(sa, strm));
 }
 
+// Anchor workspace of a layer split: one arrival counter per sequence, then
+// each (sequence, split)'s partial sums.
+static size_t anchor_counter_bytes(int32_t S) { return align256((size_t)S * sizeof(uint32_t)); }
+
 size_t kka_pool_anchor_workspace(const kka_kpool* kp, const kka_seqs* seqs, int32_t window) {
   (void)window;
   if (check_kpool(kp) != KKA_OK || check_seqs(seqs) != KKA_OK) return 0;
   const LayerSplit ls = layer_split(seqs->num_seqs, kp->num_layers);
-  return ls.n_split > 1 ? align256((size_t)seqs->num_seqs * ls.n_split * kp->head_dim * sizeof(float)) : 0;
+  if (ls.n_split <= 1) return 0;
+  return anchor_counter_bytes(seqs->num_seqs) +
+         align256((size_t)seqs->num_seqs * ls.n_split * kp->head_dim * sizeof(float));
 }
 
 kka_status kka_pool_anchor(const kka_kpool* kp, const kka_seqs* seqs, int32_t window, const float* head_weight,
@@ -418,7 +431,10 @@ kka_status kka_pool_anchor(const kka_kpool* kp, const kka_seqs* seqs, int32_t wi
   a.n_items = seqs->num_seqs;
   a.weights = head_weight;
   a.out = anchor_out;
-  a.partial = ls.n_split > 1 ? static_cast<float*>(workspace) : nullptr;
+  a.done = ls.n_split > 1 ? static_cast<uint32_t*>(workspace) : nullptr;
+  a.partial = ls.n_split > 1
+                  ? reinterpret_cast<float*>(static_cast<char*>(workspace) + anchor_counter_bytes(seqs->num_seqs))
+                  : nullptr;
   a.window = window;
   a.err = err;
   return launched(launch_anchor(a, static_cast<hipStream_t>(stream)));

@@ -79,6 +79,7 @@ struct PoolArgs {
   float* out;             // v_b rows / anchor rows
   int64_t vb_stride;      // rows per sequence in `out`, 0 = row is the global block id
   float* partial;         // layer-split partial sums, or per-(l,h) token sums
+  uint32_t* done;         // per-item arrival counters of a layer split (zero between calls)
   float* stats_q;         // per-(item, l, h) sums of squares
   uint32_t* err;
   PoolShape ps;
@@ -194,6 +195,41 @@ __device__ __forceinline__ int32_t find_seq(const int32_t* __restrict__ offs, in
 }
 
 __device__ __forceinline__ void raise_err(uint32_t* err, uint32_t bit) { atomicOr(err, bit); }
+
+// Values handed from one work-group to another inside one launch (work-
+// groups on any XCD, and each XCD has its own L2) are stored and loaded
+// with device-scope relaxed atomics, which write through and read past the
+// non-coherent L2, instead of paying a device-scope release fence (a whole-
+// L2 write-back) per work-group.  The handoff's order comes from the
+// hardware rather than from release / acquire: the producer waits for its
+// stores to be acknowledged (vmcnt 0) before its device-scope counter
+// increment (arrive), and the consumer loads only after its own increment
+// has returned the last count.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A work-group's arrival at the end of its share of an item split over n
+// work-groups, once all of its device-scope stores have completed: true in
+// every thread of the work-group that arrives last.  The counter wraps back
+// to 0 on that arrival, ready for the next launch; a counter found at n or
+// above (a workspace not zeroed before its first use) raises
+// KKA_DEVERR_WORKSPACE.  `flag` is a __shared__ word of the work-group.
+__device__ __forceinline__ bool arrive(uint32_t* done, uint32_t n, uint32_t* err, uint32_t& flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned top = n - 1u;
+    const unsigned old = atomicInc(done, top);
+    if (old > top) raise_err(err, KKA_DEVERR_WORKSPACE);
+    flag = old == top;
+  }
+  __syncthreads();
+  return flag != 0u;
+}
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already valid.

@@ -115,6 +115,22 @@ __device__ __forceinline__ void stash8(float* red, int tid, const float (&acc)[8
   r4[2 * tid + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
+// Sum over the n shares of a layer split, in split order, of the partial at
+// src + j * stride (device-scope loads, a batch of 8 issued before the first
+// add).
+__device__ __forceinline__ float split_sum(const float* src, int32_t n, int32_t stride) {
+  float sum = 0.f;
+  for (int32_t j0 = 0; j0 < n; j0 += 8) {
+    float t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = load_agent(src + (int64_t)min(j0 + u, n - 1) * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < n) sum += t[u];
+  }
+  return sum;
+}
+
 // ------------------------------------------------------------ v_b, one pass
 
 template <int MODE, int MAXT>
@@ -181,38 +197,21 @@ __global__ __launch_bounds__(MAXT) void pool_kernel(PoolArgs a) {
 
   stash8(red, tid, acc);
   __syncthreads();
-  for (int32_t d = tid; d < a.D; d += a.ps.nt) {
-    const float sum = column_sum(red, a.D, a.ps.nt, d);
-    if (a.n_split == 1) {
-      if (it.row >= 0) {
-        const float denom = MODE == kGiven ? (float)it.n_b : (float)((int64_t)it.n_b * LH);
-        a.out[it.row * a.D + d] = it.n_b > 0 ? sum / denom : 0.f;
-      }
-    } else {
-      a.partial[((int64_t)item * a.n_split + j) * a.D + d] = sum;
-    }
+  const float denom = MODE == kGiven ? (float)it.n_b : (float)((int64_t)it.n_b * LH);
+  if (a.n_split == 1) {
+    if (it.row >= 0)
+      for (int32_t d = tid; d < a.D; d += a.ps.nt)
+        a.out[it.row * a.D + d] = it.n_b > 0 ? column_sum(red, a.D, a.ps.nt, d) / denom : 0.f;
+    return;
   }
-}
-
-// Sums the layer-split partials of each item in split order.
-template <int MODE>
-__global__ __launch_bounds__(256) void pool_finish_kernel(PoolArgs a) {
-  const int32_t item = blockIdx.x;
-  const Item it = locate(a, item, false);
-  if (it.row < 0) return;
-  const int32_t LH = a.L * a.H;
-  for (int32_t d = threadIdx.x; d < a.D; d += blockDim.x) {
-    const float* src = a.partial + (int64_t)item * a.n_split * a.D + d;
-    float sum = 0.f;
-    for (int32_t j0 = 0; j0 < a.n_split; j0 += 8) {
-      float t[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) t[u] = src[(int64_t)min(j0 + u, a.n_split - 1) * a.D];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (j0 + u < a.n_split) sum += t[u];
-    }
-    const float denom = MODE == kGiven ? (float)it.n_b : (float)((int64_t)it.n_b * LH);
+  // layer split: the work-group that finishes the item's last share adds
+  // the shares' partial sums in split order
+  float* part = a.partial + (int64_t)item * a.n_split * a.D;
+  for (int32_t d = tid; d < a.D; d += a.ps.nt) store_agent(part + (int64_t)j * a.D + d, column_sum(red, a.D, a.ps.nt, d));
+  __shared__ uint32_t last;
+  if (!arrive(a.done + item, (uint32_t)a.n_split, a.err, last) || it.row < 0) return;
+  for (int32_t d = tid; d < a.D; d += a.ps.nt) {
+    const float sum = split_sum(part + d, a.n_split, a.D);
     a.out[it.row * a.D + d] = it.n_b > 0 ? sum / denom : 0.f;
   }
 }
@@ -506,37 +505,20 @@ __global__ __launch_bounds__(MAXT) void anchor_kernel(PoolArgs a) {
   if (bad_tab) raise_err(a.err, KKA_DEVERR_BLOCK_TABLE);
   stash8(red, tid, acc);
   __syncthreads();
-  for (int32_t d = tid; d < a.D; d += a.ps.nt) {
-    const float sum = column_sum(red, a.D, a.ps.nt, d);
-    if (a.n_split == 1) {
-      const float denom = MODE == kGiven ? (float)W : (float)((int64_t)W * LH);
-      a.out[(int64_t)s * a.D + d] = W > 0 ? sum / denom : 0.f;
-    } else {
-      a.partial[((int64_t)s * a.n_split + j) * a.D + d] = sum;
-    }
+  const float denom = MODE == kGiven ? (float)W : (float)((int64_t)W * LH);
+  if (a.n_split == 1) {
+    for (int32_t d = tid; d < a.D; d += a.ps.nt)
+      a.out[(int64_t)s * a.D + d] = W > 0 ? column_sum(red, a.D, a.ps.nt, d) / denom : 0.f;
+    return;
   }
-}
-
-// Sums each sequence's layer-split partials in split order (loads of a
-// batch of 8 splits are issued before the first add).
-template <int MODE>
-__global__ __launch_bounds__(256) void anchor_finish_kernel(PoolArgs a) {
-  const int32_t s = blockIdx.x;
-  const int32_t T = a.seq_len[s] > 0 ? a.seq_len[s] : 0;
-  const int32_t W = a.window < T ? a.window : T;
-  const int32_t LH = a.L * a.H;
-  for (int32_t d = threadIdx.x; d < a.D; d += blockDim.x) {
-    const float* src = a.partial + (int64_t)s * a.n_split * a.D + d;
-    float sum = 0.f;
-    for (int32_t j0 = 0; j0 < a.n_split; j0 += 8) {
-      float t[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) t[u] = src[(int64_t)min(j0 + u, a.n_split - 1) * a.D];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (j0 + u < a.n_split) sum += t[u];
-    }
-    const float denom = MODE == kGiven ? (float)W : (float)((int64_t)W * LH);
+  // layer split: the work-group that finishes the sequence's last share
+  // adds the shares' partial sums in split order
+  float* part = a.partial + (int64_t)s * a.n_split * a.D;
+  for (int32_t d = tid; d < a.D; d += a.ps.nt) store_agent(part + (int64_t)j * a.D + d, column_sum(red, a.D, a.ps.nt, d));
+  __shared__ uint32_t last;
+  if (!arrive(a.done + s, (uint32_t)a.n_split, a.err, last)) return;
+  for (int32_t d = tid; d < a.D; d += a.ps.nt) {
+    const float sum = split_sum(part + d, a.n_split, a.D);
     a.out[(int64_t)s * a.D + d] = W > 0 ? sum / denom : 0.f;
   }
 }
@@ -557,15 +539,7 @@ hipError_t launch_pool(const PoolArgs& a, int mode, hipStream_t st) {
       if (mode == kGiven) hipLaunchKernelGGL((pool_kernel<kGiven, 1024>), grid, block, dyn, st, a);
       else hipLaunchKernelGGL((pool_kernel<kUniform, 1024>), grid, block, dyn, st, a);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (a.n_split > 1) {
-      const dim3 fb((unsigned)small_block(a.D));
-      if (mode == kGiven) hipLaunchKernelGGL((pool_finish_kernel<kGiven>), dim3(a.n_items), fb, 0, st, a);
-      else hipLaunchKernelGGL((pool_finish_kernel<kUniform>), dim3(a.n_items), fb, 0, st, a);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
+    return hipGetLastError();
   }
   return hipSuccess;
 }
@@ -608,15 +582,7 @@ hipError_t launch_anchor(const PoolArgs& a, hipStream_t st) {
     if (given) hipLaunchKernelGGL((anchor_kernel<kGiven, 1024>), grid, block, dyn, st, a);
     else hipLaunchKernelGGL((anchor_kernel<kUniform, 1024>), grid, block, dyn, st, a);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.n_split > 1) {
-    const dim3 fb((unsigned)small_block(a.D));
-    if (given) hipLaunchKernelGGL((anchor_finish_kernel<kGiven>), dim3((unsigned)a.S), fb, 0, st, a);
-    else hipLaunchKernelGGL((anchor_finish_kernel<kUniform>), dim3((unsigned)a.S), fb, 0, st, a);
-    e = hipGetLastError();
-  }
-  return e;
+  return hipGetLastError();
 }
 
 }  // namespace kka

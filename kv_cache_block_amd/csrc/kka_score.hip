@@ -111,21 +111,8 @@ struct Level {
 };
 
 // Affinities cross work-groups inside one launch (scoring tiles on any
-// XCD, the selecting work-group on another), and each XCD has its own L2:
-// they are stored and loaded with device-scope (relaxed) atomics, which
-// write through and read past the non-coherent L2, instead of paying a
-// device-scope release fence (a whole-L2 write-back) per tile.  The
-// handoff's order comes from the hardware rather than from release /
-// acquire: a tile waits for its stores to be acknowledged (vmcnt 0) before
-// its device-scope counter increment, and the selecting work-group issues
-// its device-scope loads only after its own increment has returned the
-// last count.
-__device__ __forceinline__ void store_aff(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_aff(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// XCD, the selecting work-group on another): device-scope stores and loads
+// (store_agent, load_agent), ordered by the tile counters (arrive).
 
 // Score bits of element e: from the LDS copy (STG) or from global memory.
 // The two sources are separate instantiations so that LDS reads compile to
@@ -133,7 +120,7 @@ __device__ __forceinline__ float load_aff(const float* p) {
 template <bool STG>
 __device__ __forceinline__ uint32_t aff_key(const Level& L, const SelectShared& sm, int32_t e) {
   if constexpr (STG) return __float_as_uint(sm.aff[L.off + e]);
-  else return __float_as_uint(load_aff(L.aff + e));
+  else return __float_as_uint(load_agent(L.aff + e));
 }
 
 // Parent slot of child c (a shift for power-of-two fan-outs).
@@ -787,7 +774,7 @@ __device__ __forceinline__ void stage_rows(float* dst, const float* src, int32_t
   // copies write the value the last slot holds anyway.
   float t[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) t[u] = load_aff(src + min(u * kSelThreads + tid, n - 1));
+  for (int u = 0; u < U; ++u) t[u] = load_agent(src + min(u * kSelThreads + tid, n - 1));
 #pragma unroll
   for (int u = 0; u < U; ++u) dst[min(u * kSelThreads + tid, n - 1)] = t[u];
 }
@@ -1090,22 +1077,11 @@ void score_select_kernel(ScoreArgs a) {
     const int64_t row = vr < g.n_p ? vr
                         : vr < g.n_p + g.n_c ? (int64_t)a.max_pages + (vr - g.n_p)
                                              : (int64_t)a.max_pages + a.c_cap + (vr - g.n_p - g.n_c);
-    store_aff(aff + row, sm.aff[i]);
+    store_agent(aff + row, sm.aff[i]);
   }
-  // Every tile of the launch counts, scored or empty: once all of this
-  // work-group's affinity stores have completed (written through), one
-  // device-scope increment; atomicInc wraps the counter back to 0 on the
-  // last tile, leaving it ready for the next call.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned top = (unsigned)(a.tiles_per_seq - 1);
-    const unsigned old = atomicInc(a.done + s, top);
-    if (old > top) raise_err(a.err, KKA_DEVERR_WORKSPACE);  // counters not zeroed before the call
-    sm.last = old == top;
-  }
-  __syncthreads();
-  if (!sm.last) return;
+  // Every tile of the launch counts, scored or empty: the work-group that
+  // completes the sequence's last tile selects it.
+  if (!arrive(a.done + s, (uint32_t)a.tiles_per_seq, a.err, sm.last)) return;
   select_sequence(a, s, sm);
 }
 
@@ -1114,7 +1090,7 @@ void score_select_kernel(ScoreArgs a) {
 template <bool STG>
 __device__ __forceinline__ void lazy_put(const Level& L, int32_t e, float v, float* aff, float* out, SelectShared& sm) {
   if constexpr (STG) sm.aff[L.off + e] = v;
-  else store_aff(aff + L.off + e, v);
+  else store_agent(aff + L.off + e, v);
   if (out) out[L.off + e] = v;
 }
 

@@ -54,7 +54,7 @@ def test_header_declares_all_entry_points():
 def test_library_exports_every_declared_symbol(L):
     for name in declared():
         assert hasattr(L, name), name
-    assert L.kka_version() == int(re.search(r"#define KKA_VERSION (\d+)", open(HEADER).read()).group(1)) == 200
+    assert L.kka_version() == int(re.search(r"#define KKA_VERSION (\d+)", open(HEADER).read()).group(1)) == 300
     assert L.kka_status_string(0) == b"ok"
     assert L.kka_status_string(4).startswith(b"workspace")
 
@@ -132,14 +132,16 @@ def test_workspace_sizes(L):
     small = seqs(num_seqs=1, total_blocks=256)
     # enough blocks to fill the chip: one pass, no partials
     assert L.kka_pool_blocks_workspace(ctypes.byref(kp), ctypes.byref(big), None, 0, 0) == 0
-    # few blocks: split over layers, D floats per (block, split)
+    # few blocks: split over layers; one arrival counter per block (rounded
+    # up to 256 bytes), then D floats per (block, split): 256 blocks want 8
+    # splits of 28 layers, i.e. 4 layers each, which makes 7 splits
     n = L.kka_pool_blocks_workspace(ctypes.byref(kp), ctypes.byref(small), None, 0, 0)
-    assert n >= 256 * 2 * 128 * 4 and n % 256 == 0
+    assert n == 256 * 4 + 256 * 7 * 128 * 4
     # variance: per-(block, layer, head) sums + squares + per-(seq, head) fp64 variances
     v = L.kka_pool_blocks_workspace(ctypes.byref(kp), ctypes.byref(big), None, 0, 1)
     assert v >= 8192 * 112 * 129 * 4 + 112 * 8
     a = L.kka_pool_anchor_workspace(ctypes.byref(kp), ctypes.byref(big), 16)
-    assert a >= 28 * 128 * 4  # one sequence: split over every layer
+    assert a == 256 + 28 * 128 * 4  # one sequence split over every layer: its counter, then 28 partials
 
 
 def test_level_rows_and_score_validation(L):

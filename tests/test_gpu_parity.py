@@ -815,3 +815,49 @@ def test_parented_small_levels_many_sequences(case):
                                       af[s, lay.grid_row0:lay.grid_row0 + n_g], **case)
             np.testing.assert_array_equal(gi[s, :len(ridx)], ridx, err_msg=f"call={call} s={s}")
             np.testing.assert_array_equal(gs[s, :len(ridx)].view(np.uint32), rsc.view(np.uint32))
+
+
+def test_layer_split_combined_in_one_launch_and_counters():
+    """A small batch splits every block's and every sequence's layers over
+    several work-groups; the one that finishes an item's last share adds the
+    shares in split order in the same launch.  v_b and anchors match the
+    oracle over three steps on one set of workspaces (the arrival counters
+    are left zero), are bit-identical from step to step, and garbage
+    counters raise the workspace flag until they are re-zeroed."""
+    say("layer split counters")
+    w = ragged_workload(16, 3, 12, 2, 64, 8, 40, 300, window=24)
+    sel, npg = run_selector(w)
+    assert sel.ws_pool is not None and sel.ws_anchor is not None  # both launches are split
+    okp = oracle.KPool.of(w)
+    ref = oracle_vb(w, range(w.total_blocks))
+    ref_anc = [oracle.pool_anchor(okp, oracle.seq_table(w.block_offsets, w.block_table, s), int(w.seq_len[s]),
+                                  w.window) for s in range(w.S)]
+    first = None
+    for step in range(3):
+        if step:
+            sel.step(npg)
+            torch.cuda.synchronize()
+        assert kka.kka_device_error() == 0
+        got = vb_rows(sel, w)
+        for b, v in ref.items():
+            np.testing.assert_allclose(got[b], v, atol=ATOL, rtol=0, err_msg=f"step {step} block {b}")
+        anc = sel.anchors.cpu().numpy()
+        for s in range(w.S):
+            np.testing.assert_allclose(anc[s], ref_anc[s], atol=ATOL, rtol=0, err_msg=f"step {step} seq {s}")
+        now = (sel.level.cpu().numpy().copy(), anc.copy())
+        if first is None:
+            first = now
+        else:
+            np.testing.assert_array_equal(now[0].view(np.uint32), first[0].view(np.uint32))
+            np.testing.assert_array_equal(now[1].view(np.uint32), first[1].view(np.uint32))
+    for ws in (sel.ws_pool, sel.ws_anchor):
+        ws.fill_(0xFF)
+        sel.step(npg)
+        assert kka.kka_device_error() & kka.DEVERR_WORKSPACE
+        ws.zero_()
+        sel.step(npg)
+        torch.cuda.synchronize()
+        assert kka.kka_device_error() == 0
+    got = vb_rows(sel, w)
+    for b, v in ref.items():
+        np.testing.assert_allclose(got[b], v, atol=ATOL, rtol=0, err_msg=f"after re-zero block {b}")
