@@ -149,14 +149,16 @@ typedef enum kka_weight_mode {
  *             the chip, a block's layers are split over several work-groups:
  *             the workspace then starts with one uint32 arrival counter per
  *             block (4 * blocks bytes, rounded up to 256), followed by the
- *             shares' partial sums, and the work-group that finishes a
- *             block's last share adds them (in split order) and writes v_b,
- *             all in one launch.  The counters must be zero before the first
- *             call that uses the workspace (allocate it zero-filled); every
- *             call leaves them zero.  A counter found at or above the split
- *             count raises KKA_DEVERR_WORKSPACE and that block's v_b is not
- *             written (re-zero the counters).  Calls that run concurrently
- *             must not share a workspace.
+ *             shares' partial sums, which are added in split order.  A call
+ *             reading at most 32 MiB of keys (full blocks counted) adds them
+ *             in the same launch, in the work-group that finishes a block's
+ *             last share, which it finds through the counters; a larger call
+ *             adds them in a second launch.  The counters must be zero before
+ *             the first call that uses the workspace (allocate it
+ *             zero-filled); every call leaves them zero.  A counter found at
+ *             or above the split count raises KKA_DEVERR_WORKSPACE and that
+ *             block's v_b is not written (re-zero the counters).  Calls that
+ *             run concurrently must not share a workspace.
  */
 KKA_API kka_status kka_pool_blocks(const kka_kpool* kp, const kka_seqs* seqs, const int32_t* blocks, int32_t num_blocks,
                            int32_t mode, float* head_weight, float* vb_out, int64_t vb_seq_stride, void* workspace,
@@ -176,7 +178,8 @@ KKA_API size_t kka_pool_blocks_workspace(const kka_kpool* kp, const kka_seqs* se
  * workspace   >= kka_pool_anchor_workspace() bytes, 16-byte aligned (NULL
  *             allowed when that size is 0); with a layer split, one uint32
  *             arrival counter per sequence then the shares' partial sums,
- *             with the same rules as kka_pool_blocks' workspace.
+ *             with the same rules as kka_pool_blocks' workspace (full
+ *             windows counted for the 32 MiB bound).
  * Rules: window >= 0.
  */
 KKA_API kka_status kka_pool_anchor(const kka_kpool* kp, const kka_seqs* seqs, int32_t window, const float* head_weight,
@@ -438,7 +441,7 @@ KKA_API const char* kka_status_string(kka_status s);
  * kka_score_topk workspace holds per-sequence tile counters that must be
  * zero at first use.  0.3.0: so do the kka_pool_blocks and kka_pool_anchor
  * workspaces of layer-split launches (per-block / per-sequence arrival
- * counters; the split shares are combined in the same launch). */
+ * counters; small launches combine the split shares in the same launch). */
 #define KKA_VERSION 300
 
 /* Version of the loaded library, same encoding (equals KKA_VERSION when the

@@ -208,7 +208,9 @@ kka_status kka_pool_blocks(const kka_kpool* kp, const kka_seqs* seqs, const int3
   const LayerSplit ls = layer_split(items, a.L);
   a.n_split = ls.n_split;
   a.lps = ls.lps;
-  a.done = ls.n_split > 1 ? reinterpret_cast<uint32_t*>(wsb) : nullptr;
+  // upper bound of the launch's key bytes: full blocks
+  const double key_bytes = (double)items * kp->block_size * a.L * a.H * a.D * 2.0;
+  a.done = ls.n_split > 1 && key_bytes <= kSplitOneLaunchBytes ? reinterpret_cast<uint32_t*>(wsb) : nullptr;
   a.partial = ls.n_split > 1 ? reinterpret_cast<float*>(wsb + ws.counters) : nullptr;
   a.weights = mode == KKA_WEIGHT_GIVEN ? head_weight : nullptr;
   return launched(launch_pool(a, mode, s));
@@ -431,7 +433,9 @@ kka_status kka_pool_anchor(const kka_kpool* kp, const kka_seqs* seqs, int32_t wi
   a.n_items = seqs->num_seqs;
   a.weights = head_weight;
   a.out = anchor_out;
-  a.done = ls.n_split > 1 ? static_cast<uint32_t*>(workspace) : nullptr;
+  // upper bound of the launch's key bytes: full windows
+  const double key_bytes = (double)seqs->num_seqs * window * a.L * a.H * a.D * 2.0;
+  a.done = ls.n_split > 1 && key_bytes <= kSplitOneLaunchBytes ? static_cast<uint32_t*>(workspace) : nullptr;
   a.partial = ls.n_split > 1
                   ? reinterpret_cast<float*>(static_cast<char*>(workspace) + anchor_counter_bytes(seqs->num_seqs))
                   : nullptr;

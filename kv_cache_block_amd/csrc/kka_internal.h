@@ -53,6 +53,14 @@ struct LayerSplit {
   int32_t n_split, lps;
 };
 
+// A layer-split launch that reads at most this many key bytes (latency-
+// bound) combines its shares in the same launch through per-item arrival
+// counters; a larger one (bandwidth-bound) leaves them to a second kernel:
+// under a saturating read stream, waiting for the shares' write-through
+// stores to be acknowledged at the end of every work-group measured slower
+// than the second launch (7B shape, 32K tokens: 157 against 150 us).
+constexpr double kSplitOneLaunchBytes = 32.0 * 1024 * 1024;
+
 inline LayerSplit layer_split(int64_t items, int32_t L) {
   LayerSplit ls;
   int64_t want = items >= kPoolTargetGroups ? 1 : (kPoolTargetGroups + items - 1) / (items > 0 ? items : 1);

@@ -204,14 +204,42 @@ __global__ __launch_bounds__(MAXT) void pool_kernel(PoolArgs a) {
         a.out[it.row * a.D + d] = it.n_b > 0 ? column_sum(red, a.D, a.ps.nt, d) / denom : 0.f;
     return;
   }
-  // layer split: the work-group that finishes the item's last share adds
-  // the shares' partial sums in split order
+  // layer split: shares' partial sums, added in split order by
+  // pool_finish_kernel or (a.done set) by the work-group that finishes the
+  // item's last share
   float* part = a.partial + (int64_t)item * a.n_split * a.D;
+  if (!a.done) {
+    for (int32_t d = tid; d < a.D; d += a.ps.nt) part[(int64_t)j * a.D + d] = column_sum(red, a.D, a.ps.nt, d);
+    return;
+  }
   for (int32_t d = tid; d < a.D; d += a.ps.nt) store_agent(part + (int64_t)j * a.D + d, column_sum(red, a.D, a.ps.nt, d));
   __shared__ uint32_t last;
   if (!arrive(a.done + item, (uint32_t)a.n_split, a.err, last) || it.row < 0) return;
   for (int32_t d = tid; d < a.D; d += a.ps.nt) {
     const float sum = split_sum(part + d, a.n_split, a.D);
+    a.out[it.row * a.D + d] = it.n_b > 0 ? sum / denom : 0.f;
+  }
+}
+
+// Sums the layer-split partials of each item in split order.
+template <int MODE>
+__global__ __launch_bounds__(256) void pool_finish_kernel(PoolArgs a) {
+  const int32_t item = blockIdx.x;
+  const Item it = locate(a, item, false);
+  if (it.row < 0) return;
+  const int32_t LH = a.L * a.H;
+  for (int32_t d = threadIdx.x; d < a.D; d += blockDim.x) {
+    const float* src = a.partial + (int64_t)item * a.n_split * a.D + d;
+    float sum = 0.f;
+    for (int32_t j0 = 0; j0 < a.n_split; j0 += 8) {
+      float t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = src[(int64_t)min(j0 + u, a.n_split - 1) * a.D];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < a.n_split) sum += t[u];
+    }
+    const float denom = MODE == kGiven ? (float)it.n_b : (float)((int64_t)it.n_b * LH);
     a.out[it.row * a.D + d] = it.n_b > 0 ? sum / denom : 0.f;
   }
 }
@@ -511,14 +539,43 @@ __global__ __launch_bounds__(MAXT) void anchor_kernel(PoolArgs a) {
       a.out[(int64_t)s * a.D + d] = W > 0 ? column_sum(red, a.D, a.ps.nt, d) / denom : 0.f;
     return;
   }
-  // layer split: the work-group that finishes the sequence's last share
-  // adds the shares' partial sums in split order
+  // layer split: shares' partial sums, added in split order by
+  // anchor_finish_kernel or (a.done set) by the work-group that finishes
+  // the sequence's last share
   float* part = a.partial + (int64_t)s * a.n_split * a.D;
+  if (!a.done) {
+    for (int32_t d = tid; d < a.D; d += a.ps.nt) part[(int64_t)j * a.D + d] = column_sum(red, a.D, a.ps.nt, d);
+    return;
+  }
   for (int32_t d = tid; d < a.D; d += a.ps.nt) store_agent(part + (int64_t)j * a.D + d, column_sum(red, a.D, a.ps.nt, d));
   __shared__ uint32_t last;
   if (!arrive(a.done + s, (uint32_t)a.n_split, a.err, last)) return;
   for (int32_t d = tid; d < a.D; d += a.ps.nt) {
     const float sum = split_sum(part + d, a.n_split, a.D);
+    a.out[(int64_t)s * a.D + d] = W > 0 ? sum / denom : 0.f;
+  }
+}
+
+// Sums each sequence's layer-split partials in split order (loads of a
+// batch of 8 splits are issued before the first add).
+template <int MODE>
+__global__ __launch_bounds__(256) void anchor_finish_kernel(PoolArgs a) {
+  const int32_t s = blockIdx.x;
+  const int32_t T = a.seq_len[s] > 0 ? a.seq_len[s] : 0;
+  const int32_t W = a.window < T ? a.window : T;
+  const int32_t LH = a.L * a.H;
+  for (int32_t d = threadIdx.x; d < a.D; d += blockDim.x) {
+    const float* src = a.partial + (int64_t)s * a.n_split * a.D + d;
+    float sum = 0.f;
+    for (int32_t j0 = 0; j0 < a.n_split; j0 += 8) {
+      float t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = src[(int64_t)min(j0 + u, a.n_split - 1) * a.D];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < a.n_split) sum += t[u];
+    }
+    const float denom = MODE == kGiven ? (float)W : (float)((int64_t)W * LH);
     a.out[(int64_t)s * a.D + d] = W > 0 ? sum / denom : 0.f;
   }
 }
@@ -539,6 +596,11 @@ hipError_t launch_pool(const PoolArgs& a, int mode, hipStream_t st) {
       if (mode == kGiven) hipLaunchKernelGGL((pool_kernel<kGiven, 1024>), grid, block, dyn, st, a);
       else hipLaunchKernelGGL((pool_kernel<kUniform, 1024>), grid, block, dyn, st, a);
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.n_split == 1 || a.done) return e;
+    const dim3 fb((unsigned)small_block(a.D));
+    if (mode == kGiven) hipLaunchKernelGGL((pool_finish_kernel<kGiven>), dim3(a.n_items), fb, 0, st, a);
+    else hipLaunchKernelGGL((pool_finish_kernel<kUniform>), dim3(a.n_items), fb, 0, st, a);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -582,6 +644,11 @@ hipError_t launch_anchor(const PoolArgs& a, hipStream_t st) {
     if (given) hipLaunchKernelGGL((anchor_kernel<kGiven, 1024>), grid, block, dyn, st, a);
     else hipLaunchKernelGGL((anchor_kernel<kUniform, 1024>), grid, block, dyn, st, a);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_split == 1 || a.done) return e;
+  const dim3 fb((unsigned)small_block(a.D));
+  if (given) hipLaunchKernelGGL((anchor_finish_kernel<kGiven>), dim3((unsigned)a.S), fb, 0, st, a);
+  else hipLaunchKernelGGL((anchor_finish_kernel<kUniform>), dim3((unsigned)a.S), fb, 0, st, a);
   return hipGetLastError();
 }
 
