@@ -150,10 +150,11 @@ typedef enum kka_weight_mode {
  *             the workspace then starts with one uint32 arrival counter per
  *             block (4 * blocks bytes, rounded up to 256), followed by the
  *             shares' partial sums, which are added in split order.  A call
- *             reading at most 32 MiB of keys (full blocks counted) adds them
- *             in the same launch, in the work-group that finishes a block's
- *             last share, which it finds through the counters; a larger call
- *             adds them in a second launch.  The counters must be zero before
+ *             of at most one work-group per compute unit (blocks times
+ *             splits) that reads at most 32 MiB of keys (full blocks counted)
+ *             adds them in the same launch, in the work-group that finishes a
+ *             block's last share, which it finds through the counters; other
+ *             calls add them in a second launch.  The counters must be zero before
  *             the first call that uses the workspace (allocate it
  *             zero-filled); every call leaves them zero.  A counter found at
  *             or above the split count raises KKA_DEVERR_WORKSPACE and that
@@ -178,8 +179,8 @@ KKA_API size_t kka_pool_blocks_workspace(const kka_kpool* kp, const kka_seqs* se
  * workspace   >= kka_pool_anchor_workspace() bytes, 16-byte aligned (NULL
  *             allowed when that size is 0); with a layer split, one uint32
  *             arrival counter per sequence then the shares' partial sums,
- *             with the same rules as kka_pool_blocks' workspace (full
- *             windows counted for the 32 MiB bound).
+ *             with the same rules as kka_pool_blocks' workspace
+ *             (sequences times splits work-groups, full windows counted).
  * Rules: window >= 0.
  */
 KKA_API kka_status kka_pool_anchor(const kka_kpool* kp, const kka_seqs* seqs, int32_t window, const float* head_weight,
@@ -441,7 +442,8 @@ KKA_API const char* kka_status_string(kka_status s);
  * kka_score_topk workspace holds per-sequence tile counters that must be
  * zero at first use.  0.3.0: so do the kka_pool_blocks and kka_pool_anchor
  * workspaces of layer-split launches (per-block / per-sequence arrival
- * counters; small launches combine the split shares in the same launch). */
+ * counters; the smallest launches combine the split shares in the same
+ * launch). */
 #define KKA_VERSION 300
 
 /* Version of the loaded library, same encoding (equals KKA_VERSION when the

@@ -210,7 +210,7 @@ kka_status kka_pool_blocks(const kka_kpool* kp, const kka_seqs* seqs, const int3
   a.lps = ls.lps;
   // upper bound of the launch's key bytes: full blocks
   const double key_bytes = (double)items * kp->block_size * a.L * a.H * a.D * 2.0;
-  a.done = ls.n_split > 1 && key_bytes <= kSplitOneLaunchBytes ? reinterpret_cast<uint32_t*>(wsb) : nullptr;
+  a.done = split_in_one_launch(items, ls.n_split, key_bytes) ? reinterpret_cast<uint32_t*>(wsb) : nullptr;
   a.partial = ls.n_split > 1 ? reinterpret_cast<float*>(wsb + ws.counters) : nullptr;
   a.weights = mode == KKA_WEIGHT_GIVEN ? head_weight : nullptr;
   return launched(launch_pool(a, mode, s));
@@ -435,7 +435,7 @@ kka_status kka_pool_anchor(const kka_kpool* kp, const kka_seqs* seqs, int32_t wi
   a.out = anchor_out;
   // upper bound of the launch's key bytes: full windows
   const double key_bytes = (double)seqs->num_seqs * window * a.L * a.H * a.D * 2.0;
-  a.done = ls.n_split > 1 && key_bytes <= kSplitOneLaunchBytes ? static_cast<uint32_t*>(workspace) : nullptr;
+  a.done = split_in_one_launch(seqs->num_seqs, ls.n_split, key_bytes) ? static_cast<uint32_t*>(workspace) : nullptr;
   a.partial = ls.n_split > 1
                   ? reinterpret_cast<float*>(static_cast<char*>(workspace) + anchor_counter_bytes(seqs->num_seqs))
                   : nullptr;

@@ -53,13 +53,22 @@ struct LayerSplit {
   int32_t n_split, lps;
 };
 
-// A layer-split launch that reads at most this many key bytes (latency-
-// bound) combines its shares in the same launch through per-item arrival
-// counters; a larger one (bandwidth-bound) leaves them to a second kernel:
-// under a saturating read stream, waiting for the shares' write-through
-// stores to be acknowledged at the end of every work-group measured slower
-// than the second launch (7B shape, 32K tokens: 157 against 150 us).
+// A layer-split launch of at most one work-group per compute unit that
+// reads at most this many key bytes (pure latency: one sequence's anchor)
+// combines its shares in the same launch through per-item arrival counters;
+// others leave them to a second kernel.  The wait for the shares' write-
+// through stores to be acknowledged and the last work-group's loads past
+// the L2 cost more than the second launch once many work-groups take part
+// (anchors of 32 sequences, 896 work-groups: 19.2 against 17.1 us; 7B
+// K-pool of 32K tokens under a saturating read stream: 157 against 150 us)
+// and less for one sequence's anchor (28 work-groups: 12.2 against 14.4).
 constexpr double kSplitOneLaunchBytes = 32.0 * 1024 * 1024;
+
+int32_t device_cus();  // compute units of the current device (cached; defined with the scoring launchers)
+
+inline bool split_in_one_launch(int64_t items, int32_t n_split, double key_bytes) {
+  return n_split > 1 && items * n_split <= device_cus() && key_bytes <= kSplitOneLaunchBytes;
+}
 
 inline LayerSplit layer_split(int64_t items, int32_t L) {
   LayerSplit ls;

@@ -116,16 +116,19 @@ __device__ __forceinline__ void stash8(float* red, int tid, const float (&acc)[8
 }
 
 // Sum over the n shares of a layer split, in split order, of the partial at
-// src + j * stride (device-scope loads, a batch of 8 issued before the first
-// add).
+// src + j * stride.  The loads are device-scope (they read past the L2, a
+// memory round trip each), so up to 32 shares (every share of a layer
+// split of up to 32 layers) are requested in one round before the first
+// add; loads past the last share re-read it.
 __device__ __forceinline__ float split_sum(const float* src, int32_t n, int32_t stride) {
+  constexpr int kRound = 32;
   float sum = 0.f;
-  for (int32_t j0 = 0; j0 < n; j0 += 8) {
-    float t[8];
+  for (int32_t j0 = 0; j0 < n; j0 += kRound) {
+    float t[kRound];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) t[u] = load_agent(src + (int64_t)min(j0 + u, n - 1) * stride);
+    for (int u = 0; u < kRound; ++u) t[u] = load_agent(src + (int64_t)min(j0 + u, n - 1) * stride);
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < kRound; ++u)
       if (j0 + u < n) sum += t[u];
   }
   return sum;

@@ -1205,21 +1205,6 @@ __global__ __launch_bounds__(kSelThreads) void lazy_kernel(ScoreArgs a, float* l
 // head_dim 512 so that a lane's row and anchor pieces stay in registers.
 constexpr int32_t score_lpr(int32_t D) { return D / 4 > 8 * 16 ? 16 : 8; }
 
-// Compute units of the current device (cached per device; callers on
-// several host threads may fill an entry at once with the same value).
-int32_t device_cus() {
-  static std::atomic<int32_t> cus[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int32_t n = cus[dev].load(std::memory_order_relaxed);
-  if (n <= 0) {
-    int q = 0;
-    if (hipDeviceGetAttribute(&q, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || q <= 0) q = 256;
-    n = q;
-    cus[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
 
 template <int LPR, int NQ>
 hipError_t launch_nq(const ScoreArgs& a0, bool lazy, float* lazy_out, hipStream_t st) {
@@ -1276,6 +1261,22 @@ hipError_t dispatch(const ScoreArgs& a, bool lazy, float* lazy_out, hipStream_t 
 }
 
 }  // namespace
+
+// Compute units of the current device (cached per device; callers on
+// several host threads may fill an entry at once with the same value).
+int32_t device_cus() {
+  static std::atomic<int32_t> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int32_t n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    int q = 0;
+    if (hipDeviceGetAttribute(&q, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || q <= 0) q = 256;
+    n = q;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 // A tile's affinities are gathered in the selection's LDS row buffer.
 static_assert((kSelThreads / 8) * KKA_SCORE_LOADS * KKA_SCORE_PASSES <= kLdsRows, "tile rows exceed LDS");

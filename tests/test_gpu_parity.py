@@ -817,15 +817,20 @@ def test_parented_small_levels_many_sequences(case):
             np.testing.assert_array_equal(gs[s, :len(ridx)].view(np.uint32), rsc.view(np.uint32))
 
 
-def test_layer_split_combined_in_one_launch_and_counters():
+@pytest.mark.parametrize("one_launch", [True, False])
+def test_layer_split_shares_and_counters(one_launch):
     """A small batch splits every block's and every sequence's layers over
-    several work-groups; the one that finishes an item's last share adds the
-    shares in split order in the same launch.  v_b and anchors match the
-    oracle over three steps on one set of workspaces (the arrival counters
-    are left zero), are bit-identical from step to step, and garbage
-    counters raise the workspace flag until they are re-zeroed."""
-    say("layer split counters")
-    w = ragged_workload(16, 3, 12, 2, 64, 8, 40, 300, window=24)
+    several work-groups.  With at most one work-group per compute unit
+    (13 blocks, 2 sequences, 12 layers) the one that finishes an item's last
+    share adds the shares in split order in the same launch, else (50
+    blocks, 600 work-groups) a second kernel does.  v_b and anchors match
+    the oracle over three steps on one set of workspaces (the arrival
+    counters are left zero) and are bit-identical from step to step; in the
+    one-launch case garbage counters raise the workspace flag until they
+    are re-zeroed."""
+    say(f"layer split one_launch={one_launch}")
+    w = ragged_workload(16, 2, 12, 2, 64, 8, 40, 64, window=24) if one_launch else \
+        ragged_workload(16, 3, 12, 2, 64, 8, 40, 300, window=24)
     sel, npg = run_selector(w)
     assert sel.ws_pool is not None and sel.ws_anchor is not None  # both launches are split
     okp = oracle.KPool.of(w)
@@ -850,6 +855,8 @@ def test_layer_split_combined_in_one_launch_and_counters():
         else:
             np.testing.assert_array_equal(now[0].view(np.uint32), first[0].view(np.uint32))
             np.testing.assert_array_equal(now[1].view(np.uint32), first[1].view(np.uint32))
+    if not one_launch:
+        return
     for ws in (sel.ws_pool, sel.ws_anchor):
         ws.fill_(0xFF)
         sel.step(npg)
