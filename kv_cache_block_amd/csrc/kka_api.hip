@@ -61,6 +61,12 @@ kka_status check_seqs(const kka_seqs* sq) {
   return KKA_OK;
 }
 
+// Key bytes of one layer of one pooled block (full block): what one layer
+// of a split share reads.
+inline int64_t pool_layer_bytes(const kka_kpool* kp) {
+  return (int64_t)kp->block_size * kp->num_kv_heads * kp->head_dim * 2;
+}
+
 // Byte layout of the pooling workspace: layer-split pooling keeps one
 // arrival counter per item, then each (item, split)'s partial sums; variance
 // pooling keeps per-(block, layer, head) sums, sums of squares and fp64
@@ -78,7 +84,7 @@ PoolWs pool_ws(const kka_kpool* kp, const kka_seqs* sq, int64_t items, int32_t m
     w.q = align256(tb * LH * sizeof(float));
     w.var = align256((size_t)sq->num_seqs * LH * sizeof(double));
   } else {
-    const LayerSplit ls = layer_split(items, kp->num_layers);
+    const LayerSplit ls = layer_split(items, kp->num_layers, pool_layer_bytes(kp));
     if (ls.n_split > 1) {
       w.counters = align256((size_t)items * sizeof(uint32_t));
       w.partial = align256((size_t)items * ls.n_split * D * sizeof(float));
@@ -205,7 +211,7 @@ kka_status kka_pool_blocks(const kka_kpool* kp, const kka_seqs* seqs, const int3
     return launched(launch_pool_combine(a, head_weight, s));
   }
   if (items == 0) return KKA_OK;
-  const LayerSplit ls = layer_split(items, a.L);
+  const LayerSplit ls = layer_split(items, a.L, pool_layer_bytes(kp));
   a.n_split = ls.n_split;
   a.lps = ls.lps;
   // upper bound of the launch's key bytes: full blocks

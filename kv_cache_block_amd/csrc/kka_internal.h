@@ -48,7 +48,8 @@ inline PoolShape pool_shape(int32_t H, int32_t D) {
 }
 
 // Layer split of a pooling launch: enough groups to fill the chip, never a
-// split finer than one layer.  Depends only on (items, L).
+// split finer than one layer (nor, with layer_bytes, shares smaller than
+// kMinShareBytes).  Depends only on its arguments.
 struct LayerSplit {
   int32_t n_split, lps;
 };
@@ -70,13 +71,26 @@ inline bool split_in_one_launch(int64_t items, int32_t n_split, double key_bytes
   return n_split > 1 && items * n_split <= device_cus() && key_bytes <= kSplitOneLaunchBytes;
 }
 
-inline LayerSplit layer_split(int64_t items, int32_t L) {
+// Pooling splits a block's layers into shares of at least this many key
+// bytes (layer_bytes: one layer of one item): a smaller share is dominated
+// by its work-group's fixed costs (0.5B shape, blocks of 98 KB kept whole:
+// 256 work-groups and no combine, 17.1 -> 13.1 us).  Anchors pass 0: their
+// work-groups walk tokens and layers serially, and fewer, larger shares
+// measured slower (one 32K sequence: 12.2 -> 21.0 us at this minimum).
+constexpr int64_t kMinShareBytes = 128 * 1024;
+
+inline LayerSplit layer_split(int64_t items, int32_t L, int64_t layer_bytes = 0) {
   LayerSplit ls;
   int64_t want = items >= kPoolTargetGroups ? 1 : (kPoolTargetGroups + items - 1) / (items > 0 ? items : 1);
   if (want > L) want = L;
   if (want < 1) want = 1;
-  ls.lps = (int32_t)((L + want - 1) / want);
-  ls.n_split = (L + ls.lps - 1) / ls.lps;
+  int64_t lps = (L + want - 1) / want;
+  if (layer_bytes > 0) {
+    const int64_t min_lps = (kMinShareBytes + layer_bytes - 1) / layer_bytes;
+    if (lps < min_lps) lps = min_lps < L ? min_lps : L;
+  }
+  ls.lps = (int32_t)lps;
+  ls.n_split = (int32_t)((L + lps - 1) / lps);
   return ls;
 }
 

@@ -134,9 +134,13 @@ def test_workspace_sizes(L):
     assert L.kka_pool_blocks_workspace(ctypes.byref(kp), ctypes.byref(big), None, 0, 0) == 0
     # few blocks: split over layers; one arrival counter per block (rounded
     # up to 256 bytes), then D floats per (block, split): 256 blocks want 8
-    # splits of 28 layers, i.e. 4 layers each, which makes 7 splits
+    # splits of 28 layers, but a share keeps at least 128 KiB of keys (8
+    # layers of 16 KiB), which makes 4 splits
     n = L.kka_pool_blocks_workspace(ctypes.byref(kp), ctypes.byref(small), None, 0, 0)
-    assert n == 256 * 4 + 256 * 7 * 128 * 4
+    assert n == 256 * 4 + 256 * 4 * 128 * 4
+    # blocks of 96 KiB (0.5B shape) are not split at all: no workspace
+    kp_small = kpool(num_layers=24, num_kv_heads=2, head_dim=64, block_size=16, num_phys_blocks=256)
+    assert L.kka_pool_blocks_workspace(ctypes.byref(kp_small), ctypes.byref(small), None, 0, 0) == 0
     # variance: per-(block, layer, head) sums + squares + per-(seq, head) fp64 variances
     v = L.kka_pool_blocks_workspace(ctypes.byref(kp), ctypes.byref(big), None, 0, 1)
     assert v >= 8192 * 112 * 129 * 4 + 112 * 8

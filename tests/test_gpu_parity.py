@@ -820,17 +820,18 @@ def test_parented_small_levels_many_sequences(case):
 @pytest.mark.parametrize("one_launch", [True, False])
 def test_layer_split_shares_and_counters(one_launch):
     """A small batch splits every block's and every sequence's layers over
-    several work-groups.  With at most one work-group per compute unit
-    (13 blocks, 2 sequences, 12 layers) the one that finishes an item's last
-    share adds the shares in split order in the same launch, else (50
-    blocks, 600 work-groups) a second kernel does.  v_b and anchors match
+    several work-groups (blocks of 16 KiB per layer: shares of 8 layers).
+    With at most one work-group per compute unit (13 blocks, 2 sequences)
+    the one that finishes an item's last share adds the shares in split
+    order in the same launch, else (151 blocks, 302 work-groups) a second
+    kernel does.  v_b and anchors match
     the oracle over three steps on one set of workspaces (the arrival
     counters are left zero) and are bit-identical from step to step; in the
     one-launch case garbage counters raise the workspace flag until they
     are re-zeroed."""
     say(f"layer split one_launch={one_launch}")
-    w = ragged_workload(16, 2, 12, 2, 64, 8, 40, 64, window=24) if one_launch else \
-        ragged_workload(16, 3, 12, 2, 64, 8, 40, 300, window=24)
+    w = ragged_workload(16, 2, 12, 4, 128, 16, 80, 120, window=24) if one_launch else \
+        ragged_workload(16, 10, 12, 4, 128, 16, 200, 280, window=24)
     sel, npg = run_selector(w)
     assert sel.ws_pool is not None and sel.ws_anchor is not None  # both launches are split
     okp = oracle.KPool.of(w)
