@@ -146,7 +146,8 @@ typedef enum kka_weight_mode {
  *             (vb_seq_stride == 0); a row is head_dim floats.
  * workspace   device, 16-byte aligned, >= kka_pool_blocks_workspace() bytes
  *             (may be NULL when that size is 0).  With fewer blocks than fill
- *             the chip, a block's layers are split over several work-groups:
+ *             the chip, a block's layers are split over several work-groups
+ *             (shares of at least 128 KiB of keys, full blocks counted):
  *             the workspace then starts with one uint32 arrival counter per
  *             block (4 * blocks bytes, rounded up to 256), followed by the
  *             shares' partial sums, which are added in split order.  A call
