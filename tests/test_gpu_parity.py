@@ -869,3 +869,74 @@ def test_layer_split_shares_and_counters(one_launch):
     got = vb_rows(sel, w)
     for b, v in ref.items():
         np.testing.assert_allclose(got[b], v, atol=ATOL, rtol=0, err_msg=f"after re-zero block {b}")
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_selection_random_configurations(seed):
+    """Seeded sweep over selection configurations: flat or hierarchical,
+    fan-outs 1-20, k per level from 0 to beyond the level's size, 1-300
+    sequences of 0-700 pages (so one-launch and two-launch batches, levels
+    of every ranking path, parented and not), head_dim 8-256, and a share
+    of exactly-zero and tied scores.  Every sequence bit-exact against the
+    oracle's selection of the GPU's own affinities, and the lazy pass
+    bit-identical to the full pass."""
+    rng = np.random.default_rng(1000 + seed)
+    hier = int(rng.integers(0, 2))
+    ppc, cpg = int(rng.integers(1, 21)), int(rng.integers(1, 21))
+    S = int(rng.choice([1, 3, 17, 64, 300]))
+    max_pages = int(rng.integers(1, 701))
+    D = int(rng.choice([8, 16, 64, 128, 256]))
+    kp_ = int(rng.integers(1, 1025)) if rng.random() < 0.3 else int(rng.integers(1, 129))
+    case = dict(hierarchical=hier, k_grid=int(rng.integers(0, 40)) if hier else 0,
+                k_chunk=int(rng.integers(0, 200)) if hier else 0, k_page=kp_, pages_per_chunk=ppc,
+                chunks_per_grid=cpg)
+    say(f"random selection seed={seed} S={S} max_pages={max_pages} D={D} {case}")
+    lay = kka.LevelLayout(S, max_pages, D, bool(hier), ppc, cpg)
+    lvl = np.zeros((S, lay.rows_per_seq, D), np.float32)
+    if rng.random() < 0.3:  # integer-valued vectors: exact ties, exact 0 / 0.5 / 1 affinities
+        lvl[:, :max_pages] = rng.integers(-1, 2, (S, max_pages, D)).astype(np.float32)
+    else:
+        lvl[:, :max_pages] = rng.standard_normal((S, max_pages, D), dtype=np.float32)
+    anc = rng.standard_normal((S, D), dtype=np.float32)
+    n_pages = rng.integers(0, max_pages + 1, S).astype(np.int32)
+    level = torch.from_numpy(lvl).cuda()
+    npg = torch.from_numpy(n_pages).cuda()
+    kka.kka_build_levels(lay, level, npg)
+    K = case["k_page"]
+    idx = torch.full((S, K), -9, dtype=torch.int32, device="cuda")
+    sc = torch.full((S, K), 7.0, dtype=torch.float32, device="cuda")
+    cnt = torch.full((S,), -9, dtype=torch.int32, device="cuda")
+    aff = torch.zeros((S, lay.rows_per_seq), dtype=torch.float32, device="cuda")
+    kka.kka_score_topk(lay, level, npg, torch.from_numpy(anc).cuda(), k_page=K, k_grid=case["k_grid"],
+                       k_chunk=case["k_chunk"], page_idx_out=idx, page_score_out=sc, n_selected_out=cnt,
+                       affinity_out=aff)
+    torch.cuda.synchronize()
+    assert kka.kka_device_error() == 0
+    af, gi, gs, gc = aff.cpu().numpy(), idx.cpu().numpy(), sc.cpu().numpy(), cnt.cpu().numpy()
+    for s in range(S):
+        n_p = int(n_pages[s])
+        if hier:
+            n_c = -(-n_p // ppc)
+            n_g = -(-n_c // cpg)
+            a_c = af[s, lay.chunk_row0:lay.chunk_row0 + n_c]
+            a_g = af[s, lay.grid_row0:lay.grid_row0 + n_g]
+        else:
+            a_c = a_g = None
+        ridx, rsc = oracle.select(af[s, :n_p], a_c, a_g, **case)
+        assert gc[s] == len(ridx), f"s={s}"
+        np.testing.assert_array_equal(gi[s, :len(ridx)], ridx, err_msg=f"s={s} n_p={n_p}")
+        np.testing.assert_array_equal(gs[s, :len(ridx)].view(np.uint32), rsc.view(np.uint32), err_msg=f"s={s}")
+        assert (gi[s, len(ridx):] == -1).all() and (gs[s, len(ridx):] == 0).all()
+    # the lazy pass (one work-group per sequence, children of kept parents
+    # only) selects exactly what the full pass selects
+    idx2 = torch.full((S, K), -9, dtype=torch.int32, device="cuda")
+    sc2 = torch.full((S, K), 7.0, dtype=torch.float32, device="cuda")
+    cnt2 = torch.full((S,), -9, dtype=torch.int32, device="cuda")
+    kka.kka_score_topk(lay, level, npg, torch.from_numpy(anc).cuda(), k_page=K, k_grid=case["k_grid"],
+                       k_chunk=case["k_chunk"], page_idx_out=idx2, page_score_out=sc2, n_selected_out=cnt2,
+                       lazy=True)
+    torch.cuda.synchronize()
+    assert kka.kka_device_error() == 0
+    np.testing.assert_array_equal(idx2.cpu().numpy(), gi)
+    np.testing.assert_array_equal(sc2.cpu().numpy().view(np.uint32), gs.view(np.uint32))
+    np.testing.assert_array_equal(cnt2.cpu().numpy(), gc)
