@@ -81,7 +81,7 @@ PoolWs pool_ws(const kka_kpool* kp, const kka_seqs* sq, int64_t items, int32_t m
   if (mode == KKA_WEIGHT_VARIANCE) {
     const size_t tb = (size_t)sq->total_blocks;
     w.partial = align256(tb * LH * D * sizeof(float));
-    w.q = align256(tb * LH * sizeof(float));
+    w.q = align256(tb * LH * sizeof(double));
     w.var = align256((size_t)sq->num_seqs * LH * sizeof(double));
   } else {
     const LayerSplit ls = layer_split(items, kp->num_layers, pool_layer_bytes(kp));
@@ -191,7 +191,7 @@ kka_status kka_pool_blocks(const kka_kpool* kp, const kka_seqs* seqs, const int3
     a.n_split = ls.n_split;
     a.lps = ls.lps;
     a.partial = reinterpret_cast<float*>(wsb);
-    a.stats_q = reinterpret_cast<float*>(wsb + ws.partial);
+    a.stats_q = reinterpret_cast<double*>(wsb + ws.partial);
     hipError_t e = launch_pool_stats(a, s);
     if (e != hipSuccess) return KKA_ERR_DEVICE;
     WeightArgs w = {};

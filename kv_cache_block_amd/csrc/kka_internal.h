@@ -111,7 +111,7 @@ struct PoolArgs {
   int64_t vb_stride;      // rows per sequence in `out`, 0 = row is the global block id
   float* partial;         // layer-split partial sums, or per-(l,h) token sums
   uint32_t* done;         // per-item arrival counters of a layer split (zero between calls)
-  float* stats_q;         // per-(item, l, h) sums of squares
+  double* stats_q;        // per-(item, l, h) sums of squares (fp64: see pool_stats_kernel)
   uint32_t* err;
   PoolShape ps;
   int32_t window;         // anchor only
@@ -119,7 +119,7 @@ struct PoolArgs {
 
 struct WeightArgs {
   const float* s1;  // [total_blocks][L*H][D] token sums
-  const float* q;   // [total_blocks][L*H] sums of squares
+  const double* q;  // [total_blocks][L*H] sums of squares
   double* var;      // [S][L*H]
   float* head_weight;
   const int32_t* seq_len;

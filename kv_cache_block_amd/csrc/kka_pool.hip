@@ -255,10 +255,16 @@ __global__ __launch_bounds__(256) void pool_finish_kernel(PoolArgs a) {
 // block's tokens, kUnroll loads in flight, so its 8 token sums need no
 // reduction across threads and are stored from registers.  The m row slots
 // of a group take m layers at a time; only the sums of squares of a head's
-// D/8 columns are added through LDS, once per round of layers.
+// D/8 columns are added through LDS, once per round of layers.  The sums
+// of squares are fp64 (squares of bf16 values are exact there, and so are
+// their sums for any realistic spread of magnitudes): the variance pass then
+// finds exactly 0 for a head whose keys do not change over the sequence (a
+// sequence of one token, say), which the definition maps to uniform
+// weights, instead of fp32 rounding noise that the normalisation would
+// blow up into weights.
 template <int MAXT>
 __global__ __launch_bounds__(MAXT) void pool_stats_kernel(PoolArgs a) {
-  __shared__ float redq[MAXT];
+  __shared__ double redq[MAXT];
   const int tid = threadIdx.x;
   const int32_t item = blockIdx.x / a.n_split;
   const int32_t j = blockIdx.x - item * a.n_split;
@@ -276,7 +282,7 @@ __global__ __launch_bounds__(MAXT) void pool_stats_kernel(PoolArgs a) {
     const int32_t l = lr + slot;
     if (l < l1) {
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      float sq = 0.f;
+      double sq = 0.0;
       const uint16_t* tp = a.k + (int64_t)l * a.sL + it.p * a.sB + (int64_t)h * a.sH + (int64_t)dg * 8;
       int32_t ti = 0;
       for (; ti + kUnroll <= n_tok; ti += kUnroll) {
@@ -290,8 +296,8 @@ __global__ __launch_bounds__(MAXT) void pool_stats_kernel(PoolArgs a) {
             const float x0 = bf16_lo(v[u][c]), x1 = bf16_hi(v[u][c]);
             acc[2 * c] += x0;
             acc[2 * c + 1] += x1;
-            sq = fmaf(x0, x0, sq);
-            sq = fmaf(x1, x1, sq);
+            sq = fma((double)x0, (double)x0, sq);
+            sq = fma((double)x1, (double)x1, sq);
           }
         }
       }
@@ -302,8 +308,8 @@ __global__ __launch_bounds__(MAXT) void pool_stats_kernel(PoolArgs a) {
           const float x0 = bf16_lo(v[c]), x1 = bf16_hi(v[c]);
           acc[2 * c] += x0;
           acc[2 * c + 1] += x1;
-          sq = fmaf(x0, x0, sq);
-          sq = fmaf(x1, x1, sq);
+          sq = fma((double)x0, (double)x0, sq);
+          sq = fma((double)x1, (double)x1, sq);
         }
       }
       float4* dst = reinterpret_cast<float4*>(a.partial + (((int64_t)item * a.L + l) * a.H) * a.D + (int64_t)q * 8);
@@ -317,7 +323,7 @@ __global__ __launch_bounds__(MAXT) void pool_stats_kernel(PoolArgs a) {
       const int32_t sl = tid / a.H, hh = tid - sl * a.H;
       const int32_t ll = lr + sl;
       if (ll < l1) {
-        float s = 0.f;
+        double s = 0.0;
         for (int32_t x = 0; x < DG; ++x) s += redq[sl * a.ps.rg + hh * DG + x];
         a.stats_q[((int64_t)item * a.L + ll) * a.H + hh] = s;
       }
@@ -325,6 +331,9 @@ __global__ __launch_bounds__(MAXT) void pool_stats_kernel(PoolArgs a) {
     __syncthreads();
   }
 }
+
+// Relative floor of a head's one-pass variance (see head_var_kernel).
+constexpr double kVarFloor = 0x1p-24;
 
 // Pass 2: one group per (sequence, head): temporal variance of the head,
 //   var = ( sum_tau |x_tau|^2 / T  -  sum_d (sum_tau x_tau,d / T)^2 ) / D,
@@ -389,7 +398,7 @@ __global__ __launch_bounds__(256) void head_var_kernel(WeightArgs w) {
     }
   }
   double qs = 0.0;
-  for (int32_t b = b0 + tid; b < b1; b += 256) qs += (double)w.q[(int64_t)b * w.LH + lh];
+  for (int32_t b = b0 + tid; b < b1; b += 256) qs += w.q[(int64_t)b * w.LH + lh];
   r1[tid] = m2;
   r2[tid] = qs;
   __syncthreads();
@@ -401,8 +410,13 @@ __global__ __launch_bounds__(256) void head_var_kernel(WeightArgs w) {
     __syncthreads();
   }
   if (tid == 0) {
-    double v = T > 0 ? (r2[0] / (double)T - r1[0]) / (double)w.D : 0.0;
-    w.var[(int64_t)s * w.LH + lh] = v > 0.0 ? v : 0.0;
+    // The one-pass form E[x^2] - E[x]^2 cancels for a head whose keys do not
+    // vary: a result within its fp64 rounding (below 2^-24 of the mean
+    // square, far under any real key statistics) is a head of variance 0,
+    // as one token, or the same key at every token, has by definition.
+    const double msq = T > 0 ? r2[0] / (double)T : 0.0;
+    const double v = T > 0 ? (msq - r1[0]) / (double)w.D : 0.0;
+    w.var[(int64_t)s * w.LH + lh] = v > kVarFloor * msq / (double)w.D ? v : 0.0;
   }
 }
 

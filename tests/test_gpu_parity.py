@@ -940,3 +940,76 @@ def test_selection_random_configurations(seed):
     np.testing.assert_array_equal(idx2.cpu().numpy(), gi)
     np.testing.assert_array_equal(sc2.cpu().numpy().view(np.uint32), gs.view(np.uint32))
     np.testing.assert_array_equal(cnt2.cpu().numpy(), gc)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_pool_and_anchor_random_shapes(seed):
+    """Seeded sweep over key-pool shapes (layers 1-32, KV heads 1-8,
+    head_dim 8-256, blocks of 1-64 tokens, 1-24 ragged sequences, windows
+    1-40; at most 16M key elements), so that pooling and anchors run unsplit,
+    split and combined in one launch, and split with a second launch;
+    uniform or head-variance weights.  v_b, weights and anchors against the
+    oracle."""
+    rng = np.random.default_rng(2000 + seed)
+    L = int(rng.integers(1, 33))
+    H = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([8, 16, 32, 64, 128, 256]))
+    B = int(rng.choice([1, 4, 8, 16, 32, 64]))
+    S = int(rng.integers(1, 25))
+    per_token = L * H * D
+    max_len = max(1, min(600, (16 << 20) // (per_token * S)))
+    lengths = rng.integers(0, max_len + 1, S)
+    lengths[0] = max(1, lengths[0])
+    mode = "variance" if rng.random() < 0.4 else "uniform"
+    window = int(rng.integers(1, 41))
+    say(f"pool random seed={seed} L={L} H={H} D={D} B={B} S={S} max_len={max_len} {mode} W={window}")
+    w = ragged_workload(3000 + seed, S, L, H, D, B, 0, 0, mode=mode, window=window, lengths=lengths,
+                        offset=0.5 if mode == "variance" else 0.0)
+    sel, _ = run_selector(w)
+    assert kka.kka_device_error() == 0
+    okp = oracle.KPool.of(w)
+    wref = None
+    if mode == "variance":
+        wref = oracle.weights_all(okp, w.seq_len, w.block_offsets, w.block_table)
+        np.testing.assert_allclose(sel.head_weight.cpu().numpy(), wref, rtol=WEIGHT_RTOL, atol=0)
+    got = vb_rows(sel, w)
+    ref = oracle_vb(w, range(w.total_blocks), wref)
+    for b, v in ref.items():
+        np.testing.assert_allclose(got[b], v, atol=ATOL, rtol=0, err_msg=f"block {b}")
+    anc = sel.anchors.cpu().numpy()
+    for s in range(w.S):
+        a = oracle.pool_anchor(okp, oracle.seq_table(w.block_offsets, w.block_table, s), int(w.seq_len[s]),
+                               w.window, None if wref is None else wref[s])
+        np.testing.assert_allclose(anc[s], a, atol=ATOL, rtol=0, err_msg=f"anchor {s}")
+
+
+def test_variance_weights_of_constant_sequences_are_uniform():
+    """Head-variance weights where the temporal variance is exactly 0: a
+    sequence of one token, and a sequence whose keys repeat the same token
+    at every position (over several blocks).  The definition then gives
+    uniform weights; the GPU must find exactly 0 (not fp32 rounding noise,
+    which the normalisation would turn into arbitrary weights).  The other
+    sequences' weights and every v_b against the oracle."""
+    say("variance weights of constant sequences")
+    L, H, D, B = 22, 8, 128, 32
+    w = ragged_workload(41, 4, L, H, D, B, 0, 0, mode="variance", lengths=[63, 1, 150, 40])
+    f = synth.bf16_bits_to_f32(w.k).reshape(L, w.P, B, H, D)
+    # sequence 2: every token repeats its first token
+    for i in range(int(w.block_offsets[2]), int(w.block_offsets[3])):
+        p = int(w.block_table[i])
+        p0 = int(w.block_table[w.block_offsets[2]])
+        f[:, p, :, :, :] = f[:, p0, 0:1, :, :]
+    w.k = synth.to_bf16_bits(f)
+    sel, _ = run_selector(w)
+    assert kka.kka_device_error() == 0
+    okp = oracle.KPool.of(w)
+    wref = oracle.weights_all(okp, w.seq_len, w.block_offsets, w.block_table)
+    wgpu = sel.head_weight.cpu().numpy()
+    uniform = np.float32(1.0 / (L * H))
+    for s in (1, 2):
+        np.testing.assert_array_equal(wref[s], np.full(L * H, uniform, np.float32))
+        np.testing.assert_array_equal(wgpu[s], np.full(L * H, uniform, np.float32), err_msg=f"seq {s}")
+    np.testing.assert_allclose(wgpu, wref, rtol=WEIGHT_RTOL, atol=0)
+    got = vb_rows(sel, w)
+    for b, v in oracle_vb(w, range(w.total_blocks), wref).items():
+        np.testing.assert_allclose(got[b], v, atol=ATOL, rtol=0, err_msg=f"block {b}")
