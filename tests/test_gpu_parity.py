@@ -877,9 +877,11 @@ def test_selection_random_configurations(seed):
     fan-outs 1-20, k per level from 0 to beyond the level's size, 1-300
     sequences of 0-700 pages (so one-launch and two-launch batches, levels
     of every ranking path, parented and not), head_dim 8-256, and a share
-    of exactly-zero and tied scores.  Every sequence bit-exact against the
-    oracle's selection of the GPU's own affinities, and the lazy pass
-    bit-identical to the full pass."""
+    of exactly-zero and tied scores.  Chunk and grid vectors and every
+    present row's affinity against the oracle (from the GPU's own page
+    vectors and anchor); every selection bit-exact against the oracle's
+    selection of the GPU's own affinities, and the lazy pass bit-identical
+    to the full pass."""
     rng = np.random.default_rng(1000 + seed)
     hier = int(rng.integers(0, 2))
     ppc, cpg = int(rng.integers(1, 21)), int(rng.integers(1, 21))
@@ -913,15 +915,25 @@ def test_selection_random_configurations(seed):
     torch.cuda.synchronize()
     assert kka.kka_device_error() == 0
     af, gi, gs, gc = aff.cpu().numpy(), idx.cpu().numpy(), sc.cpu().numpy(), cnt.cpu().numpy()
+    lv = level.cpu().numpy()
     for s in range(S):
         n_p = int(n_pages[s])
+        rows = np.arange(n_p)
         if hier:
             n_c = -(-n_p // ppc)
             n_g = -(-n_c // cpg)
             a_c = af[s, lay.chunk_row0:lay.chunk_row0 + n_c]
             a_g = af[s, lay.grid_row0:lay.grid_row0 + n_g]
+            if n_p:
+                oc, og = oracle.build_levels(lv[s, :n_p], ppc, cpg)
+                np.testing.assert_allclose(lv[s, lay.chunk_row0:lay.chunk_row0 + n_c], oc, atol=ATOL, rtol=0)
+                np.testing.assert_allclose(lv[s, lay.grid_row0:lay.grid_row0 + n_g], og, atol=ATOL, rtol=0)
+            rows = np.concatenate([rows, lay.chunk_row0 + np.arange(n_c), lay.grid_row0 + np.arange(n_g)])
         else:
             a_c = a_g = None
+        if len(rows):
+            np.testing.assert_allclose(af[s, rows], oracle.affinity(lv[s, rows], anc[s]), atol=ATOL, rtol=0,
+                                       err_msg=f"s={s}")
         ridx, rsc = oracle.select(af[s, :n_p], a_c, a_g, **case)
         assert gc[s] == len(ridx), f"s={s}"
         np.testing.assert_array_equal(gi[s, :len(ridx)], ridx, err_msg=f"s={s} n_p={n_p}")
