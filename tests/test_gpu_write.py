@@ -228,3 +228,46 @@ def test_7b_shape_64_sequences():
         torch.cuda.synchronize()
         if t in (0, 7, steps - 1):
             b.check(vb, tag=f"t={t}")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_pool_on_write_random_shapes(seed):
+    """Seeded sweep: layers 1-12, KV heads 1-8, head_dim 8-512 (at most 1024
+    16-byte pieces per token), blocks of 1-33 tokens, 1-12 sequences with
+    ragged prefills (0 to a few blocks, pooled by kka_pool_blocks), uniform
+    or frozen random weights, a seeded first step and 1-40 running steps
+    crossing block boundaries; pool contents bit for bit and every block
+    vector against the oracle after the first, a middle and the last step."""
+    rng = np.random.default_rng(4000 + seed)
+    L = int(rng.integers(1, 13))
+    H = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([8, 16, 24, 64, 128, 256, 512]))
+    while H * D // 8 > 1024:
+        H //= 2
+    B = int(rng.integers(1, 34))
+    S = int(rng.integers(1, 13))
+    steps = int(rng.integers(1, 41))
+    prefill = rng.integers(0, 3 * B + 1, S).astype(np.int32)
+    given = rng.random() < 0.5
+    say(f"pool-on-write random seed={seed} L={L} H={H} D={D} B={B} S={S} steps={steps} given={given}")
+    cap = [-(-(int(n) + steps) // B) for n in prefill]
+    b = Batch(4100 + seed, L, H, D, B, cap=cap, prefill=prefill)
+    stride = max(cap)
+    weights = None
+    hw = None
+    if given:
+        wr = rng.random((S, L * H)).astype(np.float32) + 0.05
+        weights = (wr / wr.sum(axis=1, keepdims=True)).astype(np.float32)
+        hw = torch.from_numpy(weights).cuda()
+    vb = torch.zeros((S, stride, D), dtype=torch.float32, device="cuda")
+    kka.kka_pool_blocks(b.kp, b.prefill_seqs(), vb, mode=kka.WEIGHT_GIVEN if given else kka.WEIGHT_UNIFORM,
+                        head_weight=hw, vb_seq_stride=stride)
+    running = torch.zeros((S, D), dtype=torch.float32, device="cuda")
+    for t in range(steps):
+        nk = b.step_tokens()
+        kka.kka_pool_on_write(b.kp, b.seqs, vb, running, new_k=nk, seed=(t == 0), vb_seq_stride=stride,
+                              mode=kka.WEIGHT_GIVEN if given else kka.WEIGHT_UNIFORM, head_weight=hw)
+        torch.cuda.synchronize()
+        if t in (0, steps // 2, steps - 1):
+            b.check(vb, weights=weights, tag=f"t={t}")
+    assert kka.kka_device_error() == 0
