@@ -183,3 +183,49 @@ def test_attention_128k_full_size_properties():
     np.testing.assert_array_equal(sc[0].view(np.uint32), rsc.view(np.uint32))
     run = w.extra["anchor_run"]
     assert set(range(run * 32, run * 32 + 32)) <= set(idx[0].tolist())
+
+
+def _attention_shape(rng):
+    """One random shape that one of the two logit kernels accepts (the rules of
+    kka_attention_topk), and the kernel it goes to."""
+    while True:
+        D = int(rng.choice([8, 16, 32, 64, 128, 256, 512]))
+        H = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.integers(1, 17))
+        B = int(rng.choice([1, 2, 4, 8, 16, 24, 32, 48, 64, 5, 12]))
+        mfma = D in (32, 64, 128, 256) and G <= 16 and (16 % B == 0 or B % 16 == 0)
+        vector = G <= 8 and (D // 8) * H <= 256 and H * G * (B + 1) <= 15360
+        if mfma or vector:
+            return D, H, G, B, "matrix" if mfma else "vector"
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_attention_random_shapes(seed):
+    """Seeded sweep over shapes both logit kernels take (head_dim 8-512, KV
+    heads 1-8, 1-16 query heads per KV head, blocks of 1-64 tokens, 1-12 ragged
+    sequences with empty ones and ragged tails, k 0-40, scale 0.25-2 over
+    sqrt(head_dim)): block masses and the top-k against the oracle."""
+    rng = np.random.default_rng(5000 + seed)
+    D, H, G, B, path = _attention_shape(rng)
+    L = int(rng.integers(1, 7))
+    S = int(rng.integers(1, 13))
+    Hq = H * G
+    max_len = max(1, min(900, (2 << 20) // (L * H * D * S)))
+    lengths = rng.integers(0, max_len + 1, S)
+    if S > 1:
+        lengths[int(rng.integers(0, S))] = 0
+    k = int(rng.integers(0, 41))
+    scale = float(rng.uniform(0.25, 2.0)) / math.sqrt(D)
+    say(f"attention random seed={seed} {path} D={D} H={H} G={G} B={B} L={L} S={S} max_len={max_len} k={k}")
+    w = ragged_workload(5100 + seed, S, L, H, D, B, 0, 0, lengths=lengths)
+    q = rng.standard_normal((w.S, L, Hq, D)).astype(np.float32)
+    out, idx, sc, cnt = run_attention(w, q, Hq, k, scale)
+    if k == 0:
+        okp = oracle.KPool.of(w)
+        for s in range(w.S):
+            T = int(w.seq_len[s])
+            tab = oracle.seq_table(w.block_offsets, w.block_table, s)
+            ref = oracle.attention_blocks(okp, tab, T, q[s], scale)
+            np.testing.assert_allclose(out[s, :len(ref)], ref, rtol=RTOL, atol=ATOL_MASS, err_msg=f"s={s}")
+    else:
+        check(w, q, Hq, k, scale, out, idx, sc, cnt, f"random seed={seed}")
