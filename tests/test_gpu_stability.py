@@ -210,3 +210,56 @@ def test_stability_serving_batch_spike_and_parity():
         assert (scores[s][topic == v.anchor_topic[s]] == 1.0).all()
         assert (scores[s][topic == other[s]] == np.float32(0.05)).all()
         assert (scores[s][(topic != v.anchor_topic[s]) & (topic != other[s])] == 0.0).all()
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_stability_random_configurations(seed):
+    """Seeded sweep: 1-40 sequences of up to 3000 pages (so that both the
+    one-launch and the two-launch scoring paths run), head_dim 8-520, flat
+    or hierarchical layouts with random fan-outs and k, window 1-32, theta
+    0.3-0.7, 6-24 steps; on odd seeds sequences gain pages between steps
+    (their words zero-filled beforehand).  Words and scores against the
+    oracle on the GPU's own affinities, the selection against the plain
+    pass."""
+    rng = np.random.default_rng(6000 + seed)
+    S = int(rng.integers(1, 41))
+    max_pages = int(rng.integers(1, 3001))
+    D = int(rng.choice([8, 24, 64, 128, 256, 520]))
+    hier = bool(rng.random() < 0.6)
+    ppc, cpg = int(rng.integers(1, 33)), int(rng.integers(1, 17))
+    cfg = dict(hierarchical=int(hier), pages_per_chunk=ppc, chunks_per_grid=cpg,
+               k_grid=int(rng.integers(1, 9)) if hier else 0, k_chunk=int(rng.integers(1, 33)) if hier else 0,
+               k_page=int(rng.integers(0, 97)))
+    W = int(rng.integers(1, 33))
+    theta = float(rng.uniform(0.3, 0.7))
+    steps = int(rng.integers(6, 25))
+    grow = seed % 2 == 1
+    final = rng.integers(0, max_pages + 1, S)
+    if grow:
+        start = np.minimum(final, rng.integers(0, max_pages + 1, S))
+        npg_list = [np.minimum(final, start + (final - start) * t // max(1, steps - 1)).astype(np.int32)
+                    for t in range(steps)]
+    else:
+        npg_list = [final.astype(np.int32)] * steps
+    say(f"stability random seed={seed} S={S} max_pages={max_pages} D={D} {cfg} W={W} theta={theta:.3f} "
+        f"steps={steps} grow={grow}")
+    lay, level, _, dirs = levels(6100 + seed, S, max_pages, D, cfg, final)
+    if grow:
+        history = torch.zeros((S, max_pages), dtype=torch.int32, device="cuda")
+        stab = torch.full((S, max_pages), SENTINEL_SCORE, dtype=torch.float32, device="cuda")
+    else:
+        history, stab = fresh_state(lay, final)
+    npg_steps = [torch.from_numpy(n).cuda() for n in npg_list]
+    if grow and cfg["hierarchical"]:
+        kka.kka_build_levels(lay, level, npg_steps[0])
+    anchors = drifting_anchors(6200 + seed, dirs, S, steps)
+    aff_hist = []
+    for t, aff in run_steps(lay, level, npg_steps, anchors, cfg, W, theta, history, stab):
+        if grow and cfg["hierarchical"] and t + 1 < steps:
+            kka.kka_build_levels(lay, level, npg_steps[t + 1])
+        aff_hist.append(aff)
+    check_against_oracle(aff_hist, npg_list, W, theta, history, stab, f"seed={seed}", absent_sentinel=not grow)
+    if grow:
+        words = history.cpu().numpy()
+        for s in range(S):
+            assert (words[s, int(final[s]):] == 0).all(), f"s={s}: absent words touched"
