@@ -337,15 +337,15 @@ constexpr double kVarFloor = 0x1p-24;
 
 // Pass 2: one group per (sequence, head): temporal variance of the head,
 //   var = ( sum_tau |x_tau|^2 / T  -  sum_d (sum_tau x_tau,d / T)^2 ) / D,
-// from the pass-1 sums, combined in fp64.  For head_dim <= 256 the group
-// splits into 256 / D lane groups of D lanes, group g summing blocks
-// g, g + ng, ... with kVarUnroll independent loads in flight; the groups'
-// sums are then added in group order (a fixed order, so the result is
-// reproducible).
+// from the pass-1 sums, combined in fp64.  D / 4 lanes cover a head's row
+// of sums with 16-byte loads; the 256 threads form 256 / (D / 4) such lane
+// groups, group g summing blocks g, g + ng, ... with kVarUnroll independent
+// loads in flight.  The groups' sums are then added in group order (a fixed
+// order, so the result is reproducible).
 constexpr int kVarUnroll = 4;
 
 __global__ __launch_bounds__(256) void head_var_kernel(WeightArgs w) {
-  __shared__ double part[256];
+  __shared__ double part[1024];  // [ng][D]: ng * D = 4 * 256 at most
   __shared__ double r1[256];
   __shared__ double r2[256];
   const int tid = threadIdx.x;
@@ -355,47 +355,43 @@ __global__ __launch_bounds__(256) void head_var_kernel(WeightArgs w) {
   const int32_t b1 = min(max(w.offs[s + 1], 0), w.total_blocks);
   const int32_t b0 = min(max(w.offs[s], 0), b1);
   const int64_t T = w.seq_len[s] > 0 ? w.seq_len[s] : 0;
-  const int64_t bstride = (int64_t)w.LH * w.D;  // floats from one block's sums to the next block's
-  const float* base = w.s1 + (int64_t)lh * w.D;
+  const int32_t nl = w.D / 4;  // lanes per row (head_dim is a multiple of 8, at most 1024)
+  const int32_t ng = 256 / nl;
+  const int32_t g = tid / nl, c = tid - g * nl;
+  const int64_t bstride = (int64_t)w.LH * nl;  // float4s from one block's sums to the next block's
+  const float4* base = reinterpret_cast<const float4*>(w.s1 + (int64_t)lh * w.D) + c;
+  if (g < ng) {
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    int32_t b = b0 + g;
+    for (; b + (kVarUnroll - 1) * ng < b1; b += kVarUnroll * ng) {
+      float4 x[kVarUnroll];
+#pragma unroll
+      for (int u = 0; u < kVarUnroll; ++u) x[u] = base[(int64_t)(b + u * ng) * bstride];
+#pragma unroll
+      for (int u = 0; u < kVarUnroll; ++u) {
+        acc[0] += (double)x[u].x;
+        acc[1] += (double)x[u].y;
+        acc[2] += (double)x[u].z;
+        acc[3] += (double)x[u].w;
+      }
+    }
+    for (; b < b1; b += ng) {
+      const float4 x = base[(int64_t)b * bstride];
+      acc[0] += (double)x.x;
+      acc[1] += (double)x.y;
+      acc[2] += (double)x.z;
+      acc[3] += (double)x.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) part[g * w.D + 4 * c + e] = acc[e];
+  }
+  __syncthreads();
   double m2 = 0.0;
-  if (w.D <= 256) {
-    const int32_t ng = 256 / w.D;
-    const int32_t g = tid / w.D, d = tid - g * w.D;
-    double acc = 0.0;
-    if (g < ng) {
-      int32_t b = b0 + g;
-      for (; b + (kVarUnroll - 1) * ng < b1; b += kVarUnroll * ng) {
-        float x[kVarUnroll];
-#pragma unroll
-        for (int u = 0; u < kVarUnroll; ++u) x[u] = base[(int64_t)(b + u * ng) * bstride + d];
-#pragma unroll
-        for (int u = 0; u < kVarUnroll; ++u) acc += (double)x[u];
-      }
-      for (; b < b1; b += ng) acc += (double)base[(int64_t)b * bstride + d];
-    }
-    part[tid] = acc;
-    __syncthreads();
-    if (tid < w.D) {
-      double s1 = 0.0;
-      for (int32_t q = 0; q < ng; ++q) s1 += part[q * w.D + tid];
-      const double mean = T > 0 ? s1 / (double)T : 0.0;
-      m2 = mean * mean;
-    }
-  } else {
-    for (int32_t d = tid; d < w.D; d += 256) {
-      double acc = 0.0;
-      int32_t b = b0;
-      for (; b + kVarUnroll - 1 < b1; b += kVarUnroll) {
-        float x[kVarUnroll];
-#pragma unroll
-        for (int u = 0; u < kVarUnroll; ++u) x[u] = base[(int64_t)(b + u) * bstride + d];
-#pragma unroll
-        for (int u = 0; u < kVarUnroll; ++u) acc += (double)x[u];
-      }
-      for (; b < b1; ++b) acc += (double)base[(int64_t)b * bstride + d];
-      const double mean = T > 0 ? acc / (double)T : 0.0;
-      m2 += mean * mean;
-    }
+  for (int32_t d = tid; d < w.D; d += 256) {
+    double s1 = 0.0;
+    for (int32_t q = 0; q < ng; ++q) s1 += part[q * w.D + d];
+    const double mean = T > 0 ? s1 / (double)T : 0.0;
+    m2 += mean * mean;
   }
   double qs = 0.0;
   for (int32_t b = b0 + tid; b < b1; b += 256) qs += w.q[(int64_t)b * w.LH + lh];
@@ -439,26 +435,56 @@ __global__ __launch_bounds__(256) void head_norm_kernel(WeightArgs w) {
         total > 0.0 ? (float)(w.var[(int64_t)s * w.LH + x] / total) : (float)(1.0 / (double)w.LH);
 }
 
-// Pass 3: v_b = sum_{l,h} w[s][l,h] * s1[b][l][h][:] / n_b.
-__global__ __launch_bounds__(256) void pool_combine_kernel(PoolArgs a, const float* __restrict__ wts) {
+// Pass 3: v_b = sum_{l,h} w[s][l,h] * s1[b][l][h][:] / n_b.  One group of
+// head_dim threads per block: D / 4 lanes cover a row with 16-byte loads,
+// and lane group g (of 4) accumulates heads lh = g, g + 4, ... in order; the
+// four group sums are added as (g0 + g1) + (g2 + g3), a fixed order.
+constexpr int kCombineUnroll = 4;
+
+__global__ __launch_bounds__(1024) void pool_combine_kernel(PoolArgs a, const float* __restrict__ wts) {
+  extern __shared__ float4 gsum[];  // [3][D / 4]: the sums of groups 1..3
   const int32_t item = blockIdx.x;
   const Item it = locate(a, item, false);
-  if (it.row < 0) return;
+  if (it.row < 0) return;  // the same for every thread of the group
   const int32_t LH = a.L * a.H;
-  for (int32_t d = threadIdx.x; d < a.D; d += blockDim.x) {
-    // four accumulators (heads lh = 0, 1, 2, 3 mod 4), added in a fixed
-    // order, so the loads and FMAs of four heads overlap
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    const float* src = a.partial + (int64_t)item * LH * a.D + d;
-    const float* wr = wts + (int64_t)it.s * LH;
-    int32_t lh = 0;
-    for (; lh + 3 < LH; lh += 4) {
+  const int32_t nl = a.D / 4;
+  const int32_t g = threadIdx.x / nl, c = threadIdx.x - g * nl;
+  const float4* src = reinterpret_cast<const float4*>(a.partial + (int64_t)item * LH * a.D) + c;
+  const float* wr = wts + (int64_t)it.s * LH;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  int32_t lh = g;
+  for (; lh + 4 * (kCombineUnroll - 1) < LH; lh += 4 * kCombineUnroll) {
+    float4 x[kCombineUnroll];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] = fmaf(wr[lh + u], src[(int64_t)(lh + u) * a.D], acc[u]);
+    for (int u = 0; u < kCombineUnroll; ++u) x[u] = src[(int64_t)(lh + 4 * u) * nl];
+#pragma unroll
+    for (int u = 0; u < kCombineUnroll; ++u) {
+      const float wv = wr[lh + 4 * u];
+      acc.x = fmaf(wv, x[u].x, acc.x);
+      acc.y = fmaf(wv, x[u].y, acc.y);
+      acc.z = fmaf(wv, x[u].z, acc.z);
+      acc.w = fmaf(wv, x[u].w, acc.w);
     }
-    for (; lh < LH; ++lh) acc[lh & 3] = fmaf(wr[lh], src[(int64_t)lh * a.D], acc[lh & 3]);
-    const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    a.out[it.row * a.D + d] = it.n_b > 0 ? sum / (float)it.n_b : 0.f;
+  }
+  for (; lh < LH; lh += 4) {
+    const float wv = wr[lh];
+    const float4 x = src[(int64_t)lh * nl];
+    acc.x = fmaf(wv, x.x, acc.x);
+    acc.y = fmaf(wv, x.y, acc.y);
+    acc.z = fmaf(wv, x.z, acc.z);
+    acc.w = fmaf(wv, x.w, acc.w);
+  }
+  if (g > 0) gsum[(g - 1) * nl + c] = acc;
+  __syncthreads();
+  if (g == 0) {
+    const float4 a1 = gsum[c], a2 = gsum[nl + c], a3 = gsum[2 * nl + c];
+    const float nb = (float)it.n_b;
+    float4 v;
+    v.x = it.n_b > 0 ? ((acc.x + a1.x) + (a2.x + a3.x)) / nb : 0.f;
+    v.y = it.n_b > 0 ? ((acc.y + a1.y) + (a2.y + a3.y)) / nb : 0.f;
+    v.z = it.n_b > 0 ? ((acc.z + a1.z) + (a2.z + a3.z)) / nb : 0.f;
+    v.w = it.n_b > 0 ? ((acc.w + a1.w) + (a2.w + a3.w)) / nb : 0.f;
+    reinterpret_cast<float4*>(a.out + it.row * a.D)[c] = v;
   }
 }
 
@@ -643,8 +669,9 @@ hipError_t launch_head_weights(const WeightArgs& w, hipStream_t st) {
 
 hipError_t launch_pool_combine(const PoolArgs& a, const float* wts, hipStream_t st) {
   if (a.n_items <= 0) return hipSuccess;
-  hipLaunchKernelGGL(pool_combine_kernel, dim3((unsigned)a.n_items), dim3((unsigned)small_block(a.D)), 0, st, a,
-                     wts);
+  // head_dim threads (four lane groups of head_dim / 4), 3 * head_dim * 4 bytes of LDS
+  hipLaunchKernelGGL(pool_combine_kernel, dim3((unsigned)a.n_items), dim3((unsigned)a.D),
+                     (size_t)3 * a.D * sizeof(float), st, a, wts);
   return hipGetLastError();
 }
 
