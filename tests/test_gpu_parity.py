@@ -80,7 +80,7 @@ def test_pool_uniform_matches_oracle(shape):
         np.testing.assert_allclose(got[b], v, atol=ATOL, rtol=0, err_msg=f"block {b}")
 
 
-@pytest.mark.parametrize("shape", POOL_SHAPES[:3])
+@pytest.mark.parametrize("shape", POOL_SHAPES)
 def test_pool_variance_weights_match_oracle(shape):
     S, L, H, D, B, lo, hi = shape
     say(f"pool variance {shape}")
