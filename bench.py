@@ -593,10 +593,23 @@ def cpu_baseline(w, step_bytes, seconds):
         if el >= seconds or reps >= 50:
             break
     gbps = reps * step_bytes / el / 1e9
+    # the per-decode-step part alone (chunk and grid vectors, affinities, hierarchical top-K)
+    n_sel = 0
+    t1 = time.perf_counter()
+    while True:
+        oracle.score_select(pages, a, w.select)
+        n_sel += 1
+        el_sel = time.perf_counter() - t1
+        if el_sel >= min(2.0, seconds) or n_sel >= 200:
+            break
     return {"value": round(gbps, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} whole step(s) of the same 131072-token workload ({reps * step_bytes / 1e9:.2f} GB "
                       f"of algorithmic bytes) in {el:.1f} s on one host core",
-            "ms_per_step": round(el * 1e3 / reps, 1), "host": host_info()}
+            "ms_per_step": round(el * 1e3 / reps, 1),
+            "levels_score_topk_ms_per_step": round(el_sel * 1e3 / n_sel, 3),
+            "levels_score_topk_sample": f"{n_sel} decode step(s) of the same sequence: chunk and grid vectors, "
+                                        "affinity of every row, hierarchical top-K",
+            "host": host_info()}
 
 
 def cpu_baseline_all_cores(w, step_bytes, seconds):

@@ -106,3 +106,16 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(kka, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         kka.lib()
+
+
+def test_cpu_baseline_fields_on_a_small_workload():
+    """The oracle leg of the benchmark on a reduced 7B-shape sequence (256
+    blocks of 16 tokens, 2 layers): whole-step rate, per-step time and the
+    decode-step part timed alone."""
+    import synth
+    w = synth.config3(0, n_blocks=256, L=2)
+    step_bytes = 256 * 16 * 2 * w.H * w.D * 2
+    cb = bench.cpu_baseline(w, step_bytes, 0.2)
+    assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["unit"] == "GB/s"
+    assert cb["value"] > 0 and cb["ms_per_step"] > 0 and cb["levels_score_topk_ms_per_step"] > 0
+    assert cb["levels_score_topk_ms_per_step"] < cb["ms_per_step"]
