@@ -355,9 +355,16 @@ typedef struct kka_select {
  * of the batch fits on the chip at once, the call is one launch on
  * `stream`: the work-group that completes a sequence's last tile selects
  * that sequence (affinities pass between work-groups through device-scope
- * stores and loads).  Larger batches run as two launches: the scoring
- * pass, then one selecting work-group per sequence.  Results are the same
- * either way.
+ * stores and loads).  Larger batches whose levels are small -- every level
+ * offers at most 256 candidates (all grids; the chunks of the kept grids;
+ * the pages of the kept chunks; all pages of a flat layout) and every k is
+ * at most 256 -- are one launch too: a work-group per sequence selects
+ * coarse to fine on its own, re-scoring its candidate rows with the
+ * scoring tiles' code, and no work-group reads what another writes.  Other
+ * batches run as two launches: the scoring pass, then one selecting
+ * work-group per sequence.  KKA_SCORE_TWO_LAUNCH=1 in the environment sends
+ * every call to the two-launch path.  Results are the same, bit for bit,
+ * on every path.
  */
 KKA_API kka_status kka_score_topk(const kka_level_layout* lay, const float* level_buf, const int32_t* n_pages,
                           const float* anchors, const kka_select* sel, float* affinity_out, int32_t* page_idx_out,

@@ -245,14 +245,40 @@ def new_workspace(nbytes: int, device="cuda") -> Optional[torch.Tensor]:
     return torch.zeros(int(nbytes), dtype=torch.uint8, device=device)
 
 
+def _torch_stream(stream, device) -> Optional[torch.cuda.Stream]:
+    """`stream` as a torch stream object when it is not torch's current stream
+    on `device` (None when it is, or when stream is None)."""
+    if stream is None:
+        return None
+    cur = torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        st = stream
+    else:
+        st = torch.cuda.ExternalStream(int(stream), device=device)
+    return None if st.cuda_stream == cur.cuda_stream else st
+
+
+def order_after_current(stream, device, *tensors):
+    """Makes work enqueued on `stream` start after everything already queued
+    on torch's current stream (zero fills, uploads), and tells torch's
+    allocator that `tensors` are in use on `stream`, so their memory is not
+    handed out again before that work ends.  No-op on the current stream."""
+    st = _torch_stream(stream, device)
+    if st is None:
+        return
+    st.wait_stream(torch.cuda.current_stream(device))
+    for t in tensors:
+        if t is not None:
+            t.record_stream(st)
+
+
 def _ws(ws: Optional[torch.Tensor], need: int, device, stream=None) -> tuple:
     if need <= 0 and ws is None:
         return None, 0, None
     if ws is None:
+        # zero-filled on torch's current stream; the call may run on another
         ws = new_workspace(need, device)
-        if stream is not None:
-            # zero-filled on torch's current stream; the call runs on `stream`
-            torch.cuda.current_stream(ws.device).synchronize()
+        order_after_current(stream, ws.device, ws)
     if ws.numel() * ws.element_size() < need:
         raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, needs {need}")
     return _dev(ws, "workspace"), ws.numel() * ws.element_size(), ws
@@ -360,8 +386,11 @@ def kka_build_levels(lay: LevelLayout, level_buf: torch.Tensor, n_pages: torch.T
     _check(lib().kka_build_levels(ctypes.byref(lay.c), lp, npp, fd, _stream(stream)), "kka_build_levels")
 
 
-def kka_score_topk_workspace(lay: LevelLayout, with_affinity_out: bool) -> int:
-    sel = c_select(0, 0, 0)
+def kka_score_topk_workspace(lay: LevelLayout, with_affinity_out: bool, k_page: int = 0, k_grid: int = 0,
+                             k_chunk: int = 0) -> int:
+    """Workspace bytes of a kka_score_topk call (tile counters, plus scratch
+    affinities when affinity_out is not given)."""
+    sel = c_select(int(k_grid), int(k_chunk), int(k_page))
     return int(lib().kka_score_topk_workspace(ctypes.byref(lay.c), ctypes.byref(sel), 1 if with_affinity_out else 0))
 
 
@@ -383,7 +412,7 @@ def kka_score_topk(lay: LevelLayout, level_buf: torch.Tensor, n_pages: torch.Ten
     sc = _dev(page_score_out, "page_score_out", torch.float32, min_numel=S * k_page, allow_none=True)
     cnt = _dev(n_selected_out, "n_selected_out", torch.int32, min_numel=S, allow_none=True)
     aff = _dev(affinity_out, "affinity_out", torch.float32, min_numel=S * lay.rows_per_seq, allow_none=True)
-    need = kka_score_topk_workspace(lay, affinity_out is not None)
+    need = kka_score_topk_workspace(lay, affinity_out is not None, k_page, k_grid, k_chunk)
     wp, wbytes, keep = _ws(workspace, need, level_buf.device, stream)
     sel = c_select(int(k_grid), int(k_chunk), int(k_page))
     if history is not None:

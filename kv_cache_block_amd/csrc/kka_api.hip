@@ -4,6 +4,7 @@
 #include <mutex>
 
 #include <cmath>
+#include <cstdlib>
 
 #include "kka_internal.h"
 
@@ -72,7 +73,7 @@ inline int64_t pool_layer_bytes(const kka_kpool* kp) {
 // pooling keeps per-(block, layer, head) sums, sums of squares and fp64
 // per-(sequence, head) variances.
 struct PoolWs {
-  size_t counters = 0, partial = 0, q = 0, var = 0, total = 0;
+  size_t counters = 0, partial = 0, q = 0, var = 0, csum = 0, total = 0;
 };
 
 PoolWs pool_ws(const kka_kpool* kp, const kka_seqs* sq, int64_t items, int32_t mode) {
@@ -83,6 +84,7 @@ PoolWs pool_ws(const kka_kpool* kp, const kka_seqs* sq, int64_t items, int32_t m
     w.partial = align256(tb * LH * D * sizeof(float));
     w.q = align256(tb * LH * sizeof(double));
     w.var = align256((size_t)sq->num_seqs * LH * sizeof(double));
+    w.csum = align256((size_t)sq->num_seqs * D * sizeof(double));
   } else {
     const LayerSplit ls = layer_split(items, kp->num_layers, pool_layer_bytes(kp));
     if (ls.n_split > 1) {
@@ -90,7 +92,7 @@ PoolWs pool_ws(const kka_kpool* kp, const kka_seqs* sq, int64_t items, int32_t m
       w.partial = align256((size_t)items * ls.n_split * D * sizeof(float));
     }
   }
-  w.total = w.counters + w.partial + w.q + w.var;
+  w.total = w.counters + w.partial + w.q + w.var + w.csum;
   return w;
 }
 
@@ -139,6 +141,21 @@ bool level_geom(const kka_level_layout* lay, LevelGeom& g) {
 }
 
 inline kka_status launched(hipError_t e) { return e == hipSuccess ? KKA_OK : KKA_ERR_DEVICE; }
+
+// KKA_SCORE_TWO_LAUNCH=1 in the environment sends every scoring call to the
+// two-launch path (scoring launch, then selection launch; same results).
+inline bool two_launch_forced() {
+  const char* force = std::getenv("KKA_SCORE_TWO_LAUNCH");
+  return force && force[0] == '1';
+}
+
+// Whether the levels of this layout and these k fit the small selector of
+// the one-launch path for large batches.
+inline bool small_levels(const kka_level_layout* lay, const LevelGeom& g, const kka_select* sel) {
+  const bool h = lay->hierarchical != 0;
+  return small_select_fits(h, lay->max_pages, g.c_cap, g.g_cap, h ? lay->pages_per_chunk : 1,
+                           h ? lay->chunks_per_grid : 1, h ? sel->k_grid : 0, h ? sel->k_chunk : 0, sel->k_page);
+}
 
 }  // namespace
 }  // namespace kka
@@ -198,17 +215,26 @@ kka_status kka_pool_blocks(const kka_kpool* kp, const kka_seqs* seqs, const int3
     w.s1 = a.partial;
     w.q = a.stats_q;
     w.var = reinterpret_cast<double*>(wsb + ws.partial + ws.q);
+    w.csum = reinterpret_cast<double*>(wsb + ws.partial + ws.q + ws.var);
     w.head_weight = head_weight;
     w.seq_len = seqs->seq_len;
     w.offs = seqs->block_offsets;
+    w.table = seqs->block_table;
+    w.k = kp->k;
+    w.sL = kp->stride_layer;
+    w.sB = kp->stride_block;
+    w.sH = kp->stride_head;
+    w.P = kp->num_phys_blocks;
     w.S = seqs->num_seqs;
+    w.L = a.L;
+    w.H = a.H;
     w.LH = a.L * a.H;
     w.D = a.D;
     w.B = a.B;
     w.total_blocks = seqs->total_blocks;
     w.err = err;
     if ((e = launch_head_weights(w, s)) != hipSuccess) return KKA_ERR_DEVICE;
-    return launched(launch_pool_combine(a, head_weight, s));
+    return launched(launch_pool_combine(a, head_weight, w.csum, s));
   }
   if (items == 0) return KKA_OK;
   const LayerSplit ls = layer_split(items, a.L, pool_layer_bytes(kp));
@@ -527,12 +553,15 @@ kka_status prepare_score(const kka_level_layout* lay, const float* level_buf, co
   a.ppc = lay->hierarchical ? lay->pages_per_chunk : 1;
   a.cpg = lay->hierarchical ? lay->chunks_per_grid : 1;
   a.c_cap = g.c_cap;
+  a.g_cap = g.g_cap;
   a.n_pages = n_pages;
   a.anchors = anchors;
   // workspace: per-sequence tile counters, then scratch affinities
-  a.done = static_cast<uint32_t*>(workspace);
+  const bool forced = two_launch_forced();
+  a.small = !forced && small_levels(lay, g, sel) ? 1 : 0;
+  a.done = forced ? nullptr : static_cast<uint32_t*>(workspace);
   a.aff = affinity_out ? affinity_out
-                       : reinterpret_cast<float*>(static_cast<char*>(workspace) + score_counter_bytes(a.S));
+                       : reinterpret_cast<float*>(static_cast<char*>(workspace) + score_counter_bytes(lay->num_seqs));
   a.k_g = lay->hierarchical ? sel->k_grid : 0;
   a.k_c = lay->hierarchical ? sel->k_chunk : 0;
   a.k_p = sel->k_page;
@@ -542,7 +571,8 @@ kka_status prepare_score(const kka_level_layout* lay, const float* level_buf, co
   a.rows_per_tile = score_rows_per_tile(a.D);
   const int64_t tiles = (g.rows + a.rows_per_tile - 1) / a.rows_per_tile;
   a.tiles_per_seq = (int32_t)(tiles > 0 ? tiles : 1);
-  if ((int64_t)a.S * a.tiles_per_seq > 0x7fffffffLL) return KKA_ERR_SHAPE;
+  // the grid of any path fits: tiles of at least 16 rows, plus one selecting group per sequence
+  if ((int64_t)a.S * ((g.rows + 15) / 16 + 1) > 0x7fffffffLL) return KKA_ERR_SHAPE;
   a.err = err;
   return KKA_OK;
 }

@@ -29,6 +29,24 @@ constexpr int kMaxGridFloats = 16384;
 constexpr int64_t kMaxPagesPerSeq = (int64_t)1 << 30;
 // Affinity rows of one sequence a selecting work-group keeps in LDS.
 constexpr int kSelectLdsRows = 9216;
+// Candidates, and kept elements, per level that the one-launch selector
+// holds (small_select_fits).
+constexpr int kSmallSelect = 256;
+
+// True when a selection fits the one-launch path: a hierarchical layout
+// whose levels never offer more than kSmallSelect candidates (every grid;
+// the chunks of at most k_grid kept grids; the pages of at most k_chunk
+// kept chunks) or a flat one of at most kSmallSelect pages, and k at most
+// kSmallSelect at every level.  c_cap, g_cap: chunk and grid rows of the
+// layout; the counts of any sequence are at most these.
+inline bool small_select_fits(bool hier, int64_t max_pages, int64_t c_cap, int64_t g_cap, int64_t ppc, int64_t cpg,
+                              int64_t k_g, int64_t k_c, int64_t k_p) {
+  if (k_p > kSmallSelect) return false;
+  if (!hier) return max_pages <= kSmallSelect;
+  if (k_g > kSmallSelect || k_c > kSmallSelect) return false;
+  const int64_t kg = k_g < g_cap ? k_g : g_cap, kc = k_c < c_cap ? k_c : c_cap;
+  return g_cap <= kSmallSelect && kg * cpg <= kSmallSelect && kc * ppc <= kSmallSelect;
+}
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -111,22 +129,39 @@ struct PoolArgs {
   int64_t vb_stride;      // rows per sequence in `out`, 0 = row is the global block id
   float* partial;         // layer-split partial sums, or per-(l,h) token sums
   uint32_t* done;         // per-item arrival counters of a layer split (zero between calls)
-  double* stats_q;        // per-(item, l, h) sums of squares (fp64: see pool_stats_kernel)
+  double* stats_q;        // per-(item, l, h) sums of squares of x - c (see pool_stats_kernel)
   uint32_t* err;
   PoolShape ps;
   int32_t window;         // anchor only
 };
 
 struct WeightArgs {
-  const float* s1;  // [total_blocks][L*H][D] token sums
-  const double* q;  // [total_blocks][L*H] sums of squares
+  const float* s1;  // [total_blocks][L*H][D] token sums of x - c (c: see shift_block)
+  const double* q;  // [total_blocks][L*H] sums of (x - c)^2
   double* var;      // [S][L*H]
+  double* csum;     // [S][D] sum over heads of weight * c
   float* head_weight;
   const int32_t* seq_len;
   const int32_t* offs;
-  int32_t S, LH, D, B, total_blocks;
+  const int32_t* table;
+  const uint16_t* k;
+  int64_t sL, sB, sH, P;
+  int32_t S, L, H, LH, D, B, total_blocks;
   uint32_t* err;
 };
+
+// Physical block holding the first token of sequence s, whose keys shift the
+// head-variance statistics, or -1 (the shift is then 0) when the sequence
+// has no token or its first table entry is unusable.  Every variance-mode
+// kernel takes the shift from here, so they agree on it.
+__device__ __forceinline__ int64_t shift_block(const int32_t* __restrict__ seq_len, const int32_t* __restrict__ offs,
+                                               const int32_t* __restrict__ table, int32_t total_blocks, int64_t P,
+                                               int32_t s) {
+  const int32_t b0 = offs[s], b1 = offs[s + 1];
+  if (seq_len[s] <= 0 || b0 < 0 || b0 >= b1 || b1 > total_blocks) return -1;
+  const int64_t p = table[b0];
+  return p >= 0 && p < P ? p : -1;
+}
 
 // Pool-on-write: one new token per sequence.
 struct WriteArgs {
@@ -190,7 +225,7 @@ struct LevelArgs {
 struct ScoreArgs {
   const float* lvl;
   int64_t rows_per_seq;
-  int32_t S, max_pages, D, hier, ppc, cpg, c_cap;
+  int32_t S, max_pages, D, hier, ppc, cpg, c_cap, g_cap;
   const int32_t* n_pages;
   const float* anchors;
   float* aff;            // affinity rows, aff + s * rows_per_seq + row
@@ -199,7 +234,8 @@ struct ScoreArgs {
   float* score_out;
   int32_t* cnt_out;
   int32_t tiles_per_seq, rows_per_tile;
-  uint32_t* done;        // per-sequence count of finished scoring tiles (zero between calls)
+  int32_t small;         // 1: every level fits the one-launch selector (small_select_fits)
+  uint32_t* done;        // per-sequence count of finished scoring tiles (zero between calls), or null
   uint32_t* err;
   // stability filter (page rows only; hist == nullptr: off)
   uint32_t* hist;        // window words, hist + s * max_pages + page
@@ -268,7 +304,7 @@ __device__ __forceinline__ bool arrive(uint32_t* done, uint32_t n, uint32_t* err
 hipError_t launch_pool(const PoolArgs& a, int mode, hipStream_t st);          // uniform / given
 hipError_t launch_pool_stats(const PoolArgs& a, hipStream_t st);              // variance pass 1
 hipError_t launch_head_weights(const WeightArgs& w, hipStream_t st);          // variance pass 2
-hipError_t launch_pool_combine(const PoolArgs& a, const float* w, hipStream_t st);  // variance pass 3
+hipError_t launch_pool_combine(const PoolArgs& a, const float* w, const double* csum, hipStream_t st);  // pass 3
 hipError_t launch_anchor(const PoolArgs& a, hipStream_t st);
 hipError_t launch_levels(const LevelArgs& a, hipStream_t st);
 hipError_t launch_pool_on_write(const WriteArgs& a, hipStream_t st);

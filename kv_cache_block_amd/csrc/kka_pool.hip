@@ -248,23 +248,59 @@ __global__ __launch_bounds__(256) void pool_finish_kernel(PoolArgs a) {
 }
 
 // ------------------------------------------------- variance weights, 3 passes
+//
+// The weight of head (l, h) is the temporal variance of its keys, averaged
+// over head_dim.  The statistics are taken about a shift c: the keys of the
+// sequence's first token (shift_block), so that the sums hold x - c and
+// (x - c)^2.  x - c of two bf16 values is exact in fp32 for any realistic
+// spread of magnitudes and is of the order of the head's spread, not of its
+// offset; the variance  sum (x - c)^2 / T - (sum (x - c) / T)^2  then loses
+// nothing to cancellation, and a head whose keys never change (one token,
+// or the same key at every token) has x - c = 0 everywhere and variance
+// exactly 0, as the definition gives.
 
-// Pass 1: per block and (layer, head): token sums s1[b][l][h][:] and the sum
-// of squares q[b][l][h], one streaming pass over the keys.  A thread owns one
-// 16-byte column (8 dims of one head) of one layer and walks all of the
-// block's tokens, kUnroll loads in flight, so its 8 token sums need no
-// reduction across threads and are stored from registers.  The m row slots
-// of a group take m layers at a time; only the sums of squares of a head's
-// D/8 columns are added through LDS, once per round of layers.  The sums
-// of squares are fp64 (squares of bf16 values are exact there, and so are
-// their sums for any realistic spread of magnitudes): the variance pass then
-// finds exactly 0 for a head whose keys do not change over the sequence (a
-// sequence of one token, say), which the definition maps to uniform
-// weights, instead of fp32 rounding noise that the normalisation would
-// blow up into weights.
-template <int MAXT>
+// Loads the shift of one thread's 16-byte column (8 dims) at layer l.
+__device__ __forceinline__ void load_shift(const PoolArgs& a, int64_t p0, int32_t l, int32_t h, int32_t dg,
+                                           float (&c)[8]) {
+  if (p0 < 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = 0.f;
+    return;
+  }
+  const u32x4 v = *reinterpret_cast<const u32x4*>(a.k + (int64_t)l * a.sL + p0 * a.sB + (int64_t)h * a.sH +
+                                                  (int64_t)dg * 8);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    c[2 * e] = bf16_lo(v[e]);
+    c[2 * e + 1] = bf16_hi(v[e]);
+  }
+}
+
+__device__ __forceinline__ void stats8(float (&s1)[8], float (&s2)[8], const float (&c)[8], u32x4 v) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float x0 = bf16_lo(v[e]) - c[2 * e];
+    const float x1 = bf16_hi(v[e]) - c[2 * e + 1];
+    s1[2 * e] += x0;
+    s1[2 * e + 1] += x1;
+    s2[2 * e] = fmaf(x0, x0, s2[2 * e]);
+    s2[2 * e + 1] = fmaf(x1, x1, s2[2 * e + 1]);
+  }
+}
+
+// Pass 1: per block and (layer, head): the token sums of x - c, s1[b][l][h][:],
+// and the sum of (x - c)^2, q[b][l][h], one streaming pass over the keys.  A
+// thread owns one 16-byte column (8 dims of one head) of one layer and walks
+// all of the block's tokens, kUnroll loads in flight, in fp32 (one sum per
+// dim, over at most block_size tokens); its 8 sums of x - c leave from
+// registers.  The squares of a head's D/8 columns are added in fp64: with
+// WAVE, inside the wavefront by a butterfly over the head's lanes (D/8 a
+// power of two up to 64: a head's lanes then never straddle a wavefront), so
+// the work-group has no barrier at all; otherwise through LDS, once per round
+// of m layers.
+template <int MAXT, bool WAVE>
 __global__ __launch_bounds__(MAXT) void pool_stats_kernel(PoolArgs a) {
-  __shared__ double redq[MAXT];
+  __shared__ double redq[WAVE ? 1 : MAXT];
   const int tid = threadIdx.x;
   const int32_t item = blockIdx.x / a.n_split;
   const int32_t j = blockIdx.x - item * a.n_split;
@@ -277,12 +313,16 @@ __global__ __launch_bounds__(MAXT) void pool_stats_kernel(PoolArgs a) {
   const int32_t l0 = j * a.lps;
   const int32_t l1 = min(a.L, l0 + a.lps);
   const int32_t n_tok = it.n_b;
+  const int64_t p0 = n_tok > 0 ? shift_block(a.seq_len, a.offs, a.table, a.total_blocks, a.P, it.s) : -1;
 
   for (int32_t lr = l0; lr < l1; lr += a.ps.m) {
     const int32_t l = lr + slot;
+    double sq = 0.0;
     if (l < l1) {
-      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      double sq = 0.0;
+      float c[8];
+      load_shift(a, p0, l, h, dg, c);
+      float s1[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      float s2[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       const uint16_t* tp = a.k + (int64_t)l * a.sL + it.p * a.sB + (int64_t)h * a.sH + (int64_t)dg * 8;
       int32_t ti = 0;
       for (; ti + kUnroll <= n_tok; ti += kUnroll) {
@@ -290,58 +330,46 @@ __global__ __launch_bounds__(MAXT) void pool_stats_kernel(PoolArgs a) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) v[u] = load16(tp + (int64_t)(ti + u) * a.sT);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float x0 = bf16_lo(v[u][c]), x1 = bf16_hi(v[u][c]);
-            acc[2 * c] += x0;
-            acc[2 * c + 1] += x1;
-            sq = fma((double)x0, (double)x0, sq);
-            sq = fma((double)x1, (double)x1, sq);
-          }
-        }
+        for (int u = 0; u < kUnroll; ++u) stats8(s1, s2, c, v[u]);
       }
-      for (; ti < n_tok; ++ti) {
-        const u32x4 v = load16(tp + (int64_t)ti * a.sT);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float x0 = bf16_lo(v[c]), x1 = bf16_hi(v[c]);
-          acc[2 * c] += x0;
-          acc[2 * c + 1] += x1;
-          sq = fma((double)x0, (double)x0, sq);
-          sq = fma((double)x1, (double)x1, sq);
-        }
-      }
+      for (; ti < n_tok; ++ti) stats8(s1, s2, c, load16(tp + (int64_t)ti * a.sT));
       float4* dst = reinterpret_cast<float4*>(a.partial + (((int64_t)item * a.L + l) * a.H) * a.D + (int64_t)q * 8);
-      dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      dst[0] = make_float4(s1[0], s1[1], s1[2], s1[3]);
+      dst[1] = make_float4(s1[4], s1[5], s1[6], s1[7]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sq += (double)s2[e];
+    }
+    if constexpr (WAVE) {
+      // a head's DG lanes are an aligned group inside one wavefront, all on
+      // the same layer: every lane of the group takes part
+      for (int32_t o = 1; o < DG; o <<= 1) sq += __shfl_xor(sq, o);
+      if (l < l1 && dg == 0) a.stats_q[((int64_t)item * a.L + l) * a.H + h] = sq;
+    } else {
       redq[tid] = sq;
-    }
-    __syncthreads();
-    // sum of squares per (layer, head) of this round, columns in order
-    if (tid < a.ps.m * a.H) {
-      const int32_t sl = tid / a.H, hh = tid - sl * a.H;
-      const int32_t ll = lr + sl;
-      if (ll < l1) {
-        double s = 0.0;
-        for (int32_t x = 0; x < DG; ++x) s += redq[sl * a.ps.rg + hh * DG + x];
-        a.stats_q[((int64_t)item * a.L + ll) * a.H + hh] = s;
+      __syncthreads();
+      // sum of squares per (layer, head) of this round, columns in order
+      if (tid < a.ps.m * a.H) {
+        const int32_t sl = tid / a.H, hh = tid - sl * a.H;
+        const int32_t ll = lr + sl;
+        if (ll < l1) {
+          double t = 0.0;
+          for (int32_t x = 0; x < DG; ++x) t += redq[sl * a.ps.rg + hh * DG + x];
+          a.stats_q[((int64_t)item * a.L + ll) * a.H + hh] = t;
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
-// Relative floor of a head's one-pass variance (see head_var_kernel).
-constexpr double kVarFloor = 0x1p-24;
-
 // Pass 2: one group per (sequence, head): temporal variance of the head,
-//   var = ( sum_tau |x_tau|^2 / T  -  sum_d (sum_tau x_tau,d / T)^2 ) / D,
-// from the pass-1 sums, combined in fp64.  D / 4 lanes cover a head's row
-// of sums with 16-byte loads; the 256 threads form 256 / (D / 4) such lane
-// groups, group g summing blocks g, g + ng, ... with kVarUnroll independent
-// loads in flight.  The groups' sums are then added in group order (a fixed
-// order, so the result is reproducible).
+//   var = ( sum_tau |x_tau - c|^2 / T  -  sum_d (sum_tau (x_tau,d - c_d) / T)^2 ) / D,
+// from the pass-1 sums, combined in fp64 (clamped at 0 against rounding).
+// D / 4 lanes cover a head's row of sums with 16-byte loads; the 256
+// threads form 256 / (D / 4) such lane groups, group g summing blocks g,
+// g + ng, ... with kVarUnroll independent loads in flight.  The groups' sums
+// are then added in group order (a fixed order, so the result is
+// reproducible).
 constexpr int kVarUnroll = 4;
 
 __global__ __launch_bounds__(256) void head_var_kernel(WeightArgs w) {
@@ -406,19 +434,19 @@ __global__ __launch_bounds__(256) void head_var_kernel(WeightArgs w) {
     __syncthreads();
   }
   if (tid == 0) {
-    // The one-pass form E[x^2] - E[x]^2 cancels for a head whose keys do not
-    // vary: a result within its fp64 rounding (below 2^-24 of the mean
-    // square, far under any real key statistics) is a head of variance 0,
-    // as one token, or the same key at every token, has by definition.
-    const double msq = T > 0 ? r2[0] / (double)T : 0.0;
-    const double v = T > 0 ? (msq - r1[0]) / (double)w.D : 0.0;
-    w.var[(int64_t)s * w.LH + lh] = v > kVarFloor * msq / (double)w.D ? v : 0.0;
+    const double v = T > 0 ? (r2[0] / (double)T - r1[0]) / (double)w.D : 0.0;
+    w.var[(int64_t)s * w.LH + lh] = v > 0.0 ? v : 0.0;
   }
 }
 
-// Pass 2b: weights = variance / sum of variances (uniform when the sum is 0).
+// Pass 2b: weights = variance / sum of variances (uniform when the sum is
+// 0), rounded to fp32; and the shift term of the block vectors,
+//   csum[s][d] = sum_{l,h} w[l,h] * c[l,h][d]   (fp64),
+// so that pass 3 adds it back: the weighted mean of a block's keys is the
+// weighted mean of x - c plus this constant.
 __global__ __launch_bounds__(256) void head_norm_kernel(WeightArgs w) {
   __shared__ double r[256];
+  __shared__ float wf[4096];  // L*H <= 4096
   const int tid = threadIdx.x;
   const int32_t s = blockIdx.x;
   double v = 0.0;
@@ -430,18 +458,44 @@ __global__ __launch_bounds__(256) void head_norm_kernel(WeightArgs w) {
     __syncthreads();
   }
   const double total = r[0];
-  for (int32_t x = tid; x < w.LH; x += 256)
-    w.head_weight[(int64_t)s * w.LH + x] =
-        total > 0.0 ? (float)(w.var[(int64_t)s * w.LH + x] / total) : (float)(1.0 / (double)w.LH);
+  for (int32_t x = tid; x < w.LH; x += 256) {
+    const float wx = total > 0.0 ? (float)(w.var[(int64_t)s * w.LH + x] / total) : (float)(1.0 / (double)w.LH);
+    w.head_weight[(int64_t)s * w.LH + x] = wx;
+    wf[x] = wx;
+  }
+  __syncthreads();
+  const int64_t p0 = shift_block(w.seq_len, w.offs, w.table, w.total_blocks, w.P, s);
+  constexpr int kShiftLoads = 16;  // independent loads in flight per thread
+  for (int32_t d = tid; d < w.D; d += 256) {
+    double cs = 0.0;
+    if (p0 >= 0) {
+      const uint16_t* src = w.k + p0 * w.sB + d;
+      for (int32_t lh0 = 0; lh0 < w.LH; lh0 += kShiftLoads) {
+        float c[kShiftLoads];
+#pragma unroll
+        for (int u = 0; u < kShiftLoads; ++u) {
+          const int32_t lh = min(lh0 + u, w.LH - 1);
+          const int32_t l = lh / w.H, h = lh - l * w.H;
+          c[u] = __uint_as_float((uint32_t)src[(int64_t)l * w.sL + (int64_t)h * w.sH] << 16);
+        }
+#pragma unroll
+        for (int u = 0; u < kShiftLoads; ++u)
+          if (lh0 + u < w.LH) cs = fma((double)wf[lh0 + u], (double)c[u], cs);
+      }
+    }
+    w.csum[(int64_t)s * w.D + d] = cs;
+  }
 }
 
-// Pass 3: v_b = sum_{l,h} w[s][l,h] * s1[b][l][h][:] / n_b.  One group of
-// head_dim threads per block: D / 4 lanes cover a row with 16-byte loads,
-// and lane group g (of 4) accumulates heads lh = g, g + 4, ... in order; the
-// four group sums are added as (g0 + g1) + (g2 + g3), a fixed order.
+// Pass 3: v_b = sum_{l,h} w[s][l,h] * s1[b][l][h][:] / n_b + csum[s][:].  One
+// group of head_dim threads per block: D / 4 lanes cover a row with 16-byte
+// loads, and lane group g (of 4) accumulates heads lh = g, g + 4, ... in
+// order; the four group sums are added as (g0 + g1) + (g2 + g3), a fixed
+// order, divided by n_b and added to the shift term in fp64.
 constexpr int kCombineUnroll = 4;
 
-__global__ __launch_bounds__(1024) void pool_combine_kernel(PoolArgs a, const float* __restrict__ wts) {
+__global__ __launch_bounds__(1024) void pool_combine_kernel(PoolArgs a, const float* __restrict__ wts,
+                                                            const double* __restrict__ csum) {
   extern __shared__ float4 gsum[];  // [3][D / 4]: the sums of groups 1..3
   const int32_t item = blockIdx.x;
   const Item it = locate(a, item, false);
@@ -478,12 +532,13 @@ __global__ __launch_bounds__(1024) void pool_combine_kernel(PoolArgs a, const fl
   __syncthreads();
   if (g == 0) {
     const float4 a1 = gsum[c], a2 = gsum[nl + c], a3 = gsum[2 * nl + c];
-    const float nb = (float)it.n_b;
+    const double nb = (double)it.n_b;
+    const double* cs = csum + (int64_t)it.s * a.D + 4 * c;
     float4 v;
-    v.x = it.n_b > 0 ? ((acc.x + a1.x) + (a2.x + a3.x)) / nb : 0.f;
-    v.y = it.n_b > 0 ? ((acc.y + a1.y) + (a2.y + a3.y)) / nb : 0.f;
-    v.z = it.n_b > 0 ? ((acc.z + a1.z) + (a2.z + a3.z)) / nb : 0.f;
-    v.w = it.n_b > 0 ? ((acc.w + a1.w) + (a2.w + a3.w)) / nb : 0.f;
+    v.x = it.n_b > 0 ? (float)((double)((acc.x + a1.x) + (a2.x + a3.x)) / nb + cs[0]) : 0.f;
+    v.y = it.n_b > 0 ? (float)((double)((acc.y + a1.y) + (a2.y + a3.y)) / nb + cs[1]) : 0.f;
+    v.z = it.n_b > 0 ? (float)((double)((acc.z + a1.z) + (a2.z + a3.z)) / nb + cs[2]) : 0.f;
+    v.w = it.n_b > 0 ? (float)((double)((acc.w + a1.w) + (a2.w + a3.w)) / nb + cs[3]) : 0.f;
     reinterpret_cast<float4*>(a.out + it.row * a.D)[c] = v;
   }
 }
@@ -653,8 +708,16 @@ hipError_t launch_pool_stats(const PoolArgs& a, hipStream_t st) {
   if (a.n_items <= 0) return hipSuccess;
   const dim3 grid((unsigned)((int64_t)a.n_items * a.n_split));
   const dim3 block((unsigned)a.ps.nt);
-  if (a.ps.nt <= 256) hipLaunchKernelGGL((pool_stats_kernel<256>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((pool_stats_kernel<1024>), grid, block, 0, st, a);
+  // a head's columns reduce inside one wavefront when D/8 is a power of two up to 64
+  const int32_t DG = a.D / 8;
+  const bool wave = DG <= 64 && (DG & (DG - 1)) == 0;
+  if (a.ps.nt <= 256) {
+    if (wave) hipLaunchKernelGGL((pool_stats_kernel<256, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((pool_stats_kernel<256, false>), grid, block, 0, st, a);
+  } else {
+    if (wave) hipLaunchKernelGGL((pool_stats_kernel<1024, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((pool_stats_kernel<1024, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -667,11 +730,11 @@ hipError_t launch_head_weights(const WeightArgs& w, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_pool_combine(const PoolArgs& a, const float* wts, hipStream_t st) {
+hipError_t launch_pool_combine(const PoolArgs& a, const float* wts, const double* csum, hipStream_t st) {
   if (a.n_items <= 0) return hipSuccess;
   // head_dim threads (four lane groups of head_dim / 4), 3 * head_dim * 4 bytes of LDS
   hipLaunchKernelGGL(pool_combine_kernel, dim3((unsigned)a.n_items), dim3((unsigned)a.D),
-                     (size_t)3 * a.D * sizeof(float), st, a, wts);
+                     (size_t)3 * a.D * sizeof(float), st, a, wts, csum);
   return hipGetLastError();
 }
 

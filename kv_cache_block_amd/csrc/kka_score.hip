@@ -20,8 +20,12 @@
 // Selection, written for latency: for batches whose tiles all fit on the
 // chip at once, the work-group that finishes a sequence's last scoring
 // tile (a per-sequence counter) selects that sequence in the same launch
-// (score_select_kernel); larger batches run the lighter score_kernel and
-// then select_kernel, one work-group per sequence.  The sequence's
+// (score_select_kernel); larger batches whose levels are small (the serving
+// workload) score and select in one launch too, with a selecting
+// work-group per sequence that re-scores its few candidate rows beside the
+// scoring tiles (score_topk_kernel, see the small coarse-to-fine selection
+// below); other batches run the lighter score_kernel and then
+// select_kernel, one work-group per sequence.  The sequence's
 // affinity rows are staged into LDS in one round of loads (sequences of
 // more than kLdsRows rows are selected from memory), then each level is
 // selected: up to 64 candidates (children of kept parents, or every row)
@@ -947,29 +951,27 @@ __device__ __forceinline__ void stability_step(const ScoreArgs& a, uint32_t h, f
   if (stab) *stab = (float)__popc(nh) / (float)a.stab_w;
 }
 
-// Scoring pass for batches too large for one wave of fused work-groups:
-// 256-thread work-groups without LDS (more of them resident per compute
-// unit), each scoring one tile; the kernel boundary publishes the
-// affinities to the selection launch that follows.  With the stability
-// filter a tile's affinities are gathered in LDS and the affinities, window
-// words and scores are read and written one row per thread, as whole
-// lines: one lane per row group would write a quarter line per store
-// (measured 2.5 % slower on the serving batch).
-template <int LPR, int NQ, int R, bool STAB>
-__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
-  constexpr int NG = 256 / LPR;  // row groups per work-group
-  __shared__ float g_aff[STAB ? kPlainTileMax : 1];
+// One scoring tile: rows [tile * rows_per_tile, ...) of sequence s, by NT
+// threads in row groups of LPR lanes, R rows per group per pass.  Used by
+// the scoring launch of the two-launch path and by the streaming
+// work-groups of the one-launch path.  With the stability filter a tile's
+// affinities are gathered in LDS (g_aff) and the affinities, window words
+// and scores are read and written one row per thread, as whole lines: one
+// lane per row group would write a quarter line per store (measured 2.5 %
+// slower on the serving batch).  Without affinity_out and without the
+// filter there is nothing to write and the caller does not launch tiles.
+template <int NT, int LPR, int NQ, int R, bool STAB>
+__device__ __forceinline__ void score_tile(const ScoreArgs& a, int32_t s, int32_t tile, float* g_aff) {
+  constexpr int NG = NT / LPR;  // row groups per work-group
   const int tid = threadIdx.x;
-  const int32_t s = blockIdx.x / a.tiles_per_seq;
-  const int32_t tile = blockIdx.x - s * a.tiles_per_seq;
-  const SeqGeom g = seq_geom(a, s, tid == 0 && tile == 0);
+  const SeqGeom g = seq_geom(a, s, false);
   const int32_t nv = g.n_p + g.n_c + g.n_g;
   const int32_t v0 = tile * a.rows_per_tile;
   if (v0 >= nv) return;
   const int32_t v1 = min(nv, v0 + a.rows_per_tile);
   const int32_t Q = a.D >> 2;
   const f32x4* seq = reinterpret_cast<const f32x4*>(a.lvl + (int64_t)s * a.rows_per_seq * a.D);
-  float* aff = a.aff + (int64_t)s * a.rows_per_seq;
+  float* aff = a.aff ? a.aff + (int64_t)s * a.rows_per_seq : nullptr;
   const int32_t grp = tid / LPR, lg = tid % LPR;
   const AnchorRegs<LPR, NQ> A = load_anchor<LPR, NQ>(a, s, lg);
 
@@ -1002,15 +1004,28 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   }
   if constexpr (STAB) {
     __syncthreads();
-    if (tid < v1 - v0) {
-      const int32_t vr = v0 + tid;
+    for (int32_t i = tid; i < v1 - v0; i += NT) {
+      const int32_t vr = v0 + i;
       const int64_t row = vr < g.n_p ? vr
                           : vr < g.n_p + g.n_c ? (int64_t)a.max_pages + (vr - g.n_p)
                                                : (int64_t)a.max_pages + a.c_cap + (vr - g.n_p - g.n_c);
-      aff[row] = g_aff[tid];
-      if (vr < g.n_p) stability_step(a, hist[vr], g_aff[tid], hist + vr, stab ? stab + vr : nullptr);
+      if (aff) aff[row] = g_aff[i];
+      if (vr < g.n_p) stability_step(a, hist[vr], g_aff[i], hist + vr, stab ? stab + vr : nullptr);
     }
   }
+}
+
+// Scoring pass of the two-launch path: 256-thread work-groups without LDS
+// (more of them resident per compute unit), each scoring one tile; the
+// kernel boundary publishes the affinities to the selection launch that
+// follows.
+template <int LPR, int NQ, int R, bool STAB>
+__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+  __shared__ float g_aff[STAB ? kPlainTileMax : 1];
+  const int32_t s = blockIdx.x / a.tiles_per_seq;
+  const int32_t tile = blockIdx.x - s * a.tiles_per_seq;
+  if (threadIdx.x == 0 && tile == 0) seq_geom(a, s, true);  // reports a bad page count once
+  score_tile<256, LPR, NQ, R, STAB>(a, s, tile, g_aff);
 }
 
 // Scoring tile, then selection: every work-group scores one tile of one
@@ -1201,10 +1216,356 @@ __global__ __launch_bounds__(kSelThreads) void lazy_kernel(ScoreArgs a, float* l
   write_selection(a, sm, s, kp);
 }
 
+// ------------------------------------------- small coarse-to-fine selection
+//
+// For batches too large for the one-launch handoff (more tiles than fit on
+// the chip at once) whose levels are small (a few hundred candidates per
+// level, k up to a few hundred: the serving workload), one work-group per
+// sequence selects on its own beside the scoring tiles: it scores every
+// grid, keeps the top k_grid, scores the chunks of the kept grids, keeps the
+// top k_chunk, scores the pages of the kept chunks and keeps the top k_page
+// (section 5.1's order), with the same row code as the scoring tiles, so the
+// affinities it selects on are bit for bit the ones the tiles write.  Rows
+// under unkept parents score +0 by definition and are never read; the
+// selection equals the one over every row.  Nothing passes between
+// work-groups, and the selecting groups' latency hides behind the stream of
+// the batch's rows.
+
+// Candidates per level, and kept elements per level, that the small
+// selector holds (the host sends larger geometries to the two-launch path).
+constexpr int kSmallCand = kSmallSelect;
+
+struct SmallSel {
+  alignas(16) uint64_t key[kSmallCand];  // candidate keys (0: the candidate scores 0, or is absent)
+  alignas(16) uint64_t res[kSmallCand];  // kept keys in rank order
+  int32_t kept[kSmallCand];              // kept elements of the level above, in rank order
+  int32_t zero_e[kSmallCand];            // live candidates scoring exactly 0
+  uint32_t pbits[kBitmapWords];          // keep flags of the level above's elements
+  float g_aff[kPlainTileMax];            // scoring tiles: a tile's affinities (stability filter)
+  int32_t n_zero;
+  int32_t wcnt[16];                      // per-wave counts (up to 1024 threads)
+};
+
+// Value of lane (lane ^ J) of one 32-bit register of the wavefront: DPP quad
+// permutes for J = 1, 2, swizzles (xor within 32 lanes) for J = 4 .. 16, a
+// permute through LDS for J = 32.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  if constexpr (J == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  else if constexpr (J == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  else if constexpr (J < 32) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (J << 10) | 0x1F);
+  else return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((((int)threadIdx.x & 63) ^ J) << 2), (int)v);
+}
+
+// One compare-exchange step of a bitonic network over the lanes: blocks of
+// SIZE lanes alternate direction (the block of 64 is descending), partners J
+// lanes apart.
+template <int SIZE, int J>
+__device__ __forceinline__ uint64_t bitonic_step(uint64_t x) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t lo = xor_lane<J>((uint32_t)x);
+  const uint32_t hi = xor_lane<J>((uint32_t)(x >> 32));
+  const uint64_t y = ((uint64_t)hi << 32) | lo;
+  const bool desc = (lane & SIZE) == 0 || SIZE == 64;
+  const bool lower = (lane & J) == 0;
+  return (lower == desc) ? (x > y ? x : y) : (x < y ? x : y);
+}
+
+template <int SIZE, int J>
+__device__ __forceinline__ uint64_t bitonic_merge(uint64_t x) {
+  x = bitonic_step<SIZE, J>(x);
+  if constexpr (J > 1) x = bitonic_merge<SIZE, J / 2>(x);
+  return x;
+}
+
+template <int SIZE>
+__device__ __forceinline__ uint64_t bitonic_sort(uint64_t x) {
+  if constexpr (SIZE > 2) x = bitonic_sort<SIZE / 2>(x);
+  return bitonic_merge<SIZE, SIZE / 2>(x);
+}
+
+// Sorts one key per lane of a wavefront into descending order (lane j ends
+// up with the j-th largest).
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) { return bitonic_sort<64>(x); }
+
+// Keys greater than x in a descending run of 64 keys: binary search for the
+// first key <= x over the 65 possible answers 0..64 (seven halvings).
+__device__ __forceinline__ int32_t count_above(const uint64_t* run, uint64_t x) {
+  int32_t lo = 0, hi = 64;
+#pragma unroll
+  for (int it = 0; it < 7; ++it) {
+    if (lo < hi) {
+      const int32_t mid = (lo + hi) >> 1;  // < 64 while lo < hi <= 64
+      if (run[mid] > x) lo = mid + 1;
+      else hi = mid;
+    }
+  }
+  return lo;
+}
+
+// Ranks the m candidate keys sm.key[0, m) (m <= kSmallCand; non-zero keys
+// are distinct, 0 marks a candidate scoring 0 or a slot past the
+// candidates): the key with r larger keys goes to sm.res[r] when r <
+// k_eff.  Wavefront w sorts keys [64w, 64w + 64) in registers; with more
+// than one run, the sorted runs go to LDS and each key's rank is its place
+// in its own run plus the keys above it in every other run.  Returns the
+// number of non-zero (positive-score) keys.
+template <int NT>
+__device__ int32_t small_rank(SmallSel& sm, int32_t m, int32_t k_eff) {
+  static_assert(NT / 64 >= kSmallCand / 64, "one wavefront per run of 64 candidates");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t n_runs = (m + 63) >> 6;
+  uint64_t x = 0ull;
+  if (wave < n_runs) {  // whole wavefronts
+    const int32_t c = 64 * wave + lane;
+    x = wave_sort_desc(c < m ? sm.key[c] : 0ull);
+    const uint64_t bal = __ballot(x != 0ull);
+    if (lane == 0) sm.wcnt[wave] = (int32_t)__popcll(bal);
+  }
+  if (n_runs > 1) {
+    __syncthreads();  // every run has read its keys: overwrite with the sorted runs
+    if (wave < n_runs) sm.key[64 * wave + lane] = x;
+  }
+  __syncthreads();
+  int32_t P = 0;
+  for (int32_t w = 0; w < n_runs; ++w) P += sm.wcnt[w];
+  if (wave < n_runs && x != 0ull) {
+    int32_t r = lane;
+    for (int32_t v = 0; v < n_runs; ++v)
+      if (v != wave) r += count_above(sm.key + 64 * v, x);
+    if (r < k_eff) sm.res[r] = x;
+  }
+  __syncthreads();
+  return P;
+}
+
+// When only P < k_eff candidates score above 0, slots P .. k_eff-1 take the
+// lowest-index elements of the level scoring exactly 0: children of unkept
+// parents (fan > 0 and their parent's bit clear in sm.pbits) and live
+// candidates of zero affinity (sm.zero_e), in index order.
+template <int NT>
+__device__ void small_fill_zeros(SmallSel& sm, int32_t n_lev, int32_t fan, int32_t P, int32_t k_eff) {
+  constexpr int W = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  const int32_t need = k_eff - P;
+  const int32_t nz = sm.n_zero;
+  int32_t found = 0;
+  for (int32_t e0 = 0; e0 < n_lev && found < need; e0 += NT) {
+    const int32_t e = e0 + tid;
+    bool zero = false;
+    if (e < n_lev) {
+      const int32_t par = fan > 0 ? e / fan : 0;
+      if (fan > 0 && !((sm.pbits[par >> 5] >> (par & 31)) & 1u)) {
+        zero = true;
+      } else {
+        for (int32_t z = 0; z < nz && !zero; ++z) zero = sm.zero_e[z] == e;
+      }
+    }
+    const uint64_t bal = __ballot(zero);
+    if (lane == 0) sm.wcnt[wave] = (int32_t)__popcll(bal);
+    __syncthreads();
+    int32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      if (w < wave) before += sm.wcnt[w];
+      tot += sm.wcnt[w];
+    }
+    const int32_t rank = found + before + (int32_t)__popcll(bal & lt_mask);
+    if (zero && rank < need) sm.res[P + rank] = composite(0u, e);
+    found += tot;
+    __syncthreads();
+  }
+}
+
+// Selection of sequence s by one work-group of NT threads (see above).  The
+// first scored level's rows sit at a fixed place, so its first pass of
+// loads goes out with the page count and the anchor.  RS rows per row group
+// are in flight per pass.
+template <int NT, int LPR, int NQ, int RS>
+__device__ void small_select(const ScoreArgs& a, int32_t s, SmallSel& sm) {
+  constexpr int NG = NT / LPR;
+  const int tid = threadIdx.x;
+  const int32_t grp = tid / LPR, lg = tid % LPR;
+  const int32_t Q = a.D >> 2;
+  const f32x4* seq = reinterpret_cast<const f32x4*>(a.lvl + (int64_t)s * a.rows_per_seq * a.D);
+  // The first level's rows (every grid, or every page of a flat layout) sit
+  // at a fixed place whatever the sequence's length: its first pass of row
+  // loads goes out with the page count and the anchor, and rows past the
+  // level's end (known once the page count arrives) are dropped.
+  const int32_t lev0 = a.hier ? 0 : 2;
+  const int32_t off0 = a.hier ? a.max_pages + a.c_cap : 0;
+  const int32_t cap0 = a.hier ? a.g_cap : a.max_pages;  // rows the first level can hold
+  float v0[RS];
+  f32x4 x0[RS][NQ];
+  {
+#pragma unroll
+    for (int r = 0; r < RS; ++r) {
+      const int32_t c = grp + NG * r;
+      if (cap0 > 0) {
+        load_row<LPR, NQ>(seq + (int64_t)(off0 + (c < cap0 ? c : cap0 - 1)) * Q, lg, Q, x0[r]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) x0[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
+  const SeqGeom g = seq_geom(a, s, tid == 0);
+  const AnchorRegs<LPR, NQ> A = load_anchor<LPR, NQ>(a, s, lg);
+#pragma unroll
+  for (int r = 0; r < RS; ++r) v0[r] = row_affinity<LPR, NQ>(x0[r], A);
+  int32_t n_par = 0;  // kept elements of the level above
+  for (int32_t lev = lev0; lev < 3; ++lev) {
+    int32_t n_lev, fan, off;  // elements, children per parent (0: every element a candidate), first row
+    if (lev == 0) {
+      n_lev = g.n_g;
+      fan = 0;
+      off = a.max_pages + a.c_cap;
+    } else if (lev == 1) {
+      n_lev = g.n_c;
+      fan = a.cpg;
+      off = a.max_pages;
+    } else {
+      n_lev = g.n_p;
+      fan = a.hier ? a.ppc : 0;
+      off = 0;
+    }
+    const int32_t m = min(fan ? n_par * fan : n_lev, kSmallCand);
+    if (tid == 0) sm.n_zero = 0;
+    __syncthreads();  // n_zero, the kept list and keep flags of the level above
+    int32_t c_start = grp;
+    if (lev == lev0) {
+      // the first pass, scored above (no parents: candidate = element)
+#pragma unroll
+      for (int r = 0; r < RS; ++r) {
+        const int32_t c = grp + NG * r;
+        if (lg == 0 && c < m) {
+          const uint32_t bits = __float_as_uint(v0[r]);
+          sm.key[c] = bits != 0u ? composite(bits, c) : 0ull;
+          if (bits == 0u) sm.zero_e[atomicAdd(&sm.n_zero, 1)] = c;
+        }
+      }
+      c_start += NG * RS;
+    }
+    for (int32_t c0 = c_start; c0 < m; c0 += NG * RS) {
+      f32x4 x[RS][NQ];
+      int32_t e[RS];
+#pragma unroll
+      for (int r = 0; r < RS; ++r) {
+        const int32_t c = c0 + NG * r;
+        int32_t el = -1;
+        if (c < m) {
+          el = fan ? sm.kept[c / fan] * fan + (c - (c / fan) * fan) : c;
+          if (el >= n_lev) el = -1;  // past the end of a ragged last parent
+        }
+        e[r] = el;
+        // candidates past the end load row `off` (unconditional loads issue back to back)
+        load_row<LPR, NQ>(seq + (int64_t)(off + (el >= 0 ? el : 0)) * Q, lg, Q, x[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < RS; ++r) {
+        const float v = row_affinity<LPR, NQ>(x[r], A);
+        const int32_t c = c0 + NG * r;
+        if (lg == 0 && c < m) {
+          const uint32_t bits = __float_as_uint(v);
+          sm.key[c] = (e[r] >= 0 && bits != 0u) ? composite(bits, e[r]) : 0ull;
+          if (e[r] >= 0 && bits == 0u) sm.zero_e[atomicAdd(&sm.n_zero, 1)] = e[r];
+        }
+      }
+    }
+    __syncthreads();
+    const int32_t k = lev == 0 ? a.k_g : (lev == 1 ? a.k_c : a.k_p);
+    const int32_t k_eff = min(min(k, n_lev), kSmallCand);
+    const int32_t P = k_eff > 0 ? small_rank<NT>(sm, m, k_eff) : 0;
+    if (P < k_eff) small_fill_zeros<NT>(sm, n_lev, fan, P, k_eff);
+    __syncthreads();
+    if (lev < 2) {
+      // the kept elements become the next level's parents
+      for (int32_t w = tid; w < (n_lev + 31) / 32 && w < kBitmapWords; w += NT) sm.pbits[w] = 0u;
+      __syncthreads();
+      for (int32_t i = tid; i < k_eff; i += NT) {
+        const int32_t el = (int32_t)(~(uint32_t)sm.res[i]);
+        sm.kept[i] = el;
+        atomicOr(&sm.pbits[el >> 5], 1u << (el & 31));
+      }
+    }
+    n_par = k_eff;
+  }
+  __syncthreads();
+  for (int32_t i = tid; i < a.k_p; i += NT) {
+    int32_t idx = -1;
+    float sc = 0.f;
+    if (i < n_par) {
+      const uint64_t c = sm.res[i];
+      idx = (int32_t)(~(uint32_t)c);
+      sc = __uint_as_float((uint32_t)(c >> 32));
+    }
+    a.idx_out[(int64_t)s * a.k_p + i] = idx;
+    if (a.score_out) a.score_out[(int64_t)s * a.k_p + i] = sc;
+  }
+  if (tid == 0 && a.cnt_out) a.cnt_out[s] = n_par;
+}
+
+// One launch of scoring and selection: work-groups 0 .. S-1 select (one per
+// sequence, small_select); the others, when a.tiles_per_seq > 0, score
+// tile (blockIdx - S) % tiles_per_seq of sequence (blockIdx - S) /
+// tiles_per_seq for affinity_out and the stability filter.  No work-group
+// reads what another writes.
+template <int NT, int LPR, int NQ, int RS, int RT, bool STAB>
+__global__ __launch_bounds__(NT) void score_topk_kernel(ScoreArgs a) {
+  __shared__ SmallSel sm;
+  const int32_t b = blockIdx.x;
+  if (b < a.S) {
+    small_select<NT, LPR, NQ, RS>(a, b, sm);
+    return;
+  }
+  const int32_t t = b - a.S;
+  const int32_t s = t / a.tiles_per_seq;
+  score_tile<NT, LPR, NQ, RT, STAB>(a, s, t - s * a.tiles_per_seq, sm.g_aff);
+}
+
 // Lanes sharing one row: 8 (whole 128-byte lines per row group), 16 above
 // head_dim 512 so that a lane's row and anchor pieces stay in registers.
 constexpr int32_t score_lpr(int32_t D) { return D / 4 > 8 * 16 ? 16 : 8; }
 
+
+// Shape of the one-launch path for large batches, where the scoring tiles'
+// stream is the call's time and the selecting groups run beside it: 256
+// threads per group and score_kernel's loads (4 float4 per lane per pass,
+// two passes per tile), so the kernel stays near score_kernel's register
+// count and residency; the selecting groups read RS rows per row group per
+// pass.
+template <int LPR, int NQ>
+struct FusedShape {
+  static constexpr int NT = 256;
+  static constexpr int RS = NQ >= KKA_SCORE_LOADS ? 1 : KKA_SCORE_LOADS / NQ;
+  static constexpr int RT = RS;
+  static constexpr int PT = KKA_SCORE_PASSES;
+  static constexpr int32_t kTileRows = (NT / LPR) * RT * PT;
+  static_assert(kTileRows <= kPlainTileMax, "tile rows exceed the gather buffer");
+};
+
+template <int LPR, int NQ>
+hipError_t launch_small(const ScoreArgs& a0, hipStream_t st) {
+  using F = FusedShape<LPR, NQ>;
+  ScoreArgs a = a0;
+  // without affinity_out and the stability filter there is nothing to score
+  // for: the selecting groups alone
+  const bool streams = a0.aff != nullptr || a0.hist != nullptr;
+  int64_t tiles = 0;
+  if (streams) {
+    a.rows_per_tile = F::kTileRows;
+    tiles = (a.rows_per_seq + a.rows_per_tile - 1) / a.rows_per_tile;
+    a.tiles_per_seq = (int32_t)(tiles > 0 ? tiles : 1);
+    tiles = a.tiles_per_seq;
+  }
+  const dim3 grid((unsigned)((int64_t)a.S * (1 + tiles)));
+  if (a.hist)
+    hipLaunchKernelGGL((score_topk_kernel<F::NT, LPR, NQ, F::RS, F::RT, true>), grid, dim3(F::NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((score_topk_kernel<F::NT, LPR, NQ, F::RS, F::RT, false>), grid, dim3(F::NT), 0, st, a);
+  return hipGetLastError();
+}
 
 template <int LPR, int NQ>
 hipError_t launch_nq(const ScoreArgs& a0, bool lazy, float* lazy_out, hipStream_t st) {
@@ -1214,18 +1575,15 @@ hipError_t launch_nq(const ScoreArgs& a0, bool lazy, float* lazy_out, hipStream_
     hipLaunchKernelGGL((lazy_kernel<LPR, NQ, RL>), dim3((unsigned)a0.S), dim3(kSelThreads), 0, st, a0, lazy_out);
     return hipGetLastError();
   }
-  // Latency-bound batches (one wave of fused work-groups, two per compute
-  // unit, covers every tile) score and select in one launch; larger ones
-  // stream the rows with the lighter scoring kernel and select after it.
-  // The fused kernel is latency-bound: all of a lane's row loads go out in
-  // one pass over its tile (one HBM round trip).
-  constexpr int RF = NQ >= KKA_SCORE_LOADS * KKA_SCORE_PASSES ? 1 : KKA_SCORE_LOADS * KKA_SCORE_PASSES / NQ;
   ScoreArgs a = a0;
+  // Latency-bound batches (one wave of 512-thread work-groups, two per
+  // compute unit, covers every tile) score and select in one launch, the
+  // selection handed to the work-group that finishes a sequence's last tile.
+  // All of a lane's row loads go out in one pass over its tile.
+  constexpr int RF = NQ >= KKA_SCORE_LOADS * KKA_SCORE_PASSES ? 1 : KKA_SCORE_LOADS * KKA_SCORE_PASSES / NQ;
   constexpr int32_t kFusedRows = (kSelThreads / LPR) * RF;
-  constexpr int32_t kPlainRows = (256 / LPR) * R * KKA_SCORE_PASSES;
-  static_assert(kPlainRows <= kPlainTileMax, "a score_kernel tile has at most one row per thread");
   const int64_t fused_tiles = (a.rows_per_seq + kFusedRows - 1) / kFusedRows;
-  if ((int64_t)a.S * fused_tiles <= 2 * (int64_t)device_cus()) {
+  if (a.done && (int64_t)a.S * fused_tiles <= 2 * (int64_t)device_cus()) {
     a.rows_per_tile = kFusedRows;
     a.tiles_per_seq = (int32_t)(fused_tiles > 0 ? fused_tiles : 1);
     const dim3 grid((unsigned)((int64_t)a.S * a.tiles_per_seq));
@@ -1235,6 +1593,14 @@ hipError_t launch_nq(const ScoreArgs& a0, bool lazy, float* lazy_out, hipStream_
       hipLaunchKernelGGL((score_select_kernel<LPR, NQ, RF, false>), grid, dim3(kSelThreads), 0, st, a);
     return hipGetLastError();
   }
+  // Larger batches whose levels fit the small selector: one launch, a
+  // selecting group per sequence beside the scoring tiles (its latency hides
+  // behind the stream of the batch's rows).
+  if (a.small) return launch_small<LPR, NQ>(a, st);
+  // Otherwise two launches: the scoring pass, then one selecting work-group
+  // per sequence (the kernel boundary orders the affinities between them).
+  constexpr int32_t kPlainRows = (256 / LPR) * R * KKA_SCORE_PASSES;
+  static_assert(kPlainRows <= kPlainTileMax, "a score_kernel tile has at most one row per thread");
   const int64_t tiles = (a.rows_per_seq + kPlainRows - 1) / kPlainRows;
   a.rows_per_tile = kPlainRows;
   a.tiles_per_seq = (int32_t)(tiles > 0 ? tiles : 1);
@@ -1278,9 +1644,6 @@ int32_t device_cus() {
   return n;
 }
 
-// A tile's affinities are gathered in the selection's LDS row buffer.
-static_assert((kSelThreads / 8) * KKA_SCORE_LOADS * KKA_SCORE_PASSES <= kLdsRows, "tile rows exceed LDS");
-
 // Rows the smaller (256-thread) scoring work-group covers for a given
 // head_dim: the launch sizes its tiles from this or twice this.
 int32_t score_rows_per_tile(int32_t D) {
@@ -1291,6 +1654,9 @@ int32_t score_rows_per_tile(int32_t D) {
   const int32_t R = NQ >= KKA_SCORE_LOADS ? 1 : KKA_SCORE_LOADS / NQ;
   return (256 / lpr) * R * KKA_SCORE_PASSES;
 }
+
+// A fused tile's affinities are gathered in the selection's LDS row buffer.
+static_assert((kSelThreads / 8) * KKA_SCORE_LOADS * KKA_SCORE_PASSES <= kLdsRows, "tile rows exceed LDS");
 
 hipError_t launch_score_topk(const ScoreArgs& a, hipStream_t st) { return dispatch(a, false, nullptr, st); }
 

@@ -11,9 +11,10 @@ from typing import Optional
 
 import torch
 
-from . import (WEIGHT_GIVEN, WEIGHT_UNIFORM, WEIGHT_VARIANCE, KPool, LevelLayout, Seqs, kka_build_levels,
-               kka_pool_anchor, kka_pool_anchor_workspace, kka_pool_blocks, kka_pool_blocks_workspace,
-               kka_pool_on_write, kka_score_topk, kka_score_topk_workspace, new_workspace)
+from . import (WEIGHT_GIVEN, WEIGHT_UNIFORM, WEIGHT_VARIANCE, KPool, LevelLayout, Seqs, _torch_stream,
+               kka_build_levels, kka_pool_anchor, kka_pool_anchor_workspace, kka_pool_blocks,
+               kka_pool_blocks_workspace, kka_pool_on_write, kka_score_topk, kka_score_topk_workspace, new_workspace,
+               order_after_current)
 
 
 class Selector:
@@ -42,13 +43,28 @@ class Selector:
         self.head_weight = torch.zeros((S, LH), dtype=torch.float32, device=device) if mode != WEIGHT_UNIFORM else None
         self.ws_pool = new_workspace(kka_pool_blocks_workspace(kp, seqs, mode), device)
         self.ws_anchor = new_workspace(kka_pool_anchor_workspace(kp, seqs, window), device)
-        self.ws_score = new_workspace(kka_score_topk_workspace(self.lay, keep_affinity), device)
+        self.ws_score = new_workspace(kka_score_topk_workspace(self.lay, keep_affinity, k_page,
+                                                               select.get("k_grid", 0), select.get("k_chunk", 0)),
+                                      device)
         # stability filter state (section 5.3): window words and scores per page
         self.stability_window, self.stability_theta = stability_window, stability_theta
         self.history = self.stability = None
         if stability_window:
             self.history = torch.zeros((S, max_pages), dtype=torch.int32, device=device)
             self.stability = torch.zeros((S, max_pages), dtype=torch.float32, device=device)
+        self._streams_seen = set()
+
+    def _on(self, stream):
+        """Before the first launch on a stream other than torch's current one:
+        order it after the current stream's work (the zero fills of this
+        object's buffers and workspaces) and mark the buffers as used there."""
+        st = _torch_stream(stream, self.level.device)
+        if st is None or st.cuda_stream in self._streams_seen:
+            return
+        order_after_current(st, self.level.device, self.level, self.anchors, self.page_idx, self.page_score,
+                            self.n_selected, self.affinity, self.head_weight, self.ws_pool, self.ws_anchor,
+                            self.ws_score, self.history, self.stability, getattr(self, "running", None))
+        self._streams_seen.add(st.cuda_stream)
 
     @property
     def anchor_weights(self) -> Optional[torch.Tensor]:
@@ -57,14 +73,16 @@ class Selector:
     def pool(self, stream=None):
         """Block vectors of every block into the page rows of the level buffer
         (variance mode also computes and freezes the head weights)."""
+        self._on(stream)
         kka_pool_blocks(self.kp, self.seqs, self.level, mode=self.mode, head_weight=self.head_weight,
                         vb_seq_stride=self.lay.rows_per_seq, workspace=self.ws_pool, stream=stream)
 
     def repool(self, blocks: torch.Tensor, workspace: Optional[torch.Tensor] = None, stream=None):
-        """Re-pool a subset of blocks with the frozen weights (incremental update)."""
+        """Re-pool a subset of blocks with the frozen weights (incremental update).
+        Without a workspace the binding allocates a zero-filled one ordered
+        before the launch on `stream` and kept alive until it ends."""
         mode = WEIGHT_GIVEN if self.mode != WEIGHT_UNIFORM else WEIGHT_UNIFORM
-        if workspace is None:
-            workspace = new_workspace(kka_pool_blocks_workspace(self.kp, self.seqs, mode, blocks), self.level.device)
+        self._on(stream)
         kka_pool_blocks(self.kp, self.seqs, self.level, mode=mode, head_weight=self.head_weight, blocks=blocks,
                         vb_seq_stride=self.lay.rows_per_seq, workspace=workspace, stream=stream)
 
@@ -76,22 +94,27 @@ class Selector:
             self.running = torch.zeros((self.seqs.num_seqs, self.kp.head_dim), dtype=torch.float32,
                                        device=self.level.device)
             seed = True
+            self._streams_seen.clear()  # a new buffer: order it on every stream again
+        self._on(stream)
         mode = WEIGHT_GIVEN if self.mode != WEIGHT_UNIFORM else WEIGHT_UNIFORM
         kka_pool_on_write(self.kp, self.seqs, self.level, self.running, new_k=new_k, mode=mode,
                           head_weight=self.head_weight, seed=seed, vb_seq_stride=self.lay.rows_per_seq,
                           stream=stream)
 
     def anchor(self, stream=None):
+        self._on(stream)
         kka_pool_anchor(self.kp, self.seqs, self.window, self.anchors, head_weight=self.head_weight,
                         workspace=self.ws_anchor, stream=stream)
 
     def levels(self, n_pages: torch.Tensor, first_dirty_page: Optional[torch.Tensor] = None, stream=None):
+        self._on(stream)
         kka_build_levels(self.lay, self.level, n_pages, first_dirty_page, stream=stream)
 
     def score(self, n_pages: torch.Tensor, anchors: Optional[torch.Tensor] = None, stream=None, lazy: bool = False):
         """Affinity + top-K; lazy=True scores only children of kept parents.
         With a stability window the single pass also advances every page's
         window word and stability score."""
+        self._on(stream)
         stab = {}
         if getattr(self, "history", None) is not None and not lazy:
             stab = dict(history=self.history, stability_out=self.stability, window=self.stability_window,
