@@ -40,6 +40,11 @@ TAG_VB = 18
 TAG_ANCHOR = 19
 TAG_RUN_POS = 20
 TAG_QUERY = 21
+TAG_HEAD_ROLE = 22
+TAG_RELEVANCE = 23
+TAG_BLOCK_DIR = 24
+TAG_POS_DIR = 25
+TAG_NOISE = 26
 
 
 def build(force: bool = True) -> str:
@@ -424,6 +429,66 @@ def config5(seed: int = 0, n_seqs: int = 32, len_lo: int = 4096, len_hi: int = 6
                         "block_table": table_after}
     w.extra["head_var"] = var.reshape(L, H)
     return w
+
+
+def positional_heads_workload(seed: int = 0, n_topic_heads: int = 16, amp_topic: float = 1.0,
+                              amp_pos: float = 0.3, noise: float = 0.2, query_amp: float = 8.0):
+    """0.5B key shape (24 layers x 2 KV heads x head_dim 64, 4096 tokens in
+    blocks of 16, identity table, anchor = last 8 tokens, flat top-16) with
+    two kinds of heads, for the overlap of key-key selection with attention
+    (the page's section 3.3 and 6.1 experiment):
+
+    * n_topic_heads "topic" heads (a seeded choice among the 48): every block
+      b has a relevance r_b ~ U(0, 1) (the last block, which holds the
+      anchor, has r = 1), and its keys are amp_topic * sqrt(D) * (r_b * u_h +
+      sqrt(1 - r_b^2) * w_bh) with u_h the head's anchor direction and w_bh a
+      per-block direction orthogonal to it: a large spread over the context.
+    * the other heads are "positional": amp_pos * sqrt(D) * (cos(th_t) e1 +
+      sin(th_t) e2), th_t = pi * t / T, the same two directions for every
+      such head -- a component that drifts with position, not with content,
+      and a small spread over the context.
+    * every element also carries N(0, noise).
+
+    Queries [L][14][D] (7 query heads per KV head): amp along u_h for the
+    query heads of topic heads, zero for the others, so attention follows
+    the graded relevance and the positional heads attend uniformly.
+    Returns (KWorkload, queries, relevance[256], topic_head_mask[L][H])."""
+    L, H, D, B, nb, Hq = 24, 2, 64, 16, 256, 14
+    T = nb * B
+    LH = L * H
+    role = np.zeros(LH, dtype=bool)
+    role[permutation(seed, TAG_HEAD_ROLE, LH)[:n_topic_heads]] = True
+    rel = uniform(seed, TAG_RELEVANCE, nb).astype(np.float64)
+    rel[-1] = 1.0
+    u = unit_dirs(seed, TAG_TOPIC_DIR, LH, D).astype(np.float64)             # [LH][D]
+    wdir = unit_dirs(seed, TAG_BLOCK_DIR, nb * LH, D).astype(np.float64).reshape(nb, LH, D)
+    wdir -= np.einsum("bhd,hd->bh", wdir, u)[..., None] * u[None]            # orthogonal to u_h
+    wdir /= np.linalg.norm(wdir, axis=-1, keepdims=True)
+    e = unit_dirs(seed, TAG_POS_DIR, 2, D).astype(np.float64)
+    e[1] -= (e[1] @ e[0]) * e[0]
+    e[1] /= np.linalg.norm(e[1])
+    th = np.pi * np.arange(T) / T
+    pos = amp_pos * math.sqrt(D) * (np.cos(th)[:, None] * e[0] + np.sin(th)[:, None] * e[1])   # [T][D]
+    topic = amp_topic * math.sqrt(D) * (rel[:, None, None] * u[None] +
+                                        np.sqrt(1.0 - rel ** 2)[:, None, None] * wdir)        # [nb][LH][D]
+    keys = np.empty((T, LH, D), dtype=np.float64)
+    keys[:, role] = np.repeat(topic[:, role], B, axis=0)
+    keys[:, ~role] = pos[:, None, :]
+    keys += normal(seed, TAG_NOISE, T * LH * D, 0.0, noise).reshape(T, LH, D)
+    # [T][L][H][D] -> [L][P=nb][B][H][D]
+    k = keys.reshape(nb, B, L, H, D).transpose(2, 0, 1, 3, 4)
+    w = kpool_from_f32("quality_0.5b_positional_heads", k.astype(np.float32), [T], [0, nb],
+                       np.arange(nb, dtype=np.int32), window=8, mode="uniform",
+                       select={"hierarchical": 0, "k_grid": 0, "k_chunk": 0, "k_page": 16,
+                               "pages_per_chunk": 16, "chunks_per_grid": 16})
+    w.seed = seed
+    q = np.zeros((L, Hq, D), dtype=np.float32)
+    G = Hq // H
+    for l in range(L):
+        for h in range(H):
+            if role[l * H + h]:
+                q[l, h * G:(h + 1) * G] = (query_amp * u[l * H + h]).astype(np.float32)
+    return w, q, rel, role.reshape(L, H)
 
 
 def kpool_from_f32(name: str, keys: np.ndarray, seq_len, block_offsets, block_table, window: int = 16,

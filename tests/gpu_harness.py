@@ -9,7 +9,9 @@ affinities.
 """
 from __future__ import annotations
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -106,3 +108,78 @@ def check_selection(sel: Selector, s: int, n_p: int, tag: str = ""):
 def oracle_vb(w, blocks, weights=None):
     kp = oracle.KPool.of(w)
     return oracle.pool_blocks(kp, w.seq_len, w.block_offsets, w.block_table, weights, blocks=set(blocks))
+
+
+def host_threads() -> int:
+    """Worker threads for the oracle at full size: the cores this process may
+    run on, at most 16 (the GPU host's share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def pmap(fn, items):
+    """[fn(x) for x in items] on host_threads() threads.  The oracle's C
+    calls run without Python's lock, so independent blocks and sequences
+    pool in parallel; each call is the unchanged single-threaded oracle."""
+    items = list(items)
+    if len(items) <= 1:
+        return [fn(x) for x in items]
+    with ThreadPoolExecutor(max_workers=host_threads()) as ex:
+        return list(ex.map(fn, items, chunksize=max(1, len(items) // (8 * host_threads()))))
+
+
+def oracle_vb_all(w, weights=None, seq_len=None, block_offsets=None, block_table=None) -> np.ndarray:
+    """Oracle v_b of every logical block [total_blocks][D], in parallel.
+    weights: None (uniform) or [S][L*H]; the CSR arrays default to w's."""
+    kp = oracle.KPool.of(w)
+    T = w.seq_len if seq_len is None else seq_len
+    off = w.block_offsets if block_offsets is None else block_offsets
+    tab = w.block_table if block_table is None else block_table
+    S = len(T)
+    seq_of = np.repeat(np.arange(S), np.diff(off))
+
+    def one(b):
+        s = int(seq_of[b])
+        i = b - int(off[s])
+        return oracle.pool_block(kp, int(tab[b]), oracle.n_valid(T, kp.B, i, s),
+                                 None if weights is None else weights[s])
+    n = int(off[-1])
+    return np.stack(pmap(one, range(n))) if n else np.zeros((0, w.D), np.float32)
+
+
+def oracle_weights_all(w, seq_len=None, block_offsets=None, block_table=None) -> np.ndarray:
+    """Oracle head weights [S][L*H] of every sequence, in parallel."""
+    kp = oracle.KPool.of(w)
+    T = w.seq_len if seq_len is None else seq_len
+    off = w.block_offsets if block_offsets is None else block_offsets
+    tab = w.block_table if block_table is None else block_table
+    rows = pmap(lambda s: oracle.head_weights(kp, oracle.seq_table(off, tab, s), int(T[s])), range(len(T)))
+    return np.stack(rows)
+
+
+def oracle_anchors_all(w, weights=None, seq_len=None, block_offsets=None, block_table=None) -> np.ndarray:
+    """Oracle anchors [S][D] of every sequence, in parallel."""
+    kp = oracle.KPool.of(w)
+    T = w.seq_len if seq_len is None else seq_len
+    off = w.block_offsets if block_offsets is None else block_offsets
+    tab = w.block_table if block_table is None else block_table
+    rows = pmap(lambda s: oracle.pool_anchor(kp, oracle.seq_table(off, tab, s), int(T[s]), w.window,
+                                             None if weights is None else weights[s]), range(len(T)))
+    return np.stack(rows)
+
+
+def assert_rows_close(got: np.ndarray, ref: np.ndarray, what: str, atol: float = ATOL):
+    """Element-wise |got - ref| <= atol over every row; names the worst row."""
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} != {ref.shape}"
+    if got.size == 0:
+        return
+    err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+    if not (err <= atol).all() or not np.isfinite(got).all():
+        r = int(np.unravel_index(np.nanargmax(np.where(np.isfinite(err), err, np.inf)), err.shape)[0])
+        raise AssertionError(f"{what}: row {r} max abs error {float(np.max(err[r])):.3e} > {atol:g} "
+                             f"({int((err > atol).any(axis=-1).sum())} rows over)")

@@ -38,16 +38,16 @@ def test_counter_summary_calibrates_against_the_copy(tmp_path):
     factors and averaged over its dispatches."""
     hdr = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
     pool = "void kka::(anonymous namespace)::pool_kernel<0, 256>(kka::PoolArgs)"
-    score = "void kka::(anonymous namespace)::score_kernel<8, 4, 1, false>(kka::ScoreArgs)"
-    select = "kka::(anonymous namespace)::select_kernel(kka::ScoreArgs)"
+    score = "void kka::(anonymous namespace)::score_topk_kernel<256, 8, 4, 4, 4, false>(kka::ScoreArgs, float*)"
+    small = "void kka::(anonymous namespace)::score_topk_kernel<1024, 8, 4, 2, 2, false>(kka::ScoreArgs, float*)"
     copy = "__amd_rocclr_copyBuffer"
     fetch = [[copy, 1 << 20, "FETCH_SIZE", 2 * GIB_KIB], [copy, 64, "FETCH_SIZE", 1.0],
              [pool, 2097152, "FETCH_SIZE", 1000.0], [pool, 2097152, "FETCH_SIZE", 3000.0],
-             [score, 2244608, "FETCH_SIZE", 400.0], [select, 32768, "FETCH_SIZE", 40.0],
+             [score, 1146880, "FETCH_SIZE", 400.0], [small, 36864, "FETCH_SIZE", 40.0],
              [pool, 2097152, "OTHER", 9e9]]
     write = [[copy, 1 << 20, "WRITE_SIZE", GIB_KIB], [copy, 64, "WRITE_SIZE", 1.0],
              [pool, 2097152, "WRITE_SIZE", 10.0], [pool, 2097152, "WRITE_SIZE", 30.0],
-             [score, 2244608, "WRITE_SIZE", 8.0], [select, 32768, "WRITE_SIZE", 2.0]]
+             [score, 1146880, "WRITE_SIZE", 8.0], [small, 36864, "WRITE_SIZE", 2.0]]
     fcsv, wcsv = tmp_path / "fetch.csv", tmp_path / "write.csv"
     _write_csv(fcsv, hdr, fetch)
     _write_csv(wcsv, hdr, write)
@@ -61,8 +61,8 @@ def test_counter_summary_calibrates_against_the_copy(tmp_path):
     assert k["kernel_source_sha256_16"] == bench.kernel_source_hash("kka_pool.hip")
     assert k["commands"] == "cmd"
     s = json.load(open(tmp_path / os.path.basename(bench.SCORE_COUNTERS)))
-    # score 400 KiB * 0.5 + 8 KiB, select 40 KiB * 0.5 + 2 KiB
-    assert s["traffic_bytes_per_call"] == (204800 + 8192) + (20480 + 2048)
+    # the serving call (the large one-launch grid): 400 KiB * 0.5 + 8 KiB; the one-sequence launch is not it
+    assert s["traffic_bytes_per_call"] == 204800 + 8192
     assert s["kernel_source_sha256_16"] == bench.kernel_source_hash("kka_score.hip")
 
 

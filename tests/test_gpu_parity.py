@@ -11,7 +11,8 @@ import oracle
 import synth
 from kv_cache_block_amd.pipeline import Selector
 
-from gpu_harness import ATOL, WEIGHT_RTOL, check_selection, mode_of, n_pages_of, oracle_vb, run_selector, say, upload
+from gpu_harness import (ATOL, WEIGHT_RTOL, assert_rows_close, check_selection, host_threads, mode_of, n_pages_of,
+                         oracle_anchors_all, oracle_vb, oracle_vb_all, oracle_weights_all, run_selector, say, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -186,6 +187,38 @@ def test_incremental_repool_equals_scratch():
         ref = oracle.pool_block(okp, int(after["block_table"][newest[s]]), n_b, wf[s])
         np.testing.assert_allclose(lvl[s, i], ref, atol=ATOL, rtol=0)
         np.testing.assert_allclose(lvl[s, i], full[s, i], atol=1e-6, rtol=0)
+
+
+def test_repool_on_a_side_stream_matches_the_current_stream():
+    """Pool, re-pool (workspace allocated by the binding) and anchor on a
+    stream that is not torch's current one: the zero-filled workspaces are
+    ordered before the launches and the results equal the same calls on the
+    current stream, bit for bit."""
+    say("repool on a side stream")
+    w = synth.config5(7, n_seqs=5, len_lo=60, len_hi=400, L=3, H=4, D=128, B=16)
+    after = w.extra["after"]
+    dev = "cuda"
+    newest = torch.from_numpy((after["block_offsets"][1:] - 1).astype(np.int32)).to(dev)
+    results = []
+    for use_side in (False, True):
+        kp, seqs_before = upload(w)
+        seqs_after = kka.Seqs(torch.from_numpy(after["seq_len"]).to(dev),
+                              torch.from_numpy(after["block_offsets"]).to(dev),
+                              torch.from_numpy(after["block_table"]).to(dev), int(after["block_offsets"][-1]))
+        sel = Selector(kp, seqs_before, w.select, max_pages=int(np.max(np.diff(after["block_offsets"]))),
+                       window=w.window, mode=kka.WEIGHT_VARIANCE)
+        side = torch.cuda.Stream() if use_side else None
+        sel.pool(stream=side)
+        sel.seqs = seqs_after
+        sel.repool(newest, stream=side)
+        sel.anchor(stream=side)
+        if side is not None:
+            side.synchronize()
+        torch.cuda.synchronize()
+        assert kka.kka_device_error() == 0
+        results.append((sel.level.cpu().numpy(), sel.anchors.cpu().numpy(), sel.head_weight.cpu().numpy()))
+    for a, b in zip(*results):
+        np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
 # ------------------------------------------------------------------ anchor
@@ -410,20 +443,20 @@ def test_config2_parity_and_recovery():
     assert (w.block_topic[0][idx[:8]] == w.anchor_topic[0]).all()
 
 
-def test_config3_full_size_sampled_parity_and_recovery():
+def test_config3_full_size_parity_and_recovery():
     """7B shape at 131072 tokens (3.76 GB of keys), launched exactly as the
-    benchmark launches it: sampled block vectors against the oracle, the
-    anchor, every level and affinity, and the selection."""
+    benchmark launches it: every one of the 8192 block vectors against the
+    oracle (run on the host's cores, one unchanged single-threaded oracle
+    call per block), the anchor, every level row and affinity, and the
+    selection."""
     say("config3 generate (3.76 GB keys)")
     w = synth.config3(0)
     say("config3 run")
     sel, npg = run_selector(w)
-    rng = np.random.default_rng(0)
-    sample = sorted(set(rng.choice(w.total_blocks, 96, replace=False).tolist()) | {0, w.total_blocks - 1})
-    ref = oracle_vb(w, sample)
-    got = vb_rows(sel, w)
-    for b in sample:
-        np.testing.assert_allclose(got[b], ref[b], atol=ATOL, rtol=0, err_msg=f"block {b}")
+    say(f"config3 oracle: {w.total_blocks} blocks on {host_threads()} threads")
+    ref = oracle_vb_all(w)
+    got = sel.level[0, :w.total_blocks].cpu().numpy()
+    assert_rows_close(got, ref, "config3 v_b")
     okp = oracle.KPool.of(w)
     a = oracle.pool_anchor(okp, w.block_table, int(w.seq_len[0]), w.window)
     np.testing.assert_allclose(sel.anchors[0].cpu().numpy(), a, atol=ATOL, rtol=0)
@@ -457,19 +490,28 @@ def test_config4_full_size_parity_and_recovery():
         assert (v.page_topic[s][idx] == v.anchor_topic[s]).all()
 
 
+def _level_pages(lvl: np.ndarray, block_offsets) -> np.ndarray:
+    """Page rows of every sequence of a level buffer, in global block order."""
+    nb = np.diff(block_offsets)
+    return np.concatenate([lvl[s, :int(nb[s])] for s in range(len(nb))])
+
+
 @pytest.mark.timeout(900)
 def test_ragged_variance_batch_full_size_and_decode_step():
     """32 sequences of 4096-65536 tokens (about 32 GB of bf16 keys), blocks of
     64, one shared permuted pool, head-variance weighting, flat top-48; then
     one decode step: one token appended per sequence, the newest block of
     each re-pooled with the frozen weights, anchor, score and select again.
-    Sampled against the oracle: weights of two sequences, their block
-    vectors and anchors; every sequence's selection on the GPU's own
-    affinities; every re-pooled block."""
+    Everything against the oracle (run on the host's cores): the weights of
+    all 32 sequences, the longest (64,866 tokens) included, every block
+    vector before the append, every anchor before and after it, every
+    re-pooled block, every selection; blocks the append did not touch keep
+    their bits."""
     say("ragged variance batch: generate (~32 GB of keys)")
     w = synth.config5(0)
     after = w.extra["after"]
-    say(f"ragged variance batch: upload {w.k.nbytes / 1e9:.1f} GB, {w.S} sequences, {w.P} blocks")
+    say(f"ragged variance batch: upload {w.k.nbytes / 1e9:.1f} GB, {w.S} sequences, {w.P} blocks, "
+        f"lengths {int(w.seq_len.min())}..{int(w.seq_len.max())}")
     kp, seqs = upload(w)
     max_pages = int(np.max(np.diff(after["block_offsets"])))
     sel = Selector(kp, seqs, w.select, max_pages=max_pages, window=w.window, mode=kka.WEIGHT_VARIANCE)
@@ -480,24 +522,17 @@ def test_ragged_variance_batch_full_size_and_decode_step():
     sel.score(npg)
     torch.cuda.synchronize()
     assert kka.kka_device_error() == 0
-    okp = oracle.KPool.of(w)
     wg = sel.head_weight.cpu().numpy()
-    lvl = sel.level.cpu().numpy()
+    lvl_before = sel.level.cpu().numpy()
     anc = sel.anchors.cpu().numpy()
-    order = np.argsort(w.seq_len)
-    sample = [int(order[0]), int(order[len(order) // 2])]
-    say(f"ragged variance batch: oracle on sequences {sample}")
-    for s in sample:
-        tab = oracle.seq_table(w.block_offsets, w.block_table, s)
-        wref = oracle.head_weights(okp, tab, int(w.seq_len[s]))
-        np.testing.assert_allclose(wg[s], wref, rtol=WEIGHT_RTOL, atol=0)
-        nb = len(tab)
-        for i in sorted({0, 1, nb // 2, nb - 2, nb - 1}):
-            n_b = min(w.B, int(w.seq_len[s]) - i * w.B)
-            ref = oracle.pool_block(okp, int(tab[i]), n_b, wref)
-            np.testing.assert_allclose(lvl[s, i], ref, atol=ATOL, rtol=0, err_msg=f"seq {s} block {i}")
-        a = oracle.pool_anchor(okp, tab, int(w.seq_len[s]), w.window, wref)
-        np.testing.assert_allclose(anc[s], a, atol=ATOL, rtol=0)
+    say(f"ragged variance batch: oracle weights of {w.S} sequences on {host_threads()} threads")
+    wref = oracle_weights_all(w)
+    np.testing.assert_allclose(wg, wref, rtol=WEIGHT_RTOL, atol=0)
+    say(f"ragged variance batch: oracle v_b of {w.total_blocks} blocks")
+    # end to end: the oracle pools with its own weights
+    ref_vb = oracle_vb_all(w, weights=wref)
+    assert_rows_close(_level_pages(lvl_before, w.block_offsets), ref_vb, "ragged v_b before the append")
+    assert_rows_close(anc, oracle_anchors_all(w, weights=wref), "ragged anchors before the append")
     for s in range(w.S):
         check_selection(sel, s, int(npg[s]), "ragged")
 
@@ -516,17 +551,21 @@ def test_ragged_variance_batch_full_size_and_decode_step():
     assert kka.kka_device_error() == 0
     assert torch.equal(sel.head_weight, frozen)
     lvl = sel.level.cpu().numpy()
-    wf = frozen.cpu().numpy()
+    okp = oracle.KPool.of(w)
+    nb_before = np.diff(w.block_offsets)
     for s in range(w.S):
         i = int(newest[s] - after["block_offsets"][s])
         n_b = int(after["seq_len"][s]) - i * w.B
-        ref = oracle.pool_block(okp, int(after["block_table"][newest[s]]), n_b, wf[s])
+        ref = oracle.pool_block(okp, int(after["block_table"][newest[s]]), n_b, wref[s])
         np.testing.assert_allclose(lvl[s, i], ref, atol=ATOL, rtol=0, err_msg=f"seq {s} newest block")
+        # every older block keeps the bits it had before the append
+        np.testing.assert_array_equal(lvl[s, :i].view(np.uint32), lvl_before[s, :i].view(np.uint32),
+                                      err_msg=f"seq {s} blocks untouched by the append")
+        assert i in (nb_before[s] - 1, nb_before[s])
         check_selection(sel, s, int(npg_after[s]), "ragged decode")
-    for s in sample:
-        tab = oracle.seq_table(after["block_offsets"], after["block_table"], s)
-        a = oracle.pool_anchor(okp, tab, int(after["seq_len"][s]), w.window, wf[s])
-        np.testing.assert_allclose(sel.anchors[s].cpu().numpy(), a, atol=ATOL, rtol=0)
+    anc_ref = oracle_anchors_all(w, weights=wref, seq_len=after["seq_len"], block_offsets=after["block_offsets"],
+                                 block_table=after["block_table"])
+    assert_rows_close(sel.anchors.cpu().numpy(), anc_ref, "ragged anchors after the append")
 
 
 @pytest.mark.parametrize("case", [
@@ -536,11 +575,18 @@ def test_ragged_variance_batch_full_size_and_decode_step():
     dict(hierarchical=0, k_grid=0, k_chunk=0, k_page=9, pages_per_chunk=16, chunks_per_grid=16),
 ])
 @pytest.mark.parametrize("S", [5, 600])
-def test_selection_both_launch_shapes(case, S):
-    """Few sequences score and select in one launch; 600 short sequences
-    (more tiles than fit on the chip at once) take the scoring launch and
-    then the selection launch.  Both against the oracle, on the same rules."""
-    say(f"launch shapes S={S} {case}")
+@pytest.mark.parametrize("path", ["one_launch", "two_launch"])
+def test_selection_both_launch_shapes(case, S, path, monkeypatch):
+    """Three paths on the same inputs, all against the oracle on the same
+    rules: 5 sequences score and select in one launch with the selection
+    handed to the group that finishes a sequence's last tile; 600 short
+    sequences (more tiles than fit on the chip at once) score and select in
+    one launch with a selecting group per sequence beside the scoring tiles;
+    KKA_SCORE_TWO_LAUNCH=1 forces the scoring launch then the selection
+    launch."""
+    if path == "two_launch":
+        monkeypatch.setenv("KKA_SCORE_TWO_LAUNCH", "1")
+    say(f"launch shapes S={S} {path} {case}")
     max_pages, D = 60, 8
     lay = kka.LevelLayout(S, max_pages, D, bool(case["hierarchical"]), case["pages_per_chunk"],
                           case["chunks_per_grid"])
@@ -1025,3 +1071,45 @@ def test_variance_weights_of_constant_sequences_are_uniform():
     got = vb_rows(sel, w)
     for b, v in oracle_vb(w, range(w.total_blocks), wref).items():
         np.testing.assert_allclose(got[b], v, atol=ATOL, rtol=0, err_msg=f"block {b}")
+
+
+def test_variance_weights_of_large_offset_low_variance_heads():
+    """Heads whose keys sit at a large offset and change by one bf16 ulp in a
+    few tokens only, on a 65,536-token sequence (every head like that) and a
+    shorter one (mixed with ordinary heads): the spread is far below the
+    mean square (down to ~1e-12 of it), where E[x^2] - E[x]^2 would cancel.
+    Weights against the oracle's two-pass fp64 variance at rtol 1e-6; block
+    vectors (magnitudes up to 4e4) within 3e-7 relative plus 1e-5."""
+    say("variance weights of large-offset, low-variance heads (65,536 tokens)")
+    L, H, D, B = 2, 4, 64, 64
+    w = ragged_workload(43, 2, L, H, D, B, 0, 0, mode="variance", lengths=[65536, 3000])
+    LH = L * H
+    offsets = np.array([1000.0, -300.0, 77.5, 4096.0, 0.75, -12.0, 250.0, 30000.0], np.float32)
+    p_dev = np.array([1e-4, 1e-3, 3e-3, 1e-2, 3e-4, 3e-2, 2e-3, 5e-4], np.float32)
+    ulp = np.float32(2.0) ** (np.floor(np.log2(np.abs(offsets))) - 7)  # bf16 spacing at the offset
+    n = L * w.P * B * H * D
+    u = synth.uniform(43, 120, n).reshape(L, w.P, B, H, D)
+    sign = np.where(synth.uniform(43, 121, n).reshape(L, w.P, B, H, D) < 0.5, -1.0, 1.0).astype(np.float32)
+    f = np.empty((L, w.P, B, H, D), np.float32)
+    for l in range(L):
+        for h in range(H):
+            lh = l * H + h
+            f[l, :, :, h, :] = offsets[lh] + np.where(u[l, :, :, h, :] < p_dev[lh], sign[l, :, :, h, :] * ulp[lh], 0.0)
+    # the shorter sequence: two of its heads are ordinary (noise of unit size around the offset)
+    noise = synth.normal(43, 122, n).reshape(L, w.P, B, H, D).astype(np.float32)
+    for i in range(int(w.block_offsets[1]), int(w.block_offsets[2])):
+        p = int(w.block_table[i])
+        f[0, p, :, 1, :] += noise[0, p, :, 1, :]
+        f[1, p, :, 2, :] += noise[1, p, :, 2, :]
+    w.k = synth.to_bf16_bits(f)
+    sel, _ = run_selector(w)
+    assert kka.kka_device_error() == 0
+    okp = oracle.KPool.of(w)
+    wref = oracle.weights_all(okp, w.seq_len, w.block_offsets, w.block_table)
+    wgpu = sel.head_weight.cpu().numpy()
+    # the long sequence's weights are far from uniform: every head varies, by different amounts
+    assert np.ptp(wref[0]) > 0.1 and (wref[0] > 0).all()
+    np.testing.assert_allclose(wgpu, wref, rtol=WEIGHT_RTOL, atol=0)
+    got = vb_rows(sel, w)
+    for b, v in oracle_vb(w, range(w.total_blocks), wref).items():
+        np.testing.assert_allclose(got[b], v, rtol=3e-7, atol=1e-5, err_msg=f"block {b}")

@@ -671,3 +671,35 @@ def test_overlap_rate():
     assert oracle.overlap([3, 1, 2, 9], [2, 3, 4, 5], 4) == 0.5
     assert oracle.overlap([1, 2], [2, 1], 2) == 1.0
     assert oracle.overlap([], [], 0) == 0.0
+
+
+def test_variance_weighting_raises_attention_overlap_on_positional_heads():
+    """The page's quality experiment (sections 3.3 and 6.1) on a planted
+    0.5B-shape workload: two thirds of the heads are positional (a component
+    that drifts with position and is shared by every such head, small spread
+    over the context), one third carry graded topic relevance (large
+    spread), and the decode query attends through the topic heads only.  A
+    plain mean is pulled toward recent blocks by the coherent positional
+    heads; weighting heads by their temporal variance recovers the blocks
+    attention ranks highest.  The attention top-16 is unique (graded
+    relevance, no ties), and the variance-weighted top-16 overlaps it far
+    more than the uniform one."""
+    w, q, rel, role = synth.positional_heads_workload(0)
+    kp = oracle.KPool.of(w)
+    T, nb, k = int(w.seq_len[0]), w.total_blocks, 16
+    att = oracle.attention_blocks(kp, w.block_table, T, q, 1.0 / np.sqrt(w.D))
+    order = np.lexsort((np.arange(nb), -att.astype(np.float64)))
+    assert att[order[k - 1]] > att[order[k]]  # the attention top-k is unique
+    a_idx = order[:k]
+    assert rel[a_idx].min() > 0.9  # attention follows the planted relevance
+    ov = {}
+    for mode in ("uniform", "variance"):
+        wts = oracle.weights_all(kp, w.seq_len, w.block_offsets, w.block_table) if mode == "variance" else None
+        vb = oracle.pool_blocks(kp, w.seq_len, w.block_offsets, w.block_table, wts)
+        pages = np.stack([vb[b] for b in range(nb)])
+        anc = oracle.pool_anchor(kp, w.block_table, T, w.window, None if wts is None else wts[0])
+        idx, _ = oracle.select(oracle.affinity(pages, anc), hierarchical=0, k_page=k)
+        ov[mode] = oracle.overlap(idx, a_idx, k)
+        if wts is not None:  # topic heads weigh more than positional ones
+            assert wts[0][role.ravel()].min() > 3 * wts[0][~role.ravel()].max()
+    assert ov["variance"] >= 0.6 and ov["variance"] >= ov["uniform"] + 0.3, ov
