@@ -126,17 +126,19 @@ def run(args):
         if evs is not None:
             evs[1].record(stream)
         sel.anchor()
-        sel.levels(npg)
         if evs is not None:
             evs[2].record(stream)
-        sel.score(npg)
+        sel.levels(npg)
         if evs is not None:
             evs[3].record(stream)
+        sel.score(npg)
+        if evs is not None:
+            evs[4].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -147,7 +149,12 @@ def run(args):
         raise RuntimeError("device error flag raised during the benchmark")
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     pool_ms = [e[0].elapsed_time(e[1]) for e in events]
-    score_ms = [e[2].elapsed_time(e[3]) for e in events]
+    anchor_ms = [e[1].elapsed_time(e[2]) for e in events]
+    levels_ms = [e[2].elapsed_time(e[3]) for e in events]
+    score_ms = [e[3].elapsed_time(e[4]) for e in events]
+    anchor_us = 1e3 * float(np.mean(anchor_ms))
+    anchor_med_us = 1e3 * float(np.median(anchor_ms))
+    levels_us = 1e3 * float(np.mean(levels_ms))
     pool_us = 1e3 * float(np.mean(pool_ms))
     c3_score_us = 1e3 * float(np.mean(score_ms))
     pool_med_us = 1e3 * float(np.median(pool_ms))
@@ -324,7 +331,7 @@ def run(args):
     traffic = traffic_from_counters()
     out = {
         "metric": METRIC,
-        "value": round(step_gbps, 2),
+        "value": round(kpool_gbps, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -333,7 +340,7 @@ def run(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {
             "workload": "7B key shape (28 layers x 4 KV heads x head_dim 128), 131072-token context, "
@@ -344,6 +351,15 @@ def run(args):
             "accumulate_dtype": "f32",
             "step_algorithmic_bytes": step_bytes,
         },
+        "value_is": "K-pool GB/s: algorithmic bytes of one kka_pool_blocks launch over the 8192 blocks / its mean "
+                    "event-timed duration",
+        "step_GBps": round(step_gbps, 2),
+        "anchor_us": round(anchor_us, 2),
+        "anchor_median_us": round(anchor_med_us, 2),
+        "anchor_algorithmic_bytes": b_anchor,
+        "anchor_GBps": round(b_anchor / (anchor_us * 1e-6) / 1e9, 2),
+        "levels_us": round(levels_us, 2),
+        "levels_algorithmic_bytes": b_levels,
         "kpool_GBps": round(kpool_gbps, 2),
         "kpool_frac_of_peak": round(kpool_gbps / PEAK_HBM_GBPS, 4),
         "kpool_us": round(pool_us, 2),
@@ -351,7 +367,8 @@ def run(args):
         "kpool_algorithmic_bytes": b_pool,
         "score_topk_us_per_step": round(c3_score_us, 2),
         "score_topk_median_us": round(c3_score_med_us, 2),
-        "score_topk_launches": "one (score_select_kernel): the batch's tiles fit on the chip at once",
+        "score_topk_launches": "one (score_topk_kernel): a selecting work-group per sequence (coarse-to-fine, "
+                               "re-scoring its candidate rows) beside the work-groups that score every row",
         "serving_score_topk_us_per_step": round(c4_us, 2),
         "serving_score_topk_median_us": round(c4_med_us, 2),
         "serving_score_topk_warm_cache_us": round(c4_warm_us, 2),
@@ -388,7 +405,7 @@ def run(args):
         },
         "roofline_serving_score": {
             "bound": "hbm",
-            "kernel": "kka_score_topk: score_kernel then select_kernel (whole call, event-timed)",
+            "kernel": "kka_score_topk: score_topk_kernel, one launch (whole call, event-timed)",
             "achieved": round(c4_gbps, 2),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
@@ -451,6 +468,34 @@ def quality_overlaps(args, dev):
         res[name] = entry
         del k, kp, seqs
         torch.cuda.empty_cache()
+    # positional heads (shared drift with position, small spread) beside topic
+    # heads of graded relevance (large spread): the case variance weighting is for
+    w, q_np, rel, role = synth.positional_heads_workload(args.seed)
+    k = torch.from_numpy(w.k.reshape(-1).view(np.int16)).to(dev)
+    kp = kka.KPool(k, w.L, w.H, w.D, w.B, w.P)
+    seqs = kka.Seqs(torch.from_numpy(w.seq_len).to(dev), torch.from_numpy(w.block_offsets).to(dev),
+                    torch.from_numpy(w.block_table).to(dev), w.total_blocks)
+    kq, Hq = w.select["k_page"], q_np.shape[1]
+    att = torch.zeros((1, w.total_blocks), dtype=torch.float32, device=dev)
+    aidx = torch.zeros((1, kq), dtype=torch.int32, device=dev)
+    kka.kka_attention_topk(kp, seqs, torch.from_numpy(q_np[None].copy()).to(dev), Hq, att, w.total_blocks, k=kq,
+                           idx_out=aidx)
+    a_idx = aidx[0].cpu().numpy()
+    entry = {"k": kq, "attention_mean_relevance": round(float(rel[a_idx].mean()), 4),
+             "workload": "0.5B key shape, 4096 tokens, 16 topic heads of graded relevance r ~ U(0, 1) and 32 "
+                         "positional heads (a drift with position shared by all of them); the query attends "
+                         "through the topic heads"}
+    npg = torch.tensor([w.total_blocks], dtype=torch.int32, device=dev)
+    for mode_name, mode in (("uniform", kka.WEIGHT_UNIFORM), ("variance", kka.WEIGHT_VARIANCE)):
+        sel = Selector(kp, seqs, w.select, max_pages=w.total_blocks, window=w.window, mode=mode, device=dev)
+        sel.step(npg)
+        s_idx = sel.page_idx[0, :kq].cpu().numpy()
+        entry[mode_name] = {"overlap": overlap(s_idx, a_idx, kq),
+                            "mean_relevance": round(float(rel[s_idx].mean()), 4)}
+    torch.cuda.synchronize()
+    res["0.5B_positional_heads"] = entry
+    del k, kp, seqs
+    torch.cuda.empty_cache()
     return res
 
 
@@ -708,6 +753,95 @@ def profile_pass(args):
                       "score_source_sha256_16": kernel_source_hash("kka_score.hip")}), flush=True)
 
 
+def profile_pass_ragged(args):
+    """Short run for hardware-counter passes over the variance-weighted
+    K-pool of the ragged batch (32 sequences of 4096-65536 tokens, 7B key
+    shape, blocks of 64): a plain 1 GiB device copy for calibration, then
+    three kka_pool_blocks calls in variance mode."""
+    import numpy as np
+    import torch
+
+    import kv_cache_block_amd as kka
+    import synth
+    from kv_cache_block_amd.pipeline import Selector
+
+    dev = "cuda:0"
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    w = synth.config5(args.seed)
+    k = torch.from_numpy(w.k.reshape(-1).view(np.int16)).to(dev)
+    kp = kka.KPool(k, w.L, w.H, w.D, w.B, w.P)
+    seqs = kka.Seqs(torch.from_numpy(w.seq_len).to(dev), torch.from_numpy(w.block_offsets).to(dev),
+                    torch.from_numpy(w.block_table).to(dev), w.total_blocks)
+    sel = Selector(kp, seqs, w.select, max_pages=int(np.max(np.diff(w.block_offsets))), window=w.window,
+                   mode=kka.WEIGHT_VARIANCE, device=dev)
+    for _ in range(3):
+        sel.pool()
+    torch.cuda.synchronize()
+    if kka.kka_device_error() != 0:
+        raise RuntimeError("device error flag raised on the ragged batch")
+    print(json.dumps({"profile_pass": "ragged", "copy_bytes": (1 << 28) * 4, "kpool_algorithmic_bytes": kpool_bytes(w),
+                      "blocks": int(w.total_blocks), "tokens": int(w.seq_len.sum()),
+                      "kernel_source_sha256_16": kernel_source_hash("kka_pool.hip")}), flush=True)
+
+
+def write_ragged_counter_summary(fetch_csv: str, write_csv: str, stall_csv: str, out_json: str, command: str):
+    """Per-kernel HBM bytes of the variance-weighted K-pool of the ragged batch
+    from --pmc runs of --profile-pass ragged: FETCH_SIZE, WRITE_SIZE (each
+    scaled by what it reads for the 1 GiB copy) and the write-path counters
+    of a third run (raw sums per dispatch)."""
+    import csv
+    import statistics
+
+    def per_kernel(path):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            out.setdefault((r["Kernel_Name"], r["Grid_Size"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+        return out
+
+    f = per_kernel(fetch_csv)
+    w = per_kernel(write_csv)
+    st = per_kernel(stall_csv) if stall_csv != "-" else {}
+    copy_bytes = float(1 << 30)
+    ck = [k for k in f if "copyBuffer" in k[0] and k[2] == "FETCH_SIZE" and max(f[k]) > 4e5]
+    if not ck:
+        raise SystemExit("no 1 GiB copy dispatch found in the counter run")
+    fetch_factor = copy_bytes / (statistics.median(f[ck[0]]) * 1024.0)
+    wk_copy = (ck[0][0], ck[0][1], "WRITE_SIZE")
+    write_factor = copy_bytes / (statistics.median(w[wk_copy]) * 1024.0)
+    kernels = {}
+    total = 0.0
+    for k in f:
+        if "kka::" not in k[0] or k[2] != "FETCH_SIZE":
+            continue
+        fb = statistics.mean(f[k]) * 1024.0 * fetch_factor
+        wb = statistics.mean(w.get((k[0], k[1], "WRITE_SIZE"), [0.0])) * 1024.0 * write_factor
+        entry = {"fetch_bytes": round(fb), "write_bytes": round(wb), "dispatches": len(f[k])}
+        for sk, v in st.items():
+            if sk[0] == k[0] and sk[1] == k[1]:
+                entry[sk[2]] = round(statistics.mean(v))
+        kernels[f"{_short(k[0])} grid={k[1]}"] = entry
+        total += fb + wb
+    summary = {
+        "call": "kka_pool_blocks, variance mode (all kernels of one call)",
+        "workload": "32 sequences, lengths uniform in [4096, 65536], 7B key shape (28 x 4 x 128), blocks of 64, "
+                    "permuted shared pool, head-variance weights",
+        "kernel_source_sha256_16": kernel_source_hash("kka_pool.hip"),
+        "fetch_factor": round(fetch_factor, 5),
+        "write_factor": round(write_factor, 5),
+        "traffic_bytes_per_call": round(total),
+        "per_kernel": kernels,
+        "commands": command,
+    }
+    with open(out_json, "w") as fh:
+        json.dump(summary, fh, indent=1)
+    print(json.dumps({"traffic_bytes_per_call": summary["traffic_bytes_per_call"]}))
+
+
 def _short(name: str) -> str:
     name = name.replace("void ", "").replace("kka::(anonymous namespace)::", "")
     return name.split("(kka::")[0] if "(kka::" in name else name[:60]
@@ -766,19 +900,18 @@ def write_counter_summary(fetch_csv: str, write_csv: str, out_dir: str, command:
         json.dump(summary, fh, indent=1)
     print(json.dumps({"traffic_bytes_per_launch": summary["traffic_bytes_per_launch"],
                       "fetch_factor": summary["fetch_factor"], "write_factor": summary["write_factor"]}))
-    # serving batch: the 64-sequence scoring launch and the selection launch after it
-    sk = [k for k in f if "score_kernel" in k[0]]
-    sl = [k for k in f if "select_kernel" in k[0] and int(k[1]) == 64 * 512]
-    if sk and sl:
+    # serving batch: the one-launch scoring call (grid of 64 selecting groups plus the scoring tiles)
+    sk = [k for k in f if "score_topk_kernel" in k[0] and int(k[1]) > 64 * 256 * 64]
+    if sk:
         parts = {}
-        for k in (sk[0], sl[0]):
+        for k in sk[:1]:
             parts[_short(k[0])] = {"fetch_bytes": round(statistics.mean(f[k]) * 1024.0 * fetch_factor),
                                    "write_bytes": round(statistics.mean(w[k]) * 1024.0 * write_factor),
                                    "dispatches": len(f[k])}
         call = sum(v["fetch_bytes"] + v["write_bytes"] for v in parts.values())
         algo = 288563200
         score = {
-            "call": "kka_score_topk on the serving batch: score_kernel then select_kernel",
+            "call": "kka_score_topk on the serving batch: score_topk_kernel (one launch)",
             "workload": "64 sequences x 8192 fp32 block vectors (D = 128) + 512 chunk + 32 grid rows, top 4/16/64",
             "kernel_source_sha256_16": kernel_source_hash("kka_score.hip"),
             "fetch_factor": round(fetch_factor, 5),
@@ -831,7 +964,11 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-pass", action="store_true", help="short run for rocprofv3 counter passes")
+    ap.add_argument("--profile-pass", nargs="?", const="c3", choices=["c3", "ragged"],
+                    help="short run for rocprofv3 counter passes: the 128K workload and the serving batch (c3), or "
+                         "the variance-weighted K-pool of the ragged batch (ragged)")
+    ap.add_argument("--write-ragged-counter-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "STALL_CSV", "OUT"),
+                    help="summarise --pmc runs of --profile-pass ragged (no GPU needed; STALL_CSV may be -)")
     ap.add_argument("--write-counter-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_DIR"),
                     help="summarise two rocprofv3 --pmc runs of --profile-pass (no GPU needed)")
     ap.add_argument("--write-stats-summary", nargs=3, metavar=("STATS_CSV", "OUT_MD", "TITLE"),
@@ -844,12 +981,17 @@ def main():
     if args.write_stats_summary:
         write_stats_summary(*args.write_stats_summary, command=args.command)
         return
+    if args.write_ragged_counter_summary:
+        write_ragged_counter_summary(*args.write_ragged_counter_summary, command=args.command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the selection path is independent per sequence and per block, "
               "and this library runs it on a single MI355X; shard sequences or blocks across processes for more GPUs. "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-    if args.profile_pass:
+    if args.profile_pass == "ragged":
+        profile_pass_ragged(args)
+    elif args.profile_pass:
         profile_pass(args)
     else:
         run(args)
