@@ -58,7 +58,9 @@ typedef enum kka_status {
   KKA_ERR_SHAPE = 2,     /* a size, count or mode is outside its documented range */
   KKA_ERR_ALIGN = 3,     /* a pointer or stride breaks its alignment rule        */
   KKA_ERR_WORKSPACE = 4, /* workspace NULL or smaller than the *_workspace() size */
-  KKA_ERR_DEVICE = 5     /* the HIP runtime refused a launch                      */
+  KKA_ERR_DEVICE = 5,    /* the HIP runtime refused a launch                      */
+  KKA_ERR_SCRATCH = 6    /* an allocation-free call needs more than its fixed     */
+                         /* scratch array holds (kka_pool_anchor_noalloc)         */
 } kka_status;
 
 /* Bits of the device flag word returned by kka_device_error(). */
@@ -188,6 +190,29 @@ KKA_API kka_status kka_pool_anchor(const kka_kpool* kp, const kka_seqs* seqs, in
                            float* anchor_out, void* workspace, size_t workspace_bytes, void* stream);
 
 KKA_API size_t kka_pool_anchor_workspace(const kka_kpool* kp, const kka_seqs* seqs, int32_t window);
+
+/*
+ * kka_pool_anchor_noalloc -- kka_pool_anchor for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, rules and results as
+ * kka_pool_anchor (bit for bit), without a workspace: the layer-split
+ * partial sums go to a scratch array of 4 MiB that the library holds in
+ * every device's memory from its first use until the process ends, and are
+ * always added by a second kernel (no arrival counters, so nothing in the
+ * array has to be cleared between calls).  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine).
+ * Limit: kka_pool_anchor_noalloc_scratch() bytes (num_seqs * shares *
+ * head_dim * 4, shares <= num_layers; 0 when the sequences are many enough
+ * that each work-group takes all layers) must be at most 4 MiB, else
+ * KKA_ERR_SCRATCH and nothing is enqueued.  Every call on a device shares
+ * that device's array: calls that overlap on one device (two streams, two
+ * host threads) race on it and must be serialised by the caller.
+ */
+KKA_API kka_status kka_pool_anchor_noalloc(const kka_kpool* kp, const kka_seqs* seqs, int32_t window,
+                                           const float* head_weight, float* anchor_out, void* stream);
+
+/* Scratch bytes a kka_pool_anchor_noalloc call with these shapes uses. */
+KKA_API size_t kka_pool_anchor_noalloc_scratch(const kka_kpool* kp, const kka_seqs* seqs);
 
 /*
  * kka_pool_on_write -- keep block vectors current as keys are written (page
@@ -451,8 +476,8 @@ KKA_API const char* kka_status_string(kka_status s);
  * zero at first use.  0.3.0: so do the kka_pool_blocks and kka_pool_anchor
  * workspaces of layer-split launches (per-block / per-sequence arrival
  * counters; the smallest launches combine the split shares in the same
- * launch). */
-#define KKA_VERSION 300
+ * launch).  0.4.0: kka_pool_anchor_noalloc and KKA_ERR_SCRATCH. */
+#define KKA_VERSION 400
 
 /* Version of the loaded library, same encoding (equals KKA_VERSION when the
  * header and the library match). */

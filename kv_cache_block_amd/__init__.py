@@ -37,13 +37,13 @@ DEVERR_OFFSETS = 16
 DEVERR_WORKSPACE = 32
 
 _STATUS = {0: "ok", 1: "KKA_ERR_NULL", 2: "KKA_ERR_SHAPE", 3: "KKA_ERR_ALIGN", 4: "KKA_ERR_WORKSPACE",
-           5: "KKA_ERR_DEVICE"}
+           5: "KKA_ERR_DEVICE", 6: "KKA_ERR_SCRATCH"}
 
 ENTRY_POINTS = (
     "kka_pool_blocks", "kka_pool_blocks_workspace", "kka_pool_anchor", "kka_pool_anchor_workspace", "kka_pool_on_write",
     "kka_level_rows", "kka_build_levels", "kka_score_topk", "kka_score_topk_workspace", "kka_score_topk_lazy",
     "kka_score_topk_stable", "kka_attention_topk", "kka_attention_topk_workspace", "kka_device_error",
-    "kka_status_string", "kka_version",
+    "kka_status_string", "kka_version", "kka_pool_anchor_noalloc", "kka_pool_anchor_noalloc_scratch",
 )
 
 
@@ -103,6 +103,8 @@ def lib() -> ctypes.CDLL:
         L.kka_pool_blocks_workspace.argtypes = [P(c_kpool), P(c_seqs), vp, i32, i32]
         L.kka_pool_anchor.argtypes = [P(c_kpool), P(c_seqs), i32, vp, vp, vp, sz, vp]
         L.kka_pool_anchor_workspace.argtypes = [P(c_kpool), P(c_seqs), i32]
+        L.kka_pool_anchor_noalloc.argtypes = [P(c_kpool), P(c_seqs), i32, vp, vp, vp]
+        L.kka_pool_anchor_noalloc_scratch.argtypes = [P(c_kpool), P(c_seqs)]
         L.kka_pool_on_write.argtypes = [P(c_kpool), P(c_seqs), vp, i32, vp, vp, i32, vp, i64, vp]
         L.kka_attention_topk.argtypes = [P(c_kpool), P(c_seqs), vp, i32, ctypes.c_float, i32, vp, i64, vp, vp, vp,
                                          vp, sz, vp]
@@ -117,10 +119,10 @@ def lib() -> ctypes.CDLL:
         L.kka_device_error.argtypes = [vp]
         L.kka_status_string.argtypes = [ctypes.c_int]
         for f in ("kka_pool_blocks", "kka_pool_anchor", "kka_build_levels", "kka_score_topk", "kka_score_topk_lazy",
-                  "kka_score_topk_stable", "kka_pool_on_write", "kka_attention_topk"):
+                  "kka_score_topk_stable", "kka_pool_on_write", "kka_attention_topk", "kka_pool_anchor_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         for f in ("kka_pool_blocks_workspace", "kka_pool_anchor_workspace", "kka_score_topk_workspace",
-                  "kka_attention_topk_workspace"):
+                  "kka_attention_topk_workspace", "kka_pool_anchor_noalloc_scratch"):
             getattr(L, f).restype = sz
         L.kka_level_rows.restype = i64
         L.kka_device_error.restype = i32
@@ -328,6 +330,22 @@ def kka_pool_anchor(kp: KPool, seqs: Seqs, window: int, anchor_out: torch.Tensor
     _check(lib().kka_pool_anchor(ctypes.byref(kp.c), ctypes.byref(seqs.c), int(window), hw, ap, wp, wbytes,
                                  _stream(stream)), "kka_pool_anchor")
     return keep
+
+
+def kka_pool_anchor_noalloc_scratch(kp: KPool, seqs: Seqs) -> int:
+    return int(lib().kka_pool_anchor_noalloc_scratch(ctypes.byref(kp.c), ctypes.byref(seqs.c)))
+
+
+def kka_pool_anchor_noalloc(kp: KPool, seqs: Seqs, window: int, anchor_out: torch.Tensor,
+                            head_weight: Optional[torch.Tensor] = None, stream=None):
+    """kka_pool_anchor without a workspace and without any device allocation
+    (the library's fixed per-device scratch array holds the partial sums)."""
+    S, D = seqs.num_seqs, kp.head_dim
+    ap = _dev(anchor_out, "anchor_out", torch.float32, min_numel=S * D)
+    hw = _dev(head_weight, "head_weight", torch.float32, min_numel=S * kp.num_layers * kp.num_kv_heads,
+              allow_none=True)
+    _check(lib().kka_pool_anchor_noalloc(ctypes.byref(kp.c), ctypes.byref(seqs.c), int(window), hw, ap,
+                                         _stream(stream)), "kka_pool_anchor_noalloc")
 
 
 def kka_pool_on_write(kp: KPool, seqs: Seqs, vb_out: torch.Tensor, running: torch.Tensor, *,

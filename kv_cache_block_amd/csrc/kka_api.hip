@@ -476,6 +476,78 @@ kka_status kka_pool_anchor(const kka_kpool* kp, const kka_seqs* seqs, int32_t wi
   return launched(launch_anchor(a, static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Fixed device scratch of kka_pool_anchor_noalloc: the layer-split partial
+// sums of one call, one copy per device for the life of the process.  Host
+// code reaches it only through the device address hipGetSymbolAddress
+// returns for the current device (the array's name is a host-side stand-in).
+constexpr size_t kAnchorScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kAnchorScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current); nullptr if the lookup failed.
+void* anchor_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kka_pool_anchor_noalloc_scratch(const kka_kpool* kp, const kka_seqs* seqs) {
+  if (check_kpool(kp) != KKA_OK || check_seqs(seqs) != KKA_OK) return 0;
+  const LayerSplit ls = layer_split(seqs->num_seqs, kp->num_layers);
+  if (ls.n_split <= 1) return 0;
+  return (size_t)seqs->num_seqs * ls.n_split * kp->head_dim * sizeof(float);
+}
+
+kka_status kka_pool_anchor_noalloc(const kka_kpool* kp, const kka_seqs* seqs, int32_t window,
+                                   const float* head_weight, float* anchor_out, void* stream) {
+  kka_status st = check_kpool(kp);
+  if (st != KKA_OK) return st;
+  if ((st = check_seqs(seqs)) != KKA_OK) return st;
+  if (window < 0) return KKA_ERR_SHAPE;
+  if (seqs->num_seqs > 0 && !anchor_out) return KKA_ERR_NULL;
+  if (anchor_out && !aligned16(anchor_out)) return KKA_ERR_ALIGN;
+  const size_t need = kka_pool_anchor_noalloc_scratch(kp, seqs);
+  if (need > kAnchorScratchBytes) return KKA_ERR_SCRATCH;
+  if (seqs->num_seqs == 0) return KKA_OK;
+  uint32_t* err = device_error_word();
+  if (!err) return KKA_ERR_DEVICE;
+  void* scr = need > 0 ? anchor_scratch() : nullptr;
+  if (need > 0 && !scr) return KKA_ERR_DEVICE;
+  (void)hipGetLastError();
+  PoolArgs a = {};
+  fill_pool_args(a, kp, seqs);
+  const LayerSplit ls = layer_split(seqs->num_seqs, a.L);
+  a.n_split = ls.n_split;
+  a.lps = ls.lps;
+  a.n_items = seqs->num_seqs;
+  a.weights = head_weight;
+  a.out = anchor_out;
+  // shares always added by the second kernel: no arrival counters, so no
+  // part of the scratch has to hold a known value between calls
+  a.done = nullptr;
+  a.partial = ls.n_split > 1 ? static_cast<float*>(scr) : nullptr;
+  a.window = window;
+  a.err = err;
+  return launched(launch_anchor(a, static_cast<hipStream_t>(stream)));
+}
+
 int64_t kka_level_rows(const kka_level_layout* lay) {
   LevelGeom g;
   if (!level_geom(lay, g)) return -1;
@@ -656,6 +728,7 @@ const char* kka_status_string(kka_status s) {
     case KKA_ERR_ALIGN: return "a pointer or stride breaks its alignment rule";
     case KKA_ERR_WORKSPACE: return "workspace missing or too small";
     case KKA_ERR_DEVICE: return "HIP runtime error";
+    case KKA_ERR_SCRATCH: return "the call needs more than the library's fixed scratch array holds";
   }
   return "unknown status";
 }

@@ -54,9 +54,10 @@ def test_header_declares_all_entry_points():
 def test_library_exports_every_declared_symbol(L):
     for name in declared():
         assert hasattr(L, name), name
-    assert L.kka_version() == int(re.search(r"#define KKA_VERSION (\d+)", open(HEADER).read()).group(1)) == 300
+    assert L.kka_version() == int(re.search(r"#define KKA_VERSION (\d+)", open(HEADER).read()).group(1)) == 400
     assert L.kka_status_string(0) == b"ok"
     assert L.kka_status_string(4).startswith(b"workspace")
+    assert b"scratch" in L.kka_status_string(6)
 
 
 def kpool(**kw):
@@ -273,6 +274,27 @@ def test_anchor_validation(L):
     assert f(kp, sq, out=FAKE_ODD) == 3
     assert f(kp, sq, ws=None) == 4
     assert f(kpool(head_dim=7), sq) == 2
+
+
+def test_anchor_noalloc_validation_and_scratch_limit(L):
+    """The allocation-free anchor validates like kka_pool_anchor and refuses,
+    before anything is enqueued, a call whose partial sums exceed its fixed
+    4 MiB scratch (KKA_ERR_SCRATCH)."""
+    kp, sq = kpool(), seqs()
+    f = lambda kp_, sq_, W=16, out=FAKE: L.kka_pool_anchor_noalloc(ctypes.byref(kp_), ctypes.byref(sq_), W, None,
+                                                                   out, None)
+    assert f(kp, sq, W=-1) == 2
+    assert f(kp, sq, out=None) == 1
+    assert f(kp, sq, out=FAKE_ODD) == 3
+    assert f(kpool(head_dim=7), sq) == 2
+    scratch = lambda kp_, sq_: L.kka_pool_anchor_noalloc_scratch(ctypes.byref(kp_), ctypes.byref(sq_))
+    assert scratch(kp, sq) == 2 * 28 * 128 * 4          # 2 sequences, one share per layer
+    assert scratch(kp, seqs(num_seqs=4096, total_blocks=4096)) == 0  # one work-group per sequence
+    wide = kpool(num_kv_heads=1, head_dim=1024)
+    many = seqs(num_seqs=300, total_blocks=300)
+    assert scratch(wide, many) == 300 * 7 * 1024 * 4 > 4 << 20
+    assert f(wide, many) == 6
+    assert f(kp, seqs(num_seqs=0, total_blocks=0), out=None) == 0
 
 
 def test_binding_refuses_cpu_tensors():
