@@ -698,6 +698,100 @@ def cpu_baseline_all_cores(w, step_bytes, seconds):
             "ms_per_step": round(el * 1e3 / reps, 1)}
 
 
+def oracle_table(args):
+    """The oracle as it stands, timed on the host over each workload (bounded
+    samples), on one core and split over every usable core (threads calling
+    the unchanged single-threaded C oracle on disjoint items): the CPU
+    columns of the results table.  GB/s on the algorithmic bytes of what was
+    timed."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    import synth
+
+    n = max(1, host_info()["usable_cores"])
+
+    def timed(fn, items, threads, budget_s=2.0):
+        """Mean seconds of one pass of fn over items, passes repeated until
+        budget_s has gone by (one pass at least), one untimed pass first when
+        a pass is short."""
+        items = list(items)
+        slices = [items[i::threads] for i in range(threads)]
+
+        def run(part):
+            for x in part:
+                fn(x)
+
+        def one_pass(ex):
+            if ex is None:
+                run(items)
+            else:
+                list(ex.map(run, slices))
+        ex = ThreadPoolExecutor(max_workers=threads) if threads > 1 else None
+        try:
+            t0 = time.perf_counter()
+            one_pass(ex)
+            first = time.perf_counter() - t0
+            if first >= budget_s:
+                return first
+            reps, t0 = 0, time.perf_counter()
+            while reps == 0 or time.perf_counter() - t0 < budget_s:
+                one_pass(ex)
+                reps += 1
+            return (time.perf_counter() - t0) / reps
+        finally:
+            if ex is not None:
+                ex.shutdown()
+
+    out = {"host": host_info()}
+    for name, w in (("0.5B_4K_b16", synth.config1(args.seed)), ("7B_32K_b128", synth.config2(args.seed)),
+                    ("7B_128K_b16", synth.config3(args.seed))):
+        kp = oracle.KPool.of(w)
+        blocks = list(range(w.total_blocks))
+
+        def pool(b):
+            oracle.pool_block(kp, int(w.block_table[b]), oracle.n_valid(w.seq_len, kp.B, b, 0))
+        b_all = kpool_bytes(w)
+        t1 = timed(pool, blocks, 1)
+        tn = timed(pool, blocks, n)
+        out[name] = {"stage": "K-pool (every block)", "bytes": b_all, "oracle_1core_ms": round(t1 * 1e3, 1),
+                     "oracle_1core_GBps": round(b_all / t1 / 1e9, 3), "oracle_allcore_ms": round(tn * 1e3, 1),
+                     "oracle_allcore_GBps": round(b_all / tn / 1e9, 3)}
+    v = synth.config4(args.seed)
+    S, NP, D = v.vb.shape
+
+    def step(s):
+        oracle.score_select(v.vb[s], v.anchors[s], v.select)
+    b4 = score_bytes(S, NP + 512 + 32, D, v.select["k_page"])
+    t1 = timed(step, range(8), 1) * S / 8
+    tn = timed(step, range(S), n)
+    out["serving_64x8192"] = {"stage": "levels + affinity + top-K, 64 sequences (one core: 8 of them, scaled)",
+                              "bytes": b4, "oracle_1core_ms": round(t1 * 1e3, 1),
+                              "oracle_1core_GBps": round(b4 / t1 / 1e9, 3), "oracle_allcore_ms": round(tn * 1e3, 1),
+                              "oracle_allcore_GBps": round(b4 / tn / 1e9, 3)}
+    w = synth.config5(args.seed)
+    kp = oracle.KPool.of(w)
+
+    def seq_pool(s):
+        tab = oracle.seq_table(w.block_offsets, w.block_table, s)
+        wts = oracle.head_weights(kp, tab, int(w.seq_len[s]))
+        for i in range(len(tab)):
+            oracle.pool_block(kp, int(tab[i]), oracle.n_valid(w.seq_len, kp.B, i, s), wts)
+    order = np.argsort(w.seq_len)
+    sample = [int(order[k]) for k in (0, 8, 16, 24)]
+    tok_sample = sum(int(w.seq_len[s]) for s in sample)
+    t1 = timed(seq_pool, sample, 1) * int(w.seq_len.sum()) / tok_sample
+    tn = timed(seq_pool, [int(x) for x in order[::-1]], n)
+    b5 = kpool_bytes(w)
+    out["ragged32_b64_variance"] = {"stage": "weights + weighted K-pool (one core: 4 sequences, scaled by tokens)",
+                                    "bytes": b5, "oracle_1core_ms": round(t1 * 1e3, 1),
+                                    "oracle_1core_GBps": round(b5 / t1 / 1e9, 3),
+                                    "oracle_allcore_ms": round(tn * 1e3, 1),
+                                    "oracle_allcore_GBps": round(b5 / tn / 1e9, 3), "threads": n}
+    print(json.dumps(out), flush=True)
+
+
 def profile_pass(args):
     """Short run for hardware-counter passes: a plain 1 GiB device copy
     (calibrates FETCH_SIZE / WRITE_SIZE against known bytes), then a few
@@ -964,6 +1058,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--oracle-table", action="store_true",
+                    help="time the oracle on every workload, one core and all cores (no GPU needed)")
     ap.add_argument("--profile-pass", nargs="?", const="c3", choices=["c3", "ragged"],
                     help="short run for rocprofv3 counter passes: the 128K workload and the serving batch (c3), or "
                          "the variance-weighted K-pool of the ragged batch (ragged)")
@@ -983,6 +1079,9 @@ def main():
         return
     if args.write_ragged_counter_summary:
         write_ragged_counter_summary(*args.write_ragged_counter_summary, command=args.command)
+        return
+    if args.oracle_table:
+        oracle_table(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the selection path is independent per sequence and per block, "

@@ -35,6 +35,12 @@
  *  - Results are deterministic: no floating-point atomics; the same inputs
  *    give the same bits, wherever blocks sit in the physical pool.
  *  - bf16 keys are widened exactly and accumulated in fp32.
+ *  - A few small launches (a layer-split pooling or anchor launch of at most
+ *    one work-group per compute unit; a scoring batch whose tiles all fit on
+ *    the chip) hand values from one work-group to another inside the launch
+ *    through device-scope stores, an arrival counter and device-scope
+ *    loads.  KKA_NO_HANDOFF=1 in the environment makes every call use a
+ *    second launch instead; the results are the same bits.
  */
 #ifndef KKA_H_
 #define KKA_H_

@@ -10,6 +10,11 @@
 
 namespace kka {
 
+bool handoff_disabled() {
+  const char* v = std::getenv("KKA_NO_HANDOFF");
+  return v && v[0] == '1';
+}
+
 // Per-device flag word for errors that only device-resident data reveals.
 __device__ uint32_t g_device_error;
 
@@ -631,7 +636,7 @@ kka_status prepare_score(const kka_level_layout* lay, const float* level_buf, co
   // workspace: per-sequence tile counters, then scratch affinities
   const bool forced = two_launch_forced();
   a.small = !forced && small_levels(lay, g, sel) ? 1 : 0;
-  a.done = forced ? nullptr : static_cast<uint32_t*>(workspace);
+  a.done = forced || handoff_disabled() ? nullptr : static_cast<uint32_t*>(workspace);
   a.aff = affinity_out ? affinity_out
                        : reinterpret_cast<float*>(static_cast<char*>(workspace) + score_counter_bytes(lay->num_seqs));
   a.k_g = lay->hierarchical ? sel->k_grid : 0;

@@ -85,8 +85,13 @@ constexpr double kSplitOneLaunchBytes = 32.0 * 1024 * 1024;
 
 int32_t device_cus();  // compute units of the current device (cached; defined with the scoring launchers)
 
+// KKA_NO_HANDOFF=1 in the environment: no launch hands values from one
+// work-group to another (layer-split shares are added by a second kernel,
+// small scoring batches select in a second launch); results are the same.
+bool handoff_disabled();  // defined with the C-ABI layer
+
 inline bool split_in_one_launch(int64_t items, int32_t n_split, double key_bytes) {
-  return n_split > 1 && items * n_split <= device_cus() && key_bytes <= kSplitOneLaunchBytes;
+  return n_split > 1 && items * n_split <= device_cus() && key_bytes <= kSplitOneLaunchBytes && !handoff_disabled();
 }
 
 // Pooling splits a block's layers into shares of at least this many key

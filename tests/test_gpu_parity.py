@@ -917,6 +917,29 @@ def test_layer_split_shares_and_counters(one_launch):
         np.testing.assert_allclose(got[b], v, atol=ATOL, rtol=0, err_msg=f"after re-zero block {b}")
 
 
+def test_no_handoff_switch_gives_the_same_bits(monkeypatch):
+    """Launches that hand values between work-groups (a small layer-split
+    pool and anchor, a scoring batch that fits on the chip) against the same
+    calls with KKA_NO_HANDOFF=1, which adds the shares and selects in a
+    second launch: the same bits for every block vector, anchor, affinity
+    and selection."""
+    say("no-handoff switch")
+    case = dict(hierarchical=1, k_grid=2, k_chunk=3, k_page=5, pages_per_chunk=4, chunks_per_grid=3)
+    w = ragged_workload(17, 2, 12, 4, 128, 16, 80, 120, window=24, select=case)
+    outs = []
+    for flag in ("0", "1"):
+        monkeypatch.setenv("KKA_NO_HANDOFF", flag)
+        sel, npg = run_selector(w)
+        assert kka.kka_device_error() == 0
+        outs.append([t.cpu().numpy() for t in (sel.level, sel.anchors, sel.affinity, sel.page_idx, sel.page_score,
+                                                sel.n_selected)])
+        if flag == "1":
+            for s in range(w.S):
+                check_selection(sel, s, int(npg[s]), "no handoff")
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
 @pytest.mark.parametrize("seed", range(40))
 def test_selection_random_configurations(seed):
     """Seeded sweep over selection configurations: flat or hierarchical,
