@@ -183,6 +183,10 @@ def run(args):
     if not torch.equal(sel.page_idx, full_idx):
         raise RuntimeError("lazy scoring selected different pages than the full pass")
     c3_lazy_rows = lazy_rows(n_g, w.select)
+    # the launch floor of this stream: a one-element torch add, event-timed
+    # like the calls above (what any launch costs before it does any work)
+    tiny = torch.zeros(1, dtype=torch.float32, device=dev)
+    floor_us = time_calls(lambda i: tiny.add_(1.0), args.steps, max(3, args.warmup), stream)
 
     # c3 attention reference (QK^T softmax averaged over layers and query
     # heads, per block) for one planted decode query with 28 query heads, and
@@ -378,6 +382,8 @@ def run(args):
                             "top 4/16/64, three rotating buffer sets (cold last-level cache)",
         "serving_algorithmic_bytes": b4,
         "lazy_score_topk_us_per_step": round(c3_lazy_us, 2),
+        "launch_floor_us": round(floor_us, 2),
+        "launch_floor": "one-element torch add_ on the same stream, event-timed like the score calls",
         "lazy_rows_scored_per_seq": c3_lazy_rows,
         "serving_lazy_score_topk_us_per_step": round(c4_lazy_us, 2),
         "serving_lazy_rows_scored_per_seq": c4_lazy_rows,

@@ -850,22 +850,205 @@ __device__ __forceinline__ int32_t select_levels(const ScoreArgs& a, const SeqGe
   return kp;
 }
 
+// ------------------------------------------- lean selection of small levels
+//
+// Hierarchical levels small enough to rank without the general machinery:
+// at most 64 grids, at most 64 chunk candidates (children of the kept
+// grids) and at most 256 page candidates, at most 64 kept per level (the
+// serving and 128K shapes: 32 grids, 4 x 16 chunks, 16 x 16 pages, top
+// 4 / 16 / 64).  Wavefront 0 stages the chunk and grid rows and ranks
+// grids and chunks alone, with no work-group barrier, while the page rows
+// are still arriving; four wavefronts then rank the page candidates, each
+// its 64 among themselves (a sorted run), then against the other three
+// runs.  A level with fewer positive-score candidates than it keeps needs
+// the zero fill, and the general path selects instead, from the same
+// staged rows.
+
+// Lanes of one wavefront read each other's LDS stores.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Keys among the wavefront's first m (lane l's key stored at copy[l]; m
+// wave-uniform, a multiple of 16 at most 64) larger than this lane's x.
+__device__ __forceinline__ int32_t rank_in_wave(uint64_t x, uint64_t* copy, int32_t m) {
+  wave_sync();  // earlier reads of the copy are done
+  copy[threadIdx.x & 63] = x;
+  wave_sync();
+  const u64x2* p = reinterpret_cast<const u64x2*>(copy);
+  int32_t r = 0;
+  // batches of eight 16-byte reads: the scheduler would otherwise hoist all
+  // 32 (128 registers) ahead of the compares
+  for (int u = 0; u < m / 2; u += 8) {
+    u64x2 y[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) y[v] = p[u + v];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) r += (int32_t)(y[v].x > x) + (int32_t)(y[v].y > x);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return r;
+}
+
+// Top k of up to 64 candidates on one wavefront: lane l < m holds
+// candidate l (element e, or -1, and its score bits); the kept elements go
+// to list[rank].  Candidates without a positive score take keys below every
+// positive one (the lane number).  False when fewer than k score above 0.
+__device__ __forceinline__ bool rank_level64(int32_t e, uint32_t bits, int32_t k, int32_t m, uint64_t* copy,
+                                             int32_t* list) {
+  const int lane = threadIdx.x & 63;
+  const bool pos = e >= 0 && bits != 0u;
+  const uint64_t x = pos ? composite(bits, e) : (uint64_t)lane;
+  // lanes from m on hold no candidate: their keys (below every positive
+  // one) need not be compared
+  const int32_t r = rank_in_wave(x, copy, min((m + 15) & ~15, 64));
+  if ((int32_t)__popcll(__ballot(pos)) < k) return false;
+  if (pos && r < k) list[r] = e;
+  wave_sync();
+  return true;
+}
+
+// Top k (<= 64) of up to 256 candidates: thread t < 256 holds candidate t;
+// every thread of the work-group calls it.  Each of wavefronts 0-3 ranks
+// its 64 keys, writes them as a strictly descending run (with every eighth
+// key), and a key's rank is its place in its run plus the keys above it in
+// the other three runs.  Kept keys go to sm.buf[rank].  False (in every
+// thread) when fewer than k score above 0.
+__device__ __forceinline__ bool rank_level256(int32_t e, uint32_t bits, int32_t k, SelectShared& sm) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool pos = e >= 0 && bits != 0u;
+  const uint64_t x = pos ? composite(bits, e) : (uint64_t)tid;
+  int32_t r = 0;
+  if (wave < 4) {
+    r = rank_in_wave(x, sm.ck + 64 * wave, 64);
+    const uint64_t bal = __ballot(pos);
+    if (lane == 0) sm.wave_tot[wave] = (int32_t)__popcll(bal);
+    sm.runs.key[64 * wave + r] = x;
+    if ((r & 7) == 7) sm.runs.piv[8 * wave + (r >> 3)] = x;
+  }
+  __syncthreads();
+  const int32_t P = sm.wave_tot[0] + sm.wave_tot[1] + sm.wave_tot[2] + sm.wave_tot[3];
+  if (P < k) return false;
+  if (wave < 4) {
+    int32_t R = r;
+#pragma unroll
+    for (int v = 1; v < 4; ++v) R += run_count_above(sm.runs, (wave + v) & 3, x);
+    if (pos && R < k) sm.buf[R] = x;
+  }
+  __syncthreads();
+  return true;
+}
+
+// Stages the sequence's affinity rows into LDS and selects its levels on
+// the lean path; returns the kept page count, or -1 when a level needs the
+// zero fill (every row is staged either way).
+__device__ __forceinline__ int32_t select_lean_levels(const ScoreArgs& a, const SeqGeom& g, const float* aff,
+                                                      SelectShared& sm) {
+  constexpr int NP = kSelThreads - 64;          // threads staging the page rows
+  constexpr int UP = (kLdsRows + NP - 1) / NP;  // page rows per thread, at most
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t n_lo = a.max_pages;                             // page rows
+  const int32_t n_hi = (int32_t)a.rows_per_seq - a.max_pages;  // chunk and grid rows
+  const int32_t kg = min(a.k_g, g.n_g), kc = min(a.k_c, g.n_c), kp = min(a.k_p, g.n_p);
+  if (wave == 0) {
+    // wavefront 0 stages the chunk and grid rows and ranks grids and chunks
+    // while the other wavefronts stage the page rows
+    float hi[kLeanHiRows / 64];
+#pragma unroll
+    for (int u = 0; u < kLeanHiRows / 64; ++u)
+      if (u * 64 < n_hi) hi[u] = load_agent(aff + n_lo + min(u * 64 + lane, n_hi - 1));
+#pragma unroll
+    for (int u = 0; u < kLeanHiRows / 64; ++u)
+      if (u * 64 < n_hi) sm.aff[n_lo + min(u * 64 + lane, n_hi - 1)] = hi[u];
+    wave_sync();
+    const int32_t off_g = a.max_pages + a.c_cap;
+    const int32_t eg = lane < g.n_g ? lane : -1;
+    bool good = rank_level64(eg, eg >= 0 ? __float_as_uint(sm.aff[off_g + eg]) : 0u, kg, g.n_g, sm.ck, sm.plist);
+    if (good) {
+      const int32_t pr = lane / a.cpg;
+      int32_t ec = -1;
+      if (pr < kg) {
+        const int32_t c = sm.plist[pr] * a.cpg + (lane - pr * a.cpg);
+        ec = c < g.n_c ? c : -1;
+      }
+      good = rank_level64(ec, ec >= 0 ? __float_as_uint(sm.aff[a.max_pages + ec]) : 0u, kc, kg * a.cpg, sm.ck,
+                          sm.plist + 64);
+    }
+    if (lane == 0) sm.cnt[0] = good ? 1 : 0;
+  } else {
+    const int t = tid - 64;
+    float lo[UP];
+#pragma unroll
+    for (int u = 0; u < UP; ++u)
+      if (u * NP < n_lo) lo[u] = load_agent(aff + min(u * NP + t, n_lo - 1));
+#pragma unroll
+    for (int u = 0; u < UP; ++u)
+      if (u * NP < n_lo) sm.aff[min(u * NP + t, n_lo - 1)] = lo[u];
+  }
+  __syncthreads();
+  if (sm.cnt[0] == 0) return -1;
+  int32_t ep = -1;
+  if (tid < 256) {
+    const int32_t pr = tid / a.ppc;
+    if (pr < kc) {
+      const int32_t p = sm.plist[64 + pr] * a.ppc + (tid - pr * a.ppc);
+      ep = p < g.n_p ? p : -1;
+    }
+  }
+  if (!rank_level256(ep, ep >= 0 ? __float_as_uint(sm.aff[ep]) : 0u, kp, sm)) return -1;
+  return kp;
+}
+
+// The general path restricted to the levels of a lean layout (at most 256
+// candidates a level): for the rare lean sequence that needs the zero fill.
+__device__ __forceinline__ int32_t select_level_lean(const Level& L, int32_t k, SelectShared& sm, uint32_t* kept) {
+  const int32_t k_eff = k < L.n ? k : L.n;
+  if (k_eff <= 0) return 0;
+  const int32_t m = L.fanout ? L.n_par * L.fanout : L.n;
+  if (m <= 64) return select_one_group<true>(L, m, k_eff, sm, kept);
+  if (m <= 128) return select_small<true, 2>(L, m, k_eff, sm, kept);
+  if (m <= 192) return select_small<true, 3>(L, m, k_eff, sm, kept);
+  return select_small<true, 4>(L, m, k_eff, sm, kept);
+}
+
 // Selection of sequence s from its affinity rows in a.aff, by the whole
-// work-group.
+// work-group.  LEAN: the layout passes lean_levels_fit.
+template <bool LEAN>
 __device__ __forceinline__ void select_sequence(const ScoreArgs& a, int32_t s, SelectShared& sm) {
   const float* aff = a.aff + (int64_t)s * a.rows_per_seq;
   const SeqGeom g = seq_geom(a, s, false);  // issued before the staging loads
-  const bool staged = a.rows_per_seq <= kLdsRows;
-  if (staged) stage_rows(sm.aff, aff, (int32_t)a.rows_per_seq);
-  clear_select_state(a, g, sm);
-  __syncthreads();
-  const int32_t kp = staged ? select_levels<true>(a, g, aff, sm) : select_levels<false>(a, g, aff, sm);
-  write_selection(a, sm, s, kp);
+  if constexpr (LEAN) {
+    int32_t kp = select_lean_levels(a, g, aff, sm);  // stages every row
+    if (kp < 0) {
+      // a level needs the zero fill: the general path on the staged rows
+      clear_select_state(a, g, sm);
+      __syncthreads();
+      kp = 0;
+      for (int32_t lev = 0; lev < 3; ++lev) {
+        const Level L = make_level(a, g, lev, aff, kp, sm);
+        kp = select_level_lean(L, lev == 0 ? a.k_g : (lev == 1 ? a.k_c : a.k_p), sm,
+                               lev == 0 ? sm.kept_grid : (lev == 1 ? sm.kept_chunk : nullptr));
+      }
+    }
+    write_selection(a, sm, s, kp);
+  } else {
+    const bool staged = a.rows_per_seq <= kLdsRows;
+    if (staged) stage_rows(sm.aff, aff, (int32_t)a.rows_per_seq);
+    clear_select_state(a, g, sm);
+    __syncthreads();
+    const int32_t kp = staged ? select_levels<true>(a, g, aff, sm) : select_levels<false>(a, g, aff, sm);
+    write_selection(a, sm, s, kp);
+  }
 }
 
+template <bool LEAN>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(ScoreArgs a) {
   __shared__ SelectShared sm;
-  select_sequence(a, blockIdx.x, sm);
+  select_sequence<LEAN>(a, blockIdx.x, sm);
 }
 
 // (1 + cos) / 2 clamped to [0, 1]; NaN and -0 become +0.
@@ -1033,8 +1216,8 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 // per-sequence counter, incremented once each tile's device-scope
 // affinity stores have completed) selects that sequence.  Other sequences'
 // tiles keep streaming meanwhile, and the selection needs no second launch.
-template <int LPR, int NQ, int R, bool STAB>
-__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(NQ * R <= 8 ? 4 : 1)))
+template <int LPR, int NQ, int R, bool STAB, bool LEAN>
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(NQ * R <= 8 && !LEAN ? 4 : 1)))
 void score_select_kernel(ScoreArgs a) {
   __shared__ SelectShared sm;
   constexpr int NG = kSelThreads / LPR;  // row groups per work-group
@@ -1097,7 +1280,7 @@ void score_select_kernel(ScoreArgs a) {
   // Every tile of the launch counts, scored or empty: the work-group that
   // completes the sequence's last tile selects it.
   if (!arrive(a.done + s, (uint32_t)a.tiles_per_seq, a.err, sm.last)) return;
-  select_sequence(a, s, sm);
+  select_sequence<LEAN>(a, s, sm);
 }
 
 // Affinity v of element e of a level (lazy scoring) to LDS (STG) or to
@@ -1171,7 +1354,95 @@ __device__ __forceinline__ int32_t lazy_levels(const ScoreArgs& a, const SeqGeom
   return kp;
 }
 
+// Lazy scoring of a lean layout (lean_levels_fit; the grid level's rows all
+// in the first pass, NG * R >= 64): every level's candidates are scored in
+// one pass of the row groups into the LDS row copy (and `out`), wavefront 0
+// ranks grids and chunks and four wavefronts the pages (as in
+// select_lean_levels).  Returns the kept page count, or -1 when a level
+// needs the zero fill.
 template <int LPR, int NQ, int R>
+__device__ __forceinline__ int32_t lazy_lean_levels(const ScoreArgs& a, const SeqGeom& g, const f32x4* seq, float* out,
+                                                    const AnchorRegs<LPR, NQ>& A, SelectShared& sm,
+                                                    const float (&v0)[R]) {
+  constexpr int NG = kSelThreads / LPR;
+  static_assert(NG * R >= 256, "one pass of the row groups covers a lean level");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t grp = tid / LPR, lg = tid % LPR;
+  const int32_t Q = a.D >> 2;
+  const int32_t kg = min(a.k_g, g.n_g), kc = min(a.k_c, g.n_c), kp = min(a.k_p, g.n_p);
+  const int32_t off_g = a.max_pages + a.c_cap;
+  // grids: scored with the anchor's arrival (v0)
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int32_t c = grp + NG * r;
+    if (lg == 0 && c < g.n_g) {
+      sm.aff[off_g + c] = v0[r];
+      if (out) out[off_g + c] = v0[r];
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int32_t eg = lane < g.n_g ? lane : -1;
+    const bool good = rank_level64(eg, eg >= 0 ? __float_as_uint(sm.aff[off_g + eg]) : 0u, kg, g.n_g, sm.ck, sm.plist);
+    if (lane == 0) sm.cnt[0] = good ? 1 : 0;
+  }
+  __syncthreads();
+  if (sm.cnt[0] == 0) return -1;
+  // chunks of the kept grids, then pages of the kept chunks
+  for (int32_t lev = 1; lev < 3; ++lev) {
+    const int32_t fan = lev == 1 ? a.cpg : a.ppc;
+    const int32_t n_lev = lev == 1 ? g.n_c : g.n_p;
+    const int32_t n_par = lev == 1 ? kg : kc;
+    const int32_t* par = sm.plist + (lev == 1 ? 0 : 64);
+    const int32_t off = lev == 1 ? a.max_pages : 0;
+    const int32_t m = n_par * fan;
+    f32x4 x[R][NQ];
+    int32_t e[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int32_t c = grp + NG * r;
+      int32_t el = -1;
+      if (c < m) {
+        const int32_t pr = c / fan;
+        el = par[pr] * fan + (c - pr * fan);
+        if (el >= n_lev) el = -1;
+      }
+      e[r] = el;
+      // lanes past the candidates load row `off` (unconditional loads issue back to back)
+      load_row<LPR, NQ>(seq + (int64_t)(off + (el >= 0 ? el : 0)) * Q, lg, Q, x[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float v = row_affinity<LPR, NQ>(x[r], A);
+      if (lg == 0 && e[r] >= 0) {
+        sm.aff[off + e[r]] = v;
+        if (out) out[off + e[r]] = v;
+      }
+    }
+    __syncthreads();
+    int32_t ec = -1;
+    if (tid < m && (lev == 2 || wave == 0)) {
+      const int32_t pr = tid / fan;
+      ec = par[pr] * fan + (tid - pr * fan);
+      if (ec >= n_lev) ec = -1;
+    }
+    const uint32_t bits = ec >= 0 ? __float_as_uint(sm.aff[off + ec]) : 0u;
+    if (lev == 1) {
+      if (wave == 0) {
+        const bool good = rank_level64(ec, bits, kc, m, sm.ck, sm.plist + 64);
+        if (lane == 0) sm.cnt[0] = good ? 1 : 0;
+      }
+      __syncthreads();
+      if (sm.cnt[0] == 0) return -1;
+    } else if (!rank_level256(ec, bits, kp, sm)) {
+      return -1;
+    }
+  }
+  return kp;
+}
+
+template <int LPR, int NQ, int R, bool LEAN>
 __global__ __launch_bounds__(kSelThreads) void lazy_kernel(ScoreArgs a, float* lazy_out) {
   __shared__ SelectShared sm;
   constexpr int NG = kSelThreads / LPR;
@@ -1209,10 +1480,15 @@ __global__ __launch_bounds__(kSelThreads) void lazy_kernel(ScoreArgs a, float* l
   const SeqGeom g = geom_of(a, n_p, tid == 0);
   float* aff = a.aff + (int64_t)s * a.rows_per_seq;
   float* out = lazy_out ? lazy_out + (int64_t)s * a.rows_per_seq : nullptr;
-  clear_select_state(a, g, sm);
-  __syncthreads();
-  const int32_t kp = a.rows_per_seq <= kLdsRows ? lazy_levels<true, EARLY, LPR, NQ, R>(a, g, seq, aff, out, A, sm, v0)
-                                                : lazy_levels<false, EARLY, LPR, NQ, R>(a, g, seq, aff, out, A, sm, v0);
+  int32_t kp = -1;
+  if constexpr (LEAN) kp = lazy_lean_levels<LPR, NQ, R>(a, g, seq, out, A, sm, v0);
+  if (kp < 0) {
+    // the general path (also when a lean level needs the zero fill)
+    clear_select_state(a, g, sm);
+    __syncthreads();
+    kp = a.rows_per_seq <= kLdsRows ? lazy_levels<true, EARLY, LPR, NQ, R>(a, g, seq, aff, out, A, sm, v0)
+                                    : lazy_levels<false, EARLY, LPR, NQ, R>(a, g, seq, aff, out, A, sm, v0);
+  }
   write_selection(a, sm, s, kp);
 }
 
@@ -1572,7 +1848,13 @@ hipError_t launch_nq(const ScoreArgs& a0, bool lazy, float* lazy_out, hipStream_
   constexpr int R = NQ >= KKA_SCORE_LOADS ? 1 : KKA_SCORE_LOADS / NQ;
   if (lazy) {
     constexpr int RL = NQ >= 16 ? 1 : 16 / NQ;  // 16 row loads in flight per lane
-    hipLaunchKernelGGL((lazy_kernel<LPR, NQ, RL>), dim3((unsigned)a0.S), dim3(kSelThreads), 0, st, a0, lazy_out);
+    constexpr bool kLeanOk = NQ < 16 && (kSelThreads / LPR) * RL >= 256;  // early grid rows, one pass a level
+    if (kLeanOk && lean_levels_fit(a0))
+      hipLaunchKernelGGL((lazy_kernel<LPR, NQ, RL, kLeanOk>), dim3((unsigned)a0.S), dim3(kSelThreads), 0, st, a0,
+                         lazy_out);
+    else
+      hipLaunchKernelGGL((lazy_kernel<LPR, NQ, RL, false>), dim3((unsigned)a0.S), dim3(kSelThreads), 0, st, a0,
+                         lazy_out);
     return hipGetLastError();
   }
   ScoreArgs a = a0;
@@ -1587,10 +1869,17 @@ hipError_t launch_nq(const ScoreArgs& a0, bool lazy, float* lazy_out, hipStream_
     a.rows_per_tile = kFusedRows;
     a.tiles_per_seq = (int32_t)(fused_tiles > 0 ? fused_tiles : 1);
     const dim3 grid((unsigned)((int64_t)a.S * a.tiles_per_seq));
-    if (a.hist)
-      hipLaunchKernelGGL((score_select_kernel<LPR, NQ, RF, true>), grid, dim3(kSelThreads), 0, st, a);
+    // the lean selection (more registers: one work-group per compute unit)
+    // when one work-group per compute unit covers every tile
+    const bool lean = lean_levels_fit(a) && (int64_t)a.S * fused_tiles <= (int64_t)device_cus();
+    if (a.hist && lean)
+      hipLaunchKernelGGL((score_select_kernel<LPR, NQ, RF, true, true>), grid, dim3(kSelThreads), 0, st, a);
+    else if (a.hist)
+      hipLaunchKernelGGL((score_select_kernel<LPR, NQ, RF, true, false>), grid, dim3(kSelThreads), 0, st, a);
+    else if (lean)
+      hipLaunchKernelGGL((score_select_kernel<LPR, NQ, RF, false, true>), grid, dim3(kSelThreads), 0, st, a);
     else
-      hipLaunchKernelGGL((score_select_kernel<LPR, NQ, RF, false>), grid, dim3(kSelThreads), 0, st, a);
+      hipLaunchKernelGGL((score_select_kernel<LPR, NQ, RF, false, false>), grid, dim3(kSelThreads), 0, st, a);
     return hipGetLastError();
   }
   // Larger batches whose levels fit the small selector: one launch, a
@@ -1611,7 +1900,10 @@ hipError_t launch_nq(const ScoreArgs& a0, bool lazy, float* lazy_out, hipStream_
     hipLaunchKernelGGL((score_kernel<LPR, NQ, R, false>), grid, dim3(256), 0, st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.S), dim3(kSelThreads), 0, st, a);
+  if (lean_levels_fit(a))
+    hipLaunchKernelGGL(select_kernel<true>, dim3((unsigned)a.S), dim3(kSelThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(select_kernel<false>, dim3((unsigned)a.S), dim3(kSelThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1662,7 +1954,10 @@ hipError_t launch_score_topk(const ScoreArgs& a, hipStream_t st) { return dispat
 
 hipError_t launch_select(const ScoreArgs& a, hipStream_t st) {
   if (a.S <= 0) return hipSuccess;
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.S), dim3(kSelThreads), 0, st, a);
+  if (lean_levels_fit(a))
+    hipLaunchKernelGGL(select_kernel<true>, dim3((unsigned)a.S), dim3(kSelThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(select_kernel<false>, dim3((unsigned)a.S), dim3(kSelThreads), 0, st, a);
   return hipGetLastError();
 }
 
