@@ -889,7 +889,51 @@ def profile_pass_ragged(args):
                       "kernel_source_sha256_16": kernel_source_hash("kka_pool.hip")}), flush=True)
 
 
-def write_ragged_counter_summary(fetch_csv: str, write_csv: str, stall_csv: str, out_json: str, command: str):
+_POOL_PASSES = {
+    "ragged": ("kka_pool_blocks, variance mode (all kernels of one call)",
+               "32 sequences, lengths uniform in [4096, 65536], 7B key shape (28 x 4 x 128), blocks of 64, "
+               "permuted shared pool, head-variance weights"),
+    "c1": ("kka_pool_blocks, uniform (one call)",
+           "0.5B key shape (24 x 2 x 64), 4096 tokens, block 16 (256 blocks), permuted shared pool"),
+    "c2": ("kka_pool_blocks, uniform (one call)",
+           "7B key shape (28 x 4 x 128), 32768 tokens, block 128 (256 blocks), permuted shared pool"),
+}
+
+
+def profile_pass_pool(args, which: str):
+    """Short run for hardware-counter passes over one K-pool workload (the
+    0.5B or 7B/32K uniform pool): a plain 1 GiB device copy for
+    calibration, then three kka_pool_blocks calls."""
+    import numpy as np
+    import torch
+
+    import kv_cache_block_amd as kka
+    import synth
+    from kv_cache_block_amd.pipeline import Selector
+
+    dev = "cuda:0"
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    w = synth.config1(args.seed) if which == "c1" else synth.config2(args.seed)
+    k = torch.from_numpy(w.k.reshape(-1).view(np.int16)).to(dev)
+    kp = kka.KPool(k, w.L, w.H, w.D, w.B, w.P)
+    seqs = kka.Seqs(torch.from_numpy(w.seq_len).to(dev), torch.from_numpy(w.block_offsets).to(dev),
+                    torch.from_numpy(w.block_table).to(dev), w.total_blocks)
+    sel = Selector(kp, seqs, w.select, max_pages=int(np.max(np.diff(w.block_offsets))), window=w.window,
+                   mode=kka.WEIGHT_UNIFORM, device=dev)
+    for _ in range(3):
+        sel.pool()
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_pass": which, "copy_bytes": (1 << 28) * 4, "kpool_algorithmic_bytes": kpool_bytes(w),
+                      "kernel_source_sha256_16": kernel_source_hash("kka_pool.hip")}), flush=True)
+
+
+def write_ragged_counter_summary(fetch_csv: str, write_csv: str, stall_csv: str, out_json: str, command: str,
+                                 which: str = "ragged"):
     """Per-kernel HBM bytes of the variance-weighted K-pool of the ragged batch
     from --pmc runs of --profile-pass ragged: FETCH_SIZE, WRITE_SIZE (each
     scaled by what it reads for the 1 GiB copy) and the write-path counters
@@ -926,10 +970,10 @@ def write_ragged_counter_summary(fetch_csv: str, write_csv: str, stall_csv: str,
                 entry[sk[2]] = round(statistics.mean(v))
         kernels[f"{_short(k[0])} grid={k[1]}"] = entry
         total += fb + wb
+    call, workload = _POOL_PASSES[which]
     summary = {
-        "call": "kka_pool_blocks, variance mode (all kernels of one call)",
-        "workload": "32 sequences, lengths uniform in [4096, 65536], 7B key shape (28 x 4 x 128), blocks of 64, "
-                    "permuted shared pool, head-variance weights",
+        "call": call,
+        "workload": workload,
         "kernel_source_sha256_16": kernel_source_hash("kka_pool.hip"),
         "fetch_factor": round(fetch_factor, 5),
         "write_factor": round(write_factor, 5),
@@ -937,6 +981,11 @@ def write_ragged_counter_summary(fetch_csv: str, write_csv: str, stall_csv: str,
         "per_kernel": kernels,
         "commands": command,
     }
+    if which != "ragged":
+        import synth
+        w = synth.config1(0) if which == "c1" else synth.config2(0)
+        summary["kpool_algorithmic_bytes"] = kpool_bytes(w)
+        summary["traffic_over_algorithmic"] = round(total / kpool_bytes(w), 5)
     with open(out_json, "w") as fh:
         json.dump(summary, fh, indent=1)
     print(json.dumps({"traffic_bytes_per_call": summary["traffic_bytes_per_call"]}))
@@ -1066,9 +1115,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--oracle-table", action="store_true",
                     help="time the oracle on every workload, one core and all cores (no GPU needed)")
-    ap.add_argument("--profile-pass", nargs="?", const="c3", choices=["c3", "ragged"],
+    ap.add_argument("--profile-pass", nargs="?", const="c3", choices=["c3", "ragged", "c1", "c2"],
                     help="short run for rocprofv3 counter passes: the 128K workload and the serving batch (c3), or "
                          "the variance-weighted K-pool of the ragged batch (ragged)")
+    ap.add_argument("--write-pool-counter-summary", nargs=4, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV", "OUT"),
+                    help="summarise --pmc runs of --profile-pass c1 or c2 (no GPU needed)")
     ap.add_argument("--write-ragged-counter-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "STALL_CSV", "OUT"),
                     help="summarise --pmc runs of --profile-pass ragged (no GPU needed; STALL_CSV may be -)")
     ap.add_argument("--write-counter-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_DIR"),
@@ -1083,6 +1134,12 @@ def main():
     if args.write_stats_summary:
         write_stats_summary(*args.write_stats_summary, command=args.command)
         return
+    if args.write_pool_counter_summary:
+        which, fetch_csv, write_csv, out_json = args.write_pool_counter_summary
+        if which not in ("c1", "c2"):
+            raise SystemExit("--write-pool-counter-summary: WORKLOAD is c1 or c2")
+        write_ragged_counter_summary(fetch_csv, write_csv, "-", out_json, command=args.command, which=which)
+        return
     if args.write_ragged_counter_summary:
         write_ragged_counter_summary(*args.write_ragged_counter_summary, command=args.command)
         return
@@ -1096,6 +1153,8 @@ def main():
         sys.exit(2)
     if args.profile_pass == "ragged":
         profile_pass_ragged(args)
+    elif args.profile_pass in ("c1", "c2"):
+        profile_pass_pool(args, args.profile_pass)
     elif args.profile_pass:
         profile_pass(args)
     else:
