@@ -1136,3 +1136,72 @@ def test_variance_weights_of_large_offset_low_variance_heads():
     got = vb_rows(sel, w)
     for b, v in oracle_vb(w, range(w.total_blocks), wref).items():
         np.testing.assert_allclose(got[b], v, rtol=3e-7, atol=1e-5, err_msg=f"block {b}")
+
+
+# Layouts at the limits of the lean selection (at most 64 grids, 64 chunk
+# candidates, 256 page candidates and k = 64 a level) and one step past
+# each (the general path): head_dim 32 and 128, ragged and empty
+# sequences, integer-valued vectors for exact affinity ties.  The single
+# pass is checked against the oracle, the lazy pass bit for bit against
+# the single pass.
+LEAN_LIMITS = [
+    # (pages_per_chunk, chunks_per_grid, max_pages, k_grid, k_chunk, k_page)
+    (4, 4, 1024, 16, 64, 64),    # 64 grids, 64 chunk and 256 page candidates, k = 64: lean
+    (4, 4, 1024, 16, 64, 65),    # k_page past the limit: general
+    (4, 4, 1024, 17, 64, 64),    # 68 chunk candidates: general
+    (16, 16, 8192, 4, 16, 64),   # the serving shape: lean
+    (5, 3, 900, 7, 21, 40),      # fan-outs that are not powers of two: lean
+    (16, 4, 4096, 16, 65, 64),   # k_chunk past the limit: general
+]
+
+
+def _lean_case_levels(S, max_pages, D, ppc, cpg, n_pages, ties, seed):
+    lay = kka.LevelLayout(S, max_pages, D, True, ppc, cpg)
+    rng = np.random.default_rng(seed)
+    lvl = np.zeros((S, lay.rows_per_seq, D), np.float32)
+    if ties:
+        lvl[:, :max_pages] = rng.integers(-1, 2, (S, max_pages, D)).astype(np.float32)
+        anchors = rng.integers(-1, 2, (S, D)).astype(np.float32)
+    else:
+        lvl[:, :max_pages] = rng.standard_normal((S, max_pages, D)).astype(np.float32)
+        anchors = rng.standard_normal((S, D)).astype(np.float32)
+    for s, n in enumerate(n_pages):
+        lvl[s, n:max_pages] = 0.0
+    return lay, lvl, anchors
+
+
+@pytest.mark.parametrize("ties", [False, True])
+@pytest.mark.parametrize("D", [32, 128])
+@pytest.mark.parametrize("geom", LEAN_LIMITS)
+def test_lean_level_limits(geom, D, ties):
+    ppc, cpg, max_pages, kg, kc, kp = geom
+    say(f"lean limits {geom} D={D} ties={ties}")
+    n_pages = [max_pages, max_pages - 1, 1, 0, 17, max_pages // 2 + 3]
+    S = len(n_pages)
+    lay, lvl, anchors = _lean_case_levels(S, max_pages, D, ppc, cpg, n_pages, ties, seed=max_pages + D + kp)
+    cfg = dict(hierarchical=1, k_grid=kg, k_chunk=kc, k_page=kp, pages_per_chunk=ppc, chunks_per_grid=cpg)
+    dev = "cuda"
+    level = torch.from_numpy(lvl).to(dev)
+    npg = torch.tensor(n_pages, dtype=torch.int32, device=dev)
+    kka.kka_build_levels(lay, level, npg)
+    sel = Selector.__new__(Selector)
+    sel.lay, sel.sel, sel.level = lay, cfg, level
+    sel.anchors = torch.from_numpy(anchors).to(dev)
+    sel.page_idx = torch.zeros((S, kp), dtype=torch.int32, device=dev)
+    sel.page_score = torch.zeros((S, kp), dtype=torch.float32, device=dev)
+    sel.n_selected = torch.zeros(S, dtype=torch.int32, device=dev)
+    sel.affinity = torch.zeros((S, lay.rows_per_seq), dtype=torch.float32, device=dev)
+    sel.ws_score = kka.new_workspace(kka.kka_score_topk_workspace(lay, True))
+    sel.score(npg)
+    torch.cuda.synchronize()
+    for s in range(S):
+        check_selection(sel, s, n_pages[s], tag=f"lean {geom} D={D}")
+    full = (sel.page_idx.clone(), sel.page_score.clone(), sel.n_selected.clone())
+    sel.page_idx.fill_(-7)
+    sel.page_score.fill_(-7.0)
+    sel.n_selected.fill_(-7)
+    sel.score(npg, lazy=True)
+    torch.cuda.synchronize()
+    assert torch.equal(sel.page_idx, full[0]), "lazy indices differ from the single pass"
+    assert torch.equal(sel.page_score.view(torch.int32), full[1].view(torch.int32)), "lazy scores differ"
+    assert torch.equal(sel.n_selected, full[2])
