@@ -276,6 +276,15 @@ __device__ __forceinline__ void load_shift(const PoolArgs& a, int64_t p0, int32_
   }
 }
 
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// One 16-byte read of the pass-1 sums, which are read once per pass and
+// never again from the cache: non-temporal.
+__device__ __forceinline__ float4 load_sums(const float4* p) {
+  const f32x4v t = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p));
+  return make_float4(t.x, t.y, t.z, t.w);
+}
+
 __device__ __forceinline__ void stats8(float (&s1)[8], float (&s2)[8], const float (&c)[8], u32x4 v) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -333,9 +342,11 @@ __global__ __launch_bounds__(MAXT) void pool_stats_kernel(PoolArgs a) {
         for (int u = 0; u < kUnroll; ++u) stats8(s1, s2, c, v[u]);
       }
       for (; ti < n_tok; ++ti) stats8(s1, s2, c, load16(tp + (int64_t)ti * a.sT));
-      float4* dst = reinterpret_cast<float4*>(a.partial + (((int64_t)item * a.L + l) * a.H) * a.D + (int64_t)q * 8);
-      dst[0] = make_float4(s1[0], s1[1], s1[2], s1[3]);
-      dst[1] = make_float4(s1[4], s1[5], s1[6], s1[7]);
+      // streamed out (non-temporal): read back once, by head_var_kernel and
+      // pool_combine_kernel, long after this pass has moved on
+      f32x4v* dst = reinterpret_cast<f32x4v*>(a.partial + (((int64_t)item * a.L + l) * a.H) * a.D + (int64_t)q * 8);
+      __builtin_nontemporal_store(f32x4v{s1[0], s1[1], s1[2], s1[3]}, dst);
+      __builtin_nontemporal_store(f32x4v{s1[4], s1[5], s1[6], s1[7]}, dst + 1);
 #pragma unroll
       for (int e = 0; e < 8; ++e) sq += (double)s2[e];
     }
@@ -394,7 +405,7 @@ __global__ __launch_bounds__(256) void head_var_kernel(WeightArgs w) {
     for (; b + (kVarUnroll - 1) * ng < b1; b += kVarUnroll * ng) {
       float4 x[kVarUnroll];
 #pragma unroll
-      for (int u = 0; u < kVarUnroll; ++u) x[u] = base[(int64_t)(b + u * ng) * bstride];
+      for (int u = 0; u < kVarUnroll; ++u) x[u] = load_sums(base + (int64_t)(b + u * ng) * bstride);
 #pragma unroll
       for (int u = 0; u < kVarUnroll; ++u) {
         acc[0] += (double)x[u].x;
@@ -404,7 +415,7 @@ __global__ __launch_bounds__(256) void head_var_kernel(WeightArgs w) {
       }
     }
     for (; b < b1; b += ng) {
-      const float4 x = base[(int64_t)b * bstride];
+      const float4 x = load_sums(base + (int64_t)b * bstride);
       acc[0] += (double)x.x;
       acc[1] += (double)x.y;
       acc[2] += (double)x.z;
@@ -510,7 +521,7 @@ __global__ __launch_bounds__(1024) void pool_combine_kernel(PoolArgs a, const fl
   for (; lh + 4 * (kCombineUnroll - 1) < LH; lh += 4 * kCombineUnroll) {
     float4 x[kCombineUnroll];
 #pragma unroll
-    for (int u = 0; u < kCombineUnroll; ++u) x[u] = src[(int64_t)(lh + 4 * u) * nl];
+    for (int u = 0; u < kCombineUnroll; ++u) x[u] = load_sums(src + (int64_t)(lh + 4 * u) * nl);
 #pragma unroll
     for (int u = 0; u < kCombineUnroll; ++u) {
       const float wv = wr[lh + 4 * u];
@@ -522,7 +533,7 @@ __global__ __launch_bounds__(1024) void pool_combine_kernel(PoolArgs a, const fl
   }
   for (; lh < LH; lh += 4) {
     const float wv = wr[lh];
-    const float4 x = src[(int64_t)lh * nl];
+    const float4 x = load_sums(src + (int64_t)lh * nl);
     acc.x = fmaf(wv, x.x, acc.x);
     acc.y = fmaf(wv, x.y, acc.y);
     acc.z = fmaf(wv, x.z, acc.z);
