@@ -254,16 +254,16 @@ struct ScoreArgs {
 // per-sequence selectors (kka_score.hip): at most 64 grids, at most 64
 // chunk candidates (children of the kept grids), at most 256 page
 // candidates, at most 64 kept per level, at most kLeanHiRows chunk and grid
-// rows and every row staged in LDS.  Kernel arguments only: the choice holds
-// at any page count.
+// rows, at least one page row and every row staged in LDS.  Kernel
+// arguments only: the choice holds at any page count.
 constexpr int kLeanHiRows = 1024;
 inline __host__ __device__ bool lean_levels_fit(const ScoreArgs& a) {
   const int64_t kg = a.k_g < a.g_cap ? a.k_g : a.g_cap;
   const int64_t kc = a.k_c < a.c_cap ? a.k_c : a.c_cap;
   const int64_t kp = a.k_p < a.max_pages ? a.k_p : a.max_pages;
-  return a.hier && a.rows_per_seq <= kSelectLdsRows && a.rows_per_seq - a.max_pages <= kLeanHiRows &&
-         a.g_cap <= 64 && kg >= 0 && kg * a.cpg <= 64 && kc >= 0 && kc <= 64 && kc * a.ppc <= 256 && kp >= 0 &&
-         kp <= 64;
+  return a.hier && a.max_pages >= 1 && a.rows_per_seq <= kSelectLdsRows &&
+         a.rows_per_seq - a.max_pages <= kLeanHiRows && a.g_cap <= 64 && kg >= 0 && kg * a.cpg <= 64 && kc >= 0 &&
+         kc <= 64 && kc * a.ppc <= 256 && kp >= 0 && kp <= 64;
 }
 
 // ---------------------------------------------------------------- helpers

@@ -864,6 +864,11 @@ __device__ __forceinline__ int32_t select_levels(const ScoreArgs& a, const SeqGe
 // the zero fill, and the general path selects instead, from the same
 // staged rows.
 
+// x / d for a wave-uniform d >= 1: a shift when d is a power of two.
+__device__ __forceinline__ int32_t div_fan(int32_t x, int32_t d) {
+  return (d & (d - 1)) == 0 ? x >> __builtin_ctz((unsigned)d) : x / d;
+}
+
 // Lanes of one wavefront read each other's LDS stores.
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -872,24 +877,26 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // Keys among the wavefront's first m (lane l's key stored at copy[l]; m
-// wave-uniform, a multiple of 16 at most 64) larger than this lane's x.
+// wave-uniform, a multiple of 32 at most 64) larger than this lane's x.
+// The rank is a chain of LDS round trips and compares, so it is written
+// for latency: up to 32 keys (16 reads) in flight at once, and four
+// independent counts.
 __device__ __forceinline__ int32_t rank_in_wave(uint64_t x, uint64_t* copy, int32_t m) {
   wave_sync();  // earlier reads of the copy are done
   copy[threadIdx.x & 63] = x;
   wave_sync();
   const u64x2* p = reinterpret_cast<const u64x2*>(copy);
-  int32_t r = 0;
-  // batches of eight 16-byte reads: the scheduler would otherwise hoist all
-  // 32 (128 registers) ahead of the compares
-  for (int u = 0; u < m / 2; u += 8) {
-    u64x2 y[8];
+  int32_t r[4] = {0, 0, 0, 0};
+  for (int u = 0; u < m / 2; u += 16) {
+    u64x2 y[16];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) y[v] = p[u + v];
+    for (int v = 0; v < 16; ++v) y[v] = p[u + v];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) r += (int32_t)(y[v].x > x) + (int32_t)(y[v].y > x);
+    for (int v = 0; v < 16; ++v) r[v & 3] += (int32_t)(y[v].x > x) + (int32_t)(y[v].y > x);
+    // the scheduler would otherwise hoist the next 16 reads too (spills)
     __builtin_amdgcn_sched_barrier(0);
   }
-  return r;
+  return (r[0] + r[1]) + (r[2] + r[3]);
 }
 
 // Top k of up to 64 candidates on one wavefront: lane l < m holds
@@ -903,11 +910,50 @@ __device__ __forceinline__ bool rank_level64(int32_t e, uint32_t bits, int32_t k
   const uint64_t x = pos ? composite(bits, e) : (uint64_t)lane;
   // lanes from m on hold no candidate: their keys (below every positive
   // one) need not be compared
-  const int32_t r = rank_in_wave(x, copy, min((m + 15) & ~15, 64));
+  const int32_t r = rank_in_wave(x, copy, min((m + 31) & ~31, 64));
   if ((int32_t)__popcll(__ballot(pos)) < k) return false;
   if (pos && r < k) list[r] = e;
   wave_sync();
   return true;
+}
+
+// Keys of the three runs other than run w (of four strictly descending runs
+// of 64, with their block-end keys) larger than x: as run_count_above for
+// each, with the three runs' reads of a round in flight together.
+__device__ __forceinline__ int32_t count_above_other_runs(const SortedRuns& R, int32_t w, uint64_t x) {
+  int32_t c[3];
+  {
+    u64x2 pv[3][4];
+#pragma unroll
+    for (int v = 0; v < 3; ++v) {
+      const u64x2* p = reinterpret_cast<const u64x2*>(R.piv + 8 * ((w + 1 + v) & 3));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) pv[v][q] = p[q];
+    }
+#pragma unroll
+    for (int v = 0; v < 3; ++v) {
+      int32_t n = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) n += (int32_t)(pv[v][q].x > x) + (int32_t)(pv[v][q].y > x);
+      c[v] = n;
+    }
+  }
+  u64x2 bk[3][4];
+#pragma unroll
+  for (int v = 0; v < 3; ++v) {
+    const u64x2* p = reinterpret_cast<const u64x2*>(R.key + 64 * ((w + 1 + v) & 3) + 8 * (c[v] < 8 ? c[v] : 7));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bk[v][q] = p[q];
+  }
+  int32_t total = 0;
+#pragma unroll
+  for (int v = 0; v < 3; ++v) {
+    int32_t f = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) f += (int32_t)(bk[v][q].x > x) + (int32_t)(bk[v][q].y > x);
+    total += c[v] == 8 ? 64 : 8 * c[v] + f;
+  }
+  return total;
 }
 
 // Top k (<= 64) of up to 256 candidates: thread t < 256 holds candidate t;
@@ -933,9 +979,7 @@ __device__ __forceinline__ bool rank_level256(int32_t e, uint32_t bits, int32_t 
   const int32_t P = sm.wave_tot[0] + sm.wave_tot[1] + sm.wave_tot[2] + sm.wave_tot[3];
   if (P < k) return false;
   if (wave < 4) {
-    int32_t R = r;
-#pragma unroll
-    for (int v = 1; v < 4; ++v) R += run_count_above(sm.runs, (wave + v) & 3, x);
+    const int32_t R = r + count_above_other_runs(sm.runs, wave, x);
     if (pos && R < k) sm.buf[R] = x;
   }
   __syncthreads();
@@ -957,19 +1001,19 @@ __device__ __forceinline__ int32_t select_lean_levels(const ScoreArgs& a, const 
   if (wave == 0) {
     // wavefront 0 stages the chunk and grid rows and ranks grids and chunks
     // while the other wavefronts stage the page rows
+    // clamped, unconditional loads and stores (a slot past the rows repeats
+    // the last one): each store then waits for its own load only
     float hi[kLeanHiRows / 64];
 #pragma unroll
-    for (int u = 0; u < kLeanHiRows / 64; ++u)
-      if (u * 64 < n_hi) hi[u] = load_agent(aff + n_lo + min(u * 64 + lane, n_hi - 1));
+    for (int u = 0; u < kLeanHiRows / 64; ++u) hi[u] = load_agent(aff + n_lo + min(u * 64 + lane, n_hi - 1));
 #pragma unroll
-    for (int u = 0; u < kLeanHiRows / 64; ++u)
-      if (u * 64 < n_hi) sm.aff[n_lo + min(u * 64 + lane, n_hi - 1)] = hi[u];
+    for (int u = 0; u < kLeanHiRows / 64; ++u) sm.aff[n_lo + min(u * 64 + lane, n_hi - 1)] = hi[u];
     wave_sync();
     const int32_t off_g = a.max_pages + a.c_cap;
     const int32_t eg = lane < g.n_g ? lane : -1;
     bool good = rank_level64(eg, eg >= 0 ? __float_as_uint(sm.aff[off_g + eg]) : 0u, kg, g.n_g, sm.ck, sm.plist);
     if (good) {
-      const int32_t pr = lane / a.cpg;
+      const int32_t pr = div_fan(lane, a.cpg);
       int32_t ec = -1;
       if (pr < kg) {
         const int32_t c = sm.plist[pr] * a.cpg + (lane - pr * a.cpg);
@@ -983,17 +1027,15 @@ __device__ __forceinline__ int32_t select_lean_levels(const ScoreArgs& a, const 
     const int t = tid - 64;
     float lo[UP];
 #pragma unroll
-    for (int u = 0; u < UP; ++u)
-      if (u * NP < n_lo) lo[u] = load_agent(aff + min(u * NP + t, n_lo - 1));
+    for (int u = 0; u < UP; ++u) lo[u] = load_agent(aff + min(u * NP + t, n_lo - 1));
 #pragma unroll
-    for (int u = 0; u < UP; ++u)
-      if (u * NP < n_lo) sm.aff[min(u * NP + t, n_lo - 1)] = lo[u];
+    for (int u = 0; u < UP; ++u) sm.aff[min(u * NP + t, n_lo - 1)] = lo[u];
   }
   __syncthreads();
   if (sm.cnt[0] == 0) return -1;
   int32_t ep = -1;
   if (tid < 256) {
-    const int32_t pr = tid / a.ppc;
+    const int32_t pr = div_fan(tid, a.ppc);
     if (pr < kc) {
       const int32_t p = sm.plist[64 + pr] * a.ppc + (tid - pr * a.ppc);
       ep = p < g.n_p ? p : -1;
@@ -1404,7 +1446,7 @@ __device__ __forceinline__ int32_t lazy_lean_levels(const ScoreArgs& a, const Se
       const int32_t c = grp + NG * r;
       int32_t el = -1;
       if (c < m) {
-        const int32_t pr = c / fan;
+        const int32_t pr = div_fan(c, fan);
         el = par[pr] * fan + (c - pr * fan);
         if (el >= n_lev) el = -1;
       }
@@ -1423,7 +1465,7 @@ __device__ __forceinline__ int32_t lazy_lean_levels(const ScoreArgs& a, const Se
     __syncthreads();
     int32_t ec = -1;
     if (tid < m && (lev == 2 || wave == 0)) {
-      const int32_t pr = tid / fan;
+      const int32_t pr = div_fan(tid, fan);
       ec = par[pr] * fan + (tid - pr * fan);
       if (ec >= n_lev) ec = -1;
     }
