@@ -229,6 +229,9 @@ def run(args):
         write_step(0)
     torch.cuda.synchronize()
     ev_w = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_w)]
+    if hasattr(torch.cuda, "_sleep"):
+        # the host queues every timed call while the device spins (see time_calls)
+        torch.cuda._sleep(int(n_w * 100e-6 * 2.4e9))
     for i in range(n_w):
         len_w.add_(1)
         ev_w[i][0].record(stream)
@@ -273,6 +276,9 @@ def run(args):
         score4(i)
     torch.cuda.synchronize()
     ev4 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    if hasattr(torch.cuda, "_sleep"):
+        # the host queues every timed call while the device spins (see time_calls)
+        torch.cuda._sleep(int(args.steps * 100e-6 * 2.4e9))
     for i in range(args.steps):
         ev4[i][0].record(stream)
         score4(i)
@@ -511,13 +517,19 @@ def overlap(a, b, k):
 
 
 def time_calls(fn, steps, warmup, stream):
-    """Mean device time (us) of fn(i), bracketed by events on `stream`."""
+    """Mean device time (us) of fn(i), bracketed by events on `stream`.  A
+    spinning kernel queued first keeps the device busy while the host
+    queues every timed call, so no host-side gap falls between an event and
+    its call."""
     import numpy as np
     import torch
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    if hasattr(torch.cuda, "_sleep"):
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(int(steps * 100e-6 * 2.4e9))  # about 100 us of device time per call queued
     for i in range(steps):
         ev[i][0].record(stream)
         fn(i)
