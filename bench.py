@@ -179,14 +179,18 @@ def run(args):
 
     # c3 lazy (coarse-to-fine) scoring of the same levels: must select the same pages
     full_idx = sel.page_idx.clone()
-    c3_lazy_us = time_calls(lambda i: sel.score(npg, lazy=True), args.steps, max(3, args.warmup), stream)
+    def lazy3(i):
+        sel.score(npg, lazy=True)
+    c3_lazy_us = time_calls(lazy3, args.steps, max(3, args.warmup), stream)
     if not torch.equal(sel.page_idx, full_idx):
         raise RuntimeError("lazy scoring selected different pages than the full pass")
     c3_lazy_rows = lazy_rows(n_g, w.select)
     # the launch floor of this stream: a one-element torch add, event-timed
     # like the calls above (what any launch costs before it does any work)
     tiny = torch.zeros(1, dtype=torch.float32, device=dev)
-    floor_us = time_calls(lambda i: tiny.add_(1.0), args.steps, max(3, args.warmup), stream)
+    def tiny_add(i):
+        tiny.add_(1.0)
+    floor_us = time_calls(tiny_add, args.steps, max(3, args.warmup), stream)
 
     # c3 attention reference (QK^T softmax averaged over layers and query
     # heads, per block) for one planted decode query with 28 query heads, and
@@ -288,7 +292,9 @@ def run(args):
     c4_us = 1e3 * float(np.mean(c4_ms))
     c4_med_us = 1e3 * float(np.median(c4_ms))
     # the same calls on one buffer set: the level rows stay in the last-level cache
-    c4_warm_us = time_calls(lambda i: score4(0), args.steps, args.warmup, stream)
+    def score4_warm(i):
+        score4(0)
+    c4_warm_us = time_calls(score4_warm, args.steps, args.warmup, stream)
     rows4 = lay4.rows_per_seq
     b4 = score_bytes(S, rows4, D, kp4)
     c4_gbps = b4 / (c4_us * 1e-6) / 1e9
@@ -377,23 +383,31 @@ def run(args):
         "kpool_algorithmic_bytes": b_pool,
         "score_topk_us_per_step": round(c3_score_us, 2),
         "score_topk_median_us": round(c3_score_med_us, 2),
-        "score_topk_launches": "one (score_topk_kernel): a selecting work-group per sequence (coarse-to-fine, "
-                               "re-scoring its candidate rows) beside the work-groups that score every row",
+        "score_topk_launches": "one (score_select_kernel): 69 work-groups score every row; the one that "
+                               "finishes the sequence's last tile selects it (lean selection)",
+        "serving_score_topk_launches": "one (score_topk_kernel): a selecting work-group per sequence "
+                                       "(coarse-to-fine, re-scoring its candidate rows) beside the work-groups "
+                                       "that score every row",
         "serving_score_topk_us_per_step": round(c4_us, 2),
         "serving_score_topk_median_us": round(c4_med_us, 2),
         "serving_score_topk_warm_cache_us": round(c4_warm_us, 2),
+        "serving_score_topk_warm_cache_median_us": median_of(score4_warm),
         "serving_score_topk_GBps": round(c4_gbps, 2),
         "serving_score_topk_frac_of_peak": round(c4_gbps / PEAK_HBM_GBPS, 4),
         "serving_workload": "64 sequences x 8192 fp32 block vectors (D=128) + 512 chunk + 32 grid rows each, "
                             "top 4/16/64, three rotating buffer sets (cold last-level cache)",
         "serving_algorithmic_bytes": b4,
         "lazy_score_topk_us_per_step": round(c3_lazy_us, 2),
+        "lazy_score_topk_median_us": median_of(lazy3),
         "launch_floor_us": round(floor_us, 2),
+        "launch_floor_median_us": median_of(tiny_add),
         "launch_floor": "one-element torch add_ on the same stream, event-timed like the score calls",
         "lazy_rows_scored_per_seq": c3_lazy_rows,
         "serving_lazy_score_topk_us_per_step": round(c4_lazy_us, 2),
+        "serving_lazy_score_topk_median_us": median_of(lazy4),
         "serving_lazy_rows_scored_per_seq": c4_lazy_rows,
         "serving_stable_score_topk_us_per_step": round(c4_stable_us, 2),
+        "serving_stable_score_topk_median_us": median_of(stable4),
         "pool_on_write_us_per_step": round(write_us, 2),
         "pool_on_write_workload": "64 sequences x 7B key shape, one token appended per sequence (keys stored into "
                                   "the paged pool, open block's vector updated)",
@@ -535,7 +549,18 @@ def time_calls(fn, steps, warmup, stream):
         fn(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    return 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    ms = [e[0].elapsed_time(e[1]) for e in ev]
+    _MEDIANS[fn] = 1e3 * float(np.median(ms))
+    return 1e3 * float(np.mean(ms))
+
+
+# median (us) of the last time_calls of each function: one stalled call moves
+# a mean of 50 by microseconds, a median not at all
+_MEDIANS = {}
+
+
+def median_of(fn) -> float:
+    return round(_MEDIANS.get(fn, float("nan")), 2)
 
 
 def reported_configs(args, dev, stream):
