@@ -167,8 +167,13 @@ typedef enum kka_weight_mode {
  *             the first call that uses the workspace (allocate it
  *             zero-filled); every call leaves them zero.  A counter found at
  *             or above the split count raises KKA_DEVERR_WORKSPACE and that
- *             block's v_b is not written (re-zero the counters).  Calls that
- *             run concurrently must not share a workspace.
+ *             block's v_b is not written (re-zero the counters).  In VARIANCE
+ *             mode the workspace holds instead the statistics pass's sums:
+ *             per block and (layer, KV head) the head_dim token sums of the
+ *             shifted keys (fp32) and their sum of squares (fp64), then per
+ *             sequence the L*H head variances and the head_dim shift terms
+ *             (fp64); nothing has to be zeroed.  Calls that run concurrently
+ *             must not share a workspace.
  */
 KKA_API kka_status kka_pool_blocks(const kka_kpool* kp, const kka_seqs* seqs, const int32_t* blocks, int32_t num_blocks,
                            int32_t mode, float* head_weight, float* vb_out, int64_t vb_seq_stride, void* workspace,
