@@ -66,6 +66,31 @@ def test_counter_summary_calibrates_against_the_copy(tmp_path):
     assert s["kernel_source_sha256_16"] == bench.kernel_source_hash("kka_score.hip")
 
 
+def test_pool_counter_summary_of_a_reported_workload(tmp_path):
+    """The 0.5B K-pool's counter pass: bytes per call from the same copy
+    calibration, beside the workload's algorithmic bytes."""
+    hdr = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    pool = "void kka::(anonymous namespace)::pool_kernel<0, 256>(kka::PoolArgs)"
+    copy = "__amd_rocclr_copyBuffer"
+    fetch = [[copy, 1 << 20, "FETCH_SIZE", 2 * GIB_KIB], [pool, 65536, "FETCH_SIZE", 49000.0],
+             [pool, 65536, "FETCH_SIZE", 51000.0]]
+    write = [[copy, 1 << 20, "WRITE_SIZE", GIB_KIB], [pool, 65536, "WRITE_SIZE", 64.0],
+             [pool, 65536, "WRITE_SIZE", 64.0]]
+    fcsv, wcsv = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    _write_csv(fcsv, hdr, fetch)
+    _write_csv(wcsv, hdr, write)
+    out = tmp_path / "c1.json"
+    bench.write_ragged_counter_summary(str(fcsv), str(wcsv), "-", str(out), command="cmd", which="c1")
+    k = json.load(open(out))
+    # mean fetch 50,000 KiB * 0.5, mean write 64 KiB
+    assert k["traffic_bytes_per_call"] == 25_600_000 + 65_536
+    assert k["kpool_algorithmic_bytes"] == 25_232_384
+    assert k["traffic_over_algorithmic"] == round((25_600_000 + 65_536) / 25_232_384, 5)
+    assert k["per_kernel"]["pool_kernel<0, 256> grid=65536"]["dispatches"] == 2
+    assert k["kernel_source_sha256_16"] == bench.kernel_source_hash("kka_pool.hip")
+    assert "0.5B" in k["workload"]
+
+
 def test_counter_summary_needs_the_copy(tmp_path):
     hdr = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
     rows = [["void kka::(anonymous namespace)::pool_kernel<0, 256>(kka::PoolArgs)", 2097152, "FETCH_SIZE", 1.0]]
