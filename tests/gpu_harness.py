@@ -105,6 +105,33 @@ def check_selection(sel: Selector, s: int, n_p: int, tag: str = ""):
     return idx_ref
 
 
+def check_end_to_end(sel: Selector, s: int, pages_ref: np.ndarray, anchor_ref: np.ndarray, tag: str = "") -> int:
+    """The oracle's own selection of sequence s, from its own block vectors
+    and anchor (levels, affinities and top-K all in the oracle), against the
+    GPU's: the same count, and the selected scores equal position by
+    position within ATOL, so selected indices can differ only between
+    blocks whose scores do.  Returns the number of positions whose indices
+    differ."""
+    cfg = sel.sel
+    n_p = len(pages_ref)
+    D = sel.lay.head_dim
+    ac = ag = None
+    if cfg["hierarchical"]:
+        ppc, cpg = cfg["pages_per_chunk"], cfg["chunks_per_grid"]
+        oc, og = oracle.build_levels(pages_ref, ppc, cpg) if n_p else (np.zeros((0, D), np.float32),) * 2
+        ac, ag = oracle.affinity(oc, anchor_ref), oracle.affinity(og, anchor_ref)
+    ap = oracle.affinity(pages_ref, anchor_ref)
+    idx, sc = oracle.select(ap, ac, ag, hierarchical=cfg["hierarchical"], k_grid=cfg.get("k_grid", 0),
+                            k_chunk=cfg.get("k_chunk", 0), k_page=cfg["k_page"],
+                            pages_per_chunk=cfg.get("pages_per_chunk", 16), chunks_per_grid=cfg.get("chunks_per_grid", 16))
+    k_eff = len(idx)
+    assert int(sel.n_selected[s].item()) == k_eff, f"{tag} end-to-end count s={s}"
+    got_idx = sel.page_idx[s].cpu().numpy()[:k_eff]
+    got_sc = sel.page_score[s].cpu().numpy()[:k_eff]
+    np.testing.assert_allclose(got_sc, sc, atol=ATOL, rtol=0, err_msg=f"{tag} end-to-end scores s={s}")
+    return int((got_idx != idx).sum())
+
+
 def oracle_vb(w, blocks, weights=None):
     kp = oracle.KPool.of(w)
     return oracle.pool_blocks(kp, w.seq_len, w.block_offsets, w.block_table, weights, blocks=set(blocks))

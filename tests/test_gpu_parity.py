@@ -11,8 +11,9 @@ import oracle
 import synth
 from kv_cache_block_amd.pipeline import Selector
 
-from gpu_harness import (ATOL, WEIGHT_RTOL, assert_rows_close, check_selection, host_threads, mode_of, n_pages_of,
-                         oracle_anchors_all, oracle_vb, oracle_vb_all, oracle_weights_all, run_selector, say, upload)
+from gpu_harness import (ATOL, WEIGHT_RTOL, assert_rows_close, check_end_to_end, check_selection, host_threads, mode_of,
+                         n_pages_of, oracle_anchors_all, oracle_vb, oracle_vb_all, oracle_weights_all, run_selector, say,
+                         upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -414,6 +415,8 @@ def test_config1_parity_and_recovery():
     idx = check_selection(sel, 0, int(npg[0]), "c1")
     prec = np.mean(w.block_topic[0][idx] == w.anchor_topic[0])
     assert prec >= 0.75
+    pages = np.stack([ref[b] for b in range(w.total_blocks)])
+    say(f"config1 end to end: {check_end_to_end(sel, 0, pages, a, 'c1')} positions differ")
 
 
 def test_config1_variance_mode_parity():
@@ -441,6 +444,11 @@ def test_config2_parity_and_recovery():
         np.testing.assert_allclose(got[b], ref[b], atol=ATOL, rtol=0)
     idx = check_selection(sel, 0, int(npg[0]), "c2")
     assert (w.block_topic[0][idx[:8]] == w.anchor_topic[0]).all()
+    okp = oracle.KPool.of(w)
+    a = oracle.pool_anchor(okp, w.block_table, int(w.seq_len[0]), w.window)
+    np.testing.assert_allclose(sel.anchors[0].cpu().numpy(), a, atol=ATOL, rtol=0)
+    pages = np.stack([ref[b] for b in range(w.total_blocks)])
+    say(f"config2 end to end: {check_end_to_end(sel, 0, pages, a, 'c2')} positions differ")
 
 
 def test_config3_full_size_parity_and_recovery():
@@ -463,6 +471,7 @@ def test_config3_full_size_parity_and_recovery():
     idx = check_selection(sel, 0, int(npg[0]), "c3")
     run = w.extra["anchor_run"]
     assert set(range(run * 32, run * 32 + 32)) <= set(idx.tolist())
+    say(f"config3 end to end: {check_end_to_end(sel, 0, ref, a, 'c3')} positions differ")
 
 
 def test_config4_full_size_parity_and_recovery():
