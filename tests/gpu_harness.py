@@ -25,9 +25,9 @@ WEIGHT_RTOL = 1e-6
 
 
 def say(msg: str):
-    """Progress line that pytest does not capture (names the case before GPU work)."""
-    sys.__stderr__.write(f"[gpu] {msg}\n")
-    sys.__stderr__.flush()
+    """Progress line that pytest does not hold back (names the case before GPU work)."""
+    from conftest import progress
+    progress(f"[gpu] {msg}")
 
 
 def upload(w, device="cuda"):
