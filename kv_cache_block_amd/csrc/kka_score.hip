@@ -37,7 +37,11 @@
 // << 32 | ~index): unique, and larger means higher score then lower index.
 // When fewer than k candidates score above zero, the lowest-index rows
 // scoring exactly 0 (masked or zero affinity) fill the remaining slots in
-// index order.
+// index order.  Small hierarchical levels (at most 64 grids, 64 chunk and
+// 256 page candidates, k at most 64: the 128K and serving shapes) take a
+// leaner path in the one-launch, two-launch and lazy selectors: wavefront
+// 0 ranks grids and chunks alone while the others stage the page rows, and
+// four wavefronts rank the pages (see the lean selection below).
 #include <atomic>
 
 #include "kka_internal.h"
