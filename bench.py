@@ -95,6 +95,66 @@ def traffic_from_counters(algo_bytes_unused=None):
     return c.get("traffic_bytes_per_launch")
 
 
+_HIP = None
+
+
+def _hip_runtime():
+    """The HIP runtime library this process has loaded (torch's), so that
+    its events and torch's streams belong to one runtime."""
+    global _HIP
+    if _HIP is None:
+        import ctypes
+        with open("/proc/self/maps") as f:
+            paths = [ln.split()[-1] for ln in f if "libamdhip64" in ln]
+        if not paths:
+            raise RuntimeError("the HIP runtime is not loaded in this process")
+        H = ctypes.CDLL(paths[0])
+        H.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        H.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        H.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        H.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _HIP = H
+    return _HIP
+
+
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence:
+    recording it skips the system-scope cache write-back and invalidate that
+    a default event (torch.cuda.Event) performs, which adds about 2 us to
+    every interval such events bracket.  Its timestamp is still taken once
+    the work queued before it on the stream has completed.  Same interface
+    as torch.cuda.Event for record() and elapsed_time() (milliseconds)."""
+
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self):
+        import ctypes
+        self._H = _hip_runtime()
+        self._ev = ctypes.c_void_p()
+        rc = self._H.hipEventCreateWithFlags(ctypes.byref(self._ev), self.FLAGS)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream):
+        import ctypes
+        rc = self._H.hipEventRecord(self._ev, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end) -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        rc = self._H.hipEventElapsedTime(ctypes.byref(ms), self._ev, end._ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def __del__(self):
+        if getattr(self, "_ev", None) is not None and self._ev.value:
+            self._H.hipEventDestroy(self._ev)
+            self._ev = None
+
+
 def run(args):
     import numpy as np
     import torch
@@ -138,7 +198,7 @@ def run(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[TimingEvent() for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -191,6 +251,17 @@ def run(args):
     def tiny_add(i):
         tiny.add_(1.0)
     floor_us = time_calls(tiny_add, args.steps, max(3, args.warmup), stream)
+    # the score call and the floor again between torch's default events
+    # (a system-scope fence at each record), for comparison with timings
+    # taken that way
+    def torch_event():
+        return torch.cuda.Event(enable_timing=True)
+    def score3_torch(i):
+        sel.score(npg)
+    def tiny_add_torch(i):
+        tiny.add_(1.0)
+    c3_score_torch_us = time_calls(score3_torch, args.steps, max(3, args.warmup), stream, event=torch_event)
+    floor_torch_us = time_calls(tiny_add_torch, args.steps, max(3, args.warmup), stream, event=torch_event)
 
     # c3 attention reference (QK^T softmax averaged over layers and query
     # heads, per block) for one planted decode query with 28 query heads, and
@@ -232,7 +303,7 @@ def run(args):
     for _ in range(max(3, args.warmup)):
         write_step(0)
     torch.cuda.synchronize()
-    ev_w = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_w)]
+    ev_w = [[TimingEvent() for _ in range(2)] for _ in range(n_w)]
     if hasattr(torch.cuda, "_sleep"):
         # the host queues every timed call while the device spins (see time_calls)
         torch.cuda._sleep(int(n_w * 100e-6 * 2.4e9))
@@ -279,7 +350,7 @@ def run(args):
     for i in range(max(3, args.warmup)):
         score4(i)
     torch.cuda.synchronize()
-    ev4 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    ev4 = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
     if hasattr(torch.cuda, "_sleep"):
         # the host queues every timed call while the device spins (see time_calls)
         torch.cuda._sleep(int(args.steps * 100e-6 * 2.4e9))
@@ -402,6 +473,11 @@ def run(args):
         "launch_floor_us": round(floor_us, 2),
         "launch_floor_median_us": median_of(tiny_add),
         "launch_floor": "one-element torch add_ on the same stream, event-timed like the score calls",
+        "event_timing": "HIP events created with hipEventDisableSystemFence (timing only) around each call; the "
+                        "*_torch_event_* fields time the same calls between torch.cuda.Event pairs",
+        "score_topk_torch_event_us": round(c3_score_torch_us, 2),
+        "score_topk_torch_event_median_us": median_of(score3_torch),
+        "launch_floor_torch_event_us": round(floor_torch_us, 2),
         "lazy_rows_scored_per_seq": c3_lazy_rows,
         "serving_lazy_score_topk_us_per_step": round(c4_lazy_us, 2),
         "serving_lazy_score_topk_median_us": median_of(lazy4),
@@ -530,17 +606,18 @@ def overlap(a, b, k):
     return len(set(list(a)[:k]) & set(list(b)[:k])) / k if k else 0.0
 
 
-def time_calls(fn, steps, warmup, stream):
-    """Mean device time (us) of fn(i), bracketed by events on `stream`.  A
-    spinning kernel queued first keeps the device busy while the host
-    queues every timed call, so no host-side gap falls between an event and
-    its call."""
+def time_calls(fn, steps, warmup, stream, event=None):
+    """Mean device time (us) of fn(i), bracketed by timing events (or
+    `event()` instances) on `stream`.  A spinning kernel queued first keeps
+    the device busy while the host queues every timed call, so no host-side
+    gap falls between an event and its call."""
     import numpy as np
     import torch
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    make = event or TimingEvent
+    ev = [[make() for _ in range(2)] for _ in range(steps)]
     if hasattr(torch.cuda, "_sleep"):
         with torch.cuda.stream(stream):
             torch.cuda._sleep(int(steps * 100e-6 * 2.4e9))  # about 100 us of device time per call queued
@@ -580,7 +657,7 @@ def reported_configs(args, dev, stream):
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
 
     def cold_us(fn, steps):
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        ev = [[TimingEvent() for _ in range(2)] for _ in range(steps)]
         for i in range(steps):
             flush.zero_()
             ev[i][0].record(stream)

@@ -1104,6 +1104,18 @@ __device__ __forceinline__ float affinity_of(float dot, float nr, float sqrt_na,
   return v > 0.f ? (v < 1.f ? v : 1.f) : 0.f;
 }
 
+// Buffer-resource loads: a raw buffer load whose byte offset lies past the
+// resource's range (at most 2^31 - 1 bytes) reads zero and touches no
+// memory, so a lane without data issues the same load as the others, with
+// no branch and no select, and every load of a pass is in flight at once.
+constexpr int32_t kOutOfRange = 0x7ffffff0;  // a byte offset past any range here
+constexpr int kBufAux = KKA_SCORE_NT ? 2 : 0;  // cache policy bits of row loads: 2 = non-temporal
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int64_t bytes) {
+  // gfx9 raw buffer: stride 0, `bytes` records of one byte, default format word
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int32_t)bytes, 0x00020000);
+}
+
 // The anchor as held by one lane of an LPR-lane row group: float4 pieces
 // lg, lg + LPR, ... of the row, plus the squared norm (every lane of the
 // group holds the full sum after a fixed butterfly).
@@ -1113,16 +1125,28 @@ struct AnchorRegs {
   float na, sqrt_na;
 };
 
+// The anchor's pieces go through a buffer resource over its head_dim
+// floats: a piece past head_dim reads zero without a branch, so the loads
+// never wait for one another (nor for row loads already in flight).
+// issue_anchor requests the pieces, finish_anchor forms the norm once they
+// are needed; load_anchor does both.
 template <int LPR, int NQ>
-__device__ __forceinline__ AnchorRegs<LPR, NQ> load_anchor(const ScoreArgs& a, int32_t s, int32_t lg) {
-  AnchorRegs<LPR, NQ> r;
+__device__ __forceinline__ void issue_anchor(const ScoreArgs& a, int32_t s, int32_t lg, AnchorRegs<LPR, NQ>& r) {
   const int32_t Q = a.D >> 2;
-  const f32x4* anc = reinterpret_cast<const f32x4*>(a.anchors + (int64_t)s * a.D);
-  r.na = 0.f;
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.anchors + (int64_t)s * a.D, (int64_t)a.D * 4);
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
     const int32_t qi = lg + LPR * j;
-    r.av[j] = qi < Q ? anc[qi] : f32x4{0.f, 0.f, 0.f, 0.f};
+    const int32_t off = qi < Q ? qi * 16 : kOutOfRange;
+    r.av[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  }
+}
+
+template <int LPR, int NQ>
+__device__ __forceinline__ void finish_anchor(AnchorRegs<LPR, NQ>& r) {
+  r.na = 0.f;
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
     r.na = fmaf(r.av[j].x, r.av[j].x, r.na);
     r.na = fmaf(r.av[j].y, r.av[j].y, r.na);
     r.na = fmaf(r.av[j].z, r.av[j].z, r.na);
@@ -1131,6 +1155,13 @@ __device__ __forceinline__ AnchorRegs<LPR, NQ> load_anchor(const ScoreArgs& a, i
 #pragma unroll
   for (int o = 1; o < LPR; o <<= 1) r.na += __shfl_xor(r.na, o);
   r.sqrt_na = sqrtf(r.na);
+}
+
+template <int LPR, int NQ>
+__device__ __forceinline__ AnchorRegs<LPR, NQ> load_anchor(const ScoreArgs& a, int32_t s, int32_t lg) {
+  AnchorRegs<LPR, NQ> r;
+  issue_anchor<LPR, NQ>(a, s, lg, r);
+  finish_anchor<LPR, NQ>(r);
   return r;
 }
 
@@ -1143,6 +1174,19 @@ __device__ __forceinline__ void load_row(const f32x4* rowp, int32_t lg, int32_t 
     const int32_t qi = lg + LPR * j;
     const f32x4 t = load_row4(rowp + min(qi, Q - 1));
     x[j] = qi < Q ? t : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// This lane's pieces of row `row` of the resource (row < 0: zeros, nothing
+// read); pieces past head_dim read as zero.
+template <int LPR, int NQ>
+__device__ __forceinline__ void load_row_buf(__amdgpu_buffer_rsrc_t rs, int32_t row, int32_t lg, int32_t Q,
+                                             f32x4 (&x)[NQ]) {
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int32_t qi = lg + LPR * j;
+    const int32_t off = row >= 0 && qi < Q ? (row * Q + qi) * 16 : kOutOfRange;
+    x[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kBufAux));
   }
 }
 
@@ -1400,33 +1444,91 @@ __device__ __forceinline__ int32_t lazy_levels(const ScoreArgs& a, const SeqGeom
   return kp;
 }
 
-// Lazy scoring of a lean layout (lean_levels_fit; the grid level's rows all
-// in the first pass, NG * R >= 64): every level's candidates are scored in
-// one pass of the row groups into the LDS row copy (and `out`), wavefront 0
-// ranks grids and chunks and four wavefronts the pages (as in
-// select_lean_levels).  Returns the kept page count, or -1 when a level
-// needs the zero fill.
+// One round of lazy scoring on the lean path: candidates c = grp + NG * r
+// (r < P) of a level, element cand(c) (or -1), scored from their rows in
+// the buffer `rs` into sm.aff[off + element].  Straight-line code: every
+// lane issues the same P * NQ buffer loads (a lane without a candidate
+// reads zeros, nothing from memory), all in flight before the first use.
+// FIN: the anchor's pieces were only requested (issue_anchor); its norm is
+// formed here, after the row loads have gone out.
+template <int LPR, int NQ, int P, bool FIN, class Cand>
+__device__ __forceinline__ void lean_round(__amdgpu_buffer_rsrc_t rs, int32_t Q, int32_t off,
+                                           AnchorRegs<LPR, NQ>& A, Cand cand, float* dst) {
+  constexpr int NG = kSelThreads / LPR;
+  const int32_t grp = threadIdx.x / LPR, lg = threadIdx.x % LPR;
+  f32x4 x[P][NQ];
+  int32_t e[P];
+#pragma unroll
+  for (int r = 0; r < P; ++r) {
+    e[r] = cand(grp + NG * r);
+    load_row_buf<LPR, NQ>(rs, e[r] >= 0 ? off + e[r] : -1, lg, Q, x[r]);
+  }
+  if constexpr (FIN) {
+    // kept after the row loads: the scheduler would otherwise start the
+    // norm, and so wait for the anchor, before issuing them
+    __builtin_amdgcn_sched_barrier(0);
+    finish_anchor<LPR, NQ>(A);
+  }
+#pragma unroll
+  for (int r = 0; r < P; ++r) {
+    const float v = row_affinity<LPR, NQ>(x[r], A);
+    if (lg == 0 && e[r] >= 0) dst[off + e[r]] = v;
+  }
+}
+
+// Lazy scoring of the m (<= NG * R) candidates of one lean level: the round
+// of the fewest passes, among 1, 2, 4, ... R, that covers them (the count
+// is the work-group's, so the choice is uniform).  Each pass of loads costs
+// its data return whether the lanes read rows or zeros, so passes without a
+// candidate are not issued.
+template <int LPR, int NQ, int R, bool FIN, class Cand>
+__device__ __forceinline__ void lean_level_rows(int32_t m, __amdgpu_buffer_rsrc_t rs, int32_t Q, int32_t off,
+                                                AnchorRegs<LPR, NQ>& A, Cand cand, float* dst) {
+  constexpr int NG = kSelThreads / LPR;
+  if (m <= NG) {
+    lean_round<LPR, NQ, 1, FIN>(rs, Q, off, A, cand, dst);
+    return;
+  }
+  if constexpr (R >= 2) {
+    if (m <= 2 * NG) {
+      lean_round<LPR, NQ, 2, FIN>(rs, Q, off, A, cand, dst);
+      return;
+    }
+  }
+  if constexpr (R >= 4) {
+    if (m <= 4 * NG) {
+      lean_round<LPR, NQ, 4, FIN>(rs, Q, off, A, cand, dst);
+      return;
+    }
+  }
+  if constexpr (R >= 8) {
+    if (m <= 8 * NG) {
+      lean_round<LPR, NQ, 8, FIN>(rs, Q, off, A, cand, dst);
+      return;
+    }
+  }
+  if constexpr (R >= 16) lean_round<LPR, NQ, R, FIN>(rs, Q, off, A, cand, dst);
+}
+
+// Lazy scoring of a lean layout (lean_levels_fit; NG * R >= 256): the
+// grids' affinities are in sm.aff already (scored by the caller as soon as
+// the anchor arrived); the chunks of the kept grids and then the pages of
+// the kept chunks are scored in one round each into the LDS row copy,
+// wavefront 0 ranks grids and chunks and four wavefronts the pages (as in
+// select_lean_levels); the scored affinities go to `out` at the end.
+// Returns the kept page count, or -1 when a level needs the zero fill
+// (`out` is then left to the general path).
 template <int LPR, int NQ, int R>
 __device__ __forceinline__ int32_t lazy_lean_levels(const ScoreArgs& a, const SeqGeom& g, const f32x4* seq, float* out,
-                                                    const AnchorRegs<LPR, NQ>& A, SelectShared& sm,
-                                                    const float (&v0)[R]) {
+                                                    AnchorRegs<LPR, NQ>& A, SelectShared& sm) {
   constexpr int NG = kSelThreads / LPR;
-  static_assert(NG * R >= 256, "one pass of the row groups covers a lean level");
+  static_assert(NG * R >= 256, "one round of the row groups covers a lean level");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int32_t grp = tid / LPR, lg = tid % LPR;
   const int32_t Q = a.D >> 2;
   const int32_t kg = min(a.k_g, g.n_g), kc = min(a.k_c, g.n_c), kp = min(a.k_p, g.n_p);
   const int32_t off_g = a.max_pages + a.c_cap;
-  // grids: scored with the anchor's arrival (v0)
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int32_t c = grp + NG * r;
-    if (lg == 0 && c < g.n_g) {
-      sm.aff[off_g + c] = v0[r];
-      if (out) out[off_g + c] = v0[r];
-    }
-  }
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(seq, a.rows_per_seq * a.D * 4);
   __syncthreads();
   if (wave == 0) {
     const int32_t eg = lane < g.n_g ? lane : -1;
@@ -1443,36 +1545,15 @@ __device__ __forceinline__ int32_t lazy_lean_levels(const ScoreArgs& a, const Se
     const int32_t* par = sm.plist + (lev == 1 ? 0 : 64);
     const int32_t off = lev == 1 ? a.max_pages : 0;
     const int32_t m = n_par * fan;
-    f32x4 x[R][NQ];
-    int32_t e[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int32_t c = grp + NG * r;
-      int32_t el = -1;
-      if (c < m) {
-        const int32_t pr = div_fan(c, fan);
-        el = par[pr] * fan + (c - pr * fan);
-        if (el >= n_lev) el = -1;
-      }
-      e[r] = el;
-      // lanes past the candidates load row `off` (unconditional loads issue back to back)
-      load_row<LPR, NQ>(seq + (int64_t)(off + (el >= 0 ? el : 0)) * Q, lg, Q, x[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float v = row_affinity<LPR, NQ>(x[r], A);
-      if (lg == 0 && e[r] >= 0) {
-        sm.aff[off + e[r]] = v;
-        if (out) out[off + e[r]] = v;
-      }
-    }
+    auto child = [&](int32_t c) -> int32_t {
+      if (c >= m) return -1;
+      const int32_t pr = div_fan(c, fan);
+      const int32_t el = par[pr] * fan + (c - pr * fan);
+      return el < n_lev ? el : -1;
+    };
+    lean_level_rows<LPR, NQ, R, false>(m, rs, Q, off, A, child, sm.aff);
     __syncthreads();
-    int32_t ec = -1;
-    if (tid < m && (lev == 2 || wave == 0)) {
-      const int32_t pr = div_fan(tid, fan);
-      ec = par[pr] * fan + (tid - pr * fan);
-      if (ec >= n_lev) ec = -1;
-    }
+    const int32_t ec = (tid < m && (lev == 2 || wave == 0)) ? child(tid) : -1;
     const uint32_t bits = ec >= 0 ? __float_as_uint(sm.aff[off + ec]) : 0u;
     if (lev == 1) {
       if (wave == 0) {
@@ -1483,6 +1564,22 @@ __device__ __forceinline__ int32_t lazy_lean_levels(const ScoreArgs& a, const Se
       if (sm.cnt[0] == 0) return -1;
     } else if (!rank_level256(ec, bits, kp, sm)) {
       return -1;
+    }
+  }
+  if (out) {
+    // the scored affinities, stored once the selection is done: a store
+    // issued between two rounds of row loads would hold up the wait for
+    // the second round (memory operations complete in order)
+    if (tid < g.n_g) out[off_g + tid] = sm.aff[off_g + tid];
+    if (tid < kg * a.cpg) {
+      const int32_t pr = div_fan(tid, a.cpg);
+      const int32_t c = sm.plist[pr] * a.cpg + (tid - pr * a.cpg);
+      if (c < g.n_c) out[a.max_pages + c] = sm.aff[a.max_pages + c];
+    }
+    if (tid < kc * a.ppc) {
+      const int32_t pr = div_fan(tid, a.ppc);
+      const int32_t p = sm.plist[64 + pr] * a.ppc + (tid - pr * a.ppc);
+      if (p < g.n_p) out[p] = sm.aff[p];
     }
   }
   return kp;
@@ -1500,34 +1597,54 @@ __global__ __launch_bounds__(kSelThreads) void lazy_kernel(ScoreArgs a, float* l
   // The first scored level starts at a fixed row whatever the sequence's
   // length, so its first pass of rows is requested together with the page
   // count and the anchor, and scored as soon as they arrive; affinities of
-  // rows past the level's end (known from the page count) are dropped.
-  const int32_t n_p = a.n_pages[s];
+  // rows past the level's end (known from the page count) are dropped.  The
+  // count is read with a relaxed atomic load, which keeps its place before
+  // the row loads (a plain load was issued where the count is first used,
+  // after the round), and moved to a scalar register after the round.
+  const int32_t n_p_v = __hip_atomic_load(a.n_pages + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int32_t off0 = a.hier ? a.max_pages + a.c_cap : 0;
   const int64_t cap0 = a.hier ? a.rows_per_seq - off0 : a.max_pages;
-  constexpr bool EARLY = NQ < 16;
+  // the general path scores the first pass of its first level early
+  constexpr bool EARLY = !LEAN && NQ < 16;
   float v0[R] = {};
-  if constexpr (EARLY) {
-    f32x4 x0[R][NQ];
+  AnchorRegs<LPR, NQ> A;
+  if constexpr (LEAN) {
+    // every grid row (at most 64 of them) in one round with the anchor,
+    // straight into the LDS row copy
+    issue_anchor<LPR, NQ>(a, s, lg, A);
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(seq, a.rows_per_seq * a.D * 4);
+    lean_level_rows<LPR, NQ, R, true>((int32_t)cap0, rs, Q, off0, A,
+                                      [&](int32_t c) -> int32_t { return c < cap0 ? c : -1; }, sm.aff);
+  } else if constexpr (EARLY) {
+    // Only the passes that reach the level's rows load (a count the whole
+    // work-group shares), every lane of such a pass unconditionally: a lane
+    // past the level reloads the level's first row (the anchor when the
+    // level has no rows) and its score is dropped.  A per-lane load with
+    // the other lanes' registers zeroed made each pass's loads wait for the
+    // previous pass's.
+    f32x4 x0[R][NQ] = {};
+    const f32x4* base = cap0 > 0 ? seq + (int64_t)off0 * Q
+                                 : reinterpret_cast<const f32x4*>(a.anchors + (int64_t)s * a.D);
+    const int64_t lim = cap0 > 0 ? cap0 : 1;
+    const int32_t passes = (int32_t)min<int64_t>(R, (lim + NG - 1) / NG);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int32_t c = grp + NG * r;
-      if (c < cap0) {
-        load_row<LPR, NQ>(seq + (int64_t)(off0 + c) * Q, lg, Q, x0[r]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < NQ; ++j) x0[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      if (r < passes) load_row<LPR, NQ>(base + (int64_t)(c < lim ? c : 0) * Q, lg, Q, x0[r]);
     }
-    const AnchorRegs<LPR, NQ> A0 = load_anchor<LPR, NQ>(a, s, lg);
+    A = load_anchor<LPR, NQ>(a, s, lg);
 #pragma unroll
-    for (int r = 0; r < R; ++r) v0[r] = row_affinity<LPR, NQ>(x0[r], A0);
+    for (int r = 0; r < R; ++r) v0[r] = r < passes ? row_affinity<LPR, NQ>(x0[r], A) : 0.f;
+  } else {
+    A = load_anchor<LPR, NQ>(a, s, lg);
   }
-  const AnchorRegs<LPR, NQ> A = load_anchor<LPR, NQ>(a, s, lg);
+  __builtin_amdgcn_sched_barrier(0);
+  const int32_t n_p = __builtin_amdgcn_readfirstlane(n_p_v);
   const SeqGeom g = geom_of(a, n_p, tid == 0);
   float* aff = a.aff + (int64_t)s * a.rows_per_seq;
   float* out = lazy_out ? lazy_out + (int64_t)s * a.rows_per_seq : nullptr;
   int32_t kp = -1;
-  if constexpr (LEAN) kp = lazy_lean_levels<LPR, NQ, R>(a, g, seq, out, A, sm, v0);
+  if constexpr (LEAN) kp = lazy_lean_levels<LPR, NQ, R>(a, g, seq, out, A, sm);
   if (kp < 0) {
     // the general path (also when a lean level needs the zero fill)
     clear_select_state(a, g, sm);
