@@ -1237,22 +1237,45 @@ template <int NT, int LPR, int NQ, int R, bool STAB>
 __device__ __forceinline__ void score_tile(const ScoreArgs& a, int32_t s, int32_t tile, float* g_aff) {
   constexpr int NG = NT / LPR;  // row groups per work-group
   const int tid = threadIdx.x;
-  const SeqGeom g = seq_geom(a, s, false);
-  const int32_t nv = g.n_p + g.n_c + g.n_g;
   const int32_t v0 = tile * a.rows_per_tile;
-  if (v0 >= nv) return;
-  const int32_t v1 = min(nv, v0 + a.rows_per_tile);
   const int32_t Q = a.D >> 2;
   const f32x4* seq = reinterpret_cast<const f32x4*>(a.lvl + (int64_t)s * a.rows_per_seq * a.D);
   float* aff = a.aff ? a.aff + (int64_t)s * a.rows_per_seq : nullptr;
   const int32_t grp = tid / LPR, lg = tid % LPR;
-  const AnchorRegs<LPR, NQ> A = load_anchor<LPR, NQ>(a, s, lg);
+  // Without the filter the first pass's rows are requested together with
+  // the page count and the anchor: row v is physical row v whenever v < n_p
+  // or the sequence fills its capacity (every level full), the case of most
+  // tiles; a tile whose guess the page count proves wrong loads them again.
+  constexpr bool SPEC = !STAB;
+  AnchorRegs<LPR, NQ> A;
+  f32x4 x[R][NQ];
+  int32_t n_p;
+  if constexpr (SPEC) {
+    if (a.rows_per_seq <= 0) return;
+    const int32_t n_p_v = __hip_atomic_load(a.n_pages + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    issue_anchor<LPR, NQ>(a, s, lg, A);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t vr = v0 + grp + NG * r;
+      load_row<LPR, NQ>(seq + (vr < a.rows_per_seq ? vr : a.rows_per_seq - 1) * Q, lg, Q, x[r]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    finish_anchor<LPR, NQ>(A);
+    n_p = __builtin_amdgcn_readfirstlane(n_p_v);
+  } else {
+    n_p = a.n_pages[s];
+  }
+  const SeqGeom g = geom_of(a, n_p, false);
+  const int32_t nv = g.n_p + g.n_c + g.n_g;
+  if (v0 >= nv) return;
+  const int32_t v1 = min(nv, v0 + a.rows_per_tile);
+  if constexpr (!SPEC) A = load_anchor<LPR, NQ>(a, s, lg);
+  bool loaded = SPEC && !(v1 > g.n_p && g.n_p != a.max_pages);  // the first pass's rows are the right ones
 
   uint32_t* hist = STAB ? a.hist + (int64_t)s * a.max_pages : nullptr;
   float* stab = STAB && a.stab_out ? a.stab_out + (int64_t)s * a.max_pages : nullptr;
 
   for (int32_t v = v0 + grp; v < v1; v += NG * R) {
-    f32x4 x[R][NQ];
     int64_t row[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -1263,8 +1286,9 @@ __device__ __forceinline__ void score_tile(const ScoreArgs& a, int32_t s, int32_
                : vr < g.n_p ? vr
                : vr < g.n_p + g.n_c ? (int64_t)a.max_pages + (vr - g.n_p)
                                     : (int64_t)a.max_pages + a.c_cap + (vr - g.n_p - g.n_c);
-      load_row<LPR, NQ>(seq + row[r] * Q, lg, Q, x[r]);
+      if (!loaded) load_row<LPR, NQ>(seq + row[r] * Q, lg, Q, x[r]);
     }
+    loaded = false;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float v_aff = row_affinity<LPR, NQ>(x[r], A);
@@ -1314,44 +1338,92 @@ void score_select_kernel(ScoreArgs a) {
   const int tid = threadIdx.x;
   const int32_t s = blockIdx.x / a.tiles_per_seq;
   const int32_t tile = blockIdx.x - s * a.tiles_per_seq;
-  const SeqGeom g = seq_geom(a, s, tid == 0 && tile == 0);
-  const int32_t nv = g.n_p + g.n_c + g.n_g;
   const int32_t v0 = tile * a.rows_per_tile;
-  const int32_t v1 = min(nv, v0 + a.rows_per_tile);
   const int32_t Q = a.D >> 2;
   const f32x4* seq = reinterpret_cast<const f32x4*>(a.lvl + (int64_t)s * a.rows_per_seq * a.D);
   float* aff = a.aff + (int64_t)s * a.rows_per_seq;
   const int32_t grp = tid / LPR, lg = tid % LPR;
+  SeqGeom g;
+  int32_t v1;
 
-  if (v0 < v1) {
-    const AnchorRegs<LPR, NQ> A = load_anchor<LPR, NQ>(a, s, lg);
-    uint32_t* hist = STAB ? a.hist + (int64_t)s * a.max_pages : nullptr;
-    float* stab = STAB && a.stab_out ? a.stab_out + (int64_t)s * a.max_pages : nullptr;
-    for (int32_t v = v0 + grp; v < v1; v += NG * R) {
-      f32x4 x[R][NQ];
-      int64_t row[R];
-      uint32_t h[R];
+  if constexpr (!STAB && LEAN) {
+    // One pass covers the tile (rows_per_tile = NG * R).  Its rows are
+    // requested together with the page count and the anchor: row v is
+    // physical row v whenever v < n_p or the sequence fills its capacity
+    // (every level full), the case of most tiles.  A tile whose guess the
+    // page count proves wrong (it reaches past a ragged sequence's pages)
+    // loads its rows again.  Loads go through a buffer resource over the
+    // sequence's rows (fewer than 2^31 bytes on this path): a row past the
+    // buffer reads zeros.
+    const int32_t n_p_v = __hip_atomic_load(a.n_pages + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(seq, a.rows_per_seq * a.D * 4);
+    const int32_t n_rows = (int32_t)a.rows_per_seq;
+    AnchorRegs<LPR, NQ> A;
+    issue_anchor<LPR, NQ>(a, s, lg, A);
+    f32x4 x[R][NQ];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        // a row past the tile is replaced by row 0 (loaded, never written back)
-        const int32_t vr = v + NG * r;
-        const bool ok = vr < v1;
-        row[r] = !ok ? 0
-                 : vr < g.n_p ? vr
-                 : vr < g.n_p + g.n_c ? (int64_t)a.max_pages + (vr - g.n_p)
-                                      : (int64_t)a.max_pages + a.c_cap + (vr - g.n_p - g.n_c);
-        load_row<LPR, NQ>(seq + row[r] * Q, lg, Q, x[r]);
-        // page rows also load their window word (others load word 0: max_pages >= 1 here)
-        if constexpr (STAB) h[r] = hist[ok && vr < g.n_p ? vr : 0];
+    for (int r = 0; r < R; ++r) {
+      const int32_t vr = v0 + grp + NG * r;
+      load_row_buf<LPR, NQ>(rs, vr < n_rows ? vr : -1, lg, Q, x[r]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    finish_anchor<LPR, NQ>(A);
+    g = geom_of(a, __builtin_amdgcn_readfirstlane(n_p_v), tid == 0 && tile == 0);
+    const int32_t nv = g.n_p + g.n_c + g.n_g;
+    v1 = min(nv, v0 + a.rows_per_tile);
+    if (v0 < v1) {
+      if (v1 > g.n_p && g.n_p != a.max_pages) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int32_t vr = v0 + grp + NG * r;
+          const int32_t row = vr >= v1 ? -1
+                              : vr < g.n_p ? vr
+                              : vr < g.n_p + g.n_c ? a.max_pages + (vr - g.n_p)
+                                                   : a.max_pages + a.c_cap + (vr - g.n_p - g.n_c);
+          load_row_buf<LPR, NQ>(rs, row, lg, Q, x[r]);
+        }
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const float v_aff = row_affinity<LPR, NQ>(x[r], A);
-        const int32_t vr = v + NG * r;
-        if (lg == 0 && vr < v1) {
-          sm.aff[vr - v0] = v_aff;
-          if constexpr (STAB) {
-            if (vr < g.n_p) stability_step(a, h[r], v_aff, hist + vr, stab ? stab + vr : nullptr);
+        const int32_t vr = v0 + grp + NG * r;
+        if (lg == 0 && vr < v1) sm.aff[vr - v0] = v_aff;
+      }
+    }
+  } else {
+    g = seq_geom(a, s, tid == 0 && tile == 0);
+    const int32_t nv = g.n_p + g.n_c + g.n_g;
+    v1 = min(nv, v0 + a.rows_per_tile);
+    if (v0 < v1) {
+      const AnchorRegs<LPR, NQ> A = load_anchor<LPR, NQ>(a, s, lg);
+      uint32_t* hist = STAB ? a.hist + (int64_t)s * a.max_pages : nullptr;
+      float* stab = STAB && a.stab_out ? a.stab_out + (int64_t)s * a.max_pages : nullptr;
+      for (int32_t v = v0 + grp; v < v1; v += NG * R) {
+        f32x4 x[R][NQ];
+        int64_t row[R];
+        uint32_t h[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          // a row past the tile is replaced by row 0 (loaded, never written back)
+          const int32_t vr = v + NG * r;
+          const bool ok = vr < v1;
+          row[r] = !ok ? 0
+                   : vr < g.n_p ? vr
+                   : vr < g.n_p + g.n_c ? (int64_t)a.max_pages + (vr - g.n_p)
+                                        : (int64_t)a.max_pages + a.c_cap + (vr - g.n_p - g.n_c);
+          load_row<LPR, NQ>(seq + row[r] * Q, lg, Q, x[r]);
+          // page rows also load their window word (others load word 0: max_pages >= 1 here)
+          if constexpr (STAB) h[r] = hist[ok && vr < g.n_p ? vr : 0];
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float v_aff = row_affinity<LPR, NQ>(x[r], A);
+          const int32_t vr = v + NG * r;
+          if (lg == 0 && vr < v1) {
+            sm.aff[vr - v0] = v_aff;
+            if constexpr (STAB) {
+              if (vr < g.n_p) stability_step(a, h[r], v_aff, hist + vr, stab ? stab + vr : nullptr);
+            }
           }
         }
       }
