@@ -1242,35 +1242,27 @@ __device__ __forceinline__ void score_tile(const ScoreArgs& a, int32_t s, int32_
   const f32x4* seq = reinterpret_cast<const f32x4*>(a.lvl + (int64_t)s * a.rows_per_seq * a.D);
   float* aff = a.aff ? a.aff + (int64_t)s * a.rows_per_seq : nullptr;
   const int32_t grp = tid / LPR, lg = tid % LPR;
-  // Without the filter the first pass's rows are requested together with
-  // the page count and the anchor: row v is physical row v whenever v < n_p
-  // or the sequence fills its capacity (every level full), the case of most
-  // tiles; a tile whose guess the page count proves wrong loads them again.
-  constexpr bool SPEC = !STAB;
+  // The first pass's rows are requested together with the page count and
+  // the anchor: row v is physical row v whenever v < n_p or the sequence
+  // fills its capacity (every level full), the case of most tiles; a tile
+  // whose guess the page count proves wrong loads them again.
+  if (a.rows_per_seq <= 0) return;
+  const int32_t n_p_v = __hip_atomic_load(a.n_pages + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   AnchorRegs<LPR, NQ> A;
+  issue_anchor<LPR, NQ>(a, s, lg, A);
   f32x4 x[R][NQ];
-  int32_t n_p;
-  if constexpr (SPEC) {
-    if (a.rows_per_seq <= 0) return;
-    const int32_t n_p_v = __hip_atomic_load(a.n_pages + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    issue_anchor<LPR, NQ>(a, s, lg, A);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t vr = v0 + grp + NG * r;
-      load_row<LPR, NQ>(seq + (vr < a.rows_per_seq ? vr : a.rows_per_seq - 1) * Q, lg, Q, x[r]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    finish_anchor<LPR, NQ>(A);
-    n_p = __builtin_amdgcn_readfirstlane(n_p_v);
-  } else {
-    n_p = a.n_pages[s];
+  for (int r = 0; r < R; ++r) {
+    const int64_t vr = v0 + grp + NG * r;
+    load_row<LPR, NQ>(seq + (vr < a.rows_per_seq ? vr : a.rows_per_seq - 1) * Q, lg, Q, x[r]);
   }
-  const SeqGeom g = geom_of(a, n_p, false);
+  __builtin_amdgcn_sched_barrier(0);
+  finish_anchor<LPR, NQ>(A);
+  const SeqGeom g = geom_of(a, __builtin_amdgcn_readfirstlane(n_p_v), false);
   const int32_t nv = g.n_p + g.n_c + g.n_g;
   if (v0 >= nv) return;
   const int32_t v1 = min(nv, v0 + a.rows_per_tile);
-  if constexpr (!SPEC) A = load_anchor<LPR, NQ>(a, s, lg);
-  bool loaded = SPEC && !(v1 > g.n_p && g.n_p != a.max_pages);  // the first pass's rows are the right ones
+  bool loaded = !(v1 > g.n_p && g.n_p != a.max_pages);  // the first pass's rows are the right ones
 
   uint32_t* hist = STAB ? a.hist + (int64_t)s * a.max_pages : nullptr;
   float* stab = STAB && a.stab_out ? a.stab_out + (int64_t)s * a.max_pages : nullptr;
