@@ -1153,6 +1153,77 @@ def test_variance_weights_of_large_offset_low_variance_heads():
 # sequences, integer-valued vectors for exact affinity ties.  The single
 # pass is checked against the oracle, the lazy pass bit for bit against
 # the single pass.
+@pytest.mark.parametrize("seed", range(48))
+def test_lean_random_configurations(seed):
+    """Seeded sweep over hierarchical layouts within the lean limits (fan-outs
+    1-16, up to 64 grids, k_grid * chunks_per_grid <= 64, k_chunk <= 64 with
+    at most 256 page candidates, k_page <= 64), 1-17 ragged or full
+    sequences, head_dim 8-128, a share of tied scores: the one-launch
+    single pass (tiles whose first rows go out with the page count, lean
+    selection) and the lazy pass (one round of rows per level) against the
+    oracle's affinities and selection, and the lazy pass's scored rows and
+    selections bit-identical to the single pass's."""
+    rng = np.random.default_rng(50000 + seed)
+    ppc = int(rng.choice([1, 2, 3, 4, 5, 8, 16]))
+    cpg = int(rng.choice([1, 2, 3, 4, 7, 8, 16]))
+    max_pages = int(rng.integers(1, min(8192, ppc * cpg * 64) + 1))
+    S = int(rng.choice([1, 2, 3, 6, 17]))
+    D = int(rng.choice([8, 16, 32, 64, 128]))
+    case = dict(hierarchical=1, k_grid=int(rng.integers(0, 64 // cpg + 1)),
+                k_chunk=int(rng.integers(0, min(64, 256 // ppc) + 1)), k_page=int(rng.integers(1, 65)),
+                pages_per_chunk=ppc, chunks_per_grid=cpg)
+    ties = rng.random() < 0.3
+    say(f"lean random seed={seed} S={S} max_pages={max_pages} D={D} {case} ties={ties}")
+    lay = kka.LevelLayout(S, max_pages, D, True, ppc, cpg)
+    lvl = np.zeros((S, lay.rows_per_seq, D), np.float32)
+    if ties:
+        lvl[:, :max_pages] = rng.integers(-1, 2, (S, max_pages, D)).astype(np.float32)
+    else:
+        lvl[:, :max_pages] = rng.standard_normal((S, max_pages, D), dtype=np.float32)
+    anc = rng.standard_normal((S, D), dtype=np.float32)
+    n_pages = rng.integers(0, max_pages + 1, S).astype(np.int32)
+    if rng.random() < 0.3:
+        n_pages[:] = max_pages  # every level full: the tiles' first-row guess holds
+    level = torch.from_numpy(lvl).cuda()
+    npg = torch.from_numpy(n_pages).cuda()
+    kka.kka_build_levels(lay, level, npg)
+    K = case["k_page"]
+    outs = []
+    for lazy in (False, True):
+        idx = torch.full((S, K), -9, dtype=torch.int32, device="cuda")
+        sc = torch.full((S, K), 7.0, dtype=torch.float32, device="cuda")
+        cnt = torch.full((S,), -9, dtype=torch.int32, device="cuda")
+        aff = torch.zeros((S, lay.rows_per_seq), dtype=torch.float32, device="cuda")
+        kka.kka_score_topk(lay, level, npg, torch.from_numpy(anc).cuda(), k_page=K, k_grid=case["k_grid"],
+                           k_chunk=case["k_chunk"], page_idx_out=idx, page_score_out=sc, n_selected_out=cnt,
+                           affinity_out=aff, lazy=lazy)
+        torch.cuda.synchronize()
+        assert kka.kka_device_error() == 0
+        outs.append(tuple(t.cpu().numpy() for t in (aff, idx, sc, cnt)))
+    (af, gi, gs, gc), (af2, gi2, gs2, gc2) = outs
+    lv = level.cpu().numpy()
+    for s in range(S):
+        n_p = int(n_pages[s])
+        n_c = -(-n_p // ppc)
+        n_g = -(-n_c // cpg)
+        rows = np.concatenate([np.arange(n_p), lay.chunk_row0 + np.arange(n_c), lay.grid_row0 + np.arange(n_g)])
+        if len(rows):
+            np.testing.assert_allclose(af[s, rows], oracle.affinity(lv[s, rows], anc[s]), atol=ATOL, rtol=0,
+                                       err_msg=f"s={s}")
+        a_c = af[s, lay.chunk_row0:lay.chunk_row0 + n_c]
+        a_g = af[s, lay.grid_row0:lay.grid_row0 + n_g]
+        ridx, rsc = oracle.select(af[s, :n_p], a_c, a_g, **case)
+        assert gc[s] == len(ridx), f"s={s}"
+        np.testing.assert_array_equal(gi[s, :len(ridx)], ridx, err_msg=f"s={s} n_p={n_p}")
+        np.testing.assert_array_equal(gs[s, :len(ridx)].view(np.uint32), rsc.view(np.uint32), err_msg=f"s={s}")
+        assert (gi[s, len(ridx):] == -1).all() and (gs[s, len(ridx):] == 0).all()
+        scored = af2[s] != 0  # rows the lazy pass scored (others left at 0)
+        np.testing.assert_array_equal(af2[s][scored].view(np.uint32), af[s][scored].view(np.uint32))
+    np.testing.assert_array_equal(gi2, gi)
+    np.testing.assert_array_equal(gs2.view(np.uint32), gs.view(np.uint32))
+    np.testing.assert_array_equal(gc2, gc)
+
+
 LEAN_LIMITS = [
     # (pages_per_chunk, chunks_per_grid, max_pages, k_grid, k_chunk, k_page)
     (4, 4, 1024, 16, 64, 64),    # 64 grids, 64 chunk and 256 page candidates, k = 64: lean
