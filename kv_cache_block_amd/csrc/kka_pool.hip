@@ -57,7 +57,15 @@ struct Item {
 
 // Resolves work item -> (block, sequence, valid tokens, physical block, row).
 // Invalid device metadata zeroes n_b (the block then pools to zeros) and,
-// when `report`, raises the matching flag bit.
+// when `report`, raises the matching flag bit.  Called by every thread of
+// the work-group with the same item.  The metadata goes out in one round of
+// loads: the block's table entry (a relaxed atomic load, which keeps its
+// place ahead of the lookup; a plain load was issued after the lookup's
+// branches, one more memory round trip), and, for fewer than 64 sequences
+// on a whole wavefront, every offset and length, one per lane: the
+// sequence is the number of offsets <= b less one (offsets are
+// nondecreasing) and its values are read from the lanes that hold them.
+// Otherwise a binary search over the offsets.
 __device__ Item locate(const PoolArgs& a, int32_t item, bool report) {
   Item it;
   it.b = a.subset ? a.subset[item] : item;
@@ -70,9 +78,25 @@ __device__ Item locate(const PoolArgs& a, int32_t item, bool report) {
     if (report) raise_err(a.err, KKA_DEVERR_OFFSETS);
     return it;
   }
-  it.s = find_seq(a.offs, a.S, it.b);
-  it.i = it.b - a.offs[it.s];
-  if (it.i < 0 || it.b >= a.offs[it.s + 1]) {
+  const int32_t p_raw = __hip_atomic_load(a.table + it.b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  int32_t o0, o1, len;
+  if (a.S < 64 && __builtin_amdgcn_read_exec() == ~0ull) {
+    const int lane = threadIdx.x & 63;
+    const int32_t ov = lane <= a.S ? a.offs[lane] : 0;
+    const int32_t lv = lane < a.S ? a.seq_len[lane] : 0;
+    const uint64_t le = __ballot(lane < a.S && ov <= it.b);
+    it.s = le ? (int32_t)__popcll(le) - 1 : 0;
+    o0 = __builtin_amdgcn_readlane(ov, it.s);
+    o1 = __builtin_amdgcn_readlane(ov, it.s + 1);
+    len = __builtin_amdgcn_readlane(lv, it.s);
+  } else {
+    it.s = find_seq(a.offs, a.S, it.b);
+    o0 = a.offs[it.s];
+    o1 = a.offs[it.s + 1];
+    len = a.seq_len[it.s];
+  }
+  it.i = it.b - o0;
+  if (it.i < 0 || it.b >= o1) {
     if (report) raise_err(a.err, KKA_DEVERR_OFFSETS);
     return it;
   }
@@ -82,13 +106,13 @@ __device__ Item locate(const PoolArgs& a, int32_t item, bool report) {
   } else {
     it.row = it.b;
   }
-  int64_t nb = (int64_t)a.seq_len[it.s] - (int64_t)it.i * a.B;
+  int64_t nb = (int64_t)len - (int64_t)it.i * a.B;
   if (nb > a.B) nb = a.B;
   if (nb <= 0) {
     if (report) raise_err(a.err, KKA_DEVERR_SEQ_LEN);
     return it;
   }
-  const int64_t p = a.table[it.b];
+  const int64_t p = __builtin_amdgcn_readfirstlane(p_raw);
   if (p < 0 || p >= a.P) {
     if (report) raise_err(a.err, KKA_DEVERR_BLOCK_TABLE);
     return it;
