@@ -14,8 +14,12 @@
 // per pass over its tile (few registers, so eight waves per SIMD stay
 // resident; rows are read once per step, and a serving batch's level rows
 // exceed the last-level cache anyway); the fused kernel issues all 8 of a
-// lane's loads in one pass.  Dot product and row norm are reduced over the
-// row's lanes with a fixed butterfly.
+// lane's loads in one pass.  A tile requests its first rows together with
+// the page count and the anchor, taking level row v for physical row v
+// (true below the page count and whenever the sequence fills its
+// capacity) and loading them again in the rare tile where the count proves
+// otherwise.  Dot product and row norm are reduced over the row's lanes
+// with a fixed butterfly.
 //
 // Selection, written for latency: for batches whose tiles all fit on the
 // chip at once, the work-group that finishes a sequence's last scoring
@@ -41,7 +45,10 @@
 // 256 page candidates, k at most 64: the 128K and serving shapes) take a
 // leaner path in the one-launch, two-launch and lazy selectors: wavefront
 // 0 ranks grids and chunks alone while the others stage the page rows, and
-// four wavefronts rank the pages (see the lean selection below).
+// four wavefronts rank the pages (see the lean selection below).  The
+// latency-bound paths read rows and anchors through buffer resources: a
+// lane without a row issues the same load with an offset past the range
+// and reads zeros, so no load waits behind a branch or a select.
 #include <atomic>
 
 #include "kka_internal.h"
