@@ -1073,6 +1073,44 @@ def test_pool_and_anchor_random_shapes(seed):
         np.testing.assert_allclose(anc[s], a, atol=ATOL, rtol=0, err_msg=f"anchor {s}")
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_pool_odd_heads_and_many_sequences(seed):
+    """Pooling and anchors where a work-group's last wavefront is partial
+    (3, 5, 6 or 7 KV heads, so a token row is not a power-of-two number of
+    16-byte pieces) and batches of 64-100 sequences: the block lookup then
+    takes its binary-search path for some or all wavefronts, and must agree
+    with the one-round path.  v_b, weights and anchors against the oracle."""
+    rng = np.random.default_rng(7000 + seed)
+    L = int(rng.integers(1, 17))
+    H = int(rng.choice([3, 5, 6, 7]))
+    D = int(rng.choice([8, 16, 24, 64, 128]))
+    B = int(rng.choice([1, 4, 16, 64]))
+    S = int(rng.choice([5, 64, 65, 100]))
+    max_len = max(1, min(400, (8 << 20) // (L * H * D * S)))
+    lengths = rng.integers(0, max_len + 1, S)
+    lengths[0] = max(1, lengths[0])
+    mode = "variance" if rng.random() < 0.4 else "uniform"
+    window = int(rng.integers(1, 41))
+    say(f"pool odd heads seed={seed} L={L} H={H} D={D} B={B} S={S} max_len={max_len} {mode} W={window}")
+    w = ragged_workload(9000 + seed, S, L, H, D, B, 0, 0, mode=mode, window=window, lengths=lengths,
+                        offset=0.5 if mode == "variance" else 0.0)
+    sel, _ = run_selector(w)
+    assert kka.kka_device_error() == 0
+    okp = oracle.KPool.of(w)
+    wref = None
+    if mode == "variance":
+        wref = oracle.weights_all(okp, w.seq_len, w.block_offsets, w.block_table)
+        np.testing.assert_allclose(sel.head_weight.cpu().numpy(), wref, rtol=WEIGHT_RTOL, atol=0)
+    got = vb_rows(sel, w)
+    for b, v in oracle_vb(w, range(w.total_blocks), wref).items():
+        np.testing.assert_allclose(got[b], v, atol=ATOL, rtol=0, err_msg=f"block {b}")
+    anc = sel.anchors.cpu().numpy()
+    for s in range(w.S):
+        a = oracle.pool_anchor(okp, oracle.seq_table(w.block_offsets, w.block_table, s), int(w.seq_len[s]),
+                               w.window, None if wref is None else wref[s])
+        np.testing.assert_allclose(anc[s], a, atol=ATOL, rtol=0, err_msg=f"anchor {s}")
+
+
 def test_variance_weights_of_constant_sequences_are_uniform():
     """Head-variance weights where the temporal variance is exactly 0: a
     sequence of one token, and a sequence whose keys repeat the same token
