@@ -65,7 +65,10 @@ struct Item {
 // on a whole wavefront, every offset and length, one per lane: the
 // sequence is the number of offsets <= b less one (offsets are
 // nondecreasing) and its values are read from the lanes that hold them.
-// Otherwise a binary search over the offsets.
+// Otherwise a binary search over the offsets.  The table entry's atomic
+// load is workgroup-scoped, so it may hit in the L2 (the table is written
+// before the launch): an agent-scoped one goes past the L2 and, under a
+// saturating read stream, queued for tens of microseconds.
 __device__ Item locate(const PoolArgs& a, int32_t item, bool report) {
   Item it;
   it.b = a.subset ? a.subset[item] : item;
@@ -78,7 +81,7 @@ __device__ Item locate(const PoolArgs& a, int32_t item, bool report) {
     if (report) raise_err(a.err, KKA_DEVERR_OFFSETS);
     return it;
   }
-  const int32_t p_raw = __hip_atomic_load(a.table + it.b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int32_t p_raw = __hip_atomic_load(a.table + it.b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   int32_t o0, o1, len;
   if (a.S < 64 && __builtin_amdgcn_read_exec() == ~0ull) {
     const int lane = threadIdx.x & 63;

@@ -1254,7 +1254,7 @@ __device__ __forceinline__ void score_tile(const ScoreArgs& a, int32_t s, int32_
   // fills its capacity (every level full), the case of most tiles; a tile
   // whose guess the page count proves wrong loads them again.
   if (a.rows_per_seq <= 0) return;
-  const int32_t n_p_v = __hip_atomic_load(a.n_pages + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int32_t n_p_v = __hip_atomic_load(a.n_pages + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   AnchorRegs<LPR, NQ> A;
   issue_anchor<LPR, NQ>(a, s, lg, A);
   f32x4 x[R][NQ];
@@ -1354,7 +1354,7 @@ void score_select_kernel(ScoreArgs a) {
     // loads its rows again.  Loads go through a buffer resource over the
     // sequence's rows (fewer than 2^31 bytes on this path): a row past the
     // buffer reads zeros.
-    const int32_t n_p_v = __hip_atomic_load(a.n_pages + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int32_t n_p_v = __hip_atomic_load(a.n_pages + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     const __amdgpu_buffer_rsrc_t rs = buf_rsrc(seq, a.rows_per_seq * a.D * 4);
     const int32_t n_rows = (int32_t)a.rows_per_seq;
     AnchorRegs<LPR, NQ> A;
@@ -1671,8 +1671,10 @@ __global__ __launch_bounds__(kSelThreads) void lazy_kernel(ScoreArgs a, float* l
   // rows past the level's end (known from the page count) are dropped.  The
   // count is read with a relaxed atomic load, which keeps its place before
   // the row loads (a plain load was issued where the count is first used,
-  // after the round), and moved to a scalar register after the round.
-  const int32_t n_p_v = __hip_atomic_load(a.n_pages + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // after the round), and moved to a scalar register after the round; its
+  // scope is the work-group's, so it may hit in the L2 (the counts are
+  // written before the launch).
+  const int32_t n_p_v = __hip_atomic_load(a.n_pages + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   const int32_t off0 = a.hier ? a.max_pages + a.c_cap : 0;
   const int64_t cap0 = a.hier ? a.rows_per_seq - off0 : a.max_pages;
   // the general path scores the first pass of its first level early
