@@ -1196,7 +1196,8 @@ def test_lean_random_configurations(seed):
     """Seeded sweep over hierarchical layouts within the lean limits (fan-outs
     1-16, up to 64 grids, k_grid * chunks_per_grid <= 64, k_chunk <= 64 with
     at most 256 page candidates, k_page <= 64), 1-17 ragged or full
-    sequences, head_dim 8-128, a share of tied scores: the one-launch
+    sequences, head_dim 8-128 (some not a multiple of 32, so lanes whose
+    row pieces lie past head_dim), a share of tied scores: the one-launch
     single pass (tiles whose first rows go out with the page count, lean
     selection) and the lazy pass (one round of rows per level) against the
     oracle's affinities and selection, and the lazy pass's scored rows and
@@ -1206,7 +1207,7 @@ def test_lean_random_configurations(seed):
     cpg = int(rng.choice([1, 2, 3, 4, 7, 8, 16]))
     max_pages = int(rng.integers(1, min(8192, ppc * cpg * 64) + 1))
     S = int(rng.choice([1, 2, 3, 6, 17]))
-    D = int(rng.choice([8, 16, 32, 64, 128]))
+    D = int(rng.choice([8, 16, 24, 32, 40, 64, 96, 128]))  # 24, 40, 96: lanes whose pieces lie past the row
     case = dict(hierarchical=1, k_grid=int(rng.integers(0, 64 // cpg + 1)),
                 k_chunk=int(rng.integers(0, min(64, 256 // ppc) + 1)), k_page=int(rng.integers(1, 65)),
                 pages_per_chunk=ppc, chunks_per_grid=cpg)
