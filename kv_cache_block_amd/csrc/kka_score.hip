@@ -1118,6 +1118,11 @@ __device__ __forceinline__ float affinity_of(float dot, float nr, float sqrt_na,
 constexpr int32_t kOutOfRange = 0x7ffffff0;  // a byte offset past any range here
 constexpr int kBufAux = KKA_SCORE_NT ? 2 : 0;  // cache policy bits of row loads: 2 = non-temporal
 
+// The row buffers built here span a lean layout's rows (at most
+// kSelectLdsRows of at most head_dim 1024 floats): within the 2^31 bytes a
+// resource's range and its 32-bit offsets cover.
+static_assert((int64_t)kSelectLdsRows * 1024 * 4 < ((int64_t)1 << 31), "lean row buffers exceed a buffer resource");
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int64_t bytes) {
   // gfx9 raw buffer: stride 0, `bytes` records of one byte, default format word
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int32_t)bytes, 0x00020000);
