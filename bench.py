@@ -709,9 +709,7 @@ def reported_configs(args, dev, stream):
     ws_re = kka.new_workspace(kka.kka_pool_blocks_workspace(kp, sel.seqs, kka.WEIGHT_GIVEN, newest), dev)
 
     def decode():
-        sel.repool(newest, workspace=ws_re)
-        sel.anchor()
-        sel.score(npg_after)
+        sel.decode_step(newest, npg_after, workspace=ws_re)
 
     for _ in range(args.warmup):
         decode()

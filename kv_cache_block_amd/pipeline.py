@@ -132,6 +132,20 @@ class Selector:
         self.levels(n_pages, stream=stream)
         self.score(n_pages, stream=stream)
 
+    def decode_step(self, blocks: torch.Tensor, n_pages: torch.Tensor, first_dirty_page: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None, lazy: bool = False):
+        """One decode step once the new tokens are in the pool (section 5.2:
+        the block vectors of the written blocks, then anchor -> levels ->
+        affinity + top-K): re-pool `blocks` with the frozen weights, pool the
+        anchor, rebuild the levels above each sequence's first dirty page
+        (hierarchical layouts; all of them without first_dirty_page), then
+        score and select, all on `stream`."""
+        self.repool(blocks, workspace=workspace, stream=stream)
+        self.anchor(stream)
+        if self.lay.hierarchical:
+            self.levels(n_pages, first_dirty_page, stream=stream)
+        self.score(n_pages, stream=stream, lazy=lazy)
+
     # views of the level buffer
     def pages(self, s: int, n: int) -> torch.Tensor:
         return self.level[s, :n]

@@ -222,6 +222,54 @@ def test_repool_on_a_side_stream_matches_the_current_stream():
         np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+@pytest.mark.parametrize("hier", [False, True])
+def test_decode_step_equals_its_calls(hier):
+    """Selector.decode_step (re-pool of the newest blocks, anchor, levels
+    above each sequence's newest page for hierarchical layouts, score)
+    gives the same bits as the calls made one by one with a full level
+    rebuild (block vectors, levels, anchors, affinities, selections), and
+    its selections follow the oracle's rules on its own affinities; flat
+    and hierarchical layouts."""
+    say(f"decode step hier={hier}")
+    w = synth.config5(8, n_seqs=6, len_lo=100, len_hi=900, L=3, H=4, D=128, B=16)
+    after = w.extra["after"]
+    dev = "cuda"
+    select = (dict(hierarchical=1, k_grid=2, k_chunk=3, k_page=5, pages_per_chunk=4, chunks_per_grid=3) if hier
+              else dict(w.select))
+    newest_np = (after["block_offsets"][1:] - 1).astype(np.int32)
+    newest = torch.from_numpy(newest_np).to(dev)
+    first_dirty = torch.from_numpy((newest_np - after["block_offsets"][:-1]).astype(np.int32)).to(dev)
+    npg_before = torch.from_numpy(np.diff(w.block_offsets).astype(np.int32)).to(dev)
+    npg_after = torch.from_numpy(np.diff(after["block_offsets"]).astype(np.int32)).to(dev)
+    results = []
+    for one_call in (False, True):
+        kp, seqs_before = upload(w)
+        seqs_after = kka.Seqs(torch.from_numpy(after["seq_len"]).to(dev),
+                              torch.from_numpy(after["block_offsets"]).to(dev),
+                              torch.from_numpy(after["block_table"]).to(dev), int(after["block_offsets"][-1]))
+        sel = Selector(kp, seqs_before, select, max_pages=int(np.max(np.diff(after["block_offsets"]))),
+                       window=w.window, mode=kka.WEIGHT_VARIANCE)
+        sel.pool()
+        sel.levels(npg_before)
+        sel.seqs = seqs_after
+        if one_call:
+            sel.decode_step(newest, npg_after, first_dirty_page=first_dirty if hier else None)
+        else:
+            sel.repool(newest)
+            sel.anchor()
+            sel.levels(npg_after)
+            sel.score(npg_after)
+        torch.cuda.synchronize()
+        assert kka.kka_device_error() == 0
+        results.append(tuple(t.cpu().numpy() for t in (sel.level, sel.anchors, sel.affinity, sel.page_idx,
+                                                       sel.page_score, sel.n_selected)))
+        if one_call:
+            for s in range(w.S):
+                check_selection(sel, s, int(npg_after[s]), "decode step")
+    for a, b in zip(*results):
+        np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
 # ------------------------------------------------------------------ anchor
 
 @pytest.mark.parametrize("W", [0, 1, 5, 16, 17, 40, 1000])
