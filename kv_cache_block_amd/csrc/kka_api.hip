@@ -445,7 +445,7 @@ static size_t anchor_counter_bytes(int32_t S) { return align256((size_t)S * size
 size_t kka_pool_anchor_workspace(const kka_kpool* kp, const kka_seqs* seqs, int32_t window) {
   (void)window;
   if (check_kpool(kp) != KKA_OK || check_seqs(seqs) != KKA_OK) return 0;
-  const LayerSplit ls = layer_split(seqs->num_seqs, kp->num_layers);
+  const LayerSplit ls = anchor_split(seqs->num_seqs, kp->num_layers);
   if (ls.n_split <= 1) return 0;
   return anchor_counter_bytes(seqs->num_seqs) +
          align256((size_t)seqs->num_seqs * ls.n_split * kp->head_dim * sizeof(float));
@@ -468,7 +468,7 @@ kka_status kka_pool_anchor(const kka_kpool* kp, const kka_seqs* seqs, int32_t wi
   (void)hipGetLastError();
   PoolArgs a = {};
   fill_pool_args(a, kp, seqs);
-  const LayerSplit ls = layer_split(seqs->num_seqs, a.L);
+  const LayerSplit ls = anchor_split(seqs->num_seqs, a.L);
   a.n_split = ls.n_split;
   a.lps = ls.lps;
   a.n_items = seqs->num_seqs;
@@ -519,7 +519,7 @@ extern "C" {
 
 size_t kka_pool_anchor_noalloc_scratch(const kka_kpool* kp, const kka_seqs* seqs) {
   if (check_kpool(kp) != KKA_OK || check_seqs(seqs) != KKA_OK) return 0;
-  const LayerSplit ls = layer_split(seqs->num_seqs, kp->num_layers);
+  const LayerSplit ls = anchor_split(seqs->num_seqs, kp->num_layers);
   if (ls.n_split <= 1) return 0;
   return (size_t)seqs->num_seqs * ls.n_split * kp->head_dim * sizeof(float);
 }
@@ -542,7 +542,7 @@ kka_status kka_pool_anchor_noalloc(const kka_kpool* kp, const kka_seqs* seqs, in
   (void)hipGetLastError();
   PoolArgs a = {};
   fill_pool_args(a, kp, seqs);
-  const LayerSplit ls = layer_split(seqs->num_seqs, a.L);
+  const LayerSplit ls = anchor_split(seqs->num_seqs, a.L);
   a.n_split = ls.n_split;
   a.lps = ls.lps;
   a.n_items = seqs->num_seqs;

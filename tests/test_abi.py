@@ -147,6 +147,13 @@ def test_workspace_sizes(L):
     assert v >= 8192 * 112 * 129 * 4 + 112 * 8
     a = L.kka_pool_anchor_workspace(ctypes.byref(kp), ctypes.byref(big), 16)
     assert a == 256 + 28 * 128 * 4  # one sequence split over every layer: its counter, then 28 partials
+    # 32 sequences: one share per layer would take 896 work-groups, so shares
+    # of 4 layers (7 per sequence, 224 work-groups) are taken instead
+    s32 = seqs(num_seqs=32, total_blocks=32 * 256)
+    assert L.kka_pool_anchor_workspace(ctypes.byref(kp), ctypes.byref(s32), 16) == 256 + 32 * 7 * 128 * 4
+    # 64 sequences would need shares of 7 layers: one share per layer stays
+    s64 = seqs(num_seqs=64, total_blocks=64 * 128)
+    assert L.kka_pool_anchor_workspace(ctypes.byref(kp), ctypes.byref(s64), 16) == 256 + 64 * 28 * 128 * 4
 
 
 def test_level_rows_and_score_validation(L):
