@@ -41,6 +41,13 @@
  *    through device-scope stores, an arrival counter and device-scope
  *    loads.  KKA_NO_HANDOFF=1 in the environment makes every call use a
  *    second launch instead; the results are the same bits.
+ *  - A pooling launch of at least 2048 blocks, one work-group each, gives
+ *    every XCD (work-group i runs on XCD i mod 8) a contiguous share of the
+ *    blocks sized by a weight per XCD: by default 1.1 for even and 1.0 for
+ *    odd XCDs on a 256-compute-unit device, whose odd XCDs stream slower;
+ *    KKA_XCD_WEIGHTS="w0,...,w7" (eight positive numbers) sets others and
+ *    KKA_XCD_WEIGHTS=off gives one block per work-group in order.  Every
+ *    block is pooled once by the same arithmetic: the same bits either way.
  */
 #ifndef KKA_H_
 #define KKA_H_

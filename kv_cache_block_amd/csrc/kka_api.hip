@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdlib>
+#include <cstring>
 
 #include "kka_internal.h"
 
@@ -13,6 +14,31 @@ namespace kka {
 bool handoff_disabled() {
   const char* v = std::getenv("KKA_NO_HANDOFF");
   return v && v[0] == '1';
+}
+
+bool xcd_weights(double (&w)[kXcds]) {
+  const char* v = std::getenv("KKA_XCD_WEIGHTS");
+  if (v && v[0] != '\0') {
+    if (std::strcmp(v, "off") == 0) return false;
+    const char* p = v;
+    int x = 0;
+    for (; x < kXcds; ++x) {
+      char* end = nullptr;
+      const double d = std::strtod(p, &end);
+      if (end == p || !(d > 0.0) || !(d < 1e6)) break;
+      w[x] = d;
+      p = end;
+      if (x + 1 < kXcds) {
+        if (*p != ',') break;
+        ++p;
+      }
+    }
+    if (x == kXcds && *p == '\0') return true;
+    // anything else is not a list of eight weights: the default below
+  }
+  if (device_cus() != 256) return false;
+  for (int x = 0; x < kXcds; ++x) w[x] = x % 2 == 0 ? 1.1 : 1.0;
+  return true;
 }
 
 // Per-device flag word for errors that only device-resident data reveals.

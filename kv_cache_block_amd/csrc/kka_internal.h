@@ -143,6 +143,46 @@ inline LayerSplit anchor_split(int64_t S, int32_t L) {
   return ls;
 }
 
+// Per-XCD shares of a pooling launch with one work-group per item.  The
+// dispatcher hands work-group i to XCD i mod 8, and under the K-pool's read
+// stream the XCDs do not stream equally fast (MI355X: every work-group on an
+// odd-numbered XCD took about 8 % longer than on an even-numbered one, in
+// every call on every device measured), so with equal counts the launch ends
+// when the slowest XCDs do.  With shares, XCD x pools the contiguous items
+// off[x] .. off[x] + n[x] - 1, n proportional to a weight per XCD, and
+// work-group 8 r + x takes item off[x] + r (none when r >= n[x]): every item
+// is pooled once, by the same arithmetic, whatever XCD it lands on.
+constexpr int kXcds = 8;
+constexpr int64_t kXcdShareMinItems = 2048;  // several dispatch rounds; smaller launches keep one item per group
+
+struct XcdShares {
+  int32_t on;
+  int32_t n[kXcds], off[kXcds];
+};
+
+// Weights of the XCD shares for this process: KKA_XCD_WEIGHTS in the
+// environment ("w0,...,w7", eight positive numbers; "off" for one item per
+// work-group), else 1.1 for even-numbered and 1.0 for odd-numbered XCDs on a
+// 256-compute-unit device (MI355X) and none elsewhere.  False: no shares.
+bool xcd_weights(double (&w)[kXcds]);
+
+// Shares of n_items items by weight w: floor of each XCD's part, the rest one
+// item at a time from XCD 0 up.  Depends only on its arguments.
+inline XcdShares xcd_shares(int64_t n_items, const double (&w)[kXcds]) {
+  XcdShares xs = {};
+  double tot = 0.0;
+  for (int x = 0; x < kXcds; ++x) tot += w[x];
+  int64_t given = 0;
+  for (int x = 0; x < kXcds; ++x) {
+    xs.n[x] = (int32_t)((double)n_items * w[x] / tot);
+    given += xs.n[x];
+  }
+  for (int x = 0; given < n_items; x = (x + 1) % kXcds, ++given) ++xs.n[x];
+  for (int x = 0, o = 0; x < kXcds; o += xs.n[x], ++x) xs.off[x] = o;
+  xs.on = 1;
+  return xs;
+}
+
 struct PoolArgs {
   const uint16_t* k;
   int64_t sL, sB, sT, sH;
@@ -164,6 +204,7 @@ struct PoolArgs {
   uint32_t* err;
   PoolShape ps;
   int32_t window;         // anchor only
+  XcdShares xs;           // item of work-group i (uniform and given-weight pooling, one share per item)
 };
 
 struct WeightArgs {

@@ -168,8 +168,13 @@ __global__ __launch_bounds__(MAXT) void pool_kernel(PoolArgs a) {
   __shared__ float red[MAXT * 8];
   extern __shared__ float wsh[];  // [L*H] head weights (given-weight mode)
   const int tid = threadIdx.x;
-  const int32_t item = blockIdx.x / a.n_split;
+  int32_t item = blockIdx.x / a.n_split;
   const int32_t j = blockIdx.x - item * a.n_split;
+  if (a.xs.on) {  // one share per item: XCD blockIdx mod 8 takes its range
+    const int32_t x = (int32_t)(blockIdx.x % kXcds), r = (int32_t)(blockIdx.x / kXcds);
+    if (r >= a.xs.n[x]) return;
+    item = a.xs.off[x] + r;
+  }
   const Item it = locate(a, item, tid == 0 && j == 0);
   const int32_t LH = a.L * a.H;
   if (MODE == kGiven) {
@@ -720,8 +725,17 @@ inline int small_block(int32_t D) { return D >= 256 ? 256 : ((D + 63) / 64) * 64
 
 }  // namespace
 
-hipError_t launch_pool(const PoolArgs& a, int mode, hipStream_t st) {
-  const dim3 grid((unsigned)((int64_t)a.n_items * a.n_split));
+hipError_t launch_pool(const PoolArgs& a0, int mode, hipStream_t st) {
+  PoolArgs a = a0;
+  int64_t groups = (int64_t)a.n_items * a.n_split;
+  double w[kXcds];
+  if (a.n_split == 1 && a.n_items >= kXcdShareMinItems && xcd_weights(w)) {
+    a.xs = xcd_shares(a.n_items, w);
+    int32_t most = 0;
+    for (int x = 0; x < kXcds; ++x) most = a.xs.n[x] > most ? a.xs.n[x] : most;
+    groups = (int64_t)kXcds * most;
+  }
+  const dim3 grid((unsigned)groups);
   const dim3 block((unsigned)a.ps.nt);
   const size_t dyn = mode == kGiven ? sizeof(float) * (size_t)a.L * a.H : 0;
   if (a.n_items > 0) {

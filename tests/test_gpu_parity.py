@@ -82,6 +82,47 @@ def test_pool_uniform_matches_oracle(shape):
         np.testing.assert_allclose(got[b], v, atol=ATOL, rtol=0, err_msg=f"block {b}")
 
 
+@pytest.mark.parametrize("mode", ["uniform", "given"])
+def test_xcd_shares_pool_every_block_once(mode, monkeypatch):
+    """A launch of at least 2048 blocks gives XCD x (work-group i mod 8) a
+    contiguous range of blocks sized by a weight per XCD (KKA_XCD_WEIGHTS;
+    on MI355X 1.1 for even and 1.0 for odd XCDs by default), and groups past
+    their XCD's range pool nothing.  Default, equal, uneven and extreme
+    weights, the shares off, and malformed values (the default then) all give
+    every block vector the same bits, no row is left unwritten, and a sample
+    of blocks matches the oracle."""
+    say(f"xcd shares {mode}")
+    w = ragged_workload(11, 7, 2, 2, 64, 16, 5000, 8000)
+    assert w.total_blocks >= 2048
+    kp, seqs = upload(w)
+    S, LH = w.S, w.L * w.H
+    hw = None
+    if mode == "given":
+        raw = synth.uniform(11, 104, S * LH).reshape(S, LH).astype(np.float64) + 0.1
+        hw = (raw / raw.sum(axis=1, keepdims=True)).astype(np.float32)
+    hw_t = torch.from_numpy(hw).cuda() if hw is not None else None
+    kmode = kka.WEIGHT_GIVEN if mode == "given" else kka.WEIGHT_UNIFORM
+    outs = {}
+    for setting in ("off", None, "1,1,1,1,1,1,1,1", "1,2,3,4,5,6,7,8", "8,0.5,1,1,1,1,1,20", "1,2", "x", "0,1,1,1,1,1,1,1"):
+        if setting is None:
+            monkeypatch.delenv("KKA_XCD_WEIGHTS", raising=False)
+        else:
+            monkeypatch.setenv("KKA_XCD_WEIGHTS", setting)
+        out = torch.full((w.total_blocks, w.D), 7.0, dtype=torch.float32, device="cuda")
+        kka.kka_pool_blocks(kp, seqs, out, mode=kmode, head_weight=hw_t)
+        torch.cuda.synchronize()
+        assert kka.kka_device_error() == 0
+        outs[setting] = out.cpu().numpy()
+    ref = outs["off"]
+    assert not (ref == 7.0).all(axis=1).any()
+    for setting, o in outs.items():
+        np.testing.assert_array_equal(o.view(np.uint32), ref.view(np.uint32), err_msg=f"KKA_XCD_WEIGHTS={setting}")
+    sample = sorted(set(synth.uniform_int(11, 105, 48, 0, w.total_blocks - 1).tolist()) | {0, w.total_blocks - 1})
+    want = oracle_vb(w, sample, hw)
+    for b in sample:
+        np.testing.assert_allclose(outs[None][b], want[b], atol=ATOL, rtol=0, err_msg=f"block {b}")
+
+
 @pytest.mark.parametrize("shape", POOL_SHAPES)
 def test_pool_variance_weights_match_oracle(shape):
     S, L, H, D, B, lo, hi = shape
