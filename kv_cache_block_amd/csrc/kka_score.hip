@@ -1661,12 +1661,20 @@ __device__ __forceinline__ int32_t lazy_lean_levels(const ScoreArgs& a, const Se
   return kp;
 }
 
+// Work-group of the lazy pass's first sequence.  Group i runs on XCD i mod 8,
+// and a lone latency-bound group measured slower on XCD 0 than on any other
+// (one 128K sequence: 11.2-11.35 against 10.85-11.1 us on one device, 12.0
+// against 11.35 on XCD 1 on another), so a batch of fewer than 8 sequences
+// starts at group 1 and group 0 does nothing; larger batches spread from 0.
+__host__ __device__ constexpr int32_t lazy_first_group(int32_t S) { return S < 8 ? 1 : 0; }
+
 template <int LPR, int NQ, int R, bool LEAN>
 __global__ __launch_bounds__(kSelThreads) void lazy_kernel(ScoreArgs a, float* lazy_out) {
   __shared__ SelectShared sm;
   constexpr int NG = kSelThreads / LPR;
   const int tid = threadIdx.x;
-  const int32_t s = blockIdx.x;
+  const int32_t s = (int32_t)blockIdx.x - lazy_first_group(a.S);
+  if (s < 0) return;
   const int32_t grp = tid / LPR, lg = tid % LPR;
   const int32_t Q = a.D >> 2;
   const f32x4* seq = reinterpret_cast<const f32x4*>(a.lvl + (int64_t)s * a.rows_per_seq * a.D);
@@ -2090,12 +2098,11 @@ hipError_t launch_nq(const ScoreArgs& a0, bool lazy, float* lazy_out, hipStream_
   if (lazy) {
     constexpr int RL = NQ >= 16 ? 1 : 16 / NQ;  // 16 row loads in flight per lane
     constexpr bool kLeanOk = NQ < 16 && (kSelThreads / LPR) * RL >= 256;  // early grid rows, one pass a level
+    const dim3 grid((unsigned)(a0.S + lazy_first_group(a0.S)));
     if (kLeanOk && lean_levels_fit(a0))
-      hipLaunchKernelGGL((lazy_kernel<LPR, NQ, RL, kLeanOk>), dim3((unsigned)a0.S), dim3(kSelThreads), 0, st, a0,
-                         lazy_out);
+      hipLaunchKernelGGL((lazy_kernel<LPR, NQ, RL, kLeanOk>), grid, dim3(kSelThreads), 0, st, a0, lazy_out);
     else
-      hipLaunchKernelGGL((lazy_kernel<LPR, NQ, RL, false>), dim3((unsigned)a0.S), dim3(kSelThreads), 0, st, a0,
-                         lazy_out);
+      hipLaunchKernelGGL((lazy_kernel<LPR, NQ, RL, false>), grid, dim3(kSelThreads), 0, st, a0, lazy_out);
     return hipGetLastError();
   }
   ScoreArgs a = a0;
